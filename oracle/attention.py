@@ -1,0 +1,141 @@
+"""Exact decode attention over a paged KVarN cache, and the three cache-level operations.
+
+[GR] "The four-stage pipeline", stage 4: scales are applied when a tile is loaded for the
+attention computation, not when it is written, so the per-step write path stays cheap.
+[GR] "What KVarN changes in vLLM's serving path": the cache lives in fixed-size paged blocks,
+one 128-token tile per block. [GR] stage 1: the rotation is orthonormal and does not change
+attention scores, which is what lets the folded form below equal the plain one.
+
+Cache model (the library's, reading R16/R17): a sequence of L tokens holds floor(L/128)
+packed tiles at block_table[b][0 .. floor(L/128) - 1] followed by L mod 128 raw fp16 tokens
+in its staging tile staging[b][kv_head][0 .. L mod 128 - 1]. Query head h reads KV head
+h // (Hq / Hkv) (reading R19). Softmax scale sm_scale (reading R18). Outputs are float64 here
+(the library writes fp32, reading R20).
+
+Test infrastructure only (see the package header).
+"""
+
+import numpy as np
+
+from . import codec
+from .hadamard import H128
+
+T = codec.T
+D = codec.D
+
+
+# ------------------------------------------------------------------ cache-level operations
+
+
+def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS):
+    """Quantise whole prefill tiles into the block pool, in place.
+
+    k, v: [n_tiles * 128, Hkv, 128] fp16 values; tile i holds tokens 128 i .. 128 i + 127 and
+    goes to block dst_blocks[i]; pool: uint8 [num_blocks, Hkv, 13312]."""
+    k = np.asarray(k)
+    v = np.asarray(v)
+    n_tiles = len(dst_blocks)
+    hkv = k.shape[1]
+    for i in range(n_tiles):
+        rows = slice(T * i, T * i + T)
+        for h in range(hkv):
+            pool[dst_blocks[i], h] = codec.encode_record(k[rows, h, :], v[rows, h, :], iters)
+
+
+def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, pool,
+                 iters: int = codec.DEFAULT_ITERS):
+    """Write one new token per sequence into its staging tile; when the token is the 128th of
+    its tile, quantise the staging tile into block_table[b][position // 128]. In place.
+
+    k_new, v_new: [B, Hkv, 128]; positions: [B] 0-based index of the new token, negative =
+    skip this row; staging_k, staging_v: [B, Hkv, 128, 128]."""
+    for b, pos in enumerate(np.asarray(positions)):
+        if pos < 0:
+            continue
+        slot = int(pos) % T
+        staging_k[b, :, slot, :] = k_new[b]
+        staging_v[b, :, slot, :] = v_new[b]
+        if slot == T - 1:
+            blk = block_table[b, int(pos) // T]
+            for h in range(staging_k.shape[1]):
+                pool[blk, h] = codec.encode_record(staging_k[b, h], staging_v[b, h], iters)
+
+
+def _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length):
+    """Dequantised keys and values (original space) of sequence b, KV head g, length tokens."""
+    n_full = length // T
+    ks, vs = [], []
+    for i in range(n_full):
+        kh, vh = codec.decode_record(pool[block_table[b, i], g])
+        ks.append(kh)
+        vs.append(vh)
+    tail = length % T
+    ks.append(np.asarray(staging_k[b, g, :tail], dtype=np.float64))
+    vs.append(np.asarray(staging_v[b, g, :tail], dtype=np.float64))
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def softmax_attend(q, keys, values, sm_scale):
+    """Exact softmax attention of one query vector over keys/values rows (float64)."""
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[1])
+    s = sm_scale * (keys @ np.asarray(q, dtype=np.float64))
+    p = np.exp(s - s.max())
+    return (p @ values) / p.sum()
+
+
+def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+    """Plain form: dequantise every packed tile, then exact softmax attention.
+
+    q: [B, Hq, 128]; returns [B, Hq, 128] float64. A sequence of length 0 gives zeros."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, _ = q.shape
+    hkv = staging_k.shape[1]
+    group = hq // hkv
+    out = np.zeros((bsz, hq, D))
+    for b in range(bsz):
+        for g in range(hkv):
+            keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g,
+                                        int(seq_lens[b]))
+            for h in range(g * group, (g + 1) * group):
+                out[b, h] = softmax_attend(q[b, h], keys, values, sm_scale)
+    return out
+
+
+def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+    """Folded form: the per-channel key scales and the rotation go into the query, the
+    per-token key scale and zero-point into the score, the per-token value scale and
+    zero-point into the probabilities, the per-channel value scale into the per-tile partial
+    output, and the rotation back onto the summed output. Must equal decode_attention()."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, _ = q.shape
+    hkv = staging_k.shape[1]
+    group = hq // hkv
+    out = np.zeros((bsz, hq, D))
+    for b in range(bsz):
+        length = int(seq_lens[b])
+        n_full, tail = length // T, length % T
+        for g in range(hkv):
+            recs = [codec.unpack_record(pool[block_table[b, i], g]) for i in range(n_full)]
+            sk = np.asarray(staging_k[b, g, :tail], dtype=np.float64)
+            sv = np.asarray(staging_v[b, g, :tail], dtype=np.float64)
+            for h in range(g * group, (g + 1) * group):
+                if length == 0:
+                    continue
+                q_rot = q[b, h] @ H128
+                scores = []
+                for r in recs:
+                    qt = q_rot * r["k"]["c_hat"]
+                    scores.append(sm_scale * (r["k"]["s_hat"] * (r["k"]["codes"] @ qt)
+                                              + r["k"]["z_hat"] * qt.sum()))
+                scores.append(sm_scale * (sk @ q[b, h]))
+                s = np.concatenate(scores)
+                p = np.exp(s - s.max())
+                o_rot = np.zeros(D)
+                for i, r in enumerate(recs):
+                    pt = p[T * i:T * i + T]
+                    o_rot += r["v"]["c_hat"] * ((pt * r["v"]["s_hat"]) @ r["v"]["codes"]
+                                                + np.dot(pt, r["v"]["z_hat"]))
+                o = o_rot @ H128 + p[T * n_full:] @ sv
+                out[b, h] = o / p.sum()
+    return out

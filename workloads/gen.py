@@ -1,0 +1,182 @@
+"""Seeded synthetic KV-cache workloads shaped like the attention layers the KVarN pages discuss.
+
+The pages evaluate on Qwen3-4B, Qwen3-32B (16K context) and Phi-4-14B with reasoning and
+retrieval datasets; neither weights nor data are used here. These generators stand in for the
+head layouts and context lengths only, with keys and values that have the per-channel outlier
+structure the pages describe (tools.thesoundmethod.me, "KVarN: 2-Bit KV-Cache That Beats FP16
+Throughput, and Where the Catch Lives", section "Why 2-bit usually breaks": a few channels far
+larger than the rest).
+
+Every stream of random numbers is keyed by (seed, purpose[, index]) so that one sequence, one
+step or the queries can be regenerated alone, in any order:
+
+  (seed, 0)           per-(KV head, K|V) channel multipliers, then outlier channel picks
+  (seed, 1)           per-sequence context lengths (ragged workload)
+  (seed, 2)           block permutation
+  (seed, 3)           queries
+  (seed, 100 + b)     keys, then values, then per-token drift of sequence b
+  (seed, 10**6 + s)   keys then values of append step s
+
+Values are drawn in float32 and rounded to fp16 (the cache's input precision).
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+T = 128
+D = 128
+
+
+@dataclass(frozen=True)
+class Spec:
+    name: str
+    seed: int
+    hkv: int
+    hq: int
+    batch: int
+    ctx: int                      # context of every sequence (fixed-length workloads)
+    lognormal: bool               # per-channel log-normal(0, 1) multipliers
+    outlier_channels: tuple = ()  # fixed outlier channels (tiny workload)
+    outlier_count: int = 0        # seeded outlier picks per (KV head, K|V)
+    outlier_gain: float = 1.0
+    drift_sigma: float = 0.0      # per-token magnitude drift log-normal(0, sigma)
+    shuffle_blocks: bool = False
+    ragged: tuple = ()            # (lo, hi) context range, rounded to a multiple of 128
+    steps: int = 0                # append steps (write-stream workload)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def group(self) -> int:
+        return self.hq // self.hkv
+
+
+SPECS = {
+    # one KV head, one tile, channels {3, 17, 64, 101} x20
+    "tiny": Spec("tiny", 1, 1, 1, 1, 128, False, (3, 17, 64, 101), 0, 20.0),
+    # Qwen3-4B-like layer: GQA 4, batch 8, 4K context, 2% of channels x15
+    "qwen3-4b": Spec("qwen3-4b", 2, 8, 32, 8, 4096, True, (), 3, 15.0),
+    # Qwen3-32B-like layer: GQA 8, batch 16, 16K context, drift, shuffled blocks
+    "qwen3-32b-16k": Spec("qwen3-32b-16k", 3, 8, 64, 16, 16384, True, (), 3, 15.0, 0.5, True),
+    # write stream: batch 64, start at 1024 tokens, 512 append steps
+    "write-stream": Spec("write-stream", 4, 8, 32, 64, 1024, True, (), 3, 15.0, steps=512),
+    # Phi-4-14B-like ragged batch: GQA 4, 10 KV heads, contexts U[1024, 32768], 1% x20
+    "phi4-ragged": Spec("phi4-ragged", 5, 10, 40, 32, 0, True, (), 1, 20.0,
+                        shuffle_blocks=True, ragged=(1024, 32768)),
+}
+
+
+def spec(name: str, **overrides) -> Spec:
+    """A workload spec by name, optionally with fields overridden (for smaller test cases)."""
+    base = SPECS[name]
+    if not overrides:
+        return base
+    d = {f: getattr(base, f) for f in base.__dataclass_fields__}
+    d.update(overrides)
+    return Spec(**d)
+
+
+def _rng(sp: Spec, *key) -> np.random.Generator:
+    return np.random.default_rng([sp.seed, *key])
+
+
+def head_params(sp: Spec) -> np.ndarray:
+    """Per-(KV head, K|V, channel) multipliers, float32 [Hkv, 2, 128]."""
+    rng = _rng(sp, 0)
+    mult = np.ones((sp.hkv, 2, D), np.float32)
+    if sp.lognormal:
+        mult *= np.exp(rng.standard_normal((sp.hkv, 2, D))).astype(np.float32)
+    for h in range(sp.hkv):
+        for kv in range(2):
+            if sp.outlier_channels:
+                picks = np.array(sp.outlier_channels)
+            elif sp.outlier_count:
+                picks = rng.choice(D, size=sp.outlier_count, replace=False)
+            else:
+                picks = np.array([], dtype=np.int64)
+            mult[h, kv, picks] *= sp.outlier_gain
+    return mult
+
+
+def seq_lens(sp: Spec) -> np.ndarray:
+    """Context length of every sequence at prefill (int32 [B])."""
+    if sp.ragged:
+        lo, hi = sp.ragged
+        raw = _rng(sp, 1).uniform(lo, hi, size=sp.batch)
+        return (np.rint(raw / T) * T).astype(np.int32)
+    return np.full(sp.batch, sp.ctx, np.int32)
+
+
+def _sequence_kv(sp: Spec, b: int, length: int, mult: np.ndarray):
+    rng = _rng(sp, 100 + b)
+    k = rng.standard_normal((length, sp.hkv, D), dtype=np.float32) * mult[None, :, 0, :]
+    v = rng.standard_normal((length, sp.hkv, D), dtype=np.float32) * mult[None, :, 1, :]
+    if sp.drift_sigma:
+        k *= np.exp(sp.drift_sigma * rng.standard_normal((length, sp.hkv, 1), dtype=np.float32))
+        v *= np.exp(sp.drift_sigma * rng.standard_normal((length, sp.hkv, 1), dtype=np.float32))
+    k16, v16 = k.astype(np.float16), v.astype(np.float16)
+    if not (np.isfinite(k16).all() and np.isfinite(v16).all()):
+        raise ValueError("generated values overflow fp16")
+    return k16, v16
+
+
+def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None) -> dict:
+    """Prefill state of the workload.
+
+    Returns a dict with
+      k, v          fp16 [n_tiles * 128, Hkv, 128]: the full tiles of the chosen sequences,
+                    concatenated sequence after sequence (what kvarn_quantize_tiles reads)
+      dst_blocks    int32 [n_tiles]: destination block of each of those tiles
+      tail_k/tail_v list (per chosen sequence) of fp16 [len % 128, Hkv, 128] staging tokens
+      block_table   int32 [B, max_blocks] (room for max_new_tokens more tokens per sequence)
+      seq_lens      int32 [B]
+      num_blocks    int
+      sequences     the sequence indices included in k/v (default: all)."""
+    lens = seq_lens(sp)
+    max_blocks = int(max((int(l) + max_new_tokens + T - 1) // T for l in lens))
+    max_blocks = max(max_blocks, 1)
+    num_blocks = sp.batch * max_blocks
+    ids = np.arange(num_blocks, dtype=np.int32)
+    if sp.shuffle_blocks:
+        ids = _rng(sp, 2).permutation(num_blocks).astype(np.int32)
+    block_table = ids.reshape(sp.batch, max_blocks)
+    mult = head_params(sp)
+    chosen = range(sp.batch) if sequences is None else list(sequences)
+    ks, vs, dst, tk, tv = [], [], [], [], []
+    for b in chosen:
+        length = int(lens[b])
+        k, v = _sequence_kv(sp, b, length, mult)
+        n_full = length // T
+        ks.append(k[:n_full * T])
+        vs.append(v[:n_full * T])
+        dst.append(block_table[b, :n_full])
+        tk.append(k[n_full * T:])
+        tv.append(v[n_full * T:])
+    empty = np.zeros((0, sp.hkv, D), np.float16)
+    return dict(k=np.concatenate(ks) if ks else empty, v=np.concatenate(vs) if vs else empty,
+                dst_blocks=np.concatenate(dst).astype(np.int32) if dst else np.zeros(0, np.int32),
+                tail_k=tk, tail_v=tv, block_table=block_table, seq_lens=lens,
+                num_blocks=num_blocks, sequences=list(chosen))
+
+
+def query(sp: Spec, dense: bool = False) -> np.ndarray:
+    """Decode queries fp16 [B, Hq, 128], N(0, 1) (reading R21).
+
+    dense=True scales each query head so that its scores against a typical key have a
+    standard deviation near 1 under the default 1/sqrt(128) softmax scale."""
+    q = _rng(sp, 3).standard_normal((sp.batch, sp.hq, D), dtype=np.float32)
+    if dense:
+        mult = head_params(sp)
+        key_rms = np.sqrt(np.sum(mult[:, 0, :].astype(np.float64) ** 2, axis=1))  # [Hkv]
+        scale = np.sqrt(D) / key_rms
+        q *= np.repeat(scale, sp.group)[None, :, None].astype(np.float32)
+    return q.astype(np.float16)
+
+
+def append_tokens(sp: Spec, step: int):
+    """New keys and values of append step `step`: fp16 [B, Hkv, 128] each."""
+    mult = head_params(sp)
+    rng = _rng(sp, 10 ** 6 + step)
+    k = rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32) * mult[None, :, 0, :]
+    v = rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32) * mult[None, :, 1, :]
+    return k.astype(np.float16), v.astype(np.float16)
