@@ -1,0 +1,282 @@
+"""Benchmark of the KVarN K4V2 g128 hot path on one MI355X.
+
+One step = the whole path on one batch: quantise every full prefill tile of the batch into the
+paged block pool (kvarn_quantize_tiles), append one new key/value token per sequence into the
+fp16 staging tile (kvarn_append_token), and one decode-attention step over the packed tiles plus
+the staging token (kvarn_decode_attention). Default workload: the Qwen3-4B-like layer (8 KV
+heads, 32 query heads, batch 8, 4096-token context = 32 tiles per sequence, then token 4097).
+
+All inputs are resident in HBM before timing starts. Each step uses the next of several
+identical input/cache replicas so that the 256 MB last-level (Infinity) cache cannot serve a
+step from the previous one.
+
+Printed: one JSON line. value = whole-step effective HBM GB/s (algorithmic bytes of all three
+calls / step time). Also per call: decode-attention GB/s and fraction of the 8 TB/s peak,
+tiles quantised per second; the roofline of the dominant kernel (HIP events around each call
+on the launch stream); the fp64 oracle timed on a bounded sample on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+T = D = 128
+TILE = 13312
+
+WORKLOADS = {
+    # name: (spec name, spec overrides)
+    "qwen3-4b": ("qwen3-4b", {}),
+    "qwen3-32b-16k": ("qwen3-32b-16k", {}),
+    "phi4-ragged": ("phi4-ragged", {}),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen3-4b", choices=sorted(WORKLOADS))
+    p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GB")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run one device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_tok_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(lens, hkv, hq, appended):
+    """Bytes the method must move (not what an implementation happens to move)."""
+    n_full = [int(l) // T for l in lens]
+    n_stage = [int(l) % T for l in lens]
+    decode = sum(n * hkv * TILE + s * hkv * 2 * D * 2 + 4 * n + 4 for n, s in zip(n_full, n_stage))
+    decode += len(lens) * hq * D * (2 + 4)                       # q in (fp16), out (fp32)
+    return decode
+
+
+def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes):
+    """The fp64 oracle, single-threaded, on a bounded sample of the same step."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    from oracle import attention as oatt
+    from oracle import codec
+    n_q = 768                                  # tile-heads quantised (keys and values)
+    t0 = time.perf_counter()
+    n_tiles = st["k"].shape[0] // T
+    for i in range(n_q):
+        tile, head = i % n_tiles, (i * 7) % sp.hkv
+        rows = slice(T * tile, T * tile + T)
+        codec.encode_record(st["k"][rows, head], st["v"][rows, head])
+    tq = (time.perf_counter() - t0) / n_q
+    # decode: one (sequence, KV head) over an oracle-built cache of its tiles
+    n_d = 8
+    pool = np.zeros((st["num_blocks"], 1, TILE), np.uint8)
+    td_total = 0.0
+    first = np.concatenate([[0], np.cumsum(st["seq_lens"] // T)])   # first tile of each sequence
+    for r in range(n_d):
+        b, g = r % sp.batch, (3 * r) % sp.hkv
+        n = int(lens[b]) // T
+        for i in range(n):
+            rows = slice(T * (first[b] + i), T * (first[b] + i) + T)
+            pool[st["block_table"][b, i], 0] = codec.encode_record(st["k"][rows, g],
+                                                                   st["v"][rows, g])
+        sk = np.zeros((1, 1, T, D), np.float16)
+        t1 = time.perf_counter()
+        oatt.decode_attention(q[b:b + 1, g * sp.group:(g + 1) * sp.group], pool,
+                              st["block_table"][b:b + 1], lens[b:b + 1], sk, sk, sm)
+        td_total += time.perf_counter() - t1
+    td = td_total / n_d
+    est = tq * tile_heads_total + td * pairs_total
+    if limiter is not None:
+        limiter.unregister()
+    return {"value": step_bytes / est / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_q} tile-head quantisations ({tq * 1e3:.1f} ms each) and {n_d} "
+                      f"(sequence, KV head) decodes ({td * 1e3:.0f} ms each) of this step, "
+                      f"extrapolated to the step's {tile_heads_total} tile-heads and "
+                      f"{pairs_total} (sequence, KV head) pairs ({est:.1f} s per step)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
+              "described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_attention_tok_amd as kv
+    from workloads import gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    spec_name, over = WORKLOADS[args.workload]
+    sp = gen.spec(spec_name, **over)
+    st = gen.prefill(sp, max_new_tokens=1)
+    q_np = gen.query(sp)
+    k_new_np, v_new_np = gen.append_tokens(sp, 0)
+    lens_pre = st["seq_lens"].astype(np.int32)
+    pos_np = lens_pre.copy()
+    lens_np = lens_pre + 1
+    bt_np = st["block_table"]
+    cfg = kv.default_config(sp.hkv)
+    sm = 1.0 / math.sqrt(D)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    n_tiles = int(st["dst_blocks"].shape[0])
+    tile_heads = n_tiles * sp.hkv
+    q_bytes = tile_heads * (2 * T * D * 2 + TILE)
+    a_bytes = sp.batch * sp.hkv * 4 * D * 2
+    d_bytes = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True)
+    step_bytes = q_bytes + a_bytes + d_bytes
+
+    k0, v0 = dev(st["k"]), dev(st["v"])
+    per_replica = k0.numel() * 4 + st["num_blocks"] * sp.hkv * TILE
+    reps = args.replicas or max(2, min(16, math.ceil(1.2e9 / per_replica)))
+    ws_bytes = kv.decode_workspace_bytes(cfg, sp.batch, sp.hq, bt_np.shape[1])
+    R = []
+    for _ in range(reps):
+        R.append(dict(
+            k=k0.clone().view(k0.shape[0], -1), v=v0.clone().view(v0.shape[0], -1),
+            pool=torch.zeros(st["num_blocks"], sp.hkv, TILE, dtype=torch.uint8, device="cuda"),
+            sk=torch.zeros(sp.batch, sp.hkv, T, D, dtype=torch.float16, device="cuda"),
+            sv=torch.zeros(sp.batch, sp.hkv, T, D, dtype=torch.float16, device="cuda"),
+            q=dev(q_np), kn=dev(k_new_np), vn=dev(v_new_np),
+            out=torch.empty(sp.batch, sp.hq, D, dtype=torch.float32, device="cuda"),
+            ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")))
+    del k0, v0
+    dst = dev(st["dst_blocks"])
+    bt = dev(bt_np)
+    pos = dev(pos_np)
+    lens = dev(lens_np)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    import ctypes
+    lib = kv.lib()
+    cfgp = ctypes.byref(cfg)
+    V = ctypes.c_void_p
+    calls = []
+    for r in R:
+        calls.append((
+            (cfgp, V(r["k"].data_ptr()), V(r["v"].data_ptr()), r["k"].stride(0), n_tiles,
+             V(dst.data_ptr()), V(r["pool"].data_ptr()), st["num_blocks"], V(sptr)),
+            (cfgp, V(r["kn"].data_ptr()), V(r["vn"].data_ptr()), V(pos.data_ptr()),
+             V(bt.data_ptr()), bt_np.shape[1], V(r["sk"].data_ptr()), V(r["sv"].data_ptr()),
+             V(r["pool"].data_ptr()), st["num_blocks"], sp.batch, V(sptr)),
+            (cfgp, V(r["q"].data_ptr()), sp.hq, V(r["pool"].data_ptr()), st["num_blocks"],
+             V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()), V(r["sk"].data_ptr()),
+             V(r["sv"].data_ptr()), ctypes.c_float(sm), V(r["out"].data_ptr()),
+             V(r["ws"].data_ptr()), max(ws_bytes, 256), sp.batch, V(sptr))))
+    fq, fa, fd = lib.kvarn_quantize_tiles, lib.kvarn_append_token, lib.kvarn_decode_attention
+
+    def step(i, ev=None):
+        cq, ca, cd = calls[i % reps]
+        if ev is not None:
+            ev[0].record(stream)
+        assert fq(*cq) == 0
+        if ev is not None:
+            ev[1].record(stream)
+        assert fa(*ca) == 0
+        if ev is not None:
+            ev[2].record(stream)
+        assert fd(*cd) == 0
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"# workload {args.workload}: {tile_heads} tile-heads, batch {sp.batch}, "
+          f"{reps} replicas, warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tq = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
+    ta = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    td = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+    ms = elapsed / args.steps * 1e3
+    print(f"# step {ms:.4f} ms: quantise {tq * 1e6:.1f} us, append {ta * 1e6:.1f} us, "
+          f"decode {td * 1e6:.1f} us", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b_ = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b_.copy_(a)
+        torch.cuda.synchronize()
+
+    decode_gbps = d_bytes / td / 1e9
+    quant_gbps = q_bytes / tq / 1e9
+    timings = {"quantise": tq, "append": ta, "decode": td}
+    dominant = max(timings, key=timings.get)
+    ach = {"quantise": quant_gbps, "append": a_bytes / ta / 1e9, "decode": decode_gbps}[dominant]
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath)).get(args.workload, {}).get(dominant)
+        if tr and tr.get("source_digest") == source_digest():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel)",
+                           "append": "kvarn_append_token (append_token_kernel)",
+                           "decode": "kvarn_decode_attention (decode_kernel + merge_kernel)"}[dominant],
+                "algorithmic_bytes_per_launch": {"quantise": q_bytes, "append": a_bytes,
+                                                 "decode": d_bytes}[dominant],
+                "avg_launch_us": round(timings[dominant] * 1e6, 2)}
+    value = step_bytes / (elapsed / args.steps) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        pairs = sp.batch * sp.hkv
+        cpu = cpu_baseline(sp, st, q_np, lens_np, sm, tile_heads, pairs, step_bytes)
+    line = {
+        "metric": "decode-attn effective HBM GB/s (% of peak) + tiles quantised/s, K4V2 g128",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16-in/fp32-acc, u4/u2 codes",
+        "data": "synthetic (seeded generators; no model weights)",
+        "config": {"workload": args.workload, "batch": sp.batch, "kv_heads": sp.hkv,
+                   "q_heads": sp.hq, "context": int(lens_pre.max()),
+                   "tile_heads_quantised_per_step": tile_heads, "replicas": reps},
+        "decode_attn": {"gbps": round(decode_gbps, 1),
+                        "frac_of_peak": round(decode_gbps / HBM_PEAK_GBPS, 4),
+                        "us": round(td * 1e6, 2), "algorithmic_bytes": d_bytes},
+        "quantise": {"tiles_per_s": round(tile_heads / tq, 1), "gbps": round(quant_gbps, 1),
+                     "frac_of_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
+                     "us": round(tq * 1e6, 2), "algorithmic_bytes": q_bytes},
+        "append": {"us": round(ta * 1e6, 2), "algorithmic_bytes": a_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+// libkvarn C ABI: argument validation and kernel launches (declared in include/kvarn.h).
+
+#include "../../include/kvarn.h"
+#include "kvarn_kernels.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvarn_status check_config(const kvarn_config* cfg) {
+  if (cfg == nullptr) return KVARN_ERR_NULL_ARG;
+  if (cfg->num_kv_heads < 1) return KVARN_ERR_BAD_SHAPE;
+  if (cfg->head_dim != KVARN_HEAD_DIM || cfg->block_tokens != KVARN_TILE_TOKENS ||
+      cfg->k_bits != 4 || cfg->v_bits != 2 || cfg->sinkhorn_iters < 1 ||
+      cfg->sinkhorn_iters > 16)
+    return KVARN_ERR_UNSUPPORTED;
+  return KVARN_OK;
+}
+
+kvarn_status from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
+
+constexpr long long kMaxGrid = 0x7FFFFFFFLL;
+
+}  // namespace
+
+extern "C" {
+
+void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads) {
+  if (cfg == nullptr) return;
+  cfg->num_kv_heads = num_kv_heads;
+  cfg->head_dim = KVARN_HEAD_DIM;
+  cfg->block_tokens = KVARN_TILE_TOKENS;
+  cfg->k_bits = 4;
+  cfg->v_bits = 2;
+  cfg->sinkhorn_iters = 4;
+}
+
+size_t kvarn_tile_bytes(const kvarn_config* cfg) {
+  return check_config(cfg) == KVARN_OK ? (size_t)KVARN_TILE_BYTES : 0;
+}
+
+size_t kvarn_block_bytes(const kvarn_config* cfg) {
+  return check_config(cfg) == KVARN_OK ? (size_t)KVARN_TILE_BYTES * (size_t)cfg->num_kv_heads
+                                       : 0;
+}
+
+kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const void* v,
+                                  int64_t token_stride, int32_t n_tiles,
+                                  const int32_t* dst_blocks, void* block_pool,
+                                  int64_t num_blocks, void* stream) {
+  kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  if (n_tiles < 0 || num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (n_tiles == 0) return KVARN_OK;
+  if (k == nullptr || v == nullptr || dst_blocks == nullptr || block_pool == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (token_stride < (int64_t)cfg->num_kv_heads * KVARN_HEAD_DIM || token_stride % 8 != 0 ||
+      !aligned16(k) || !aligned16(v))
+    return KVARN_ERR_BAD_SHAPE;
+  if (2LL * cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
+  return from_hip(kvarn::launch_quantize_tiles(
+      static_cast<const __half*>(k), static_cast<const __half*>(v), token_stride, n_tiles,
+      cfg->num_kv_heads, dst_blocks, static_cast<uint8_t*>(block_pool), num_blocks,
+      cfg->sinkhorn_iters, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, const void* v_new,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, void* staging_k, void* staging_v,
+                                void* block_pool, int64_t num_blocks, int32_t batch,
+                                void* stream) {
+  kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  if (batch < 0 || max_blocks_per_seq < 1 || num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (batch == 0) return KVARN_OK;
+  if (k_new == nullptr || v_new == nullptr || positions == nullptr || block_table == nullptr ||
+      staging_k == nullptr || staging_v == nullptr || block_pool == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(staging_k) || !aligned16(staging_v))
+    return KVARN_ERR_BAD_SHAPE;
+  if (2LL * cfg->num_kv_heads * batch > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
+  return from_hip(kvarn::launch_append_token(
+      static_cast<const __half*>(k_new), static_cast<const __half*>(v_new), positions,
+      block_table, max_blocks_per_seq, static_cast<__half*>(staging_k),
+      static_cast<__half*>(staging_v), static_cast<uint8_t*>(block_pool), num_blocks,
+      cfg->num_kv_heads, batch, cfg->sinkhorn_iters, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
+                                          int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          size_t* bytes) {
+  kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  if (bytes == nullptr) return KVARN_ERR_NULL_ARG;
+  if (batch < 0 || max_blocks_per_seq < 1 || num_q_heads < cfg->num_kv_heads ||
+      num_q_heads % cfg->num_kv_heads != 0 ||
+      num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup)
+    return KVARN_ERR_BAD_SHAPE;
+  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  *bytes = (size_t)batch * (size_t)num_q_heads * (size_t)splits * kvarn::kPartialFloats *
+           sizeof(float);
+  return KVARN_OK;
+}
+
+kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int32_t num_q_heads,
+                                    const void* block_pool, int64_t num_blocks,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, const void* staging_k,
+                                    const void* staging_v, float sm_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, int32_t batch,
+                                    void* stream) {
+  size_t need = 0;
+  kvarn_status st = kvarn_decode_workspace_bytes(cfg, batch, num_q_heads, max_blocks_per_seq,
+                                                 &need);
+  if (st != KVARN_OK) return st;
+  if (num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (batch == 0) return KVARN_OK;
+  if (q == nullptr || block_pool == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      staging_k == nullptr || staging_v == nullptr || out == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (workspace == nullptr || workspace_bytes < need) return KVARN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVARN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(staging_k) || !aligned16(staging_v) || !aligned16(out))
+    return KVARN_ERR_BAD_SHAPE;
+  if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
+  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
+  return from_hip(kvarn::launch_decode(
+      static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads,
+      static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
+      seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
+      sm_scale, out, static_cast<float*>(workspace), splits, batch,
+      static_cast<hipStream_t>(stream)));
+}
+
+const char* kvarn_status_string(kvarn_status status) {
+  switch (status) {
+    case KVARN_OK: return "ok";
+    case KVARN_ERR_NULL_ARG: return "a required pointer is NULL";
+    case KVARN_ERR_BAD_SHAPE: return "a size or count is out of range, or a buffer is misaligned";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported config (only kvarn_k4v2_g128, head_dim 128)";
+    case KVARN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KVARN_ERR_HIP: return "HIP runtime error while launching";
+  }
+  return "unknown status";
+}
+
+int32_t kvarn_abi_version(void) { return KVARN_ABI_VERSION; }
+
+}  // extern "C"

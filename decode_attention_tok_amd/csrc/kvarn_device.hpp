@@ -1,0 +1,106 @@
+// Device-side helpers shared by the libkvarn kernels (gfx950, wave64).
+//
+// FP8 and FP16 conversions are written from the format definitions: OCP FP8 E4M3 (exponent
+// bias 7, three mantissa bits, largest finite 448, subnormals in steps of 2^-9) and IEEE
+// binary16 (bias 15, ten mantissa bits, subnormals in steps of 2^-24). Only non-negative FP8
+// values occur in the codec (scales), so the FP8 helpers handle the sign-less half.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+constexpr int kT = 128;              // tokens per tile
+constexpr int kD = 128;              // head dimension
+constexpr int kTileBytes = 13312;    // record of one (block, KV head)
+constexpr int kKCodesOff = 0;
+constexpr int kVCodesOff = 8192;
+constexpr int kKMetaOff = 12288;
+constexpr int kVMetaOff = 12800;
+constexpr int kCRel = 0, kSRel = 128, kZRel = 256;
+
+// ------------------------------------------------------------------ FP8 E4M3 (non-negative)
+
+// Decode a non-negative E4M3 code (sign bit clear, not NaN) to float, exactly.
+__device__ __forceinline__ float e4m3_to_float(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Nearest E4M3 code to v, ties to the even code; v must lie in [2^-9, 448].
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (b < 0x3C800000u) {                       // v < 2^-6: subnormal grid of 2^-9
+    return (uint32_t)rintf(v * 512.0f);        // 1..8 (8 encodes 2^-6)
+  }
+  uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  r &= 0xFFF00000u;
+  return ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
+}
+
+// Smallest E4M3 value >= v, as a code; v >= 0. Values above 448 saturate to 448.
+__device__ __forceinline__ uint32_t e4m3_ru(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  const uint32_t b = __float_as_uint(v);
+  if (b < 0x3C800000u) return (uint32_t)ceilf(v * 512.0f);
+  uint32_t r = (b + 0xFFFFFu) & 0xFFF00000u;
+  return ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);
+}
+
+// ------------------------------------------------------------------ FP16 directed rounding
+
+// Largest binary16 <= a for 0 <= a (saturates at 65504), as bits.
+__device__ __forceinline__ uint32_t fp16_rz_pos(float a) {
+  if (a >= 65504.0f) return 0x7BFFu;
+  const uint32_t b = __float_as_uint(a);
+  if (b < 0x38800000u) return (uint32_t)floorf(a * 16777216.0f);  // a < 2^-14: step 2^-24
+  return ((((b >> 23) & 0xFFu) - 112u) << 10) | ((b >> 13) & 0x3FFu);
+}
+
+// Smallest binary16 >= a for 0 < a <= 65504, as bits.
+__device__ __forceinline__ uint32_t fp16_ru_pos(float a) {
+  const uint32_t b = __float_as_uint(a);
+  if (b < 0x38800000u) return (uint32_t)ceilf(a * 16777216.0f);
+  const uint32_t r = b + 0x1FFFu;
+  return ((((r >> 23) & 0xFFu) - 112u) << 10) | ((r >> 13) & 0x3FFu);
+}
+
+// Largest binary16 <= v for v >= -65504 (callers clamp first), as bits (zero is +0).
+__device__ __forceinline__ uint32_t fp16_rd(float v) {
+  if (v >= 0.0f) return fp16_rz_pos(v);
+  return 0x8000u | fp16_ru_pos(-v);
+}
+
+__device__ __forceinline__ float fp16_bits_to_float(uint32_t h) {
+  return __half2float(__ushort_as_half((unsigned short)h));
+}
+
+// ------------------------------------------------------------------ wave reductions (wave64)
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Unpack 8 fp16 values held in a uint4.
+__device__ __forceinline__ void unpack_h8(const uint4 w, float* out) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = fp16_bits_to_float(u[i] & 0xFFFFu);
+    out[2 * i + 1] = fp16_bits_to_float(u[i] >> 16);
+  }
+}
+
+}  // namespace kvarn

@@ -1,0 +1,34 @@
+// Internal launch wrappers of the libkvarn kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kvarn {
+
+// Floats per (sequence, query head, split) partial: m, l, rotated output, raw output.
+constexpr int kPartialFloats = 2 + 2 * 128;
+constexpr int kMaxGroup = 16;
+
+hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
+                                 int n_tiles, int hkv, const int32_t* dst_blocks,
+                                 uint8_t* pool, long long num_blocks, int iters,
+                                 hipStream_t stream);
+
+hipError_t launch_append_token(const __half* k_new, const __half* v_new,
+                               const int32_t* positions, const int32_t* block_table,
+                               int max_blocks, __half* staging_k, __half* staging_v,
+                               uint8_t* pool, long long num_blocks, int hkv, int batch,
+                               int iters, hipStream_t stream);
+
+hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
+                         long long num_blocks, const int32_t* block_table, int max_blocks,
+                         const int32_t* seq_lens, const __half* staging_k,
+                         const __half* staging_v, float sm_scale, float* out, float* partials,
+                         int splits, int batch, hipStream_t stream);
+
+// Number of splits of each sequence's tiles for a decode launch (depends on sizes only).
+int decode_splits(int batch, int hkv, int max_blocks);
+
+}  // namespace kvarn

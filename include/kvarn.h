@@ -1,0 +1,179 @@
+/*
+ * kvarn.h - C ABI of libkvarn: the KVarN K4V2 g128 KV-cache codec and the paged decode
+ * attention that reads it, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources. The operations follow these pages (cited by title and section):
+ *   [GR]  groundy.com, "Huawei's KVarN puts KV-cache quantization inside vLLM's backend":
+ *         "What KVarN changes in vLLM's serving path" (preset kvarn_k4v2_g128: 4-bit keys,
+ *         2-bit values, one 128-token tile per cache block, FP8 scales and FP16 zero-points)
+ *         and "The four-stage pipeline" (Hadamard rotation along channels; Sinkhorn-like
+ *         alternating column/row standard-deviation normalisation in log space; asymmetric
+ *         round-to-nearest; scales applied when a tile is read for attention), and
+ *         "Frequently Asked Questions" (tile fixed at 128 tokens; other head dimensions
+ *         unsupported).
+ *   [TSM] tools.thesoundmethod.me, "KVarN: 2-Bit KV-Cache That Beats FP16 Throughput, and
+ *         Where the Catch Lives", "What KVarN does differently" (the two conditioning steps)
+ *         and "Where the bill lands" (rotation and per-tile statistics are state that must
+ *         stay consistent between prefill and decode).
+ *
+ * Conventions shared by every entry point.
+ *   - Pointers marked (device) are HIP device pointers; (host) are host pointers.
+ *   - fp16 means IEEE binary16, little-endian. All fp16 buffers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. Every call
+ *     validates its arguments on the host, then enqueues its kernels on `stream` and returns
+ *     without synchronising. On a validation error nothing is enqueued.
+ *   - The library allocates no device memory and keeps no state between calls; the caller
+ *     owns every buffer. Calls on different buffers may run concurrently.
+ *   - Device-side preconditions that the host cannot see (block ids, positions, lengths) are
+ *     bounds-checked in the kernels: an out-of-range block id or length never causes an
+ *     out-of-bounds access; see each entry point for the result it then produces.
+ *
+ * The packed cache. A block holds 128 tokens of every KV head: num_kv_heads tile records of
+ * 13312 bytes back to back (record of block b, KV head h at byte (b * num_kv_heads + h) * 13312
+ * of the block pool). A record, little-endian:
+ *   [0, 8192)      key codes (4 bit), token-major: token t at byte 64 t; channel j in byte
+ *                  j / 2, low nibble for even j, high nibble for odd j
+ *   [8192, 12288)  value codes (2 bit), as 1024 32-bit words. With nb = j / 16, n = j % 16,
+ *                  kb = t / 32, h = (t / 16) % 2, s = (t / 4) % 4, i = t % 4, the code of
+ *                  token t, channel j is at word 256 kb + 4 (16 s + n) + 2 h + i / 2,
+ *                  bits 2 nb + 16 (i % 2) .. +1
+ *   [12288, 12416) key per-channel scale c-hat, FP8 E4M3 (OCP), channel j at byte j
+ *   [12416, 12544) key per-token scale s-hat, FP8 E4M3, token t at byte t
+ *   [12544, 12800) key per-token zero-point z-hat, fp16, token t at bytes 2t, 2t+1
+ *   [12800, 13312) the same three arrays for the values
+ * A dequantised rotated element is c-hat_j * (s-hat_t * code_tj + z-hat_t); the original
+ * element is the rotated row times the 128-point orthonormal Sylvester Hadamard matrix.
+ *
+ * The fp16 staging tile. Tokens past the last full block of a sequence live unquantised in
+ * staging[b][h][t][0..127] (fp16, [batch][num_kv_heads][128][128]): a sequence of L tokens
+ * reads floor(L / 128) packed tiles through its block-table row and L mod 128 staging
+ * tokens. kvarn_append_token fills staging and quantises it when it holds 128 tokens; a
+ * prefill tail may also be written there directly in this plain layout.
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KVARN_API __attribute__((visibility("default")))
+#else
+#define KVARN_API
+#endif
+
+#define KVARN_ABI_VERSION 1
+#define KVARN_TILE_TOKENS 128
+#define KVARN_HEAD_DIM 128
+#define KVARN_TILE_BYTES 13312
+
+typedef enum {
+  KVARN_OK = 0,
+  KVARN_ERR_NULL_ARG = 1,    /* a required pointer is NULL                               */
+  KVARN_ERR_BAD_SHAPE = 2,   /* a size or count is out of range, or a buffer misaligned  */
+  KVARN_ERR_UNSUPPORTED = 3, /* the config is not kvarn_k4v2_g128 with head_dim 128      */
+  KVARN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required               */
+  KVARN_ERR_HIP = 5          /* the HIP runtime reported an error when launching         */
+} kvarn_status;
+
+/* The codec configuration. Only the preset kvarn_k4v2_g128 exists ([GR], "What KVarN changes
+ * in vLLM's serving path" and "Frequently Asked Questions"): head_dim 128, block_tokens 128,
+ * k_bits 4, v_bits 2. sinkhorn_iters is the fixed number of column+row normalisation rounds
+ * of [GR] "The four-stage pipeline" stage 2, whose value the pages do not give: 4 by default,
+ * 1..16 accepted. Prefill and decode must use the same config ([TSM] "Where the bill lands"). */
+typedef struct {
+  int32_t num_kv_heads;   /* >= 1                      */
+  int32_t head_dim;       /* must be 128               */
+  int32_t block_tokens;   /* must be 128               */
+  int32_t k_bits;         /* must be 4                 */
+  int32_t v_bits;         /* must be 2                 */
+  int32_t sinkhorn_iters; /* 1..16, default 4          */
+} kvarn_config;
+
+/* Fills *cfg with the preset for num_kv_heads heads (sinkhorn_iters = 4). */
+KVARN_API void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads);
+
+/* Bytes of one tile record (one KV head of one block, keys and values): 13312, or 0 if the
+ * config is invalid. */
+KVARN_API size_t kvarn_tile_bytes(const kvarn_config* cfg);
+
+/* Bytes of one block: num_kv_heads * kvarn_tile_bytes, or 0 if the config is invalid. */
+KVARN_API size_t kvarn_block_bytes(const kvarn_config* cfg);
+
+/* Write path, prefill ([GR] "The four-stage pipeline", stages 1-3, per 128-token tile).
+ * Quantises n_tiles whole tiles of keys and values into the block pool.
+ *   k, v          (device) fp16, token-major: token i of the input, KV head h, channel j at
+ *                 element i * token_stride + h * 128 + j, for i < n_tiles * 128. Tile m is
+ *                 tokens 128 m .. 128 m + 127.
+ *   token_stride  elements between consecutive tokens; >= num_kv_heads * 128, multiple of 8.
+ *   dst_blocks    (device) int32 [n_tiles]: tile m is written to block dst_blocks[m].
+ *   block_pool    (device) num_blocks blocks of kvarn_block_bytes.
+ * n_tiles = 0 is a no-op. A dst_blocks entry outside [0, num_blocks) skips that tile.
+ * Two tiles with the same destination race. */
+KVARN_API kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const void* v,
+                                  int64_t token_stride, int32_t n_tiles,
+                                  const int32_t* dst_blocks, void* block_pool,
+                                  int64_t num_blocks, void* stream);
+
+/* Write path, one decode step ([GR] "The four-stage pipeline", stage 4: the per-step write
+ * stays cheap). For each sequence b with positions[b] >= 0, writes its new key and value
+ * token into staging slot positions[b] % 128; when that slot is 127 the staging tile now
+ * holds 128 tokens and is quantised into block block_table[b][positions[b] / 128].
+ *   k_new, v_new      (device) fp16 [batch][num_kv_heads][128]
+ *   positions         (device) int32 [batch]: 0-based index of the new token; < 0 skips
+ *   block_table       (device) int32 [batch][max_blocks_per_seq]
+ *   staging_k/_v      (device) fp16 [batch][num_kv_heads][128][128], updated in place
+ *   block_pool        (device) num_blocks blocks
+ * If positions[b] / 128 >= max_blocks_per_seq or the block id is outside [0, num_blocks),
+ * the staging write still happens and the completed tile is not quantised. */
+KVARN_API kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, const void* v_new,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, void* staging_k, void* staging_v,
+                                void* block_pool, int64_t num_blocks, int32_t batch,
+                                void* stream);
+
+/* Size of the workspace kvarn_decode_attention needs for these sizes, into *bytes (host).
+ * It depends only on the arguments. */
+KVARN_API kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
+                                          int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          size_t* bytes);
+
+/* Read path ([GR] "The four-stage pipeline", stage 4, with stage 1's rotation folded into
+ * the query and the output). Exact softmax attention of one query token per (sequence,
+ * query head) over floor(L/128) dequantised packed tiles and L mod 128 fp16 staging tokens,
+ * L = seq_lens[b]. Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   q            (device) fp16 [batch][num_q_heads][128]; num_q_heads a multiple of
+ *                num_kv_heads with num_q_heads / num_kv_heads <= 16
+ *   block_pool   (device) num_blocks blocks
+ *   block_table  (device) int32 [batch][max_blocks_per_seq]
+ *   seq_lens     (device) int32 [batch]
+ *   staging_k/_v (device) fp16 [batch][num_kv_heads][128][128]
+ *   sm_scale     softmax scale applied to q . k (for example 1/sqrt(128))
+ *   out          (device) fp32 [batch][num_q_heads][128]
+ *   workspace    (device) at least kvarn_decode_workspace_bytes bytes, 256-byte aligned;
+ *                its contents on entry do not matter
+ * L = 0 gives zeros. A row with L < 0, L / 128 > max_blocks_per_seq or a block id outside
+ * [0, num_blocks) gives NaN in every output of that sequence. */
+KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int32_t num_q_heads,
+                                    const void* block_pool, int64_t num_blocks,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, const void* staging_k,
+                                    const void* staging_v, float sm_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, int32_t batch,
+                                    void* stream);
+
+/* Static, NUL-terminated description of a status. */
+KVARN_API const char* kvarn_status_string(kvarn_status status);
+
+/* KVARN_ABI_VERSION of the built library. */
+KVARN_API int32_t kvarn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

@@ -1,0 +1,150 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point include/kvarn.h
+declares, and its host-side validation returns the documented status codes before any HIP
+call (every call below fails validation, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_tok_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvarn.h")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kv.LIB_PATH):
+        pytest.skip("libkvarn.so not built")
+    return kv.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KVARN_API\s+[\w\s\*]+?\b(kvarn_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(kv.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.kvarn_abi_version() == 1
+
+
+def test_sizes(lib):
+    cfg = kv.default_config(8)
+    assert kv.tile_bytes(cfg) == 13312
+    assert kv.block_bytes(cfg) == 8 * 13312
+    bad = kv.default_config(8)
+    bad.head_dim = 64
+    assert kv.tile_bytes(bad) == 0 and kv.block_bytes(bad) == 0
+
+
+def test_workspace_bytes_depends_only_on_sizes(lib):
+    cfg = kv.default_config(8)
+    a = kv.decode_workspace_bytes(cfg, 16, 64, 128)
+    b = kv.decode_workspace_bytes(cfg, 16, 64, 128)
+    assert a == b and a > 0 and a % 4 == 0
+    assert kv.decode_workspace_bytes(cfg, 0, 64, 128) == 0
+
+
+def _call(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def _cfg(**kw):
+    c = kv.default_config(kw.pop("hkv", 2))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return ctypes.byref(c)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 64), ("block_tokens", 64), ("k_bits", 2),
+                                         ("v_bits", 4), ("sinkhorn_iters", 0),
+                                         ("sinkhorn_iters", 17)])
+def test_unsupported_configs(lib, field, value):
+    st = _call(lib, "kvarn_quantize_tiles", _cfg(**{field: value}), FAKE, FAKE, 256, 1, FAKE,
+               FAKE, 1, None)
+    assert st == UNSUP
+
+
+def test_null_config(lib):
+    assert _call(lib, "kvarn_quantize_tiles", None, FAKE, FAKE, 256, 1, FAKE, FAKE, 1, None) == NULL
+    out = ctypes.c_size_t()
+    assert _call(lib, "kvarn_decode_workspace_bytes", None, 1, 2, 1, ctypes.byref(out)) == NULL
+
+
+def test_quantize_validation(lib):
+    f = "kvarn_quantize_tiles"
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 256, 0, None, None, 0, None) == OK   # no-op
+    assert _call(lib, f, _cfg(), None, FAKE, 256, 1, FAKE, FAKE, 1, None) == NULL
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 256, -1, FAKE, FAKE, 1, None) == SHAPE
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 128, 1, FAKE, FAKE, 1, None) == SHAPE  # < Hkv*128
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 260, 1, FAKE, FAKE, 1, None) == SHAPE  # % 8
+    assert _call(lib, f, _cfg(), ctypes.c_void_p(0x1002), FAKE, 256, 1, FAKE, FAKE, 1,
+                 None) == SHAPE                                                  # misaligned
+    assert _call(lib, f, _cfg(hkv=0), FAKE, FAKE, 256, 1, FAKE, FAKE, 1, None) == SHAPE
+
+
+def test_append_validation(lib):
+    f = "kvarn_append_token"
+    args = [FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 10]
+    assert _call(lib, f, _cfg(), *args, 0, None) == OK                           # no-op
+    assert _call(lib, f, _cfg(), None, *args[1:], 2, None) == NULL
+    bad = list(args)
+    bad[4] = 0
+    assert _call(lib, f, _cfg(), *bad, 2, None) == SHAPE                         # max_blocks
+    assert _call(lib, f, _cfg(), *args, -1, None) == SHAPE
+    bad = list(args)
+    bad[5] = ctypes.c_void_p(0x1008)
+    assert _call(lib, f, _cfg(), *bad, 2, None) == SHAPE                         # misaligned
+
+
+def test_decode_validation(lib):
+    f = "kvarn_decode_attention"
+    cfg = kv.default_config(2)
+    need = kv.decode_workspace_bytes(cfg, 2, 8, 4)
+    good = [FAKE, 8, FAKE, 10, FAKE, 4, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+            ctypes.c_void_p(0x10000), need, 2, None]
+    def call(**over):
+        a = list(good)
+        names = ["q", "hq", "pool", "nblk", "bt", "maxb", "lens", "sk", "sv", "sm", "out", "ws",
+                 "wsb", "batch", "stream"]
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return _call(lib, f, _cfg(), *a)
+    assert call(batch=0) == OK
+    assert call(q=None) == NULL
+    assert call(out=None) == NULL
+    assert call(hq=7) == SHAPE                      # not a multiple of Hkv
+    assert call(hq=2 * 17) == SHAPE                 # group > 16
+    assert call(maxb=0) == SHAPE
+    assert call(ws=None) == WS
+    assert call(wsb=need - 4) == WS
+    assert call(ws=ctypes.c_void_p(0x10010)) == WS  # not 256-byte aligned
+    assert call(sm=ctypes.c_float(float("nan"))) == SHAPE
+    assert call(q=ctypes.c_void_p(0x1004)) == SHAPE
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.kvarn_status_string(code)
+    assert lib.kvarn_status_string(99) == b"unknown status"
+
+
+def test_binding_raises_on_error(lib):
+    cfg = kv.default_config(2)
+    cfg.head_dim = 64
+    with pytest.raises(kv.KvarnError) as e:
+        kv.decode_workspace_bytes(cfg, 1, 2, 1)
+    assert e.value.code == UNSUP
