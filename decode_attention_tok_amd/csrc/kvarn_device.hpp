@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t e4m3_ru(float v) {
 
 // ------------------------------------------------------------------ FP16 directed rounding
 
-// Largest binary16 <= a for 0 <= a (saturates at 65504), as bits.
+// Largest binary16 <= a for a >= +0 (sign bit clear; saturates at 65504), as bits.
 __device__ __forceinline__ uint32_t fp16_rz_pos(float a) {
   if (a >= 65504.0f) return 0x7BFFu;
   const uint32_t b = __float_as_uint(a);
@@ -69,9 +69,9 @@ __device__ __forceinline__ uint32_t fp16_ru_pos(float a) {
   return ((((r >> 23) & 0xFFu) - 112u) << 10) | ((r >> 13) & 0x3FFu);
 }
 
-// Largest binary16 <= v for v >= -65504 (callers clamp first), as bits (zero is +0).
+// Largest binary16 <= v for v >= -65504 (callers clamp first), as bits. Both zeros give +0.
 __device__ __forceinline__ uint32_t fp16_rd(float v) {
-  if (v >= 0.0f) return fp16_rz_pos(v);
+  if (!(v < 0.0f)) return fp16_rz_pos(fabsf(v));
   return 0x8000u | fp16_ru_pos(-v);
 }
 
