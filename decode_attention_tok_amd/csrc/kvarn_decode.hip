@@ -1,24 +1,33 @@
 // KVarN paged decode attention over packed K4/V2 tiles (read path) for gfx950.
 //
 // [GR] "The four-stage pipeline" (groundy.com, "Huawei's KVarN puts KV-cache quantization
-// inside vLLM's backend"), stage 4: scales are applied when a tile is read for attention.
-// Nothing is dequantised to memory. Because the rotation H of stage 1 is orthonormal and
-// symmetric, q . k = (qH) . (kH); so per tile, with q_rot = qH:
-//   q~_j   = q_rot_j * c-hat^K_j                        (per-channel key scale into the query)
+// inside vLLM's backend"), stage 4: scales are applied when a tile is read for attention;
+// nothing is dequantised to memory. The rotation H of stage 1 is orthonormal and symmetric, so
+// q . k = (qH) . (kH); per tile, with q_rot = qH:
+//   q~_j   = q_rot_j * c-hat^K_j                   (per-channel key scale into the query)
 //   s_t    = sm * (s-hat^K_t * <q~, codeK_t> + z-hat^K_t * sum_j q~_j)
-//                                                       (per-token key scale into the score)
 //   acc_j  = sum_t (p_t s-hat^V_t) codeV_tj,  beta = sum_t p_t z-hat^V_t
-//   o~_j  += c-hat^V_j * (acc_j + beta)                 (value scales into the probabilities
-//                                                        and the per-tile partial output)
-// with an online (running max / running sum) softmax across tiles, and the raw fp16 staging
-// tokens attended with the unrotated query into a second, unrotated accumulator sharing the
-// same max and sum. Each sequence's tiles are split over several workgroups (flash-decoding
-// style); a merge kernel combines the splits by log-sum-exp, rotates the packed-tile part of
-// the output back (o~ H) and normalises.
+//   o~_j  += c-hat^V_j * (acc_j + beta)            (value scales into probabilities / output)
+// with an online softmax over tiles. A second kernel adds the raw fp16 staging tokens (exact
+// fp32 attention with the unrotated query), merges the tile splits by log-sum-exp, rotates
+// the packed-tile part back (o~ H) and normalises.
 //
-// This version computes the dot products on the vector ALUs in fp32: one workgroup of 256
-// threads per (split, KV head, sequence) walks its tiles one by one; scores use thread
-// (token, channel half), the value products thread (channel, head parity).
+// Tile kernel. A workgroup of 4 waves serves one (split, KV head, sequence, head group of <= 8
+// query heads); each wave walks every 4th tile of the split with its own softmax state, and
+// the 4 states are merged in LDS. Per tile a wave issues 64 MFMAs (v_mfma_f32_16x16x32_f16):
+//   scores  D[token][col] = codeK[token][ch] x Q[ch][col]   8 token blocks x 4 channel blocks
+//   output  O[row][ch]    = W[row][token] x codeV[token][ch] 4 token blocks x 8 channel blocks
+// Key codes enter the MFMA as normal fp16 halves 1 + code / 16 (the nibble shifted into
+// mantissa bits 6..9 under exponent 0x3C00); the constant 1 contributes sum_j q~_j, which the
+// score needs anyway and subtracts exactly. (The MFMA sums products of subnormal fp16 operands
+// with far less precision than products of normal ones, so raw codes are not used as
+// subnormals.) Value codes likewise enter as 1 + code / 4 (the 2-bit field shifted to
+// mantissa bits 8..9), and sum_t p_t s-hat^V_t removes the constant part per head.
+// fp32-accurate operands are split into fp16 hi + lo parts: query column g holds hi(q~_g),
+// column 8 + g holds lo(q~_g), and one DPP row rotation by 8 adds the two partial scores;
+// the probability operand likewise has rows g (hi) and 8 + g (lo), summed once at the end.
+// The score accumulator lanes of token block pair (2 kb, 2 kb + 1) are exactly the operand
+// lanes of output token block kb, so probabilities feed the second product without shuffles.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -27,87 +36,138 @@ namespace kvarn {
 
 namespace {
 
-constexpr int kDThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTThreads = 64 * kWaves;
+constexpr int kHeadGroup = 8;                 // query heads per tile workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct DecSmem {
-  float qrot[kMaxGroup][kD];
-  float qraw[kMaxGroup][kD];
-  float qt[kMaxGroup][kD];
-  float sc[kMaxGroup][kT];
-  uint8_t cv[kT][kD];
-  float asum[kMaxGroup];
-  float m[kMaxGroup], l[kMaxGroup], alpha[kMaxGroup], beta[kMaxGroup];
-  float kc[kD], ks[kT], kz[kT], vc[kD], vs[kT], vz[kT];
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+struct WaveMeta {                  // per-wave, per-tile metadata (fp32, factors folded in)
+  float kc[kD];                    // c-hat^K_j
+  float ks[kT];                    // s-hat^K_t * sm * log2(e) * 16 / pq
+  float kz[kT];                    // z-hat^K_t * sm * log2(e)
+  float vs[kT];                    // s-hat^V_t * 32 (probability operand prescale)
+  float vz[kT];                    // z-hat^V_t
+  float vc[kD];                    // c-hat^V_j
+  float alpha[16], beta[16];       // per-row rescale and zero-point term of the last tile
 };
 
-// Online-softmax update of heads handled by this wave; sc holds log2-domain scores for the
-// first n tokens. Replaces sc[g][t] by p_t * (vs ? vs[t] : 1) and records alpha, beta.
-__device__ __forceinline__ void softmax_update(DecSmem& sm, int group, int n, bool packed) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int g = wave; g < group; g += kDThreads / 64) {
-    const float s0 = lane < n ? sm.sc[g][lane] : -INFINITY;
-    const float s1 = lane + 64 < n ? sm.sc[g][lane + 64] : -INFINITY;
-    const float mt = wave_max(fmaxf(s0, s1));
-    const float mold = sm.m[g];
-    const float mnew = fmaxf(mold, mt);
-    const float alpha = (mold == -INFINITY) ? 0.0f : exp2f(mold - mnew);
-    const float p0 = lane < n ? exp2f(s0 - mnew) : 0.0f;
-    const float p1 = lane + 64 < n ? exp2f(s1 - mnew) : 0.0f;
-    const float lsum = wave_sum(p0 + p1);
-    float beta = 0.0f;
-    if (packed) {
-      beta = wave_sum(p0 * sm.vz[lane] + p1 * sm.vz[lane + 64]);
-      sm.sc[g][lane] = p0 * sm.vs[lane];
-      sm.sc[g][lane + 64] = p1 * sm.vs[lane + 64];
+struct TileSmem {
+  float qrot[kHeadGroup][kD];      // rotated queries (fp32)
+  WaveMeta wm[kWaves];
+  float comb_m[kWaves][kHeadGroup], comb_l[kWaves][kHeadGroup];
+  float comb_o[kWaves][kHeadGroup][kD];
+  float red[kWaves];
+};
+
+__device__ __forceinline__ float dpp_ror8(float v) {   // lane (l & ~15) | ((l + 8) & 15)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  const __fp16 ha = (__fp16)a, hb = (__fp16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(half8, u);
+}
+
+// hi / lo fp16 split of x (x == hi + lo to about 2^-22 relative when normal)
+__device__ __forceinline__ void split_hl(float x, float& hi, float& lo) {
+  hi = (float)(__fp16)x;
+  lo = x - hi;
+}
+
+struct TileRegs {
+  uint4 kw[8];        // key codes: token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31
+  uint4 vw[4];        // value codes: section words 256 kb + 4 lane .. + 3
+  uint4 meta;         // 16 bytes of the record's 1 KB metadata at 12288 + 16 lane
+};
+
+__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int lane, TileRegs& r) {
+  const int m = lane & 15, s = lane >> 4;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + kKCodesOff + (16 * mb + m) * 64 + 16 * s);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    r.vw[kb] = *reinterpret_cast<const uint4*>(rec + kVCodesOff + kb * 1024 + lane * 16);
+  r.meta = *reinterpret_cast<const uint4*>(rec + kKMetaOff + lane * 16);
+}
+
+// Scatter one lane's 16 metadata bytes into the wave's fp32 tables. Lanes 0-7: c-hat^K,
+// 8-15: s-hat^K, 16-31: z-hat^K, 32-39: c-hat^V, 40-47: s-hat^V, 48-63: z-hat^V.
+__device__ __forceinline__ void decode_meta(const uint4 mw, int lane, WaveMeta& wm,
+                                            float kfac, float kzfac) {
+  const uint32_t w[4] = {mw.x, mw.y, mw.z, mw.w};
+  const int grp = lane & 31;
+  const bool isv = lane >= 32;
+  if (grp < 16) {                         // 16 FP8 values
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = e4m3_to_float((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    const int base = (grp & 7) * 16;
+    float* dst;
+    float mul;
+    if (grp < 8) {
+      dst = isv ? wm.vc : wm.kc;
+      mul = 1.0f;
     } else {
-      sm.sc[g][lane] = p0;
-      sm.sc[g][lane + 64] = p1;
+      dst = isv ? wm.vs : wm.ks;
+      mul = isv ? 32.0f : kfac;
     }
-    if (lane == 0) {
-      sm.m[g] = mnew;
-      sm.l[g] = alpha * sm.l[g] + lsum;
-      sm.alpha[g] = alpha;
-      sm.beta[g] = beta;
-    }
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      *reinterpret_cast<float4*>(dst + base + i) =
+          make_float4(f[i] * mul, f[i + 1] * mul, f[i + 2] * mul, f[i + 3] * mul);
+  } else {                                // 8 fp16 values
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = fp16_bits_to_float((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    const int base = (grp - 16) * 8;
+    float* dst = isv ? wm.vz : wm.kz;
+    const float mul = isv ? 1.0f : kzfac;
+#pragma unroll
+    for (int i = 0; i < 8; i += 4)
+      *reinterpret_cast<float4*>(dst + base + i) =
+          make_float4(f[i] * mul, f[i + 1] * mul, f[i + 2] * mul, f[i + 3] * mul);
   }
 }
 
-__global__ void __launch_bounds__(kDThreads)
-decode_kernel(const __half* __restrict__ q, int hq, int hkv, const uint8_t* __restrict__ pool,
-              long long num_blocks, const int32_t* __restrict__ block_table, int max_blocks,
-              const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
-              const __half* __restrict__ staging_v, float sm_scale,
-              float* __restrict__ partials) {
-  __shared__ DecSmem sm;
+__global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
+                    const uint8_t* __restrict__ pool, long long num_blocks,
+                    const int32_t* __restrict__ block_table, int max_blocks,
+                    const int32_t* __restrict__ seq_lens, float sm_scale,
+                    float* __restrict__ partials) {
+  __shared__ TileSmem sm;
   const int split = blockIdx.x, nsplit = gridDim.x;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  const int g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = hq / hkv;
+  const int h0 = g * group + hg * kHeadGroup;                 // first query head served
+  const int nh = min(kHeadGroup, group - hg * kHeadGroup);    // heads served (1..8)
   const int len = seq_lens[b];
   bool bad = len < 0 || (len >> 7) > max_blocks;
   const int n_full = bad ? 0 : (len >> 7);
-  const int n_stage = bad ? 0 : (len & (kT - 1));
   const int chunk = (n_full + nsplit - 1) / nsplit;
   const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
-  const bool do_stage = (split == nsplit - 1) && n_stage > 0;
-  const float scale2 = sm_scale * kLog2e;
 
-  // queries: raw and rotated (128-point FWHT in LDS, scaled by 2^-3.5)
-  for (int idx = tid; idx < group * kD; idx += kDThreads) {
+  // ---- rotated queries in LDS, and a power-of-two prescale for the fp16 query operand
+  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads) {
     const int gg = idx >> 7, j = idx & (kD - 1);
-    const float v = __half2float(q[((long long)b * hq + g * group + gg) * kD + j]);
-    sm.qraw[gg][j] = v;
-    sm.qrot[gg][j] = v;
-  }
-  if (tid < group) {
-    sm.m[tid] = -INFINITY;
-    sm.l[tid] = 0.0f;
+    sm.qrot[gg][j] = gg < nh ? __half2float(q[((long long)b * hq + h0 + gg) * kD + j]) : 0.0f;
   }
   __syncthreads();
   for (int h = 1; h < kD; h <<= 1) {
-    for (int p = tid; p < group * (kD / 2); p += kDThreads) {
-      const int gg = p / (kD / 2), pi = p % (kD / 2);
+    for (int p = tid; p < kHeadGroup * (kD / 2); p += kTThreads) {
+      const int gg = p >> 6, pi = p & 63;
       const int i = (pi / h) * 2 * h + (pi % h);
       const float a = sm.qrot[gg][i], c = sm.qrot[gg][i + h];
       sm.qrot[gg][i] = a + c;
@@ -115,96 +175,291 @@ decode_kernel(const __half* __restrict__ q, int hq, int hkv, const uint8_t* __re
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < group * kD; idx += kDThreads)
-    sm.qrot[idx >> 7][idx & (kD - 1)] *= 0.08838834764831845f;
+  float qmax = 0.0f;
+  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads) {
+    const float v = sm.qrot[idx >> 7][idx & (kD - 1)] * 0.08838834764831845f;
+    sm.qrot[idx >> 7][idx & (kD - 1)] = v;
+    qmax = fmaxf(qmax, fabsf(v));
+  }
+  qmax = wave_max(qmax);
+  if (lane == 0) sm.red[wave] = qmax;
+  __syncthreads();
+  qmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+  // |q~ * pq| <= qmax * 448 * pq <= 2^14 keeps the hi part finite in fp16
+  int qe = 0;
+  frexpf(fmaxf(qmax, 1e-30f) * 448.0f, &qe);
+  const float pq = ldexpf(1.0f, 14 - qe);
+  const float scale2 = sm_scale * kLog2e;
+  const float kfac = scale2 * 16.0f / pq;          // undoes the code / 16 encoding and pq
+  const float kzfac = scale2;
 
-  const int t = tid >> 1, hf = tid & 1;        // score mapping
-  const int jj = tid & (kD - 1), gh = tid >> 7;  // value mapping: heads gh, gh + 2, ...
-  float orot[kMaxGroup / 2], oraw[kMaxGroup / 2];
+  // lane roles: m / s for operand rows and k groups, n for columns
+  const int n = lane & 15, s = lane >> 4;
+  const int gq = n & 7;                              // head of this column / row
+  const bool colv = gq < nh;                         // column carries a real head
+  const bool colhi = n < 8;
+  WaveMeta& wm = sm.wm[wave];
+
+  // running state: score-lane view (column n) and output-row view (rows 4 s + i)
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v oacc[8];
 #pragma unroll
-  for (int k = 0; k < kMaxGroup / 2; ++k) orot[k] = oraw[k] = 0.0f;
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
-  for (int i = i0; i < i1; ++i) {
-    const long long blk = block_table[(long long)b * max_blocks + i];
-    if (blk < 0 || blk >= num_blocks) {
-      bad = true;
-      break;
+  const int ntile = i1 - i0;
+  int it = wave;
+  // Tile pipeline without extra registers: the next tile's key codes (and metadata) are
+  // loaded into the key registers once the score products have consumed them, and the next
+  // value codes into the value registers once the output products have.
+  auto block_of = [&](int idx) -> long long {
+    return block_table[(long long)b * max_blocks + i0 + idx];
+  };
+  TileRegs cur;
+  const uint8_t* rec = nullptr;
+  if (it < ntile) {
+    const long long blk = block_of(it);
+    if (blk < 0 || blk >= num_blocks) bad = true;
+    else {
+      rec = pool + (blk * hkv + g) * (long long)kTileBytes;
+      load_tile(rec, lane, cur);
     }
-    const uint8_t* rec = pool + (blk * hkv + g) * (long long)kTileBytes;
-    __syncthreads();   // previous tile fully consumed (also orders the query setup)
-    if (tid < kD) {
-      sm.kc[tid] = e4m3_to_float(rec[kKMetaOff + kCRel + tid]);
-      sm.ks[tid] = e4m3_to_float(rec[kKMetaOff + kSRel + tid]);
-      sm.kz[tid] = fp16_bits_to_float(reinterpret_cast<const uint16_t*>(rec + kKMetaOff + kZRel)[tid]);
-      sm.vc[tid] = e4m3_to_float(rec[kVMetaOff + kCRel + tid]);
-      sm.vs[tid] = e4m3_to_float(rec[kVMetaOff + kSRel + tid]);
-      sm.vz[tid] = fp16_bits_to_float(reinterpret_cast<const uint16_t*>(rec + kVMetaOff + kZRel)[tid]);
+  }
+  while (it < ntile && !bad) {
+    const int nx = it + kWaves;
+    const uint8_t* nrec = nullptr;
+    if (nx < ntile) {
+      const long long blk = block_of(nx);
+      if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
+      else bad = true;                             // finishes this tile, then stops
     }
+    decode_meta(cur.meta, lane, wm, kfac, kzfac);   // wave-local LDS tables (in-order LDS)
+
+    // ---- query operand for this tile: q~ = q_rot * c-hat^K, hi (cols 0-7) or lo (8-15)
+    half8 qb[4];
+    float asum = 0.0f;
     {
-      const uint4 w4 = reinterpret_cast<const uint4*>(rec + kVCodesOff)[tid];
-      const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+      const float* qr = sm.qrot[gq];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int w = 4 * tid + e;
-        const int kb = w >> 8, ln = (w >> 2) & 63, d = w & 3;
-        const int s = ln >> 4, n = ln & 15;
-        const int tb = 32 * kb + 16 * (d >> 1) + 4 * s + ((d & 1) << 1);
+      for (int c = 0; c < 4; ++c) {
+        float vals[8];
 #pragma unroll
-        for (int odd = 0; odd < 2; ++odd)
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb)
-            sm.cv[tb + odd][16 * nb + n] = (wv[e] >> (2 * nb + 16 * odd)) & 3u;
+        for (int e = 0; e < 8; ++e) {
+          const int qn = (e >> 1) | ((e & 1) << 2);         // nibble order 0,4,1,5,2,6,3,7
+          const int ch = 32 * s + 8 * c + qn;
+          const float qt = qr[ch] * wm.kc[ch];
+          asum += qt;
+          float hi, lo;
+          split_hl(qt * pq, hi, lo);
+          vals[e] = colv ? (colhi ? hi : lo) : 0.0f;
+        }
+        qb[c] = as_h8(pack_h2(vals[0], vals[1]), pack_h2(vals[2], vals[3]),
+                      pack_h2(vals[4], vals[5]), pack_h2(vals[6], vals[7]));
       }
     }
-    __syncthreads();
-    for (int idx = tid; idx < group * kD; idx += kDThreads)
-      sm.qt[idx >> 7][idx & (kD - 1)] = sm.qrot[idx >> 7][idx & (kD - 1)] * sm.kc[idx & (kD - 1)];
-    __syncthreads();
-    {
-      const int lane = tid & 63, wave = tid >> 6;
-      for (int gg = wave; gg < group; gg += 4) {
-        const float a = wave_sum(sm.qt[gg][lane] + sm.qt[gg][lane + 64]);
-        if (lane == 0) sm.asum[gg] = a;
+    asum += __shfl_xor(asum, 16);
+    asum += __shfl_xor(asum, 32);                 // sum over all 128 channels of column n
+
+    // ---- scores: 8 token blocks x 4 channel blocks
+    float4v sc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // nibble q of the word -> mantissa bits 6..9 of a half under exponent 0x3C00:
+        // the half is 1 + code / 16 (normal, exact); slots (q, q + 4) share a word
+        const uint32_t w = w4[c];
+        const half8 a = as_h8(((w << 6) & 0x03C003C0u) | 0x3C003C00u,
+                              ((w << 2) & 0x03C003C0u) | 0x3C003C00u,
+                              ((w >> 2) & 0x03C003C0u) | 0x3C003C00u,
+                              ((w >> 6) & 0x03C003C0u) | 0x3C003C00u);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], acc, 0, 0, 0);
+      }
+      sc[mb] = acc;
+    }
+    if (nrec != nullptr) {
+      const int m = lane & 15;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        cur.kw[mb] = *reinterpret_cast<const uint4*>(nrec + kKCodesOff + (16 * mb + m) * 64 + 16 * s);
+      cur.meta = *reinterpret_cast<const uint4*>(nrec + kKMetaOff + lane * 16);
+    }
+    // hi + lo partial scores, then the full log2-domain score per token:
+    // D = sum_j (1 + code_j / 16) q~_j pq, so <q~, code> = 16 (D / pq - sum_j q~_j)
+    const float c1 = pq * asum;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * mb + 4 * s + i;
+        const float d = sc[mb][i] + dpp_ror8(sc[mb][i]);
+        const float v = fmaf(wm.ks[t], d - c1, wm.kz[t] * asum);
+        sc[mb][i] = v;
+        tmax = fmaxf(tmax, v);
       }
     }
-    // key codes of token t, channels 64 hf .. 64 hf + 63
-    float kcode[64];
-    {
-      const uint4* kp = reinterpret_cast<const uint4*>(rec + kKCodesOff + t * 64 + hf * 32);
-      const uint4 a = kp[0], c = kp[1];
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - mnew);      // m_run = -inf on the first tile -> 0
+    float psum = 0.0f, beta = 0.0f, wsum = 0.0f;
+    // probabilities -> operand rows: hi(p s-hat^V 2^5) on rows 0-7, lo on rows 8-15
+    half8 wa[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+    for (int kb = 0; kb < 4; ++kb) {
+      float vals[8];
 #pragma unroll
-        for (int qn = 0; qn < 8; ++qn) kcode[8 * k + qn] = (float)((w[k] >> (4 * qn)) & 15u);
+      for (int e = 0; e < 8; ++e) {
+        const int mb = 2 * kb + (e >> 2), i = e & 3;
+        const int t = 16 * mb + 4 * s + i;
+        const float p = exp2f(sc[mb][i] - mnew);
+        psum += p;
+        beta = fmaf(p, wm.vz[t], beta);
+        const float wv = p * wm.vs[t];
+        wsum += wv;
+        float hi, lo;
+        split_hl(wv, hi, lo);
+        vals[e] = colv ? (colhi ? hi : lo) : 0.0f;
+      }
+      wa[kb] = as_h8(pack_h2(vals[0], vals[1]), pack_h2(vals[2], vals[3]),
+                     pack_h2(vals[4], vals[5]), pack_h2(vals[6], vals[7]));
     }
-    __syncthreads();
-    for (int gg = 0; gg < group; ++gg) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 64; ++e) dot = fmaf(sm.qt[gg][hf * 64 + e], kcode[e], dot);
-      dot += __shfl_xor(dot, 1);
-      if (hf == 0) sm.sc[gg][t] = (sm.ks[t] * dot + sm.kz[t] * sm.asum[gg]) * scale2;
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    beta += __shfl_xor(beta, 16);
+    beta += __shfl_xor(beta, 32);
+    wsum += __shfl_xor(wsum, 16);
+    wsum += __shfl_xor(wsum, 32);
+    // output rows get D / 8 per tile: D = sum_t W_t (1 + code / 4), W = 32 p s-hat^V, so
+    // sum_t p s-hat^V code = D / 8 - 4 sum_t p s-hat^V = D / 8 - wsum / 8
+    beta = fmaf(-0.125f, wsum, beta);
+    l_run = fmaf(alpha, l_run, psum);
+    m_run = mnew;
+    if (s == 0) {
+      wm.alpha[n] = alpha;
+      wm.beta[n] = colhi ? beta : 0.0f;           // the zero-point term enters the hi row once
     }
-    __syncthreads();
-    softmax_update(sm, group, kT, true);
-    __syncthreads();
+
+    // ---- output: 4 token blocks x 8 channel blocks
+    float4v po[8];
 #pragma unroll
-    for (int k = 0; k < kMaxGroup / 2; ++k) {
-      const int gg = gh + 2 * k;
-      if (gg < group) {
-        float acc = 0.0f;
-        for (int tt = 0; tt < kT; ++tt) acc = fmaf(sm.sc[gg][tt], (float)sm.cv[tt][jj], acc);
-        orot[k] = sm.alpha[gg] * orot[k] + sm.vc[jj] * (acc + sm.beta[gg]);
-        oraw[k] *= sm.alpha[gg];
+    for (int nb = 0; nb < 8; ++nb) po[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
+        // the half is 1 + code / 4 (normal, exact)
+        uint32_t f[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
+          f[d] = (x & 0x03000300u) | 0x3C003C00u;
+        }
+        const half8 bv = as_h8(f[0], f[1], f[2], f[3]);
+        po[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], bv, po[nb], 0, 0, 0);
+      }
+    }
+    if (nrec != nullptr) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        cur.vw[kb] = *reinterpret_cast<const uint4*>(nrec + kVCodesOff + kb * 1024 + lane * 16);
+    }
+    // o~ rows 4 s + i: alpha and beta of their head, c-hat^V of column 16 nb + n
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * s + i;
+      const float ar = wm.alpha[row & 7];
+      const float br = wm.beta[row];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const float cv = wm.vc[16 * nb + n];
+        oacc[nb][i] = fmaf(ar, oacc[nb][i], cv * fmaf(po[nb][i], 0.125f, br));
+      }
+    }
+    it = nx;
+  }
+
+  // ---- combine the waves' states in LDS and write one partial per (split, head)
+  // (score lanes s == 0 hold m, l of column n; rows 4 s + i hold o~ hi (s < 2) and lo parts)
+  __syncthreads();
+  if (s == 0 && colhi) {
+    sm.comb_m[wave][n] = m_run;
+    sm.comb_l[wave][n] = l_run;
+  }
+  {
+    // add the lo rows (lanes 32..63) into the hi rows (lanes 0..31)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float other = __shfl_xor(oacc[nb][i], 32);
+        if (s < 2) sm.comb_o[wave][4 * s + i][16 * nb + n] = oacc[nb][i] + other;
       }
     }
   }
+  __syncthreads();
+  const int wbad = __syncthreads_or(bad ? 1 : 0);
+  for (int idx = tid; idx < nh * kD; idx += kTThreads) {
+    const int gg = idx >> 7, j = idx & (kD - 1);
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm.comb_m[w][gg]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(sm.comb_m[w][gg] - mm);
+        ll = fmaf(f, sm.comb_l[w][gg], ll);
+        oo = fmaf(f, sm.comb_o[w][gg][j], oo);
+      }
+    }
+    float* p = partials + (((long long)b * hq + h0 + gg) * nsplit + split) * kPartialFloats;
+    if (j == 0) {
+      p[0] = wbad ? NAN : mm;
+      p[1] = wbad ? NAN : ll;
+    }
+    p[2 + j] = oo;
+  }
+}
 
-  if (do_stage && !bad) {
-    __syncthreads();
-    const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
-    const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
+// grid (hkv, batch), 256 threads: staging tokens (exact fp32), log-sum-exp merge of the tile
+// splits, o~ H + o_raw, / l, for the group of query heads of one KV head.
+constexpr int kMThreads = 256;
+
+struct MergeSmem {
+  float qraw[kMaxGroup][kD];
+  float sc[kMaxGroup][kT];
+  float ot[kMaxGroup][kD];
+  float msplit[kMaxGroup], lsum[kMaxGroup];
+};
+
+__global__ void __launch_bounds__(kMThreads)
+decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_blocks,
+                    const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
+                    const __half* __restrict__ staging_v, float sm_scale,
+                    const float* __restrict__ partials, int nsplit, float* __restrict__ out) {
+  __shared__ MergeSmem sm;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int group = hq / hkv;
+  const int len = seq_lens[b];
+  const bool bad = len < 0 || (len >> 7) > max_blocks;
+  const int n_stage = bad ? 0 : (len & (kT - 1));
+  const float scale2 = sm_scale * kLog2e;
+  const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
+  const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
+
+  for (int idx = tid; idx < group * kD; idx += kMThreads)
+    sm.qraw[idx >> 7][idx & (kD - 1)] =
+        __half2float(q[((long long)b * hq + g * group) * kD + idx]);
+  __syncthreads();
+  // staging scores: thread (t, half) over 64 channels, pair-summed
+  if (n_stage > 0) {
+    const int t = tid >> 1, hf = tid & 1;
     float kr[64];
     if (t < n_stage) {
       const uint4* kp = reinterpret_cast<const uint4*>(sk + t * kD + hf * 64);
@@ -219,82 +474,78 @@ decode_kernel(const __half* __restrict__ q, int hq, int hkv, const uint8_t* __re
 #pragma unroll
       for (int e = 0; e < 64; ++e) dot = fmaf(sm.qraw[gg][hf * 64 + e], kr[e], dot);
       dot += __shfl_xor(dot, 1);
-      if (hf == 0) sm.sc[gg][t] = dot * scale2;
+      if (hf == 0) sm.sc[gg][t] = t < n_stage ? dot * scale2 : -INFINITY;
     }
-    __syncthreads();
-    softmax_update(sm, group, n_stage, false);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kMaxGroup / 2; ++k) {
-      const int gg = gh + 2 * k;
-      if (gg < group) {
-        float acc = 0.0f;
-        for (int tt = 0; tt < n_stage; ++tt)
-          acc = fmaf(sm.sc[gg][tt], __half2float(sv[tt * kD + jj]), acc);
-        oraw[k] = sm.alpha[gg] * oraw[k] + acc;
-        orot[k] *= sm.alpha[gg];
+  }
+  __syncthreads();
+  // per head: global max over split maxima and staging scores, sum, probabilities
+  for (int gg = wave; gg < group; gg += kMThreads / 64) {
+    const float* pp = partials + ((long long)b * hq + g * group + gg) * nsplit * kPartialFloats;
+    float mm = -INFINITY;
+    bool nan = false;
+    for (int sp = lane; sp < nsplit; sp += 64) {
+      const float v = pp[sp * kPartialFloats];
+      nan |= (v != v);
+      mm = fmaxf(mm, v);
+    }
+    const float s0 = (n_stage > 0) ? sm.sc[gg][lane] : -INFINITY;
+    const float s1 = (n_stage > 0) ? sm.sc[gg][lane + 64] : -INFINITY;
+    mm = fmaxf(mm, fmaxf(s0, s1));
+    mm = wave_max(mm);
+    const int anynan = __any(nan);
+    float ls = 0.0f;
+    if (mm != -INFINITY) {
+      for (int sp = lane; sp < nsplit; sp += 64) {
+        const float v = pp[sp * kPartialFloats];
+        ls = fmaf(exp2f(v - mm), pp[sp * kPartialFloats + 1], ls);
       }
+      const float p0 = exp2f(s0 - mm), p1 = exp2f(s1 - mm);
+      if (n_stage > 0) {
+        sm.sc[gg][lane] = p0;
+        sm.sc[gg][lane + 64] = p1;
+      }
+      ls += p0 + p1;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) {
+      sm.msplit[gg] = (anynan || bad) ? NAN : mm;
+      sm.lsum[gg] = ls;
     }
   }
-
   __syncthreads();
-  // partial of (b, head, split): m, l, o~[128], o_raw[128]
-  for (int gg = tid; gg < group; gg += kDThreads) {
-    float* p = partials + (((long long)b * hq + g * group + gg) * nsplit + split) * kPartialFloats;
-    p[0] = bad ? NAN : sm.m[gg];
-    p[1] = bad ? NAN : sm.l[gg];
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxGroup / 2; ++k) {
-    const int gg = gh + 2 * k;
-    if (gg < group) {
-      float* p = partials + (((long long)b * hq + g * group + gg) * nsplit + split) * kPartialFloats;
-      p[2 + jj] = orot[k];
-      p[2 + kD + jj] = oraw[k];
+  // merged rotated output o~ and raw staging output, per (head, channel)
+  for (int idx = tid; idx < group * kD; idx += kMThreads) {
+    const int gg = idx >> 7, j = idx & (kD - 1);
+    const float* pp = partials + ((long long)b * hq + g * group + gg) * nsplit * kPartialFloats;
+    const float mm = sm.msplit[gg];
+    float ot = 0.0f;
+    if (mm == mm && mm != -INFINITY) {
+      for (int sp = 0; sp < nsplit; ++sp)
+        ot = fmaf(exp2f(pp[sp * kPartialFloats] - mm), pp[sp * kPartialFloats + 2 + j], ot);
     }
+    sm.ot[gg][j] = ot;
   }
-}
-
-// grid (hq, batch), 128 threads: log-sum-exp merge of the splits, o~ H + o_raw, / l.
-__global__ void __launch_bounds__(kD)
-merge_kernel(const float* __restrict__ partials, int hq, int nsplit, float* __restrict__ out) {
-  __shared__ float buf[kD];
-  const int h = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
-  const float* base = partials + ((long long)b * hq + h) * nsplit * kPartialFloats;
-  float mmax = -INFINITY;
-  bool nan = false;
-  for (int s = 0; s < nsplit; ++s) {
-    const float m = base[s * kPartialFloats];
-    nan |= (m != m);
-    mmax = fmaxf(mmax, m);
-  }
-  float lsum = 0.0f, orot = 0.0f, oraw = 0.0f;
-  if (mmax != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* p = base + s * kPartialFloats;
-      const float w = exp2f(p[0] - mmax);
-      lsum = fmaf(w, p[1], lsum);
-      orot = fmaf(w, p[2 + j], orot);
-      oraw = fmaf(w, p[2 + kD + j], oraw);
-    }
-  }
-  buf[j] = orot;
   __syncthreads();
-  for (int hh = 1; hh < kD; hh <<= 1) {
-    float v = 0.0f;
-    const float mine = buf[j], other = buf[j ^ hh];
-    v = (j & hh) ? (other - mine) : (mine + other);
-    __syncthreads();
-    buf[j] = v;
+  for (int h = 1; h < kD; h <<= 1) {
+    for (int p = tid; p < group * (kD / 2); p += kMThreads) {
+      const int gg = p >> 6, pi = p & 63;
+      const int i = (pi / h) * 2 * h + (pi % h);
+      const float a = sm.ot[gg][i], c = sm.ot[gg][i + h];
+      sm.ot[gg][i] = a + c;
+      sm.ot[gg][i + h] = a - c;
+    }
     __syncthreads();
   }
-  float o = 0.0f;
-  if (nan) {
-    o = NAN;
-  } else if (lsum > 0.0f) {
-    o = (buf[j] * 0.08838834764831845f + oraw) / lsum;
+  for (int idx = tid; idx < group * kD; idx += kMThreads) {
+    const int gg = idx >> 7, j = idx & (kD - 1);
+    float oraw = 0.0f;
+    for (int t = 0; t < n_stage; ++t) oraw = fmaf(sm.sc[gg][t], __half2float(sv[t * kD + j]), oraw);
+    const float mm = sm.msplit[gg], ls = sm.lsum[gg];
+    float o = 0.0f;
+    if (mm != mm) o = NAN;
+    else if (ls > 0.0f) o = (sm.ot[gg][j] * 0.08838834764831845f + oraw) / ls;
+    out[((long long)b * hq + g * group + gg) * kD + j] = o;
   }
-  out[((long long)b * hq + h) * kD + j] = o;
 }
 
 }  // namespace
@@ -302,7 +553,8 @@ merge_kernel(const float* __restrict__ partials, int hq, int nsplit, float* __re
 int decode_splits(int batch, int hkv, int max_blocks) {
   const long long pairs = (long long)batch * hkv;
   long long s = (1024 + pairs - 1) / (pairs > 0 ? pairs : 1);
-  if (s > max_blocks) s = max_blocks;
+  const long long per_wave = (max_blocks + kWaves - 1) / kWaves;   // >= one tile per wave
+  if (s > per_wave) s = per_wave;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   return (int)s;
@@ -313,12 +565,14 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
                          int splits, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3(splits, hkv, batch), dim3(kDThreads), 0, stream, q, hq,
-                     hkv, pool, num_blocks, block_table, max_blocks, seq_lens, staging_k,
-                     staging_v, sm_scale, partials);
+  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  hipLaunchKernelGGL(decode_tiles_kernel, dim3(splits, hkv * ngroups, batch), dim3(kTThreads),
+                     0, stream, q, hq, hkv, pool, num_blocks, block_table, max_blocks, seq_lens,
+                     sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(hq, batch), dim3(kD), 0, stream, partials, hq, splits,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(hkv, batch), dim3(kMThreads), 0, stream, q, hq,
+                     hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, splits,
                      out);
   return hipGetLastError();
 }

@@ -7,8 +7,8 @@
 
 namespace kvarn {
 
-// Floats per (sequence, query head, split) partial: m, l, rotated output, raw output.
-constexpr int kPartialFloats = 2 + 2 * 128;
+// Floats per (sequence, query head, split) partial: m, l, rotated output.
+constexpr int kPartialFloats = 2 + 128;
 constexpr int kMaxGroup = 16;
 
 hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
