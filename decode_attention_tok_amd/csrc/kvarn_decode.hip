@@ -71,15 +71,29 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// (x & mask) | c in one v_and_or_b32: mask in a VGPR and c in an SGPR, since a gfx9 VOP3
+// instruction cannot carry two literal constants (the compiler otherwise emits and + or).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_v, uint32_t c_s) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask_v), "s"(c_s));
+  return r;
+}
+
 __device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   uint4 u = make_uint4(a, b, c, d);
   return __builtin_bit_cast(half8, u);
 }
 
-// hi / lo fp16 split of x (x == hi + lo to about 2^-22 relative when normal)
-__device__ __forceinline__ void split_hl(float x, float& hi, float& lo) {
-  hi = (float)(__fp16)x;
-  lo = x - hi;
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// fp16 hi / lo parts of a pair (a, b), both rounded to nearest: a == hi + lo to about 2^-22
+// relative while normal. Returns the packed hi pair or the packed lo pair.
+__device__ __forceinline__ uint32_t split_pair(float a, float b, bool want_hi) {
+  const half2v h = __builtin_convertvector((float2v){a, b}, half2v);
+  const float2v hb = __builtin_convertvector(h, float2v);
+  const half2v l = __builtin_convertvector((float2v){a - hb[0], b - hb[1]}, half2v);
+  return want_hi ? __builtin_bit_cast(uint32_t, h) : __builtin_bit_cast(uint32_t, l);
 }
 
 struct TileRegs {
@@ -101,40 +115,33 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int l
 
 // Scatter one lane's 16 metadata bytes into the wave's fp32 tables. Lanes 0-7: c-hat^K,
 // 8-15: s-hat^K, 16-31: z-hat^K, 32-39: c-hat^V, 40-47: s-hat^V, 48-63: z-hat^V.
+// FP8 bytes go through the hardware E4M3 conversion (exact for every finite code).
 __device__ __forceinline__ void decode_meta(const uint4 mw, int lane, WaveMeta& wm,
                                             float kfac, float kzfac) {
   const uint32_t w[4] = {mw.x, mw.y, mw.z, mw.w};
   const int grp = lane & 31;
   const bool isv = lane >= 32;
   if (grp < 16) {                         // 16 FP8 values
-    float f[16];
+    const float mul = grp < 8 ? 1.0f : (isv ? 32.0f : kfac);
+    float* dst = grp < 8 ? (isv ? wm.vc : wm.kc) : (isv ? wm.vs : wm.ks);
+    dst += (grp & 7) * 16;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] = e4m3_to_float((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-    const int base = (grp & 7) * 16;
-    float* dst;
-    float mul;
-    if (grp < 8) {
-      dst = isv ? wm.vc : wm.kc;
-      mul = 1.0f;
-    } else {
-      dst = isv ? wm.vs : wm.ks;
-      mul = isv ? 32.0f : kfac;
+    for (int d = 0; d < 4; ++d) {
+      const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
+      const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
+      *reinterpret_cast<float4*>(dst + 4 * d) =
+          make_float4(lo[0] * mul, lo[1] * mul, hi[0] * mul, hi[1] * mul);
     }
-#pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      *reinterpret_cast<float4*>(dst + base + i) =
-          make_float4(f[i] * mul, f[i + 1] * mul, f[i + 2] * mul, f[i + 3] * mul);
   } else {                                // 8 fp16 values
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = fp16_bits_to_float((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    const int base = (grp - 16) * 8;
-    float* dst = isv ? wm.vz : wm.kz;
     const float mul = isv ? 1.0f : kzfac;
+    float* dst = (isv ? wm.vz : wm.kz) + (grp - 16) * 8;
 #pragma unroll
-    for (int i = 0; i < 8; i += 4)
-      *reinterpret_cast<float4*>(dst + base + i) =
-          make_float4(f[i] * mul, f[i + 1] * mul, f[i + 2] * mul, f[i + 3] * mul);
+    for (int d = 0; d < 4; d += 2) {
+      const float2v a = __builtin_convertvector(__builtin_bit_cast(half2v, w[d]), float2v);
+      const float2v b = __builtin_convertvector(__builtin_bit_cast(half2v, w[d + 1]), float2v);
+      *reinterpret_cast<float4*>(dst + 2 * d) =
+          make_float4(a[0] * mul, a[1] * mul, b[0] * mul, b[1] * mul);
+    }
   }
 }
 
@@ -158,6 +165,25 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const int n_full = bad ? 0 : (len >> 7);
   const int chunk = (n_full + nsplit - 1) / nsplit;
   const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  // this wave's tiles: i0 + wave + 4 j, j < nw. Lane j holds the block id of tile j (ids are
+  // fetched 64 at a time with one vector load), tile j's id is read back as a scalar.
+  const int ntile = i1 - i0;
+  const int nw = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave;
+  auto fetch_ids = [&](int j0) -> int {
+    const int j = j0 + lane;
+    return j < nw ? bt_row[kWaves * j] : 0;
+  };
+  int ids = fetch_ids(0);
+  auto block_of = [&](int j) -> long long {
+    return (long long)__builtin_amdgcn_readlane(ids, j & 63);
+  };
+  TileRegs cur;
+  if (nw > 0) {
+    const long long blk = block_of(0);
+    if (blk < 0 || blk >= num_blocks) bad = true;
+    else load_tile(pool + (blk * hkv + g) * (long long)kTileBytes, lane, cur);
+  }
 
   // ---- rotated queries in LDS, and a power-of-two prescale for the fp16 query operand
   for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads) {
@@ -191,7 +217,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const float pq = ldexpf(1.0f, 14 - qe);
   const float scale2 = sm_scale * kLog2e;
   const float kfac = scale2 * 16.0f / pq;          // undoes the code / 16 encoding and pq
-  const float kzfac = scale2;
+  const float kzfac = scale2 / pq;                 // multiplies pq * sum_j q~_j
+  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads)
+    sm.qrot[idx >> 7][idx & (kD - 1)] *= pq;
+  __syncthreads();
 
   // lane roles: m / s for operand rows and k groups, n for columns
   const int n = lane & 15, s = lane >> 4;
@@ -199,6 +228,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const bool colv = gq < nh;                         // column carries a real head
   const bool colhi = n < 8;
   WaveMeta& wm = sm.wm[wave];
+  // per-lane copies of the code masks (kept in VGPRs) and the wave-uniform exponent word
+  uint32_t kmask = 0x03C003C0u, vmask = 0x03000300u;
+  asm volatile("" : "+v"(kmask), "+v"(vmask));
+  const uint32_t one16 = __builtin_amdgcn_readfirstlane(0x3C003C00u);
 
   // running state: score-lane view (column n) and output-row view (rows 4 s + i)
   float m_run = -INFINITY, l_run = 0.0f;
@@ -206,58 +239,41 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
-  const int ntile = i1 - i0;
-  int it = wave;
   // Tile pipeline without extra registers: the next tile's key codes (and metadata) are
   // loaded into the key registers once the score products have consumed them, and the next
   // value codes into the value registers once the output products have.
-  auto block_of = [&](int idx) -> long long {
-    return block_table[(long long)b * max_blocks + i0 + idx];
-  };
-  TileRegs cur;
-  const uint8_t* rec = nullptr;
-  if (it < ntile) {
-    const long long blk = block_of(it);
-    if (blk < 0 || blk >= num_blocks) bad = true;
-    else {
-      rec = pool + (blk * hkv + g) * (long long)kTileBytes;
-      load_tile(rec, lane, cur);
-    }
-  }
-  while (it < ntile && !bad) {
-    const int nx = it + kWaves;
+  for (int j = 0; j < nw && !bad; ++j) {
     const uint8_t* nrec = nullptr;
-    if (nx < ntile) {
-      const long long blk = block_of(nx);
+    if (j + 1 < nw) {
+      if (((j + 1) & 63) == 0) ids = fetch_ids(j + 1);
+      const long long blk = block_of(j + 1);
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
       else bad = true;                             // finishes this tile, then stops
     }
     decode_meta(cur.meta, lane, wm, kfac, kzfac);   // wave-local LDS tables (in-order LDS)
 
-    // ---- query operand for this tile: q~ = q_rot * c-hat^K, hi (cols 0-7) or lo (8-15)
+    // ---- query operand for this tile: pq q~ = pq q_rot * c-hat^K, hi (cols 0-7) or lo (8-15)
+    // element e of channel block c is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
     half8 qb[4];
-    float asum = 0.0f;
+    float asum = 0.0f;                            // pq * sum_j q~_j over this lane's channels
     {
-      const float* qr = sm.qrot[gq];
+      const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[gq] + 32 * s);
+      const float4* kc4 = reinterpret_cast<const float4*>(wm.kc + 32 * s);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        float vals[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int qn = (e >> 1) | ((e & 1) << 2);         // nibble order 0,4,1,5,2,6,3,7
-          const int ch = 32 * s + 8 * c + qn;
-          const float qt = qr[ch] * wm.kc[ch];
-          asum += qt;
-          float hi, lo;
-          split_hl(qt * pq, hi, lo);
-          vals[e] = colv ? (colhi ? hi : lo) : 0.0f;
-        }
-        qb[c] = as_h8(pack_h2(vals[0], vals[1]), pack_h2(vals[2], vals[3]),
-                      pack_h2(vals[4], vals[5]), pack_h2(vals[6], vals[7]));
+        const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
+        const float4 ka = kc4[2 * c], kk = kc4[2 * c + 1];
+        const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
+        const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
+        asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
+        uint32_t u0 = split_pair(x0, x4, colhi), u1 = split_pair(x1, x5, colhi);
+        uint32_t u2 = split_pair(x2, x6, colhi), u3 = split_pair(x3, x7, colhi);
+        if (!colv) u0 = u1 = u2 = u3 = 0u;
+        qb[c] = as_h8(u0, u1, u2, u3);
       }
     }
     asum += __shfl_xor(asum, 16);
-    asum += __shfl_xor(asum, 32);                 // sum over all 128 channels of column n
+    asum += __shfl_xor(asum, 32);                 // over all 128 channels of column n
 
     // ---- scores: 8 token blocks x 4 channel blocks
     float4v sc[8];
@@ -270,10 +286,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
         // nibble q of the word -> mantissa bits 6..9 of a half under exponent 0x3C00:
         // the half is 1 + code / 16 (normal, exact); slots (q, q + 4) share a word
         const uint32_t w = w4[c];
-        const half8 a = as_h8(((w << 6) & 0x03C003C0u) | 0x3C003C00u,
-                              ((w << 2) & 0x03C003C0u) | 0x3C003C00u,
-                              ((w >> 2) & 0x03C003C0u) | 0x3C003C00u,
-                              ((w >> 6) & 0x03C003C0u) | 0x3C003C00u);
+        const half8 a = as_h8(and_or(w << 6, kmask, one16), and_or(w << 2, kmask, one16),
+                              and_or(w >> 2, kmask, one16), and_or(w >> 6, kmask, one16));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], acc, 0, 0, 0);
       }
       sc[mb] = acc;
@@ -286,16 +300,19 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       cur.meta = *reinterpret_cast<const uint4*>(nrec + kKMetaOff + lane * 16);
     }
     // hi + lo partial scores, then the full log2-domain score per token:
-    // D = sum_j (1 + code_j / 16) q~_j pq, so <q~, code> = 16 (D / pq - sum_j q~_j)
-    const float c1 = pq * asum;
+    // D = pq sum_j (1 + code_j / 16) q~_j, so pq <q~, code> = 16 (D - asum)
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
+      const int t0 = 16 * mb + 4 * s;
+      const float4 ks4 = *reinterpret_cast<const float4*>(wm.ks + t0);
+      const float4 kz4 = *reinterpret_cast<const float4*>(wm.kz + t0);
+      const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
+      const float kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mb + 4 * s + i;
         const float d = sc[mb][i] + dpp_ror8(sc[mb][i]);
-        const float v = fmaf(wm.ks[t], d - c1, wm.kz[t] * asum);
+        const float v = fmaf(ksv[i], d - asum, kzv[i] * asum);
         sc[mb][i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -303,28 +320,32 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mnew = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - mnew);      // m_run = -inf on the first tile -> 0
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);   // 0 on the first tile
     float psum = 0.0f, beta = 0.0f, wsum = 0.0f;
-    // probabilities -> operand rows: hi(p s-hat^V 2^5) on rows 0-7, lo on rows 8-15
+    // probabilities -> operand rows: hi(p s-hat^V 32) on rows 0-7, lo on rows 8-15;
+    // element e of token block kb is token 32 kb + 16 (e / 4) + 4 s + e % 4
     half8 wa[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      float vals[8];
+      uint32_t u[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int mb = 2 * kb + (e >> 2), i = e & 3;
-        const int t = 16 * mb + 4 * s + i;
-        const float p = exp2f(sc[mb][i] - mnew);
-        psum += p;
-        beta = fmaf(p, wm.vz[t], beta);
-        const float wv = p * wm.vs[t];
-        wsum += wv;
-        float hi, lo;
-        split_hl(wv, hi, lo);
-        vals[e] = colv ? (colhi ? hi : lo) : 0.0f;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mb = 2 * kb + h2, t0 = 16 * mb + 4 * s;
+        const float4 vs4 = *reinterpret_cast<const float4*>(wm.vs + t0);
+        const float4 vz4 = *reinterpret_cast<const float4*>(wm.vz + t0);
+        const float p0 = __builtin_amdgcn_exp2f(sc[mb][0] - mnew);
+        const float p1 = __builtin_amdgcn_exp2f(sc[mb][1] - mnew);
+        const float p2 = __builtin_amdgcn_exp2f(sc[mb][2] - mnew);
+        const float p3 = __builtin_amdgcn_exp2f(sc[mb][3] - mnew);
+        psum += (p0 + p1) + (p2 + p3);
+        beta = fmaf(p0, vz4.x, fmaf(p1, vz4.y, fmaf(p2, vz4.z, fmaf(p3, vz4.w, beta))));
+        const float w0 = p0 * vs4.x, w1 = p1 * vs4.y, w2 = p2 * vs4.z, w3 = p3 * vs4.w;
+        wsum += (w0 + w1) + (w2 + w3);
+        u[2 * h2] = split_pair(w0, w1, colhi);
+        u[2 * h2 + 1] = split_pair(w2, w3, colhi);
       }
-      wa[kb] = as_h8(pack_h2(vals[0], vals[1]), pack_h2(vals[2], vals[3]),
-                     pack_h2(vals[4], vals[5]), pack_h2(vals[6], vals[7]));
+      if (!colv) u[0] = u[1] = u[2] = u[3] = 0u;
+      wa[kb] = as_h8(u[0], u[1], u[2], u[3]);
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
@@ -342,25 +363,35 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       wm.beta[n] = colhi ? beta : 0.0f;           // the zero-point term enters the hi row once
     }
 
-    // ---- output: 4 token blocks x 8 channel blocks
-    float4v po[8];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) po[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
+    // ---- output: 8 channel blocks x 4 token blocks; each channel block's accumulator is
+    // folded into o~ as soon as its 4 products are done (rows 4 s + i: alpha and beta of
+    // their head, c-hat^V of column 16 nb + n)
+    {
+      const float4 a4 = *reinterpret_cast<const float4*>(wm.alpha + ((4 * s) & 7));
+      const float4 b4 = *reinterpret_cast<const float4*>(wm.beta + 4 * s);
+      const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float br[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
-        // the half is 1 + code / 4 (normal, exact)
-        uint32_t f[4];
+        float4v po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
-          f[d] = (x & 0x03000300u) | 0x3C003C00u;
+        for (int kb = 0; kb < 4; ++kb) {
+          // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
+          // the half is 1 + code / 4 (normal, exact)
+          const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
+          uint32_t f[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
+            f[d] = and_or(x, vmask, one16);
+          }
+          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], as_h8(f[0], f[1], f[2], f[3]),
+                                                      po, 0, 0, 0);
         }
-        const half8 bv = as_h8(f[0], f[1], f[2], f[3]);
-        po[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], bv, po[nb], 0, 0, 0);
+        const float cv = wm.vc[16 * nb + n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[nb][i] = fmaf(ar[i], oacc[nb][i], cv * fmaf(po[i], 0.125f, br[i]));
       }
     }
     if (nrec != nullptr) {
@@ -368,19 +399,6 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       for (int kb = 0; kb < 4; ++kb)
         cur.vw[kb] = *reinterpret_cast<const uint4*>(nrec + kVCodesOff + kb * 1024 + lane * 16);
     }
-    // o~ rows 4 s + i: alpha and beta of their head, c-hat^V of column 16 nb + n
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * s + i;
-      const float ar = wm.alpha[row & 7];
-      const float br = wm.beta[row];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const float cv = wm.vc[16 * nb + n];
-        oacc[nb][i] = fmaf(ar, oacc[nb][i], cv * fmaf(po[nb][i], 0.125f, br));
-      }
-    }
-    it = nx;
   }
 
   // ---- combine the waves' states in LDS and write one partial per (split, head)
@@ -430,10 +448,13 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 // splits, o~ H + o_raw, / l, for the group of query heads of one KV head.
 constexpr int kMThreads = 256;
 
+constexpr int kMaxSplits = 64;
+
 struct MergeSmem {
   float qraw[kMaxGroup][kD];
   float sc[kMaxGroup][kT];
   float ot[kMaxGroup][kD];
+  float wsplit[kMaxGroup][kMaxSplits];   // exp2(m_split - m) per head and split
   float msplit[kMaxGroup], lsum[kMaxGroup];
 };
 
@@ -497,7 +518,9 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
     if (mm != -INFINITY) {
       for (int sp = lane; sp < nsplit; sp += 64) {
         const float v = pp[sp * kPartialFloats];
-        ls = fmaf(exp2f(v - mm), pp[sp * kPartialFloats + 1], ls);
+        const float wgt = exp2f(v - mm);
+        sm.wsplit[gg][sp] = wgt;
+        ls = fmaf(wgt, pp[sp * kPartialFloats + 1], ls);
       }
       const float p0 = exp2f(s0 - mm), p1 = exp2f(s1 - mm);
       if (n_stage > 0) {
@@ -520,8 +543,9 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
     const float mm = sm.msplit[gg];
     float ot = 0.0f;
     if (mm == mm && mm != -INFINITY) {
-      for (int sp = 0; sp < nsplit; ++sp)
-        ot = fmaf(exp2f(pp[sp * kPartialFloats] - mm), pp[sp * kPartialFloats + 2 + j], ot);
+      const float* col = pp + 2 + j;
+#pragma unroll 8
+      for (int sp = 0; sp < nsplit; ++sp) ot = fmaf(sm.wsplit[gg][sp], col[sp * kPartialFloats], ot);
     }
     sm.ot[gg][j] = ot;
   }
@@ -552,10 +576,11 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
 
 int decode_splits(int batch, int hkv, int max_blocks) {
   const long long pairs = (long long)batch * hkv;
-  long long s = (1024 + pairs - 1) / (pairs > 0 ? pairs : 1);
+  // about 512 workgroups (2048 waves: one round at 2 waves per SIMD on 256 CUs)
+  long long s = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
   const long long per_wave = (max_blocks + kWaves - 1) / kWaves;   // >= one tile per wave
   if (s > per_wave) s = per_wave;
-  if (s > 64) s = 64;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
 }
