@@ -52,10 +52,19 @@ def parse():
     return p.parse_args()
 
 
-def source_digest():
+KERNEL_SOURCES = {
+    "quantise": ("kvarn_quantize.hip", "kvarn_device.hpp"),
+    "append": ("kvarn_quantize.hip", "kvarn_device.hpp"),
+    "decode": ("kvarn_decode.hip", "kvarn_device.hpp"),
+}
+
+
+def source_digest(part=None):
+    """Digest of the HIP sources (of one part of the path, or all of them)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_tok_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if part is None else KERNEL_SOURCES[part]
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -70,8 +79,12 @@ def algorithmic_bytes(lens, hkv, hq, appended):
     return decode
 
 
-def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes):
-    """The fp64 oracle, single-threaded, on a bounded sample of the same step."""
+def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
+                 quant_budget_s=12.0, decode_budget_s=8.0):
+    """The fp64 oracle, single-threaded, on a time-bounded sample of the same step: tile-head
+    quantisations in order until all are done or quant_budget_s has passed, then (sequence,
+    KV head) decodes over oracle-built caches until all are done or decode_budget_s has
+    passed; the per-item times are extrapolated to the whole step."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -80,21 +93,20 @@ def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes)
         limiter = None
     from oracle import attention as oatt
     from oracle import codec
-    n_q = 768                                  # tile-heads quantised (keys and values)
-    t0 = time.perf_counter()
     n_tiles = st["k"].shape[0] // T
-    for i in range(n_q):
-        tile, head = i % n_tiles, (i * 7) % sp.hkv
+    t0 = time.perf_counter()
+    n_q = 0
+    while n_q < tile_heads_total and time.perf_counter() - t0 < quant_budget_s:
+        tile, head = n_q // sp.hkv, n_q % sp.hkv
         rows = slice(T * tile, T * tile + T)
         codec.encode_record(st["k"][rows, head], st["v"][rows, head])
+        n_q += 1
     tq = (time.perf_counter() - t0) / n_q
-    # decode: one (sequence, KV head) over an oracle-built cache of its tiles
-    n_d = 8
-    pool = np.zeros((st["num_blocks"], 1, TILE), np.uint8)
-    td_total = 0.0
     first = np.concatenate([[0], np.cumsum(st["seq_lens"] // T)])   # first tile of each sequence
-    for r in range(n_d):
-        b, g = r % sp.batch, (3 * r) % sp.hkv
+    pool = np.zeros((st["num_blocks"], 1, TILE), np.uint8)
+    td_total, n_d = 0.0, 0
+    while n_d < pairs_total and td_total < decode_budget_s:
+        b, g = n_d // sp.hkv, n_d % sp.hkv
         n = int(lens[b]) // T
         for i in range(n):
             rows = slice(T * (first[b] + i), T * (first[b] + i) + T)
@@ -105,22 +117,23 @@ def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes)
         oatt.decode_attention(q[b:b + 1, g * sp.group:(g + 1) * sp.group], pool,
                               st["block_table"][b:b + 1], lens[b:b + 1], sk, sk, sm)
         td_total += time.perf_counter() - t1
+        n_d += 1
     td = td_total / n_d
     est = tq * tile_heads_total + td * pairs_total
     if limiter is not None:
         limiter.unregister()
     return {"value": step_bytes / est / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_q} tile-head quantisations ({tq * 1e3:.1f} ms each) and {n_d} "
-                      f"(sequence, KV head) decodes ({td * 1e3:.0f} ms each) of this step, "
-                      f"extrapolated to the step's {tile_heads_total} tile-heads and "
-                      f"{pairs_total} (sequence, KV head) pairs ({est:.1f} s per step)"}
+            "sample": f"{n_q} of {tile_heads_total} tile-head quantisations "
+                      f"({tq * 1e3:.2f} ms each) and {n_d} of {pairs_total} (sequence, KV head) "
+                      f"decodes ({td * 1e3:.1f} ms each) of this step on one host core, "
+                      f"extrapolated to the whole step ({est:.2f} s per step)"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is not built for "
+              "more than one GPU", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -235,12 +248,14 @@ def main():
     timings = {"quantise": tq, "append": ta, "decode": td}
     dominant = max(timings, key=timings.get)
     ach = {"quantise": quant_gbps, "append": a_bytes / ta / 1e9, "decode": decode_gbps}[dominant]
+    # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by what those
+    # counters read for a device copy of known size; null once the kernels have changed
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         tr = json.load(open(tpath)).get(args.workload, {}).get(dominant)
-        if tr and tr.get("source_digest") == source_digest():
-            traffic = tr.get("bytes_per_launch")
+        if tr and tr.get("source_digest") == source_digest(dominant):
+            traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel)",
