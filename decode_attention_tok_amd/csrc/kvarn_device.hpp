@@ -93,6 +93,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Largest value over the wave of a non-negative float (its bit pattern orders like an int):
+// DPP maxima within each row of 16 lanes, then the four rows through scalar registers.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  int v = __float_as_int(x);
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const int r = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                    max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return __int_as_float(r);
+}
+
 // Unpack 8 fp16 values held in a uint4.
 __device__ __forceinline__ void unpack_h8(const uint4 w, float* out) {
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};

@@ -1,6 +1,6 @@
 // KVarN tile quantiser (write path) for gfx950.
 //
-// One workgroup of 256 threads quantises one 128-token x 128-channel tile of one KV head,
+// One workgroup of 512 threads quantises one 128-token x 128-channel tile of one KV head,
 // keys or values, through the write-path stages of [GR] "The four-stage pipeline" (groundy.com,
 // "Huawei's KVarN puts KV-cache quantization inside vLLM's backend"):
 //   1. Hadamard rotation along channels: a 128-point fast Walsh-Hadamard transform.
@@ -15,22 +15,26 @@
 //      down of the token minimum, scale = FP8 round up of (max - zero-point) / (2^bits - 1),
 //      code = clamp(rne((y - zero-point) / scale), 0, 2^bits - 1).
 //
-// Work layout. Layout A gives thread (t, hf) = (tid / 2, tid % 2) the 64 channels
-// 64 hf .. 64 hf + 63 of token t: the transform (six butterfly stages in registers and one
-// across the lane pair, a DPP-sourced fused multiply-add), the row statistics and the codes.
-// Layout B gives thread (j, th) = (tid % 128, tid / 128) the 64 tokens 64 th .. 64 th + 63 of
+// Work layout. Layout A gives thread (t, q0, q1) = (tid / 4, tid % 2, (tid / 2) % 2) the 32
+// channels c = e + 8 q0 + 16 m + 64 q1 (e = 0..7, m = 0..3) of token t, held as x[8 m + e]:
+// channel bits 0-2 and 4-5 live in registers and bits 3 and 6 across the four lanes of a quad.
+// It does the transform (five butterfly stages in registers, two across lanes as DPP-sourced
+// fused multiply-adds), the row statistics and the codes; a thread's eight values of one m are
+// exactly one word of key nibbles, and its four values of one e are one byte of value crumbs.
+// Layout B gives thread (j, th) = (tid % 128, tid / 128) the 32 tokens 32 th .. 32 th + 31 of
 // channel j: the column statistics, read from a copy of the rotated tile kept in LDS for the
-// whole normalisation (registers hold only the layout-A copy).
+// whole normalisation.
 //
-// Sign folding. The cross-lane butterfly computes x + s * partner with s = -1 on the odd lane
-// of each pair, which leaves channels 64..127 negated. Column variances do not see a sign; the
-// row step and the rounding stage multiply by per-channel factors anyway, so the stored factor
-// for channels 64..127 carries the sign. The 1/sqrt(128) scale of the transform is folded the
-// same way into the rounding stage's per-channel factor (the normalisation is scale-free up to
-// the gauge, and the floor is relative to the tile's largest value).
+// Sign folding. A cross-lane butterfly computes x + s * partner with s = -1 on the lane holding
+// the upper index, which leaves that lane's values negated; after both cross stages a thread's
+// values carry the factor (-1)^(q0 + q1), the same for all of them. Column variances do not see
+// it, and the row statistics and the rounding stage apply it once per thread. The 1/sqrt(128)
+// scale of the transform is folded into the rounding stage's per-channel factor (the
+// normalisation is scale-free up to the gauge, and the floor is relative to the tile's
+// largest value).
 //
 // Variances use shifted one-pass sums (shift = the thread's first value), merged between the
-// two threads sharing a row or column with Chan et al.'s pairwise update.
+// threads sharing a row or column with Chan et al.'s pairwise update.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -39,26 +43,75 @@ namespace kvarn {
 
 namespace {
 
-constexpr int kQThreads = 256;
-constexpr int kXtStride = kD + 1;
+constexpr int kQThreads = 512;
+constexpr int kXs = 144;                             // LDS row stride of the rotated tile
+constexpr int kCp = kD + 4;                          // padded per-channel array length
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 2^-3.5
 
+// Position of channel c in an LDS row or per-channel array: channels 64..127 sit 4 floats
+// further on, so the quad lanes holding channel bit 6 = 0 and 1 use different banks.
+__device__ __forceinline__ int cpos(int c) { return c + ((c >> 6) << 2); }
+
 struct QuantSmem {
-  float xt[kT][kXtStride];   // rotated tile, layout A -> B; reused for packed value codes
-  float u[kT];               // per-token multipliers 1 / r_t
-  float cs[kD];              // per-channel standard deviations (unrounded c before the gauge)
-  float vsg[kD];             // per-channel multipliers 1 / c_j, negated for channels 64..127
-  float rq[kD];              // per-channel rounding factor 2^-3.5 / c-hat_j (signed likewise)
-  float colm[2][kD];         // per-half column shifted means
-  float colq[2][kD];         // per-half column centred sums of squares
-  uint32_t meta[96];         // staged FP8 s-hat (32 words) and FP16 z-hat (64 words)
-  uint32_t chat[32];         // staged FP8 c-hat
-  float red[16];
+  alignas(16) float xt[kT][kXs];   // rotated tile, layout A -> B; reused to stage the packed codes
+  float u[kT];           // per-token multipliers 1 / r_t
+  float cs[kD];          // per-channel standard deviations (unrounded c before the gauge)
+  float vinv[kCp];       // per-channel multipliers 1 / c_j (at cpos)
+  float rq[kCp];         // per-channel rounding factor 2^-3.5 / c-hat_j (at cpos)
+  float colm[4][kD];     // per-quarter column shifted means
+  float colq[4][kD];     // per-quarter column centred sums of squares
+  uint32_t meta[96];     // staged FP8 s-hat (32 words) and FP16 z-hat (64 words)
+  uint32_t chat[32];     // staged FP8 c-hat
+  float red[32];
 };
 
-// value of lane (lane ^ 1) via DPP quad_perm [1, 0, 3, 2]
-__device__ __forceinline__ float pair_swap(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+
+template <int kCtrl>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// a[i] += s * (a[i] of lane ^ 1), i = 0..7, each one v_fmac_f32 with a DPP-read first source.
+// The leading s_nop gives the two wait states a DPP read of a VGPR needs after a VALU write.
+__device__ __forceinline__ void fmac_xor1(float* a, float s) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+        "+v"(a[7])
+      : "v"(s));
+}
+
+// The same across lane ^ 2.
+__device__ __forceinline__ void fmac_xor2(float* a, float s) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+        "+v"(a[7])
+      : "v"(s));
+}
+
+// Code = rne(clamp(v, 0, qmax)) written into byte `sel` of `acc`: the conversion rounds to
+// nearest even and clamps below at 0; the upper clamp comes first.
+__device__ __forceinline__ uint32_t put_code(float v, float qmax, uint32_t sel, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(fminf(v, qmax), sel, acc);
 }
 
 __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, int tid) {
@@ -77,31 +130,36 @@ __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, i
 // Quantise one tile. `src` points at token 0, channel 0 of this KV head; token t starts at
 // src + t * token_stride. If `row127` is not null it replaces token 127 (the append path
 // passes the new token there). Writes the key or value half of the record at `rec`.
-__device__ __forceinline__ void quantize_tile(const __half* __restrict__ src, long long token_stride,
-                              const __half* __restrict__ row127, int is_v, int iters,
-                              uint8_t* __restrict__ rec, QuantSmem& sm) {
+__device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
+                                              long long token_stride,
+                                              const __half* __restrict__ row127, int is_v,
+                                              int iters, uint8_t* __restrict__ rec,
+                                              QuantSmem& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t = tid >> 1, hf = tid & 1;          // layout A
-  const int jj = tid & (kD - 1), th = tid >> 7;  // layout B
+  const int t = tid >> 2, q0 = tid & 1, q1 = (tid >> 1) & 1;   // layout A
+  const int jj = tid & (kD - 1), th = tid >> 7;                 // layout B
+  const int cbase = 8 * q0 + 64 * q1;                           // channel of x[0]
+  const int pbase = cpos(cbase);                                // its LDS position
+  const bool flip = (q0 ^ q1) != 0;                             // values carry a factor -1
 
   // ---- load (layout A) and rotate
-  float x[64];
+  float x[32];
   {
     const __half* row = (row127 != nullptr && t == kT - 1) ? row127
                                                            : src + (long long)t * token_stride;
-    const uint4* r4 = reinterpret_cast<const uint4*>(row + hf * 64);
-    uint4 w[8];
+    const uint4* r4 = reinterpret_cast<const uint4*>(row + cbase);
+    uint4 w[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = r4[k];
+    for (int m = 0; m < 4; ++m) w[m] = r4[2 * m];                // channels cbase + 16 m ..
 #pragma unroll
-    for (int k = 0; k < 8; ++k) unpack_h8(w[k], x + 8 * k);
+    for (int m = 0; m < 4; ++m) unpack_h8(w[m], x + 8 * m);
   }
 #pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
+  for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < 32; ++i) {
       if ((i & h) == 0) {
         const float a = x[i], b = x[i + h];
         x[i] = a + b;
@@ -109,28 +167,39 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src, lo
       }
     }
   }
-  const float sgn = hf ? -1.0f : 1.0f;
+  {
+    const float s1 = q0 ? -1.0f : 1.0f, s2 = q1 ? -1.0f : 1.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fmac_xor1(x + 8 * g, s1);      // channel bit 3
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fmac_xor2(x + 8 * g, s2);      // channel bit 6
+  }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    x[i] = fmaf(sgn, pair_swap(x[i]), x[i]);     // channel 64..127 values come out negated
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  amax = wave_max(amax);
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = wave_max_nonneg(amax);
   if (lane == 0) sm.red[wave] = amax;
   // ---- transpose A -> B through LDS
+  {
+    float4* row4 = reinterpret_cast<float4*>(&sm.xt[t][0]);   // rows are 16-byte aligned
 #pragma unroll
-  for (int i = 0; i < 64; i += 4)
-    *reinterpret_cast<float4*>(&sm.xt[t][hf * 64 + i]) = make_float4(x[i], x[i + 1], x[i + 2],
-                                                                      x[i + 3]);
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int h = 0; h < 8; h += 4)
+        row4[(pbase >> 2) + 4 * m + (h >> 2)] =
+            make_float4(x[8 * m + h], x[8 * m + h + 1], x[8 * m + h + 2], x[8 * m + h + 3]);
+    }
+  }
   if (tid < kT) sm.u[tid] = 1.0f;
   __syncthreads();
-  const float big = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+  float big = sm.red[0];
+#pragma unroll
+  for (int w = 1; w < kQThreads / 64; ++w) big = fmaxf(big, sm.red[w]);
   if (big == 0.0f) {                              // uniform across the workgroup
     store_record_zero_tile(rec, is_v, tid);
     return;
   }
-  const float* xcol = &sm.xt[th * 64][jj];       // column jj, tokens 64 th .., stride 129
+  const float* xcol = &sm.xt[th * 32][cpos(jj)];  // column jj, tokens 32 th .., stride kXs
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
@@ -141,63 +210,79 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src, lo
       float s1 = 0.0f, s2 = 0.0f, k0;
       if (it == 0) {
         k0 = xcol[0];
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) {
-          const float y = xcol[i * kXtStride] - k0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float y = xcol[i * kXs] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       } else {
-        const float* uu = sm.u + th * 64;
+        const float* uu = sm.u + th * 32;
         k0 = xcol[0] * uu[0];
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) {
-          const float y = fmaf(xcol[i * kXtStride], uu[i], -k0);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float y = fmaf(xcol[i * kXs], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       }
-      sm.colm[th][jj] = fmaf(s1, 0.015625f, k0);
-      sm.colq[th][jj] = fmaxf(fmaf(-s1 * 0.015625f, s1, s2), 0.0f);
+      sm.colm[th][jj] = fmaf(s1, 0.03125f, k0);
+      sm.colq[th][jj] = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
     }
     __syncthreads();
     if (th == 0) {
-      const float d = sm.colm[0][jj] - sm.colm[1][jj];
-      const float m2 = sm.colq[0][jj] + sm.colq[1][jj] + 32.0f * d * d;
-      const float sd = fmaxf(sqrtf(m2 * 0.0078125f), floor_unit * umax);
+      const float m0 = sm.colm[0][jj], m1 = sm.colm[1][jj];
+      const float m2 = sm.colm[2][jj], m3 = sm.colm[3][jj];
+      const float mean = 0.25f * ((m0 + m1) + (m2 + m3));
+      const float d0 = m0 - mean, d1 = m1 - mean, d2 = m2 - mean, d3 = m3 - mean;
+      const float qs = (sm.colq[0][jj] + sm.colq[1][jj]) + (sm.colq[2][jj] + sm.colq[3][jj]);
+      const float dd = fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, d3 * d3)));
+      const float sd = fmaxf(__builtin_amdgcn_sqrtf(fmaf(32.0f, dd, qs) * 0.0078125f),
+                             floor_unit * umax);
       sm.cs[jj] = sd;
-      const float vinv = 1.0f / sd;
-      sm.vsg[jj] = jj >= 64 ? -vinv : vinv;
-      const float vm = wave_max(vinv);
-      if (lane == 0) sm.red[4 + wave] = vm;       // waves 0 and 1
+      const float vi = __builtin_amdgcn_rcpf(sd);
+      sm.vinv[cpos(jj)] = vi;
+      const float vm = wave_max_nonneg(vi);
+      if (lane == 0) sm.red[8 + wave] = vm;       // waves 0 and 1
     }
     __syncthreads();
     if (it == iters - 1) break;                   // the last row step does not change c
-    const float vmax = fmaxf(sm.red[4], sm.red[5]);
-    // row step (layout A): std over channels of xt_tj * v_j (signs restored by vsg)
+    const float vmax = fmaxf(sm.red[8], sm.red[9]);
+    // row step (layout A): std over channels of xt_tj * v_j
     {
-      const float* vv = sm.vsg + hf * 64;
+      const float* vv = sm.vinv + pbase;
       const float k0 = x[0] * vv[0];
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float y = fmaf(x[i], vv[i], -k0);
+      for (int i = 0; i < 32; ++i) {
+        const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
         s1 += y;
         s2 = fmaf(y, y, s2);
       }
-      const float mh = fmaf(s1, 0.015625f, k0);
-      const float qh = fmaxf(fmaf(-s1 * 0.015625f, s1, s2), 0.0f);
-      const float mo = pair_swap(mh), qo = pair_swap(qh);
-      const float d = mh - mo;
-      const float m2 = qh + qo + 32.0f * d * d;
-      const float sd = fmaxf(sqrtf(m2 * 0.0078125f), floor_unit * vmax);
-      const float uinv = 1.0f / sd;
-      if (hf == 0) sm.u[t] = uinv;
-      const float um = wave_max(uinv);
-      if (lane == 0) sm.red[8 + wave] = um;
+      float mh = fmaf(s1, 0.03125f, k0);
+      if (flip) mh = -mh;
+      float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
+      {
+        const float mo = quad_swap<kDppXor1>(mh), qo = quad_swap<kDppXor1>(qh);
+        const float d = mh - mo;
+        qh = fmaf(16.0f * d, d, qh + qo);
+        mh = 0.5f * (mh + mo);
+      }
+      {
+        const float mo = quad_swap<kDppXor2>(mh), qo = quad_swap<kDppXor2>(qh);
+        const float d = mh - mo;
+        qh = fmaf(32.0f * d, d, qh + qo);
+      }
+      const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * vmax);
+      const float uinv = __builtin_amdgcn_rcpf(sd);
+      if ((tid & 3) == 0) sm.u[t] = uinv;
+      const float um = wave_max_nonneg(uinv);
+      if (lane == 0) sm.red[16 + wave] = um;
     }
     __syncthreads();
-    umax = fmaxf(fmaxf(sm.red[8], sm.red[9]), fmaxf(sm.red[10], sm.red[11]));
+    umax = sm.red[16];
+#pragma unroll
+    for (int w = 1; w < kQThreads / 64; ++w) umax = fmaxf(umax, sm.red[16 + w]);
   }
 
   // ---- gauge (geometric mean of c = 1) and FP8 rounding of c, by wave 0
@@ -206,86 +291,98 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src, lo
     const float c0 = sm.cs[lane], c1 = sm.cs[lane + 64];
     const float lsum = wave_sum(log2f(c0) + log2f(c1));
     const float g = exp2f(-lsum * 0.0078125f);
-    const uint32_t q0 = e4m3_rne(fminf(fmaxf(c0 * g, 0.001953125f), 448.0f));
-    const uint32_t q1 = e4m3_rne(fminf(fmaxf(c1 * g, 0.001953125f), 448.0f));
-    sm.rq[lane] = kInvSqrtD / e4m3_to_float(q0);
-    sm.rq[lane + 64] = -kInvSqrtD / e4m3_to_float(q1);
-    reinterpret_cast<uint8_t*>(sm.chat)[lane] = (uint8_t)q0;
-    reinterpret_cast<uint8_t*>(sm.chat)[lane + 64] = (uint8_t)q1;
+    const uint32_t e0 = e4m3_rne(fminf(fmaxf(c0 * g, 0.001953125f), 448.0f));
+    const uint32_t e1 = e4m3_rne(fminf(fmaxf(c1 * g, 0.001953125f), 448.0f));
+    sm.rq[cpos(lane)] = kInvSqrtD / e4m3_to_float(e0);
+    sm.rq[cpos(lane + 64)] = kInvSqrtD / e4m3_to_float(e1);
+    reinterpret_cast<uint8_t*>(sm.chat)[lane] = (uint8_t)e0;
+    reinterpret_cast<uint8_t*>(sm.chat)[lane + 64] = (uint8_t)e1;
   }
-  __syncthreads();
+  __syncthreads();   // also: every read of sm.xt is done, so it may hold the packed codes
   if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kCRel)[tid] = sm.chat[tid];
 
-  // ---- asymmetric RTN per token (layout A); x[] is overwritten by y, then by the codes
+  // ---- asymmetric RTN per token (layout A); p = (+-) y, sign `flip`
   const float qmax = is_v ? 3.0f : 15.0f;
-  float mn = 3.0e38f, mx = -3.0e38f;
+  float pmin = 3.0e38f, pmax = -3.0e38f;
   {
-    const float* rq = sm.rq + hf * 64;
+    const float* rr = sm.rq + pbase;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      x[i] *= rq[i];
-      mn = fminf(mn, x[i]);
-      mx = fmaxf(mx, x[i]);
+    for (int i = 0; i < 32; ++i) {
+      x[i] *= rr[16 * (i >> 3) + (i & 7)];
+      pmin = fminf(pmin, x[i]);
+      pmax = fmaxf(pmax, x[i]);
     }
   }
-  mn = fminf(mn, pair_swap(mn));
-  mx = fmaxf(mx, pair_swap(mx));
+  float mn = flip ? -pmax : pmin, mx = flip ? -pmin : pmax;
+  mn = fminf(mn, quad_swap<kDppXor1>(mn));
+  mx = fmaxf(mx, quad_swap<kDppXor1>(mx));
+  mn = fminf(mn, quad_swap<kDppXor2>(mn));
+  mx = fmaxf(mx, quad_swap<kDppXor2>(mx));
   const uint32_t zbits = fp16_rd(fmaxf(mn, -65504.0f));
   const float zf = fp16_bits_to_float(zbits);
   const uint32_t scode = e4m3_ru((mx - zf) / qmax);
   const float sf = e4m3_to_float(scode);
   const float inv_s = sf > 0.0f ? 1.0f / sf : 0.0f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) x[i] = fminf(fmaxf(rintf((x[i] - zf) * inv_s), 0.0f), qmax);
-  if (hf == 0) {
+  const float ca = flip ? -inv_s : inv_s;          // (y - z) / s = p * ca + cb
+  const float cb = -zf * inv_s;
+  if ((tid & 3) == 0) {
     reinterpret_cast<uint8_t*>(sm.meta)[t] = (uint8_t)scode;
     reinterpret_cast<uint16_t*>(sm.meta + 32)[t] = (uint16_t)zbits;
   }
 
+  uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
   if (!is_v) {
-    // key codes: token-major nibbles; this thread's 64 channels are 32 contiguous bytes
-    uint32_t w[8];
+    // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
+    // token's 16 words (channel 8 k + e at nibble e of word k)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t acc = 0;
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc |= (uint32_t)x[8 * k + q] << (4 * q);
-      w[k] = acc;
+      for (int e = 0; e < 8; e += 2) {
+        lo = put_code(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
+        hi = put_code(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
+      }
+      stage[t * 16 + q0 + 2 * m + 8 * q1] = lo | (hi << 4);
     }
-    uint4* dst = reinterpret_cast<uint4*>(rec + kKCodesOff + t * 64 + hf * 32);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     __syncthreads();
+    reinterpret_cast<uint4*>(rec + kKCodesOff)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
   } else {
-    // value codes. Byte (t, n, hf) holds the codes of channels 64 hf + 16 nb' + n, nb' = 0..3,
-    // at bits 2 nb'; the 16-bit pair (t, n) is then the token-t half of a section word.
-    __syncthreads();                               // everyone is done reading sm.xt
-    uint8_t* vb = reinterpret_cast<uint8_t*>(&sm.xt[0][0]);   // [128][16][2] bytes
+    // value codes. Byte e of this thread holds the codes of channel n = 8 q0 + e, hf = q1,
+    // nb' = m at bits 2 m; it is staged at byte 2 (t % 2) + hf of LDS word 16 (t / 2) + n,
+    // which makes every LDS word one word of the section.
+    uint8_t* sb = reinterpret_cast<uint8_t*>(stage);
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      const uint32_t b = (uint32_t)x[n] | ((uint32_t)x[16 + n] << 2) |
-                         ((uint32_t)x[32 + n] << 4) | ((uint32_t)x[48 + n] << 6);
-      vb[t * 32 + 2 * n + hf] = (uint8_t)b;
+    for (int eh = 0; eh < 8; eh += 4) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = put_code(fmaf(x[8 * m + eh + e], ca, cb), qmax, e, p);
+        d |= p << (2 * m);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sb[((t >> 1) * 16 + 8 * q0 + eh + e) * 4 + (t & 1) * 2 + q1] = (uint8_t)(d >> (8 * e));
     }
     __syncthreads();
-    const uint16_t* vh = reinterpret_cast<const uint16_t*>(vb);
-    uint32_t out[4];
+    if (tid < 256) {
+      uint32_t out[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int w = 4 * tid + e;                   // word index in the section
-      const int kb = w >> 8, ln = (w >> 2) & 63, d = w & 3;
-      const int s = ln >> 4, n = ln & 15;
-      const int tb = 32 * kb + 16 * (d >> 1) + 4 * s + ((d & 1) << 1);
-      out[e] = (uint32_t)vh[tb * 16 + n] | ((uint32_t)vh[(tb + 1) * 16 + n] << 16);
+      for (int d = 0; d < 4; ++d) {
+        const int w = 4 * tid + d;                 // word index in the section
+        const int kb = w >> 8, s = (w >> 6) & 3, n = (w >> 2) & 15, h = d >> 1, i2 = d & 1;
+        out[d] = stage[(16 * kb + 8 * h + 2 * s + i2) * 16 + n];
+      }
+      reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] = make_uint4(out[0], out[1], out[2], out[3]);
     }
-    reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] = make_uint4(out[0], out[1], out[2], out[3]);
   }
   if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kSRel)[tid] = sm.meta[tid];
   else if (tid < 96) reinterpret_cast<uint32_t*>(rec + meta + kZRel)[tid - 32] = sm.meta[tid];
 }
 
 // grid: 2 * num_kv_heads * n_tiles workgroups; id = (tile * Hkv + head) * 2 + kv
-__global__ void __launch_bounds__(kQThreads)
+__global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v,
                       long long token_stride, int n_tiles, int hkv,
                       const int32_t* __restrict__ dst_blocks, uint8_t* __restrict__ pool,
@@ -304,7 +401,7 @@ quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v
 }
 
 // grid: 2 * num_kv_heads * batch workgroups; id = (b * Hkv + head) * 2 + kv
-__global__ void __launch_bounds__(kQThreads)
+__global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                     const int32_t* __restrict__ positions,
                     const int32_t* __restrict__ block_table, int max_blocks,
