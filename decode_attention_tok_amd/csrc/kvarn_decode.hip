@@ -444,19 +444,55 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   }
 }
 
-// grid (hkv, batch), 256 threads: staging tokens (exact fp32), log-sum-exp merge of the tile
-// splits, o~ H + o_raw, / l, for the group of query heads of one KV head.
-constexpr int kMThreads = 256;
-
+// grid (hq, batch), one wave per (sequence, query head): the staging tokens (exact fp32
+// attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
+// / l. Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
+// channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32.
+constexpr int kMThreads = 64;
 constexpr int kMaxSplits = 64;
 
 struct MergeSmem {
-  float qraw[kMaxGroup][kD];
-  float sc[kMaxGroup][kT];
-  float ot[kMaxGroup][kD];
-  float wsplit[kMaxGroup][kMaxSplits];   // exp2(m_split - m) per head and split
-  float msplit[kMaxGroup], lsum[kMaxGroup];
+  float q[kD];              // raw query (fp32)
+  float p[kT];              // staging probabilities exp2(s_t - m)
+  float w[kMaxSplits];      // split weights exp2(m_split - m)
 };
+
+template <int kMask>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (kMask == 1)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (kMask == 2)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  else if constexpr (kMask == 8)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  else if constexpr (kMask == 32)
+    return __shfl_xor(v, 32);
+  else   // 4, 16: swizzle in bit-mask mode, xor within 32 lanes
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (kMask << 10) | 0x1F));
+}
+
+// One butterfly stage across lanes: the lane with the bit clear gets own + partner, the lane
+// with it set gets partner - own.
+template <int kMask>
+__device__ __forceinline__ float fwht_lane_stage(float v, int lane) {
+  return fmaf((lane & kMask) ? -1.0f : 1.0f, v, lane_xor<kMask>(v));
+}
+
+// <q, k> over 128 channels: k is one fp16 staging row, q the fp32 query in LDS.
+__device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, const float* qs) {
+  const uint4* k4 = reinterpret_cast<const uint4*>(krow);
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    float kv[8];
+    unpack_h8(k4[k], kv);
+    const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * k);
+    const float4 qc = *reinterpret_cast<const float4*>(qs + 8 * k + 4);
+    acc0 = fmaf(qa.x, kv[0], fmaf(qa.y, kv[1], fmaf(qa.z, kv[2], fmaf(qa.w, kv[3], acc0))));
+    acc1 = fmaf(qc.x, kv[4], fmaf(qc.y, kv[5], fmaf(qc.z, kv[6], fmaf(qc.w, kv[7], acc1))));
+  }
+  return acc0 + acc1;
+}
 
 __global__ void __launch_bounds__(kMThreads)
 decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_blocks,
@@ -464,112 +500,82 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out) {
   __shared__ MergeSmem sm;
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int group = hq / hkv;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int group = hq / hkv, g = h / group;
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
   const int n_stage = bad ? 0 : (len & (kT - 1));
   const float scale2 = sm_scale * kLog2e;
   const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
   const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
-
-  for (int idx = tid; idx < group * kD; idx += kMThreads)
-    sm.qraw[idx >> 7][idx & (kD - 1)] =
-        __half2float(q[((long long)b * hq + g * group) * kD + idx]);
-  __syncthreads();
-  // staging scores: thread (t, half) over 64 channels, pair-summed
-  if (n_stage > 0) {
-    const int t = tid >> 1, hf = tid & 1;
-    float kr[64];
-    if (t < n_stage) {
-      const uint4* kp = reinterpret_cast<const uint4*>(sk + t * kD + hf * 64);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) unpack_h8(kp[k], kr + 8 * k);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 64; ++e) kr[e] = 0.0f;
-    }
-    for (int gg = 0; gg < group; ++gg) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 64; ++e) dot = fmaf(sm.qraw[gg][hf * 64 + e], kr[e], dot);
-      dot += __shfl_xor(dot, 1);
-      if (hf == 0) sm.sc[gg][t] = t < n_stage ? dot * scale2 : -INFINITY;
-    }
+  {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h) * kD)[lane];
+    sm.q[2 * lane] = fp16_bits_to_float(w & 0xFFFFu);
+    sm.q[2 * lane + 1] = fp16_bits_to_float(w >> 16);
   }
   __syncthreads();
-  // per head: global max over split maxima and staging scores, sum, probabilities
-  for (int gg = wave; gg < group; gg += kMThreads / 64) {
-    const float* pp = partials + ((long long)b * hq + g * group + gg) * nsplit * kPartialFloats;
-    float mm = -INFINITY;
-    bool nan = false;
-    for (int sp = lane; sp < nsplit; sp += 64) {
-      const float v = pp[sp * kPartialFloats];
-      nan |= (v != v);
-      mm = fmaxf(mm, v);
-    }
-    const float s0 = (n_stage > 0) ? sm.sc[gg][lane] : -INFINITY;
-    const float s1 = (n_stage > 0) ? sm.sc[gg][lane + 64] : -INFINITY;
-    mm = fmaxf(mm, fmaxf(s0, s1));
-    mm = wave_max(mm);
-    const int anynan = __any(nan);
-    float ls = 0.0f;
-    if (mm != -INFINITY) {
-      for (int sp = lane; sp < nsplit; sp += 64) {
-        const float v = pp[sp * kPartialFloats];
-        const float wgt = exp2f(v - mm);
-        sm.wsplit[gg][sp] = wgt;
-        ls = fmaf(wgt, pp[sp * kPartialFloats + 1], ls);
-      }
-      const float p0 = exp2f(s0 - mm), p1 = exp2f(s1 - mm);
-      if (n_stage > 0) {
-        sm.sc[gg][lane] = p0;
-        sm.sc[gg][lane + 64] = p1;
-      }
-      ls += p0 + p1;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) {
-      sm.msplit[gg] = (anynan || bad) ? NAN : mm;
-      sm.lsum[gg] = ls;
-    }
+  // staging scores of tokens lane and lane + 64, split maxima and sums of lane's split
+  float s0 = -INFINITY, s1 = -INFINITY;
+  if (lane < n_stage) s0 = staging_dot(sk + lane * kD, sm.q) * scale2;
+  if (lane + 64 < n_stage) s1 = staging_dot(sk + (lane + 64) * kD, sm.q) * scale2;
+  const float* pp = partials + ((long long)b * hq + h) * nsplit * kPartialFloats;
+  const float msp = lane < nsplit ? pp[lane * kPartialFloats] : -INFINITY;
+  const float lsp = lane < nsplit ? pp[lane * kPartialFloats + 1] : 0.0f;
+  const bool invalid = bad || __any(msp != msp);
+  const float mm = wave_max(fmaxf(msp, fmaxf(s0, s1)));
+  float ls = 0.0f, wsp = 0.0f, p0 = 0.0f, p1 = 0.0f;
+  if (mm != -INFINITY) {
+    wsp = lane < nsplit ? exp2f(msp - mm) : 0.0f;
+    p0 = exp2f(s0 - mm);
+    p1 = exp2f(s1 - mm);
+    ls = fmaf(wsp, lsp, p0 + p1);
   }
+  ls = wave_sum(ls);
+  sm.w[lane] = wsp;
+  sm.p[lane] = p0;
+  sm.p[lane + 64] = p1;
   __syncthreads();
-  // merged rotated output o~ and raw staging output, per (head, channel)
-  for (int idx = tid; idx < group * kD; idx += kMThreads) {
-    const int gg = idx >> 7, j = idx & (kD - 1);
-    const float* pp = partials + ((long long)b * hq + g * group + gg) * nsplit * kPartialFloats;
-    const float mm = sm.msplit[gg];
-    float ot = 0.0f;
-    if (mm == mm && mm != -INFINITY) {
-      const float* col = pp + 2 + j;
-#pragma unroll 8
-      for (int sp = 0; sp < nsplit; ++sp) ot = fmaf(sm.wsplit[gg][sp], col[sp * kPartialFloats], ot);
+  // merged rotated output o~ of channels 2 lane, 2 lane + 1
+  float o0 = 0.0f, o1 = 0.0f;
+  if (mm != -INFINITY && !invalid) {
+    const float* col = pp + 2 + 2 * lane;
+#pragma unroll 4
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 v = *reinterpret_cast<const float2*>(col + sp * kPartialFloats);
+      const float w = sm.w[sp];
+      o0 = fmaf(w, v.x, o0);
+      o1 = fmaf(w, v.y, o1);
     }
-    sm.ot[gg][j] = ot;
   }
-  __syncthreads();
-  for (int h = 1; h < kD; h <<= 1) {
-    for (int p = tid; p < group * (kD / 2); p += kMThreads) {
-      const int gg = p >> 6, pi = p & 63;
-      const int i = (pi / h) * 2 * h + (pi % h);
-      const float a = sm.ot[gg][i], c = sm.ot[gg][i + h];
-      sm.ot[gg][i] = a + c;
-      sm.ot[gg][i + h] = a - c;
-    }
-    __syncthreads();
+  {
+    const float a = o0 + o1, c = o0 - o1;
+    o0 = a;
+    o1 = c;
   }
-  for (int idx = tid; idx < group * kD; idx += kMThreads) {
-    const int gg = idx >> 7, j = idx & (kD - 1);
-    float oraw = 0.0f;
-    for (int t = 0; t < n_stage; ++t) oraw = fmaf(sm.sc[gg][t], __half2float(sv[t * kD + j]), oraw);
-    const float mm = sm.msplit[gg], ls = sm.lsum[gg];
-    float o = 0.0f;
-    if (mm != mm) o = NAN;
-    else if (ls > 0.0f) o = (sm.ot[gg][j] * 0.08838834764831845f + oraw) / ls;
-    out[((long long)b * hq + g * group + gg) * kD + j] = o;
+  o0 = fwht_lane_stage<1>(o0, lane);   o1 = fwht_lane_stage<1>(o1, lane);
+  o0 = fwht_lane_stage<2>(o0, lane);   o1 = fwht_lane_stage<2>(o1, lane);
+  o0 = fwht_lane_stage<4>(o0, lane);   o1 = fwht_lane_stage<4>(o1, lane);
+  o0 = fwht_lane_stage<8>(o0, lane);   o1 = fwht_lane_stage<8>(o1, lane);
+  o0 = fwht_lane_stage<16>(o0, lane);  o1 = fwht_lane_stage<16>(o1, lane);
+  o0 = fwht_lane_stage<32>(o0, lane);  o1 = fwht_lane_stage<32>(o1, lane);
+  // raw staging output
+  float r0 = 0.0f, r1 = 0.0f;
+  const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
+  for (int t = 0; t < n_stage; ++t) {
+    const uint32_t w = vcol[t * (kD / 2)];
+    const float pt = sm.p[t];
+    r0 = fmaf(pt, fp16_bits_to_float(w & 0xFFFFu), r0);
+    r1 = fmaf(pt, fp16_bits_to_float(w >> 16), r1);
   }
+  float2 res = make_float2(0.0f, 0.0f);
+  if (invalid) {
+    res = make_float2(NAN, NAN);
+  } else if (ls > 0.0f) {
+    res.x = fmaf(o0, 0.08838834764831845f, r0) / ls;
+    res.y = fmaf(o1, 0.08838834764831845f, r1) / ls;
+  }
+  reinterpret_cast<float2*>(out + ((long long)b * hq + h) * kD)[lane] = res;
 }
 
 }  // namespace
@@ -596,7 +602,7 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
                      sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(hkv, batch), dim3(kMThreads), 0, stream, q, hq,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(kMThreads), 0, stream, q, hq,
                      hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, splits,
                      out);
   return hipGetLastError();
