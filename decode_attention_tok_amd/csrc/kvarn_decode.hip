@@ -21,13 +21,19 @@
 // mantissa bits 6..9 under exponent 0x3C00); the constant 1 contributes sum_j q~_j, which the
 // score needs anyway and subtracts exactly. (The MFMA sums products of subnormal fp16 operands
 // with far less precision than products of normal ones, so raw codes are not used as
-// subnormals.) Value codes likewise enter as 1 + code / 4 (the 2-bit field shifted to
-// mantissa bits 8..9), and sum_t p_t s-hat^V_t removes the constant part per head.
+// subnormals; a variant that left nibbles in the low mantissa bits, 1 + code / 1024 with the
+// query scaled to match, was far off as well, so every field sits just below the exponent.) Value codes likewise enter as 1 + code / 4 (the 2-bit
+// field shifted to mantissa bits 8..9), and sum_t p_t s-hat^V_t removes the constant part.
 // fp32-accurate operands are split into fp16 hi + lo parts: query column g holds hi(q~_g),
 // column 8 + g holds lo(q~_g), and one DPP row rotation by 8 adds the two partial scores;
 // the probability operand likewise has rows g (hi) and 8 + g (lo), summed once at the end.
+// After the score products the lane of column g keeps tokens 4 s + {0, 1} of each token block
+// and the lane of column 8 + g tokens 4 s + {2, 3}, so each probability is computed once; one
+// more rotation by 8 hands each lane the hi or lo halves it needs for the output operand.
 // The score accumulator lanes of token block pair (2 kb, 2 kb + 1) are exactly the operand
 // lanes of output token block kb, so probabilities feed the second product without shuffles.
+// The running maximum of a head moves only when a tile's maximum exceeds it by more than
+// 2 (log2 units), so most tiles skip the rescale of the output accumulators.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -40,17 +46,16 @@ constexpr int kWaves = 4;
 constexpr int kTThreads = 64 * kWaves;
 constexpr int kHeadGroup = 8;                 // query heads per tile workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 2.0f;                 // running-maximum slack (log2 units)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 struct WaveMeta {                  // per-wave, per-tile metadata (fp32, factors folded in)
-  float kc[kD];                    // c-hat^K_j
-  float ks[kT];                    // s-hat^K_t * sm * log2(e) * 16 / pq
-  float kz[kT];                    // z-hat^K_t * sm * log2(e)
-  float vs[kT];                    // s-hat^V_t * 32 (probability operand prescale)
-  float vz[kT];                    // z-hat^V_t
-  float vc[kD];                    // c-hat^V_j
+  float f8[4 * kD];                // c-hat^K_j * pq | s-hat^K_t * kfac | c-hat^V_j | 32 s-hat^V_t
+  float h16[2 * kT];               // z-hat^K_t * kzfac | z-hat^V_t
   float alpha[16], beta[16];       // per-row rescale and zero-point term of the last tile
 };
 
@@ -62,13 +67,45 @@ struct TileSmem {
   float red[kWaves];
 };
 
+template <int kMask>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (kMask == 1)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (kMask == 2)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  else if constexpr (kMask == 8)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  else if constexpr (kMask == 32)
+    return __shfl_xor(v, 32);
+  else   // 4, 16: swizzle in bit-mask mode, xor within 32 lanes
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (kMask << 10) | 0x1F));
+}
+
+// One butterfly stage across lanes: the lane with the bit clear gets own + partner, the lane
+// with it set gets partner - own.
+template <int kMask>
+__device__ __forceinline__ float fwht_lane_stage(float v, int lane) {
+  return fmaf((lane & kMask) ? -1.0f : 1.0f, v, lane_xor<kMask>(v));
+}
+
+// 128-point Walsh-Hadamard transform of a vector held as channels 2 lane, 2 lane + 1.
+__device__ __forceinline__ void fwht_wave(float& o0, float& o1, int lane) {
+  const float a = o0 + o1, c = o0 - o1;
+  o0 = a;
+  o1 = c;
+  o0 = fwht_lane_stage<1>(o0, lane);   o1 = fwht_lane_stage<1>(o1, lane);
+  o0 = fwht_lane_stage<2>(o0, lane);   o1 = fwht_lane_stage<2>(o1, lane);
+  o0 = fwht_lane_stage<4>(o0, lane);   o1 = fwht_lane_stage<4>(o1, lane);
+  o0 = fwht_lane_stage<8>(o0, lane);   o1 = fwht_lane_stage<8>(o1, lane);
+  o0 = fwht_lane_stage<16>(o0, lane);  o1 = fwht_lane_stage<16>(o1, lane);
+  o0 = fwht_lane_stage<32>(o0, lane);  o1 = fwht_lane_stage<32>(o1, lane);
+}
+
 __device__ __forceinline__ float dpp_ror8(float v) {   // lane (l & ~15) | ((l + 8) & 15)
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
 }
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  const __fp16 ha = (__fp16)a, hb = (__fp16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+__device__ __forceinline__ uint32_t dpp_ror8_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
 }
 
 // (x & mask) | c in one v_and_or_b32: mask in a VGPR and c in an SGPR, since a gfx9 VOP3
@@ -84,25 +121,50 @@ __device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint3
   return __builtin_bit_cast(half8, u);
 }
 
-typedef float float2v __attribute__((ext_vector_type(2)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {   // both rounded to nearest
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){a, b}, half2v));
+}
 
-// fp16 hi / lo parts of a pair (a, b), both rounded to nearest: a == hi + lo to about 2^-22
-// relative while normal. Returns the packed hi pair or the packed lo pair.
-__device__ __forceinline__ uint32_t split_pair(float a, float b, bool want_hi) {
-  const half2v h = __builtin_convertvector((float2v){a, b}, half2v);
-  const float2v hb = __builtin_convertvector(h, float2v);
-  const half2v l = __builtin_convertvector((float2v){a - hb[0], b - hb[1]}, half2v);
-  return want_hi ? __builtin_bit_cast(uint32_t, h) : __builtin_bit_cast(uint32_t, l);
+// Packed fp16 pair (a - k hi(a), b - k hi(b)) with hi = fp16 rounding and k = -negk in {0, 1}:
+// the hi parts themselves (k = 0) or the lo parts (k = 1), each one v_fma_mix (exact product
+// and sum, one rounding to fp16). a == hi + lo to about 2^-22 relative while normal.
+__device__ __forceinline__ uint32_t hi_or_lo(float a, float b, float negk) {
+  const uint32_t h = pack_h2(a, b);
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(negk), "v"(a));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(h), "v"(negk), "v"(b));
+  return r;
+}
+
+// fp16 lo parts of a pair whose packed hi parts are h.
+__device__ __forceinline__ uint32_t lo_of(uint32_t h, float a, float b) {
+  uint32_t r;
+  const float m1 = -1.0f;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(m1), "v"(a));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(h), "v"(m1), "v"(b));
+  return r;
 }
 
 struct TileRegs {
   uint4 kw[8];        // key codes: token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31
   uint4 vw[4];        // value codes: section words 256 kb + 4 lane .. + 3
-  uint4 meta;         // 16 bytes of the record's 1 KB metadata at 12288 + 16 lane
+  uint2 m8;           // 8 FP8 metadata bytes (see decode_meta)
+  uint2 m16;          // 4 fp16 zero-points
 };
 
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int lane, TileRegs& r) {
+// Per-lane byte offsets of the metadata a lane decodes. Lanes 0-15: c-hat^K, 16-31: s-hat^K,
+// 32-47: c-hat^V, 48-63: s-hat^V, 8 bytes each; lanes 0-31: z-hat^K, 32-63: z-hat^V, 4 each.
+__device__ __forceinline__ int meta8_off(int lane) {
+  return (lane < 32 ? kKMetaOff : kVMetaOff) + ((lane >> 4) & 1) * kSRel + 8 * (lane & 15);
+}
+__device__ __forceinline__ int meta16_off(int lane) {
+  return (lane < 32 ? kKMetaOff : kVMetaOff) + kZRel + 8 * (lane & 31);
+}
+
+__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int lane, int off8,
+                                          int off16, TileRegs& r) {
   const int m = lane & 15, s = lane >> 4;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb)
@@ -110,39 +172,26 @@ __device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int l
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
     r.vw[kb] = *reinterpret_cast<const uint4*>(rec + kVCodesOff + kb * 1024 + lane * 16);
-  r.meta = *reinterpret_cast<const uint4*>(rec + kKMetaOff + lane * 16);
+  r.m8 = *reinterpret_cast<const uint2*>(rec + off8);
+  r.m16 = *reinterpret_cast<const uint2*>(rec + off16);
 }
 
-// Scatter one lane's 16 metadata bytes into the wave's fp32 tables. Lanes 0-7: c-hat^K,
-// 8-15: s-hat^K, 16-31: z-hat^K, 32-39: c-hat^V, 40-47: s-hat^V, 48-63: z-hat^V.
-// FP8 bytes go through the hardware E4M3 conversion (exact for every finite code).
-__device__ __forceinline__ void decode_meta(const uint4 mw, int lane, WaveMeta& wm,
-                                            float kfac, float kzfac) {
-  const uint32_t w[4] = {mw.x, mw.y, mw.z, mw.w};
-  const int grp = lane & 31;
-  const bool isv = lane >= 32;
-  if (grp < 16) {                         // 16 FP8 values
-    const float mul = grp < 8 ? 1.0f : (isv ? 32.0f : kfac);
-    float* dst = grp < 8 ? (isv ? wm.vc : wm.kc) : (isv ? wm.vs : wm.ks);
-    dst += (grp & 7) * 16;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const float2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
-      const float2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
-      *reinterpret_cast<float4*>(dst + 4 * d) =
-          make_float4(lo[0] * mul, lo[1] * mul, hi[0] * mul, hi[1] * mul);
-    }
-  } else {                                // 8 fp16 values
-    const float mul = isv ? 1.0f : kzfac;
-    float* dst = (isv ? wm.vz : wm.kz) + (grp - 16) * 8;
-#pragma unroll
-    for (int d = 0; d < 4; d += 2) {
-      const float2v a = __builtin_convertvector(__builtin_bit_cast(half2v, w[d]), float2v);
-      const float2v b = __builtin_convertvector(__builtin_bit_cast(half2v, w[d + 1]), float2v);
-      *reinterpret_cast<float4*>(dst + 2 * d) =
-          make_float4(a[0] * mul, a[1] * mul, b[0] * mul, b[1] * mul);
-    }
-  }
+// Every lane converts its 8 FP8 bytes and 4 fp16 values (the same instructions on all lanes)
+// and stores them, times per-lane factors, at 8 lane and 4 lane of the wave's tables.
+// FP8 goes through the hardware E4M3 conversion (exact for every finite code).
+__device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int lane,
+                                            WaveMeta& wm, float fm, float fz) {
+  const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, false);
+  const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, true);
+  const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, false);
+  const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, true);
+  float4* dst = reinterpret_cast<float4*>(wm.f8 + 8 * lane);
+  dst[0] = make_float4(a[0] * fm, a[1] * fm, b[0] * fm, b[1] * fm);
+  dst[1] = make_float4(c[0] * fm, c[1] * fm, d[0] * fm, d[1] * fm);
+  const float2v e = __builtin_convertvector(__builtin_bit_cast(half2v, m16.x), float2v);
+  const float2v f = __builtin_convertvector(__builtin_bit_cast(half2v, m16.y), float2v);
+  *reinterpret_cast<float4*>(wm.h16 + 4 * lane) = make_float4(e[0] * fz, e[1] * fz, f[0] * fz,
+                                                              f[1] * fz);
 }
 
 __global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -178,56 +227,64 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   auto block_of = [&](int j) -> long long {
     return (long long)__builtin_amdgcn_readlane(ids, j & 63);
   };
+  const int off8 = meta8_off(lane), off16 = meta16_off(lane);
   TileRegs cur;
   if (nw > 0) {
     const long long blk = block_of(0);
     if (blk < 0 || blk >= num_blocks) bad = true;
-    else load_tile(pool + (blk * hkv + g) * (long long)kTileBytes, lane, cur);
+    else load_tile(pool + (blk * hkv + g) * (long long)kTileBytes, lane, off8, off16, cur);
   }
 
-  // ---- rotated queries in LDS, and a power-of-two prescale for the fp16 query operand
-  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads) {
-    const int gg = idx >> 7, j = idx & (kD - 1);
-    sm.qrot[gg][j] = gg < nh ? __half2float(q[((long long)b * hq + h0 + gg) * kD + j]) : 0.0f;
-  }
-  __syncthreads();
-  for (int h = 1; h < kD; h <<= 1) {
-    for (int p = tid; p < kHeadGroup * (kD / 2); p += kTThreads) {
-      const int gg = p >> 6, pi = p & 63;
-      const int i = (pi / h) * 2 * h + (pi % h);
-      const float a = sm.qrot[gg][i], c = sm.qrot[gg][i + h];
-      sm.qrot[gg][i] = a + c;
-      sm.qrot[gg][i + h] = a - c;
-    }
-    __syncthreads();
-  }
+  // ---- rotated queries in LDS: wave w rotates heads 2 w and 2 w + 1 (channels 2 lane, +1)
   float qmax = 0.0f;
-  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads) {
-    const float v = sm.qrot[idx >> 7][idx & (kD - 1)] * 0.08838834764831845f;
-    sm.qrot[idx >> 7][idx & (kD - 1)] = v;
-    qmax = fmaxf(qmax, fabsf(v));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int gg = 2 * wave + k;
+    float o0 = 0.0f, o1 = 0.0f;
+    if (gg < nh) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h0 + gg) * kD)[lane];
+      o0 = fp16_bits_to_float(w & 0xFFFFu);
+      o1 = fp16_bits_to_float(w >> 16);
+    }
+    fwht_wave(o0, o1, lane);
+    o0 *= 0.08838834764831845f;
+    o1 *= 0.08838834764831845f;
+    *reinterpret_cast<float2*>(&sm.qrot[gg][2 * lane]) = make_float2(o0, o1);
+    qmax = fmaxf(qmax, fmaxf(fabsf(o0), fabsf(o1)));
   }
-  qmax = wave_max(qmax);
+  qmax = wave_max_nonneg(qmax);
   if (lane == 0) sm.red[wave] = qmax;
   __syncthreads();
   qmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-  // |q~ * pq| <= qmax * 448 * pq <= 2^14 keeps the hi part finite in fp16
+  // power-of-two query prescale pq: |q~ * pq| <= qmax * 448 * pq <= 2^14 keeps the hi part
+  // finite in fp16
   int qe = 0;
   frexpf(fmaxf(qmax, 1e-30f) * 448.0f, &qe);
   const float pq = ldexpf(1.0f, 14 - qe);
   const float scale2 = sm_scale * kLog2e;
   const float kfac = scale2 * 16.0f / pq;          // undoes the code / 16 encoding and pq
   const float kzfac = scale2 / pq;                 // multiplies pq * sum_j q~_j
-  for (int idx = tid; idx < kHeadGroup * kD; idx += kTThreads)
-    sm.qrot[idx >> 7][idx & (kD - 1)] *= pq;
-  __syncthreads();
+  // per-lane metadata factors (see decode_meta): pq on c-hat^K, kfac on s-hat^K, 1 on
+  // c-hat^V, 32 on s-hat^V; kzfac on z-hat^K, 1 on z-hat^V
+  const int mgrp = lane >> 4;
+  const float fm = mgrp == 0 ? pq : (mgrp == 1 ? kfac : (mgrp == 2 ? 1.0f : 32.0f));
+  const float fz = lane < 32 ? kzfac : 1.0f;
 
   // lane roles: m / s for operand rows and k groups, n for columns
   const int n = lane & 15, s = lane >> 4;
   const int gq = n & 7;                              // head of this column / row
   const bool colv = gq < nh;                         // column carries a real head
   const bool colhi = n < 8;
+  const float negk = colhi ? 0.0f : -1.0f;           // hi parts on columns 0-7, lo on 8-15
+  const int ih = colhi ? 0 : 2;                      // this lane's rows of each score block
+  const uint32_t vmask_col = colv ? 0xFFFFFFFFu : 0u;
   WaveMeta& wm = sm.wm[wave];
+  const float* kc = wm.f8;
+  const float* ks = wm.f8 + kT;
+  const float* vc = wm.f8 + 2 * kT;
+  const float* vs = wm.f8 + 3 * kT;
+  const float* kz = wm.h16;
+  const float* vz = wm.h16 + kT;
   // per-lane copies of the code masks (kept in VGPRs) and the wave-uniform exponent word
   uint32_t kmask = 0x03C003C0u, vmask = 0x03000300u;
   asm volatile("" : "+v"(kmask), "+v"(vmask));
@@ -250,15 +307,15 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
       else bad = true;                             // finishes this tile, then stops
     }
-    decode_meta(cur.meta, lane, wm, kfac, kzfac);   // wave-local LDS tables (in-order LDS)
+    decode_meta(cur.m8, cur.m16, lane, wm, fm, fz);   // wave-local LDS tables
 
-    // ---- query operand for this tile: pq q~ = pq q_rot * c-hat^K, hi (cols 0-7) or lo (8-15)
+    // ---- query operand for this tile: q' = pq * q_rot * c-hat^K, hi (cols 0-7) or lo (8-15);
     // element e of channel block c is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
     half8 qb[4];
-    float asum = 0.0f;                            // pq * sum_j q~_j over this lane's channels
+    float asum = 0.0f;                            // sum_j q'_j over this lane's channels
     {
       const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[gq] + 32 * s);
-      const float4* kc4 = reinterpret_cast<const float4*>(wm.kc + 32 * s);
+      const float4* kc4 = reinterpret_cast<const float4*>(kc + 32 * s);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
@@ -266,10 +323,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
         const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
         const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
         asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
-        uint32_t u0 = split_pair(x0, x4, colhi), u1 = split_pair(x1, x5, colhi);
-        uint32_t u2 = split_pair(x2, x6, colhi), u3 = split_pair(x3, x7, colhi);
-        if (!colv) u0 = u1 = u2 = u3 = 0u;
-        qb[c] = as_h8(u0, u1, u2, u3);
+        qb[c] = as_h8(hi_or_lo(x0, x4, negk) & vmask_col, hi_or_lo(x1, x5, negk) & vmask_col,
+                      hi_or_lo(x2, x6, negk) & vmask_col, hi_or_lo(x3, x7, negk) & vmask_col);
       }
     }
     asum += __shfl_xor(asum, 16);
@@ -297,32 +352,36 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
         cur.kw[mb] = *reinterpret_cast<const uint4*>(nrec + kKCodesOff + (16 * mb + m) * 64 + 16 * s);
-      cur.meta = *reinterpret_cast<const uint4*>(nrec + kKMetaOff + lane * 16);
+      cur.m8 = *reinterpret_cast<const uint2*>(nrec + off8);
+      cur.m16 = *reinterpret_cast<const uint2*>(nrec + off16);
     }
-    // hi + lo partial scores, then the full log2-domain score per token:
-    // D = pq sum_j (1 + code_j / 16) q~_j, so pq <q~, code> = 16 (D - asum)
+    // hi + lo partial scores of this lane's two rows, then the log2-domain score per token:
+    // D = sum_j (1 + code_j / 16) q'_j, so pq <q~, code> = 16 (D - asum)
+    float v[8][2];
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const int t0 = 16 * mb + 4 * s;
-      const float4 ks4 = *reinterpret_cast<const float4*>(wm.ks + t0);
-      const float4 kz4 = *reinterpret_cast<const float4*>(wm.kz + t0);
-      const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
-      const float kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float d = sc[mb][i] + dpp_ror8(sc[mb][i]);
-        const float v = fmaf(ksv[i], d - asum, kzv[i] * asum);
-        sc[mb][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      const float snd0 = colhi ? sc[mb][2] : sc[mb][0];
+      const float snd1 = colhi ? sc[mb][3] : sc[mb][1];
+      const float own0 = colhi ? sc[mb][0] : sc[mb][2];
+      const float own1 = colhi ? sc[mb][1] : sc[mb][3];
+      const float d0 = own0 + dpp_ror8(snd0), d1 = own1 + dpp_ror8(snd1);
+      const int t0 = 16 * mb + 4 * s + ih;
+      const float2 ks2 = *reinterpret_cast<const float2*>(ks + t0);
+      const float2 kz2 = *reinterpret_cast<const float2*>(kz + t0);
+      v[mb][0] = fmaf(ks2.x, d0 - asum, kz2.x * asum);
+      v[mb][1] = fmaf(ks2.y, d1 - asum, kz2.y * asum);
+      tmax = fmaxf(tmax, fmaxf(v[mb][0], v[mb][1]));
     }
+    tmax = fmaxf(tmax, dpp_ror8(tmax));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);   // 0 on the first tile
+    const bool upd = tmax > m_run + kLazy;        // also true on the first tile
+    const float mnew = upd ? tmax : m_run;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+    const bool rescale = __any(upd) && j > 0;     // wave-uniform
     float psum = 0.0f, beta = 0.0f, wsum = 0.0f;
-    // probabilities -> operand rows: hi(p s-hat^V 32) on rows 0-7, lo on rows 8-15;
+    // probabilities -> operand rows: hi(32 p s-hat^V) on rows 0-7, lo on rows 8-15;
     // element e of token block kb is token 32 kb + 16 (e / 4) + 4 s + e % 4
     half8 wa[4];
 #pragma unroll
@@ -330,23 +389,26 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       uint32_t u[4];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int mb = 2 * kb + h2, t0 = 16 * mb + 4 * s;
-        const float4 vs4 = *reinterpret_cast<const float4*>(wm.vs + t0);
-        const float4 vz4 = *reinterpret_cast<const float4*>(wm.vz + t0);
-        const float p0 = __builtin_amdgcn_exp2f(sc[mb][0] - mnew);
-        const float p1 = __builtin_amdgcn_exp2f(sc[mb][1] - mnew);
-        const float p2 = __builtin_amdgcn_exp2f(sc[mb][2] - mnew);
-        const float p3 = __builtin_amdgcn_exp2f(sc[mb][3] - mnew);
-        psum += (p0 + p1) + (p2 + p3);
-        beta = fmaf(p0, vz4.x, fmaf(p1, vz4.y, fmaf(p2, vz4.z, fmaf(p3, vz4.w, beta))));
-        const float w0 = p0 * vs4.x, w1 = p1 * vs4.y, w2 = p2 * vs4.z, w3 = p3 * vs4.w;
-        wsum += (w0 + w1) + (w2 + w3);
-        u[2 * h2] = split_pair(w0, w1, colhi);
-        u[2 * h2 + 1] = split_pair(w2, w3, colhi);
+        const int mb = 2 * kb + h2, t0 = 16 * mb + 4 * s + ih;
+        const float2 vs2 = *reinterpret_cast<const float2*>(vs + t0);
+        const float2 vz2 = *reinterpret_cast<const float2*>(vz + t0);
+        const float p0 = __builtin_amdgcn_exp2f(v[mb][0] - mnew);
+        const float p1 = __builtin_amdgcn_exp2f(v[mb][1] - mnew);
+        psum += p0 + p1;
+        beta = fmaf(p0, vz2.x, fmaf(p1, vz2.y, beta));
+        const float w0 = p0 * vs2.x, w1 = p1 * vs2.y;
+        wsum += w0 + w1;
+        const uint32_t hh = pack_h2(w0, w1);
+        const uint32_t ll = lo_of(hh, w0, w1);
+        const uint32_t rcv = dpp_ror8_u(colhi ? ll : hh);
+        u[2 * h2] = (colhi ? hh : rcv) & vmask_col;       // rows 0, 1 of block mb
+        u[2 * h2 + 1] = (colhi ? rcv : ll) & vmask_col;   // rows 2, 3
       }
-      if (!colv) u[0] = u[1] = u[2] = u[3] = 0u;
       wa[kb] = as_h8(u[0], u[1], u[2], u[3]);
     }
+    psum += dpp_ror8(psum);
+    beta += dpp_ror8(beta);
+    wsum += dpp_ror8(wsum);
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
     beta += __shfl_xor(beta, 16);
@@ -364,13 +426,20 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
     }
 
     // ---- output: 8 channel blocks x 4 token blocks; each channel block's accumulator is
-    // folded into o~ as soon as its 4 products are done (rows 4 s + i: alpha and beta of
-    // their head, c-hat^V of column 16 nb + n)
+    // folded into o~ as soon as its 4 products are done (rows 4 s + i: beta of their head,
+    // c-hat^V of column 16 nb + n); rows are rescaled first when a running maximum moved
     {
-      const float4 a4 = *reinterpret_cast<const float4*>(wm.alpha + ((4 * s) & 7));
       const float4 b4 = *reinterpret_cast<const float4*>(wm.beta + 4 * s);
-      const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
       const float br[4] = {b4.x, b4.y, b4.z, b4.w};
+      if (rescale) {
+        const float4 a4 = *reinterpret_cast<const float4*>(wm.alpha + ((4 * s) & 7));
+        const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[nb][i] *= ar[i];
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         float4v po = {0.f, 0.f, 0.f, 0.f};
@@ -388,10 +457,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
           po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], as_h8(f[0], f[1], f[2], f[3]),
                                                       po, 0, 0, 0);
         }
-        const float cv = wm.vc[16 * nb + n];
+        const float cv = vc[16 * nb + n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          oacc[nb][i] = fmaf(ar[i], oacc[nb][i], cv * fmaf(po[i], 0.125f, br[i]));
+        for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], 0.125f, br[i]), oacc[nb][i]);
       }
     }
     if (nrec != nullptr) {
@@ -422,7 +490,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   __syncthreads();
   const int wbad = __syncthreads_or(bad ? 1 : 0);
   for (int idx = tid; idx < nh * kD; idx += kTThreads) {
-    const int gg = idx >> 7, j = idx & (kD - 1);
+    const int gg = idx >> 7, jj = idx & (kD - 1);
     float mm = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm.comb_m[w][gg]);
@@ -432,15 +500,15 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       for (int w = 0; w < kWaves; ++w) {
         const float f = exp2f(sm.comb_m[w][gg] - mm);
         ll = fmaf(f, sm.comb_l[w][gg], ll);
-        oo = fmaf(f, sm.comb_o[w][gg][j], oo);
+        oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
       }
     }
     float* p = partials + (((long long)b * hq + h0 + gg) * nsplit + split) * kPartialFloats;
-    if (j == 0) {
+    if (jj == 0) {
       p[0] = wbad ? NAN : mm;
       p[1] = wbad ? NAN : ll;
     }
-    p[2 + j] = oo;
+    p[2 + jj] = oo;
   }
 }
 
@@ -456,27 +524,6 @@ struct MergeSmem {
   float p[kT];              // staging probabilities exp2(s_t - m)
   float w[kMaxSplits];      // split weights exp2(m_split - m)
 };
-
-template <int kMask>
-__device__ __forceinline__ float lane_xor(float v) {
-  if constexpr (kMask == 1)
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  else if constexpr (kMask == 2)
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  else if constexpr (kMask == 8)
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
-  else if constexpr (kMask == 32)
-    return __shfl_xor(v, 32);
-  else   // 4, 16: swizzle in bit-mask mode, xor within 32 lanes
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (kMask << 10) | 0x1F));
-}
-
-// One butterfly stage across lanes: the lane with the bit clear gets own + partner, the lane
-// with it set gets partner - own.
-template <int kMask>
-__device__ __forceinline__ float fwht_lane_stage(float v, int lane) {
-  return fmaf((lane & kMask) ? -1.0f : 1.0f, v, lane_xor<kMask>(v));
-}
 
 // <q, k> over 128 channels: k is one fp16 staging row, q the fp32 query in LDS.
 __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, const float* qs) {
@@ -548,17 +595,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
       o1 = fmaf(w, v.y, o1);
     }
   }
-  {
-    const float a = o0 + o1, c = o0 - o1;
-    o0 = a;
-    o1 = c;
-  }
-  o0 = fwht_lane_stage<1>(o0, lane);   o1 = fwht_lane_stage<1>(o1, lane);
-  o0 = fwht_lane_stage<2>(o0, lane);   o1 = fwht_lane_stage<2>(o1, lane);
-  o0 = fwht_lane_stage<4>(o0, lane);   o1 = fwht_lane_stage<4>(o1, lane);
-  o0 = fwht_lane_stage<8>(o0, lane);   o1 = fwht_lane_stage<8>(o1, lane);
-  o0 = fwht_lane_stage<16>(o0, lane);  o1 = fwht_lane_stage<16>(o1, lane);
-  o0 = fwht_lane_stage<32>(o0, lane);  o1 = fwht_lane_stage<32>(o1, lane);
+  fwht_wave(o0, o1, lane);
   // raw staging output
   float r0 = 0.0f, r1 = 0.0f;
   const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
