@@ -60,7 +60,8 @@ struct WaveMeta {                  // per-wave, per-tile metadata (fp32, factors
 };
 
 struct TileSmem {
-  float qrot[kHeadGroup][kD];      // rotated queries (fp32)
+  float qrot[kHeadGroup][kD + 4];  // rotated queries (fp32); rows padded so the 8 heads read
+                                   // by one instruction start on different banks
   WaveMeta wm[kWaves];
   float comb_m[kWaves][kHeadGroup], comb_l[kWaves][kHeadGroup];
   float comb_o[kWaves][kHeadGroup][kD];
@@ -75,17 +76,24 @@ __device__ __forceinline__ float lane_xor(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
   else if constexpr (kMask == 8)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
-  else if constexpr (kMask == 32)
-    return __shfl_xor(v, 32);
-  else   // 4, 16: swizzle in bit-mask mode, xor within 32 lanes
+  else   // 4: swizzle in bit-mask mode, xor within 32 lanes
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (kMask << 10) | 0x1F));
 }
 
 // One butterfly stage across lanes: the lane with the bit clear gets own + partner, the lane
-// with it set gets partner - own.
+// with it set gets partner - own. Across lane bits 4 and 5 a permlane swap of the value with
+// itself gives (lower lane's value, upper lane's value) in every lane.
 template <int kMask>
 __device__ __forceinline__ float fwht_lane_stage(float v, int lane) {
-  return fmaf((lane & kMask) ? -1.0f : 1.0f, v, lane_xor<kMask>(v));
+  const float sgn = (lane & kMask) ? -1.0f : 1.0f;
+  if constexpr (kMask == 16 || kMask == 32) {
+    const auto r = kMask == 16
+        ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+        : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaf(sgn, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  } else {
+    return fmaf(sgn, v, lane_xor<kMask>(v));
+  }
 }
 
 // 128-point Walsh-Hadamard transform of a vector held as channels 2 lane, 2 lane + 1.
@@ -163,17 +171,40 @@ __device__ __forceinline__ int meta16_off(int lane) {
   return (lane < 32 ? kKMetaOff : kVMetaOff) + kZRel + 8 * (lane & 31);
 }
 
-__device__ __forceinline__ void load_tile(const uint8_t* __restrict__ rec, int lane, int off8,
-                                          int off16, TileRegs& r) {
-  const int m = lane & 15, s = lane >> 4;
+// Per-lane byte offsets (unsigned, so a load is a scalar tile base plus a 32-bit lane offset):
+// key codes of token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31 at koff + 1024 mb;
+// value-code section words 4 lane .. + 3 at voff + 1024 kb.
+struct LaneOffsets {
+  uint32_t koff, koff4, voff, off8, off16;
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  LaneOffsets o;
+  o.koff = kKCodesOff + (uint32_t)(lane & 15) * 64u + 16u * (uint32_t)(lane >> 4);
+  o.koff4 = o.koff + 4096u;
+  o.voff = kVCodesOff + 16u * (uint32_t)lane;
+  o.off8 = (uint32_t)meta8_off(lane);
+  o.off16 = (uint32_t)meta16_off(lane);
+  return o;
+}
+
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, const LaneOffsets& o,
+                                          TileRegs& r) {
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + kKCodesOff + (16 * mb + m) * 64 + 16 * s);
+  for (int mb = 0; mb < 4; ++mb)
+    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + o.koff + 1024u * mb);
+#pragma unroll
+  for (int mb = 4; mb < 8; ++mb)
+    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + o.koff4 + 1024u * (mb - 4));
+  r.m8 = *reinterpret_cast<const uint2*>(rec + o.off8);
+  r.m16 = *reinterpret_cast<const uint2*>(rec + o.off16);
+}
+
+__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, const LaneOffsets& o,
+                                            TileRegs& r) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
-    r.vw[kb] = *reinterpret_cast<const uint4*>(rec + kVCodesOff + kb * 1024 + lane * 16);
-  r.m8 = *reinterpret_cast<const uint2*>(rec + off8);
-  r.m16 = *reinterpret_cast<const uint2*>(rec + off16);
+    r.vw[kb] = *reinterpret_cast<const uint4*>(rec + o.voff + 1024u * kb);
 }
 
 // Every lane converts its 8 FP8 bytes and 4 fp16 values (the same instructions on all lanes)
@@ -221,18 +252,24 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave;
   auto fetch_ids = [&](int j0) -> int {
     const int j = j0 + lane;
-    return j < nw ? bt_row[kWaves * j] : 0;
+    return j < nw ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(bt_row) +
+                                                      16u * (uint32_t)j) : 0;
   };
   int ids = fetch_ids(0);
   auto block_of = [&](int j) -> long long {
     return (long long)__builtin_amdgcn_readlane(ids, j & 63);
   };
-  const int off8 = meta8_off(lane), off16 = meta16_off(lane);
+  const LaneOffsets lo = lane_offsets(lane);
   TileRegs cur;
   if (nw > 0) {
     const long long blk = block_of(0);
-    if (blk < 0 || blk >= num_blocks) bad = true;
-    else load_tile(pool + (blk * hkv + g) * (long long)kTileBytes, lane, off8, off16, cur);
+    if (blk < 0 || blk >= num_blocks) {
+      bad = true;
+    } else {
+      const uint8_t* rec = pool + (blk * hkv + g) * (long long)kTileBytes;
+      load_keys(rec, lo, cur);
+      load_values(rec, lo, cur);
+    }
   }
 
   // ---- rotated queries in LDS: wave w rotates heads 2 w and 2 w + 1 (channels 2 lane, +1)
@@ -327,8 +364,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
                       hi_or_lo(x2, x6, negk) & vmask_col, hi_or_lo(x3, x7, negk) & vmask_col);
       }
     }
-    asum += __shfl_xor(asum, 16);
-    asum += __shfl_xor(asum, 32);                 // over all 128 channels of column n
+    asum = add_xor32(add_xor16(asum));            // over all 128 channels of column n
 
     // ---- scores: 8 token blocks x 4 channel blocks
     float4v sc[8];
@@ -347,14 +383,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       }
       sc[mb] = acc;
     }
-    if (nrec != nullptr) {
-      const int m = lane & 15;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-        cur.kw[mb] = *reinterpret_cast<const uint4*>(nrec + kKCodesOff + (16 * mb + m) * 64 + 16 * s);
-      cur.m8 = *reinterpret_cast<const uint2*>(nrec + off8);
-      cur.m16 = *reinterpret_cast<const uint2*>(nrec + off16);
-    }
+    if (nrec != nullptr) load_keys(nrec, lo, cur);
     // hi + lo partial scores of this lane's two rows, then the log2-domain score per token:
     // D = sum_j (1 + code_j / 16) q'_j, so pq <q~, code> = 16 (D - asum)
     float v[8][2];
@@ -374,8 +403,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       tmax = fmaxf(tmax, fmaxf(v[mb][0], v[mb][1]));
     }
     tmax = fmaxf(tmax, dpp_ror8(tmax));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor32(max_xor16(tmax));
     const bool upd = tmax > m_run + kLazy;        // also true on the first tile
     const float mnew = upd ? tmax : m_run;
     const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
@@ -409,12 +437,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
     psum += dpp_ror8(psum);
     beta += dpp_ror8(beta);
     wsum += dpp_ror8(wsum);
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    beta += __shfl_xor(beta, 16);
-    beta += __shfl_xor(beta, 32);
-    wsum += __shfl_xor(wsum, 16);
-    wsum += __shfl_xor(wsum, 32);
+    psum = add_xor32(add_xor16(psum));
+    beta = add_xor32(add_xor16(beta));
+    wsum = add_xor32(add_xor16(wsum));
     // output rows get D / 8 per tile: D = sum_t W_t (1 + code / 4), W = 32 p s-hat^V, so
     // sum_t p s-hat^V code = D / 8 - 4 sum_t p s-hat^V = D / 8 - wsum / 8
     beta = fmaf(-0.125f, wsum, beta);
@@ -462,11 +487,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
         for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], 0.125f, br[i]), oacc[nb][i]);
       }
     }
-    if (nrec != nullptr) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        cur.vw[kb] = *reinterpret_cast<const uint4*>(nrec + kVCodesOff + kb * 1024 + lane * 16);
-    }
+    if (nrec != nullptr) load_values(nrec, lo, cur);
   }
 
   // ---- combine the waves' states in LDS and write one partial per (split, head)
@@ -482,8 +503,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
     for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float other = __shfl_xor(oacc[nb][i], 32);
-        if (s < 2) sm.comb_o[wave][4 * s + i][16 * nb + n] = oacc[nb][i] + other;
+        const float both = add_xor32(oacc[nb][i]);
+        if (s < 2) sm.comb_o[wave][4 * s + i][16 * nb + n] = both;
       }
     }
   }
