@@ -536,15 +536,12 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 // grid (hq, batch), one wave per (sequence, query head): the staging tokens (exact fp32
 // attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
 // / l. Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
-// channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32.
+// channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32. Every global load
+// that does not depend on another is issued first; split weights and staging probabilities
+// are broadcast from the lane that computed them.
 constexpr int kMThreads = 64;
 constexpr int kMaxSplits = 64;
-
-struct MergeSmem {
-  float q[kD];              // raw query (fp32)
-  float p[kT];              // staging probabilities exp2(s_t - m)
-  float w[kMaxSplits];      // split weights exp2(m_split - m)
-};
+constexpr int kMergePreload = 8;          // splits whose o~ is loaded before the weights exist
 
 // <q, k> over 128 channels: k is one fp16 staging row, q the fp32 query in LDS.
 __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, const float* qs) {
@@ -567,29 +564,34 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out) {
-  __shared__ MergeSmem sm;
+  __shared__ float qs[kD];
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   const int group = hq / hkv, g = h / group;
+  const float* pp = partials + ((long long)b * hq + h) * nsplit * kPartialFloats;
+  // independent loads: this lane's split (m, l), the first splits' o~ pairs, the query pair
+  const float msp = lane < nsplit ? pp[lane * kPartialFloats] : -INFINITY;
+  const float lsp = lane < nsplit ? pp[lane * kPartialFloats + 1] : 0.0f;
+  const float* col = pp + 2 + 2 * lane;
+  float2 ov[kMergePreload];
+#pragma unroll
+  for (int sp = 0; sp < kMergePreload; ++sp)
+    ov[sp] = sp < nsplit ? *reinterpret_cast<const float2*>(col + sp * kPartialFloats)
+                         : make_float2(0.0f, 0.0f);
+  const uint32_t qw = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h) * kD)[lane];
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
   const int n_stage = bad ? 0 : (len & (kT - 1));
   const float scale2 = sm_scale * kLog2e;
   const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
   const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
-  {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h) * kD)[lane];
-    sm.q[2 * lane] = fp16_bits_to_float(w & 0xFFFFu);
-    sm.q[2 * lane + 1] = fp16_bits_to_float(w >> 16);
-  }
+  qs[2 * lane] = fp16_bits_to_float(qw & 0xFFFFu);
+  qs[2 * lane + 1] = fp16_bits_to_float(qw >> 16);
   __syncthreads();
-  // staging scores of tokens lane and lane + 64, split maxima and sums of lane's split
+  // staging scores of tokens lane and lane + 64
   float s0 = -INFINITY, s1 = -INFINITY;
-  if (lane < n_stage) s0 = staging_dot(sk + lane * kD, sm.q) * scale2;
-  if (lane + 64 < n_stage) s1 = staging_dot(sk + (lane + 64) * kD, sm.q) * scale2;
-  const float* pp = partials + ((long long)b * hq + h) * nsplit * kPartialFloats;
-  const float msp = lane < nsplit ? pp[lane * kPartialFloats] : -INFINITY;
-  const float lsp = lane < nsplit ? pp[lane * kPartialFloats + 1] : 0.0f;
+  if (lane < n_stage) s0 = staging_dot(sk + lane * kD, qs) * scale2;
+  if (lane + 64 < n_stage) s1 = staging_dot(sk + (lane + 64) * kD, qs) * scale2;
   const bool invalid = bad || __any(msp != msp);
   const float mm = wave_max(fmaxf(msp, fmaxf(s0, s1)));
   float ls = 0.0f, wsp = 0.0f, p0 = 0.0f, p1 = 0.0f;
@@ -600,18 +602,20 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
     ls = fmaf(wsp, lsp, p0 + p1);
   }
   ls = wave_sum(ls);
-  sm.w[lane] = wsp;
-  sm.p[lane] = p0;
-  sm.p[lane + 64] = p1;
-  __syncthreads();
   // merged rotated output o~ of channels 2 lane, 2 lane + 1
   float o0 = 0.0f, o1 = 0.0f;
   if (mm != -INFINITY && !invalid) {
-    const float* col = pp + 2 + 2 * lane;
-#pragma unroll 4
-    for (int sp = 0; sp < nsplit; ++sp) {
+#pragma unroll
+    for (int sp = 0; sp < kMergePreload; ++sp) {
+      if (sp < nsplit) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
+        o0 = fmaf(w, ov[sp].x, o0);
+        o1 = fmaf(w, ov[sp].y, o1);
+      }
+    }
+    for (int sp = kMergePreload; sp < nsplit; ++sp) {
       const float2 v = *reinterpret_cast<const float2*>(col + sp * kPartialFloats);
-      const float w = sm.w[sp];
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
       o0 = fmaf(w, v.x, o0);
       o1 = fmaf(w, v.y, o1);
     }
@@ -622,7 +626,8 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
   const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
   for (int t = 0; t < n_stage; ++t) {
     const uint32_t w = vcol[t * (kD / 2)];
-    const float pt = sm.p[t];
+    const int src = __float_as_int(t < 64 ? p0 : p1);
+    const float pt = __int_as_float(__builtin_amdgcn_readlane(src, t & 63));
     r0 = fmaf(pt, fp16_bits_to_float(w & 0xFFFFu), r0);
     r1 = fmaf(pt, fp16_bits_to_float(w >> 16), r1);
   }
