@@ -21,9 +21,10 @@
 // It does the transform (five butterfly stages in registers, two across lanes as DPP-sourced
 // fused multiply-adds), the row statistics and the codes; a thread's eight values of one m are
 // exactly one word of key nibbles, and its four values of one e are one byte of value crumbs.
-// Layout B gives thread (j, th) = (tid % 128, tid / 128) the 32 tokens 32 th .. 32 th + 31 of
-// channel j: the column statistics, read from a copy of the rotated tile kept in LDS for the
-// whole normalisation.
+// Layout B gives lane (j, th) = (16 wave + lane % 16, lane / 16) the 32 tokens th, th + 4, ...,
+// th + 124 of channel j: the column statistics, read from a copy of the rotated tile kept in LDS
+// for the whole normalisation and merged over the four lanes of a channel with permlane swaps,
+// so a round needs two barriers (after the columns, after the rows).
 //
 // Sign folding. A cross-lane butterfly computes x + s * partner with s = -1 on the lane holding
 // the upper index, which leaves that lane's values negated; after both cross stages a thread's
@@ -54,12 +55,10 @@ __device__ __forceinline__ int cpos(int c) { return c + ((c >> 6) << 2); }
 
 struct QuantSmem {
   alignas(16) float xt[kT][kXs];   // rotated tile, layout A -> B; reused to stage the packed codes
-  float u[kT];           // per-token multipliers 1 / r_t
+  float u[4][kT / 4];    // per-token multipliers 1 / r_t, token t at [t % 4][t / 4]
   float cs[kD];          // per-channel standard deviations (unrounded c before the gauge)
   float vinv[kCp];       // per-channel multipliers 1 / c_j (at cpos)
   float rq[kCp];         // per-channel rounding factor 2^-3.5 / c-hat_j (at cpos)
-  float colm[4][kD];     // per-quarter column shifted means
-  float colq[4][kD];     // per-quarter column centred sums of squares
   uint32_t meta[96];     // staged FP8 s-hat (32 words) and FP16 z-hat (64 words)
   uint32_t chat[32];     // staged FP8 c-hat
   float red[32];
@@ -108,6 +107,31 @@ __device__ __forceinline__ void fmac_xor2(float* a, float s) {
       : "v"(s));
 }
 
+// Maximum over the 16 lanes of each DPP row (quad pairs, then row rotations by 4 and 8).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  return fmaxf(x, dpp_f<0x128>(x));
+}
+
+// Chan's merge of two equal-count partials (shifted mean m, centred sum of squares q) held by
+// lanes l and l ^ kBits (16 or 32): a permlane swap of a value with itself gives the lower and
+// the upper lane's value on both lanes, so both get the same bits. nab = n_a n_b / (n_a + n_b).
+template <int kBits>
+__device__ __forceinline__ void merge_pair(float& m, float& q, float nab) {
+  const auto mm = kBits == 16
+      ? __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false)
+      : __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const auto qq = kBits == 16
+      ? __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false)
+      : __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+  const float m0 = __uint_as_float(mm[0]), m1 = __uint_as_float(mm[1]);
+  const float d = m0 - m1;
+  q = fmaf(nab * d, d, __uint_as_float(qq[0]) + __uint_as_float(qq[1]));
+  m = 0.5f * (m0 + m1);
+}
+
 // Code = rne(clamp(v, 0, qmax)) written into byte `sel` of `acc`: the conversion rounds to
 // nearest even and clamps below at 0; the upper clamp comes first.
 __device__ __forceinline__ uint32_t put_code(float v, float qmax, uint32_t sel, uint32_t acc) {
@@ -139,7 +163,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int t = tid >> 2, q0 = tid & 1, q1 = (tid >> 1) & 1;   // layout A
-  const int jj = tid & (kD - 1), th = tid >> 7;                 // layout B
+  const int jj = 16 * wave + (lane & 15), th = lane >> 4;     // layout B
   const int cbase = 8 * q0 + 64 * q1;                           // channel of x[0]
   const int pbase = cpos(cbase);                                // its LDS position
   const bool flip = (q0 ^ q1) != 0;                             // values carry a factor -1
@@ -190,7 +214,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
             make_float4(x[8 * m + h], x[8 * m + h + 1], x[8 * m + h + 2], x[8 * m + h + 3]);
     }
   }
-  if (tid < kT) sm.u[tid] = 1.0f;
+  if (tid < kT) sm.u[tid & 3][tid >> 2] = 1.0f;
   __syncthreads();
   float big = sm.red[0];
 #pragma unroll
@@ -199,7 +223,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     store_record_zero_tile(rec, is_v, tid);
     return;
   }
-  const float* xcol = &sm.xt[th * 32][cpos(jj)];  // column jj, tokens 32 th .., stride kXs
+  const float* xcol = &sm.xt[th][cpos(jj)];       // column jj, tokens th + 4 i, stride 4 kXs
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
@@ -212,42 +236,38 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
         k0 = xcol[0];
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const float y = xcol[i * kXs] - k0;
+          const float y = xcol[4 * i * kXs] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       } else {
-        const float* uu = sm.u + th * 32;
+        const float* uu = sm.u[th];
         k0 = xcol[0] * uu[0];
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          const float y = fmaf(xcol[i * kXs], uu[i], -k0);
+          const float y = fmaf(xcol[4 * i * kXs], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       }
-      sm.colm[th][jj] = fmaf(s1, 0.03125f, k0);
-      sm.colq[th][jj] = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
+      float mh = fmaf(s1, 0.03125f, k0);
+      float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
+      merge_pair<16>(mh, qh, 16.0f);              // token sets th, th ^ 1 (32 tokens each)
+      merge_pair<32>(mh, qh, 32.0f);              // then th ^ 2 (64 each)
+      const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * umax);
+      if (th == 0) sm.cs[jj] = sd;
+      if (it < iters - 1) {                       // the last row step does not change c
+        const float vi = __builtin_amdgcn_rcpf(sd);
+        if (th == 0) sm.vinv[cpos(jj)] = vi;
+        const float vm = row16_max(vi);           // the wave's 16 channels are one DPP row
+        if (lane == 0) sm.red[8 + wave] = vm;
+      }
     }
     __syncthreads();
-    if (th == 0) {
-      const float m0 = sm.colm[0][jj], m1 = sm.colm[1][jj];
-      const float m2 = sm.colm[2][jj], m3 = sm.colm[3][jj];
-      const float mean = 0.25f * ((m0 + m1) + (m2 + m3));
-      const float d0 = m0 - mean, d1 = m1 - mean, d2 = m2 - mean, d3 = m3 - mean;
-      const float qs = (sm.colq[0][jj] + sm.colq[1][jj]) + (sm.colq[2][jj] + sm.colq[3][jj]);
-      const float dd = fmaf(d0, d0, fmaf(d1, d1, fmaf(d2, d2, d3 * d3)));
-      const float sd = fmaxf(__builtin_amdgcn_sqrtf(fmaf(32.0f, dd, qs) * 0.0078125f),
-                             floor_unit * umax);
-      sm.cs[jj] = sd;
-      const float vi = __builtin_amdgcn_rcpf(sd);
-      sm.vinv[cpos(jj)] = vi;
-      const float vm = wave_max_nonneg(vi);
-      if (lane == 0) sm.red[8 + wave] = vm;       // waves 0 and 1
-    }
-    __syncthreads();
-    if (it == iters - 1) break;                   // the last row step does not change c
-    const float vmax = fmaxf(sm.red[8], sm.red[9]);
+    if (it == iters - 1) break;
+    float vmax = sm.red[8];
+#pragma unroll
+    for (int w = 1; w < kQThreads / 64; ++w) vmax = fmaxf(vmax, sm.red[8 + w]);
     // row step (layout A): std over channels of xt_tj * v_j
     {
       const float* vv = sm.vinv + pbase;
@@ -275,8 +295,8 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       }
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
-      if ((tid & 3) == 0) sm.u[t] = uinv;
-      const float um = wave_max_nonneg(uinv);
+      if ((tid & 3) == 0) sm.u[t & 3][t >> 2] = uinv;
+      const float um = max_xor32(max_xor16(row16_max(uinv)));
       if (lane == 0) sm.red[16 + wave] = um;
     }
     __syncthreads();
