@@ -139,3 +139,35 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
                 o = o_rot @ H128 + p[T * n_full:] @ sv
                 out[b, h] = o / p.sum()
     return out
+
+
+# ------------------------------------------------------------------ fp16 cache (comparison path)
+
+
+def decode_attention_fp16(q, k_tiles, v_tiles, block_table, seq_lens, staging_k, staging_v,
+                          sm_scale):
+    """Exact softmax attention over an unquantised paged fp16 cache: the comparison point for
+    the packed cache ([GR] "Reported benchmarks and the verification gap" compares KVarN with
+    FP16 serving on the same model).
+
+    k_tiles, v_tiles: [num_blocks, Hkv, 128, 128] fp16, logical content of each block (token,
+    channel); block_table, seq_lens, staging and q as in decode_attention(). The same cache
+    model: floor(L/128) blocks, then L mod 128 staging tokens. Returns [B, Hq, 128] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, _ = q.shape
+    hkv = staging_k.shape[1]
+    group = hq // hkv
+    out = np.zeros((bsz, hq, D))
+    for b in range(bsz):
+        length = int(seq_lens[b])
+        n_full, tail = length // T, length % T
+        for g in range(hkv):
+            blocks = [block_table[b, i] for i in range(n_full)]
+            keys = np.concatenate([np.asarray(k_tiles[blk, g], dtype=np.float64) for blk in blocks]
+                                  + [np.asarray(staging_k[b, g, :tail], dtype=np.float64)], axis=0)
+            values = np.concatenate([np.asarray(v_tiles[blk, g], dtype=np.float64) for blk in blocks]
+                                    + [np.asarray(staging_v[b, g, :tail], dtype=np.float64)], axis=0)
+            for h in range(g * group, (g + 1) * group):
+                out[b, h] = softmax_attend(q[b, h], keys, values, sm_scale)
+    return out
+

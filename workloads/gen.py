@@ -159,6 +159,18 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None) -> dict:
                 num_blocks=num_blocks, sequences=list(chosen))
 
 
+def tiles_by_block(st: dict, hkv: int) -> tuple:
+    """The prefill tiles of a prefill() state as block-indexed arrays [num_blocks, Hkv, 128,
+    128] fp16 (K and V; blocks that hold no prefill tile are zero): the logical content of an
+    unquantised paged cache."""
+    kt = np.zeros((st["num_blocks"], hkv, T, D), np.float16)
+    vt = np.zeros_like(kt)
+    for i, blk in enumerate(st["dst_blocks"]):
+        kt[blk] = np.transpose(st["k"][T * i:T * (i + 1)], (1, 0, 2))
+        vt[blk] = np.transpose(st["v"][T * i:T * (i + 1)], (1, 0, 2))
+    return kt, vt
+
+
 def query(sp: Spec, dense: bool = False) -> np.ndarray:
     """Decode queries fp16 [B, Hq, 128], N(0, 1) (reading R21).
 
