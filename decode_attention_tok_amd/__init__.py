@@ -52,6 +52,11 @@ _SIGNATURES = {
     "kvarn_decode_attention": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P, _P,
                                               ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                               _P]),
+    "kvarn_fp16_block_bytes": (ctypes.c_size_t, [_CFG]),
+    "kvarn_fp16_write_tiles": (ctypes.c_int, [_CFG, _P, _P, _I64, _I32, _P, _P, _I64, _P]),
+    "kvarn_decode_attention_fp16": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P,
+                                                   _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                                   _I32, _P]),
     "kvarn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvarn_abi_version": (ctypes.c_int32, []),
 }
@@ -158,3 +163,40 @@ def decode_attention(cfg: Config, q, block_pool, block_table, seq_lens, staging_
                                         _ptr(seq_lens), _ptr(staging_k), _ptr(staging_v),
                                         float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                         batch, _stream(stream)))
+
+
+# ------------------------------------------------------------------ fp16 cache (comparison path)
+
+FP16_RECORD_BYTES = 65536
+
+
+def fp16_block_bytes(cfg: Config) -> int:
+    return int(lib().kvarn_fp16_block_bytes(ctypes.byref(cfg)))
+
+
+def fp16_write_tiles(cfg: Config, k, v, dst_blocks, block_pool, token_stride=None, stream=None):
+    """k, v fp16 [n_tiles * 128, ...] with stride(0) = token_stride; tile i goes to fp16 block
+    dst_blocks[i] of block_pool (uint8 device tensor of num_blocks fp16 blocks)."""
+    n_tiles = dst_blocks.numel()
+    stride = k.stride(0) if token_stride is None else token_stride
+    num_blocks = block_pool.numel() // fp16_block_bytes(cfg)
+    _check("kvarn_fp16_write_tiles",
+           lib().kvarn_fp16_write_tiles(ctypes.byref(cfg), _ptr(k), _ptr(v), stride, n_tiles,
+                                        _ptr(dst_blocks), _ptr(block_pool), num_blocks,
+                                        _stream(stream)))
+
+
+def decode_attention_fp16(cfg: Config, q, block_pool, block_table, seq_lens, staging_k,
+                          staging_v, sm_scale, out, workspace, stream=None):
+    """decode_attention() over an fp16 pool (block_pool: fp16 blocks of fp16_block_bytes)."""
+    batch, hq, _ = q.shape
+    max_blocks = block_table.shape[1]
+    num_blocks = block_pool.numel() // fp16_block_bytes(cfg)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("kvarn_decode_attention_fp16",
+           lib().kvarn_decode_attention_fp16(ctypes.byref(cfg), _ptr(q), hq, _ptr(block_pool),
+                                             num_blocks, _ptr(block_table), max_blocks,
+                                             _ptr(seq_lens), _ptr(staging_k), _ptr(staging_v),
+                                             float(sm_scale), _ptr(out), _ptr(workspace),
+                                             ws_bytes, batch, _stream(stream)))
+

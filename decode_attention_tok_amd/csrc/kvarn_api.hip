@@ -135,6 +135,64 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int3
       static_cast<hipStream_t>(stream)));
 }
 
+size_t kvarn_fp16_block_bytes(const kvarn_config* cfg) {
+  return check_config(cfg) == KVARN_OK
+             ? (size_t)KVARN_FP16_RECORD_BYTES * (size_t)cfg->num_kv_heads
+             : 0;
+}
+
+kvarn_status kvarn_fp16_write_tiles(const kvarn_config* cfg, const void* k, const void* v,
+                                    int64_t token_stride, int32_t n_tiles,
+                                    const int32_t* dst_blocks, void* block_pool,
+                                    int64_t num_blocks, void* stream) {
+  kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  if (n_tiles < 0 || num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (n_tiles == 0) return KVARN_OK;
+  if (k == nullptr || v == nullptr || dst_blocks == nullptr || block_pool == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (token_stride < (int64_t)cfg->num_kv_heads * KVARN_HEAD_DIM || token_stride % 8 != 0 ||
+      !aligned16(k) || !aligned16(v) || !aligned16(block_pool))
+    return KVARN_ERR_BAD_SHAPE;
+  if ((long long)cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
+  return from_hip(kvarn::launch_fp16_write_tiles(
+      static_cast<const __half*>(k), static_cast<const __half*>(v), token_stride, n_tiles,
+      cfg->num_kv_heads, dst_blocks, static_cast<uint8_t*>(block_pool), num_blocks,
+      static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
+                                         int32_t num_q_heads, const void* block_pool,
+                                         int64_t num_blocks, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                         const void* staging_k, const void* staging_v,
+                                         float sm_scale, float* out, void* workspace,
+                                         size_t workspace_bytes, int32_t batch, void* stream) {
+  size_t need = 0;
+  kvarn_status st = kvarn_decode_workspace_bytes(cfg, batch, num_q_heads, max_blocks_per_seq,
+                                                 &need);
+  if (st != KVARN_OK) return st;
+  if (num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (batch == 0) return KVARN_OK;
+  if (q == nullptr || block_pool == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      staging_k == nullptr || staging_v == nullptr || out == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (workspace == nullptr || workspace_bytes < need) return KVARN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVARN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(staging_k) || !aligned16(staging_v) || !aligned16(out) ||
+      !aligned16(block_pool))
+    return KVARN_ERR_BAD_SHAPE;
+  if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
+  if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
+  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  return from_hip(kvarn::launch_decode_fp16(
+      static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads,
+      static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
+      seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
+      sm_scale, out, static_cast<float*>(workspace), splits, batch,
+      static_cast<hipStream_t>(stream)));
+}
+
 const char* kvarn_status_string(kvarn_status status) {
   switch (status) {
     case KVARN_OK: return "ok";

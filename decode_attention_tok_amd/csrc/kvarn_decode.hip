@@ -535,7 +535,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 
 // grid (hq, batch), one wave per (sequence, query head): the staging tokens (exact fp32
 // attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
-// / l. Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
+// / l (the fp16-cache path's partials are not rotated: o + o_raw, / l). Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
 // channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32. Every global load
 // that does not depend on another is issued first; split weights and staging probabilities
 // are broadcast from the lane that computed them.
@@ -559,6 +559,7 @@ __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, co
   return acc0 + acc1;
 }
 
+template <bool kRotated>
 __global__ void __launch_bounds__(kMThreads)
 decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_blocks,
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
@@ -620,7 +621,8 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
       o1 = fmaf(w, v.y, o1);
     }
   }
-  fwht_wave(o0, o1, lane);
+  if constexpr (kRotated) fwht_wave(o0, o1, lane);
+  constexpr float kBack = kRotated ? 0.08838834764831845f : 1.0f;   // H / sqrt(128) or none
   // raw staging output
   float r0 = 0.0f, r1 = 0.0f;
   const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
@@ -635,10 +637,277 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
   if (invalid) {
     res = make_float2(NAN, NAN);
   } else if (ls > 0.0f) {
-    res.x = fmaf(o0, 0.08838834764831845f, r0) / ls;
-    res.y = fmaf(o1, 0.08838834764831845f, r1) / ls;
+    res.x = fmaf(o0, kBack, r0) / ls;
+    res.y = fmaf(o1, kBack, r1) / ls;
   }
   reinterpret_cast<float2*>(out + ((long long)b * hq + h) * kD)[lane] = res;
+}
+
+
+// ------------------------------------------------------------------ fp16 cache (comparison path)
+//
+// The unquantised paged cache the packed cache is compared with. Record of one (block, KV
+// head): 65,536 bytes. Keys at byte 0: token-major [t][ch] fp16. Values at byte 32,768:
+// channel-major [ch][position] fp16, where position 32 kb + 8 s + e of each row holds token
+// 32 kb + 16 (e / 4) + 4 s + e % 4: one 16-byte load then gives a lane exactly the eight tokens
+// its score accumulator rows hold (as in the packed value section), so the output product
+// needs no shuffles. Same decode structure as the packed tiles, with the query fp16 as given
+// (exact, so no hi/lo split: columns g and 8 + g both carry head g and each keeps two of its
+// four score rows) and the outputs accumulated in the MFMA accumulators (no per-tile scale).
+
+constexpr long long kFp16Rec = 65536;
+constexpr uint32_t kFp16VOff = 32768;
+constexpr float kFp16W = 32.0f;               // probability operand prescale (lo parts normal)
+
+__device__ __forceinline__ int fp16_v_token(int p) {
+  return 32 * (p >> 5) + 16 * ((p & 7) >> 2) + 4 * ((p >> 3) & 3) + (p & 3);
+}
+
+// grid: n_tiles * Hkv workgroups of 256 threads; id = tile * Hkv + head
+__global__ void __launch_bounds__(256)
+fp16_write_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v,
+                        long long token_stride, int n_tiles, int hkv,
+                        const int32_t* __restrict__ dst_blocks, uint8_t* __restrict__ pool,
+                        long long num_blocks) {
+  __shared__ uint16_t vt[kT][kD + 8];
+  const int id = blockIdx.x;
+  const int head = id % hkv, tile = id / hkv;
+  const int tid = threadIdx.x;
+  if (tile >= n_tiles) return;
+  const long long blk = dst_blocks[tile];
+  if (blk < 0 || blk >= num_blocks) return;
+  uint8_t* rec = pool + (blk * hkv + head) * kFp16Rec;
+  const __half* ks = k + (long long)tile * kT * token_stride + head * kD;
+  const __half* vs = v + (long long)tile * kT * token_stride + head * kD;
+  for (int r = tid; r < kT * 16; r += 256) {
+    const int t = r >> 4, c = r & 15;
+    *reinterpret_cast<uint4*>(rec + t * 256 + c * 16) =
+        *reinterpret_cast<const uint4*>(ks + (long long)t * token_stride + 8 * c);
+    *reinterpret_cast<uint4*>(&vt[t][8 * c]) =
+        *reinterpret_cast<const uint4*>(vs + (long long)t * token_stride + 8 * c);
+  }
+  __syncthreads();
+  for (int r = tid; r < kD * 16; r += 256) {
+    const int ch = r >> 4, pc = r & 15;
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int p0 = 8 * pc + 2 * d;
+      w[d] = (uint32_t)vt[fp16_v_token(p0)][ch] | ((uint32_t)vt[fp16_v_token(p0 + 1)][ch] << 16);
+    }
+    *reinterpret_cast<uint4*>(rec + kFp16VOff + ch * 256 + pc * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+struct alignas(16) Fp16Smem {
+  float alpha[kWaves][16];
+  float comb_m[kWaves][kHeadGroup], comb_l[kWaves][kHeadGroup];
+  float comb_o[kWaves][kHeadGroup][kD];
+};
+
+// Chunk i of a tile into buf: i < 8 -> keys of token block i (token 16 i + lane % 16, channels
+// 32 c + 8 (lane / 16) .. + 7, c = 0..3); i >= 8 -> values of channel block i - 8 (channel
+// 16 (i - 8) + lane % 16, positions 32 kb + 8 (lane / 16) .. + 7, kb = 0..3).
+__device__ __forceinline__ void fp16_chunk(const uint8_t* __restrict__ rec, int i, uint32_t off,
+                                           uint4 (&buf)[4]) {
+  const uint8_t* base = rec + (i < 8 ? 0u : kFp16VOff) + 4096u * (uint32_t)(i & 7);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) buf[c] = *reinterpret_cast<const uint4*>(base + off + 64u * c);
+}
+
+__global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
+                         const uint8_t* __restrict__ pool, long long num_blocks,
+                         const int32_t* __restrict__ block_table, int max_blocks,
+                         const int32_t* __restrict__ seq_lens, float sm_scale,
+                         float* __restrict__ partials) {
+  __shared__ Fp16Smem sm;
+  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  const int g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int group = hq / hkv;
+  const int h0 = g * group + hg * kHeadGroup;
+  const int nh = min(kHeadGroup, group - hg * kHeadGroup);
+  const int len = seq_lens[b];
+  bool bad = len < 0 || (len >> 7) > max_blocks;
+  const int n_full = bad ? 0 : (len >> 7);
+  const int chunk = (n_full + nsplit - 1) / nsplit;
+  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  const int ntile = i1 - i0;
+  const int nw = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave;
+  auto fetch_ids = [&](int j0) -> int {
+    const int j = j0 + lane;
+    return j < nw ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(bt_row) +
+                                                      16u * (uint32_t)j) : 0;
+  };
+  int ids = fetch_ids(0);
+  auto block_of = [&](int j) -> long long {
+    return (long long)__builtin_amdgcn_readlane(ids, j & 63);
+  };
+  const int n = lane & 15, s = lane >> 4;
+  const int gq = n & 7;
+  const bool colv = gq < nh;
+  const bool colhi = n < 8;
+  const uint32_t off = (uint32_t)(lane & 15) * 256u + 16u * (uint32_t)s;
+  const uint32_t vmask_col = colv ? 0xFFFFFFFFu : 0u;
+  // query operand: columns g and 8 + g carry head g as given, channel 32 c + 8 s + e
+  half8 qb[4];
+  {
+    const __half* qh = q + ((long long)b * hq + h0 + (colv ? gq : 0)) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 w = *reinterpret_cast<const uint4*>(qh + 32 * c + 8 * s);
+      w.x &= vmask_col; w.y &= vmask_col; w.z &= vmask_col; w.w &= vmask_col;
+      qb[c] = __builtin_bit_cast(half8, w);
+    }
+  }
+  const float scale2 = sm_scale * kLog2e;
+  const int ih = colhi ? 0 : 2;
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  // ring of four chunk buffers; chunk i of every tile lives in buf[i % 4] (16 chunks a tile),
+  // loaded three chunks ahead, across tile boundaries
+  uint4 buf[4][4];
+  const uint8_t* rec = nullptr;
+  if (nw > 0) {
+    const long long blk = block_of(0);
+    if (blk < 0 || blk >= num_blocks) bad = true;
+    else rec = pool + (blk * hkv + g) * kFp16Rec;
+  }
+  if (rec != nullptr) {
+    fp16_chunk(rec, 0, off, buf[0]);
+    fp16_chunk(rec, 1, off, buf[1]);
+    fp16_chunk(rec, 2, off, buf[2]);
+  }
+  for (int j = 0; j < nw && !bad; ++j) {
+    const uint8_t* nrec = nullptr;
+    if (j + 1 < nw) {
+      if (((j + 1) & 63) == 0) ids = fetch_ids(j + 1);
+      const long long blk = block_of(j + 1);
+      if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * kFp16Rec;
+      else bad = true;
+    }
+    float4v sc[8];
+    half8 wa[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < 8) {
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, buf[i & 3][c]),
+                                                       qb[c], acc, 0, 0, 0);
+        sc[i] = acc;
+      } else {
+        const int nb = i - 8;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb],
+                                                            __builtin_bit_cast(half8, buf[i & 3][kb]),
+                                                            oacc[nb], 0, 0, 0);
+      }
+      {
+        const int ni = i + 3;
+        if (ni < 16) fp16_chunk(rec, ni, off, buf[ni & 3]);
+        else if (nrec != nullptr) fp16_chunk(nrec, ni - 16, off, buf[ni & 3]);
+      }
+      if (i == 7) {
+        // scores of this lane's two rows of each block (both column lanes hold all four)
+        float v[8][2];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          v[mb][0] = (colhi ? sc[mb][0] : sc[mb][2]) * scale2;
+          v[mb][1] = (colhi ? sc[mb][1] : sc[mb][3]) * scale2;
+          tmax = fmaxf(tmax, fmaxf(v[mb][0], v[mb][1]));
+        }
+        tmax = fmaxf(tmax, dpp_ror8(tmax));
+        tmax = max_xor32(max_xor16(tmax));
+        const bool upd = tmax > m_run + kLazy;
+        const float mnew = upd ? tmax : m_run;
+        const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+        const bool rescale = __any(upd) && j > 0;
+        float psum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          uint32_t u[4];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int mb = 2 * kb + h2;
+            const float p0 = __builtin_amdgcn_exp2f(v[mb][0] - mnew);
+            const float p1 = __builtin_amdgcn_exp2f(v[mb][1] - mnew);
+            psum += p0 + p1;
+            const float w0 = p0 * kFp16W, w1 = p1 * kFp16W;
+            const uint32_t hh = pack_h2(w0, w1);
+            const uint32_t ll = lo_of(hh, w0, w1);
+            const uint32_t rcv = dpp_ror8_u(colhi ? ll : hh);
+            u[2 * h2] = (colhi ? hh : rcv) & vmask_col;
+            u[2 * h2 + 1] = (colhi ? rcv : ll) & vmask_col;
+          }
+          wa[kb] = as_h8(u[0], u[1], u[2], u[3]);
+        }
+        psum += dpp_ror8(psum);
+        psum = add_xor32(add_xor16(psum));
+        l_run = fmaf(alpha, l_run, psum);
+        m_run = mnew;
+        if (s == 0) sm.alpha[wave][n] = alpha;
+        if (rescale) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&sm.alpha[wave][(4 * s) & 7]);
+          const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[nb][r] *= ar[r];
+          }
+        }
+      }
+    }
+    rec = nrec;
+  }
+
+  // ---- combine the waves' states (outputs carry the factor kFp16W)
+  __syncthreads();
+  if (s == 0 && colhi) {
+    sm.comb_m[wave][n] = m_run;
+    sm.comb_l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float both = add_xor32(oacc[nb][r]);
+      if (s < 2) sm.comb_o[wave][4 * s + r][16 * nb + n] = both * (1.0f / kFp16W);
+    }
+  }
+  __syncthreads();
+  const int wbad = __syncthreads_or(bad ? 1 : 0);
+  for (int idx = tid; idx < nh * kD; idx += kTThreads) {
+    const int gg = idx >> 7, jj = idx & (kD - 1);
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm.comb_m[w][gg]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(sm.comb_m[w][gg] - mm);
+        ll = fmaf(f, sm.comb_l[w][gg], ll);
+        oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
+      }
+    }
+    float* pp = partials + (((long long)b * hq + h0 + gg) * nsplit + split) * kPartialFloats;
+    if (jj == 0) {
+      pp[0] = wbad ? NAN : mm;
+      pp[1] = wbad ? NAN : ll;
+    }
+    pp[2 + jj] = oo;
+  }
 }
 
 }  // namespace
@@ -665,9 +934,35 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
                      sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(hq, batch), dim3(kMThreads), 0, stream, q, hq,
-                     hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, splits,
-                     out);
+  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq, batch), dim3(kMThreads), 0, stream, q,
+                     hq, hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
+                     splits, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp16_write_tiles(const __half* k, const __half* v, long long token_stride,
+                                   int n_tiles, int hkv, const int32_t* dst_blocks,
+                                   uint8_t* pool, long long num_blocks, hipStream_t stream) {
+  const long long groups = (long long)hkv * n_tiles;
+  hipLaunchKernelGGL(fp16_write_tiles_kernel, dim3((unsigned)groups), dim3(256), 0, stream, k, v,
+                     token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* pool,
+                              long long num_blocks, const int32_t* block_table, int max_blocks,
+                              const int32_t* seq_lens, const __half* staging_k,
+                              const __half* staging_v, float sm_scale, float* out,
+                              float* partials, int splits, int batch, hipStream_t stream) {
+  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  hipLaunchKernelGGL(decode_fp16_tiles_kernel, dim3(splits, hkv * ngroups, batch),
+                     dim3(kTThreads), 0, stream, q, hq, hkv, pool, num_blocks, block_table,
+                     max_blocks, seq_lens, sm_scale, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(kMThreads), 0, stream, q,
+                     hq, hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
+                     splits, out);
   return hipGetLastError();
 }
 

@@ -28,6 +28,19 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
                          int splits, int batch, hipStream_t stream);
 
+// Unquantised fp16 paged cache (comparison path): 65,536-byte record per (block, KV head).
+constexpr long long kFp16RecordBytes = 65536;
+
+hipError_t launch_fp16_write_tiles(const __half* k, const __half* v, long long token_stride,
+                                   int n_tiles, int hkv, const int32_t* dst_blocks,
+                                   uint8_t* pool, long long num_blocks, hipStream_t stream);
+
+hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* pool,
+                              long long num_blocks, const int32_t* block_table, int max_blocks,
+                              const int32_t* seq_lens, const __half* staging_k,
+                              const __half* staging_v, float sm_scale, float* out,
+                              float* partials, int splits, int batch, hipStream_t stream);
+
 // Number of splits of each sequence's tiles for a decode launch (depends on sizes only).
 int decode_splits(int batch, int hkv, int max_blocks);
 

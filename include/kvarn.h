@@ -70,6 +70,7 @@ extern "C" {
 #define KVARN_TILE_TOKENS 128
 #define KVARN_HEAD_DIM 128
 #define KVARN_TILE_BYTES 13312
+#define KVARN_FP16_RECORD_BYTES 65536
 
 typedef enum {
   KVARN_OK = 0,
@@ -165,6 +166,38 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const voi
                                     const void* staging_v, float sm_scale, float* out,
                                     void* workspace, size_t workspace_bytes, int32_t batch,
                                     void* stream);
+
+/* ---- Unquantised fp16 paged cache: the comparison path. The pages compare KVarN with FP16
+ * serving of the same model ([GR] "Reported benchmarks and the verification gap"); these
+ * calls give the same decode over an fp16 cache with the same paging, staging and GQA
+ * rules, so the two can be measured on the same shapes. Record of one (block, KV head):
+ * KVARN_FP16_RECORD_BYTES = 65,536 bytes, keys first as fp16 [token][channel] (32,768 B),
+ * then values as fp16 [channel][position] (32,768 B), where position 32 kb + 8 s + e of a
+ * row holds token 32 kb + 16 (e / 4) + 4 s + e % 4 (kb, s in 0..3, e in 0..7). A block is
+ * num_kv_heads records, head-major, like the packed pool. */
+
+/* Bytes of one fp16 block: num_kv_heads * 65536, or 0 if the config is invalid. */
+KVARN_API size_t kvarn_fp16_block_bytes(const kvarn_config* cfg);
+
+/* Write whole tiles into the fp16 pool: the counterpart of kvarn_quantize_tiles, same
+ * arguments, layout rules and errors (k, v fp16 [n_tiles * 128][token_stride], tile i to
+ * block dst_blocks[i]; ids outside [0, num_blocks) are skipped); block_pool holds num_blocks
+ * fp16 blocks. */
+KVARN_API kvarn_status kvarn_fp16_write_tiles(const kvarn_config* cfg, const void* k, const void* v,
+                                    int64_t token_stride, int32_t n_tiles,
+                                    const int32_t* dst_blocks, void* block_pool,
+                                    int64_t num_blocks, void* stream);
+
+/* Exact softmax attention over the fp16 pool: the counterpart of kvarn_decode_attention, same
+ * arguments (block_pool holds fp16 blocks), workspace size (kvarn_decode_workspace_bytes),
+ * NaN rules and errors. */
+KVARN_API kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
+                                         int32_t num_q_heads, const void* block_pool,
+                                         int64_t num_blocks, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                         const void* staging_k, const void* staging_v,
+                                         float sm_scale, float* out, void* workspace,
+                                         size_t workspace_bytes, int32_t batch, void* stream);
 
 /* Static, NUL-terminated description of a status. */
 KVARN_API const char* kvarn_status_string(kvarn_status status);

@@ -136,6 +136,38 @@ def test_decode_validation(lib):
     assert call(q=ctypes.c_void_p(0x1004)) == SHAPE
 
 
+def test_fp16_path_validation(lib):
+    cfg = kv.default_config(8)
+    assert kv.fp16_block_bytes(cfg) == 8 * 65536
+    bad = kv.default_config(8)
+    bad.v_bits = 4
+    assert kv.fp16_block_bytes(bad) == 0
+    f = "kvarn_fp16_write_tiles"
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 256, 0, None, None, 0, None) == OK   # no-op
+    assert _call(lib, f, _cfg(), FAKE, None, 256, 1, FAKE, FAKE, 1, None) == NULL
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 128, 1, FAKE, FAKE, 1, None) == SHAPE  # < Hkv*128
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 256, 1, FAKE, ctypes.c_void_p(0x1008), 1,
+                 None) == SHAPE                                                  # misaligned pool
+    f = "kvarn_decode_attention_fp16"
+    cfgd = kv.default_config(2)
+    need = kv.decode_workspace_bytes(cfgd, 2, 8, 4)
+    good = [FAKE, 8, FAKE, 10, FAKE, 4, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+            ctypes.c_void_p(0x10000), need, 2, None]
+    def call(**over):
+        a = list(good)
+        names = ["q", "hq", "pool", "nblk", "bt", "maxb", "lens", "sk", "sv", "sm", "out", "ws",
+                 "wsb", "batch", "stream"]
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return _call(lib, f, _cfg(), *a)
+    assert call(batch=0) == OK
+    assert call(pool=None) == NULL
+    assert call(hq=7) == SHAPE
+    assert call(wsb=need - 4) == WS
+    assert call(pool=ctypes.c_void_p(0x1008)) == SHAPE
+    assert call(sm=ctypes.c_float(float("nan"))) == SHAPE
+
+
 def test_status_strings(lib):
     for code in range(6):
         assert lib.kvarn_status_string(code)
