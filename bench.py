@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
+    p.add_argument("--no-fp16-decode", action="store_true",
+                   help="skip the comparison decode over an unquantised fp16 cache")
     return p.parse_args()
 
 
@@ -70,13 +72,63 @@ def source_digest(part=None):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(lens, hkv, hq, appended):
-    """Bytes the method must move (not what an implementation happens to move)."""
+def algorithmic_bytes(lens, hkv, hq, appended, tile_bytes=TILE):
+    """Bytes the method must move (not what an implementation happens to move); tile_bytes is
+    the size of one (block, KV head) record: 13,312 packed, 65,536 for the fp16 cache."""
     n_full = [int(l) // T for l in lens]
     n_stage = [int(l) % T for l in lens]
-    decode = sum(n * hkv * TILE + s * hkv * 2 * D * 2 + 4 * n + 4 for n, s in zip(n_full, n_stage))
+    decode = sum(n * hkv * tile_bytes + s * hkv * 2 * D * 2 + 4 * n + 4
+                 for n, s in zip(n_full, n_stage))
     decode += len(lens) * hq * D * (2 + 4)                       # q in (fp16), out (fp32)
     return decode
+
+
+def fp16_decode_comparison(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm,
+                           ws_bytes, td, torch, np, dev):
+    """The same decode over an unquantised fp16 paged cache of the same tiles (the comparison
+    path), timed separately after the main loop: its own pools (replicas beyond 1.2 GB), the
+    main run's queries, staging tiles and lengths."""
+    import ctypes
+    V = ctypes.c_void_p
+    fp16_bytes = int(lib.kvarn_fp16_block_bytes(ctypes.byref(cfg)))
+    per = st["num_blocks"] * fp16_bytes
+    reps = max(2, min(16, math.ceil(1.2e9 / per)))
+    dst = dev(st["dst_blocks"])
+    k0, v0 = dev(st["k"]), dev(st["v"])
+    k0, v0 = k0.view(k0.shape[0], -1), v0.view(v0.shape[0], -1)
+    pools = []
+    for _ in range(reps):
+        pool = torch.zeros(st["num_blocks"] * fp16_bytes, dtype=torch.uint8, device="cuda")
+        kv.fp16_write_tiles(cfg, k0, v0, dst, pool)
+        pools.append(pool)
+    del k0, v0
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    f = lib.kvarn_decode_attention_fp16
+    calls = [(ctypes.byref(cfg), V(R[i % len(R)]["q"].data_ptr()), sp.hq, V(pools[i].data_ptr()),
+              st["num_blocks"], V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()),
+              V(R[i % len(R)]["sk"].data_ptr()), V(R[i % len(R)]["sv"].data_ptr()),
+              ctypes.c_float(sm), V(R[i % len(R)]["out"].data_ptr()),
+              V(R[i % len(R)]["ws"].data_ptr()), max(ws_bytes, 256), sp.batch,
+              V(stream.cuda_stream)) for i in range(reps)]
+    steps = max(10, args.steps // 4)
+    for i in range(max(2, args.warmup // 4)):
+        assert f(*calls[i % reps]) == 0
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        assert f(*calls[i % reps]) == 0
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t16 = sum(a.elapsed_time(b) for a, b in evs) / steps * 1e-3
+    b16 = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True, tile_bytes=65536)
+    print(f"# fp16-cache decode {t16 * 1e6:.1f} us over {reps} pools", file=sys.stderr,
+          flush=True)
+    return {"us": round(t16 * 1e6, 2), "gbps": round(b16 / t16 / 1e9, 1),
+            "frac_of_peak": round(b16 / t16 / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": b16,
+            "packed_speedup": round(t16 / td, 3)}
 
 
 def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
@@ -243,6 +295,11 @@ def main():
         b_.copy_(a)
         torch.cuda.synchronize()
 
+    fp16 = None
+    if not args.no_fp16_decode:
+        fp16 = fp16_decode_comparison(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R,
+                                      sm, ws_bytes, td, torch, np, dev)
+
     decode_gbps = d_bytes / td / 1e9
     quant_gbps = q_bytes / tq / 1e9
     timings = {"quantise": tq, "append": ta, "decode": td}
@@ -286,6 +343,7 @@ def main():
                      "frac_of_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
                      "us": round(tq * 1e6, 2), "algorithmic_bytes": q_bytes},
         "append": {"us": round(ta * 1e6, 2), "algorithmic_bytes": a_bytes},
+        "fp16_decode": fp16,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
