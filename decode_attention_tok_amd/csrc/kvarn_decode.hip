@@ -245,24 +245,17 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const int n_full = bad ? 0 : (len >> 7);
   const int chunk = (n_full + nsplit - 1) / nsplit;
   const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
-  // this wave's tiles: i0 + wave + 4 j, j < nw. Lane j holds the block id of tile j (ids are
-  // fetched 64 at a time with one vector load), tile j's id is read back as a scalar.
+  // this wave's tiles: i0 + wave + 4 j, j < nw. Block ids are scalar loads (the row pointer
+  // and j are wave-uniform), each issued one tile before the tile that needs it.
   const int ntile = i1 - i0;
-  const int nw = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave;
-  auto fetch_ids = [&](int j0) -> int {
-    const int j = j0 + lane;
-    return j < nw ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(bt_row) +
-                                                      16u * (uint32_t)j) : 0;
-  };
-  int ids = fetch_ids(0);
-  auto block_of = [&](int j) -> long long {
-    return (long long)__builtin_amdgcn_readlane(ids, j & 63);
-  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
   const LaneOffsets lo = lane_offsets(lane);
   TileRegs cur;
+  int id_next = nw > 1 ? bt_row[kWaves] : 0;        // tile 1
   if (nw > 0) {
-    const long long blk = block_of(0);
+    const long long blk = bt_row[0];
     if (blk < 0 || blk >= num_blocks) {
       bad = true;
     } else {
@@ -339,8 +332,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   for (int j = 0; j < nw && !bad; ++j) {
     const uint8_t* nrec = nullptr;
     if (j + 1 < nw) {
-      if (((j + 1) & 63) == 0) ids = fetch_ids(j + 1);
-      const long long blk = block_of(j + 1);
+      const long long blk = id_next;
+      if (j + 2 < nw) id_next = bt_row[kWaves * (j + 2)];
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
       else bad = true;                             // finishes this tile, then stops
     }
@@ -735,18 +728,12 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const int n_full = bad ? 0 : (len >> 7);
   const int chunk = (n_full + nsplit - 1) / nsplit;
   const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  // this wave's tiles: i0 + wave + 4 j, j < nw; block ids are scalar loads, one tile ahead
   const int ntile = i1 - i0;
-  const int nw = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave;
-  auto fetch_ids = [&](int j0) -> int {
-    const int j = j0 + lane;
-    return j < nw ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const uint8_t*>(bt_row) +
-                                                      16u * (uint32_t)j) : 0;
-  };
-  int ids = fetch_ids(0);
-  auto block_of = [&](int j) -> long long {
-    return (long long)__builtin_amdgcn_readlane(ids, j & 63);
-  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
+  int id_next = nw > 1 ? bt_row[kWaves] : 0;        // tile 1
   const int n = lane & 15, s = lane >> 4;
   const int gq = n & 7;
   const bool colv = gq < nh;
@@ -776,7 +763,7 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   uint4 buf[4][4];
   const uint8_t* rec = nullptr;
   if (nw > 0) {
-    const long long blk = block_of(0);
+    const long long blk = bt_row[0];
     if (blk < 0 || blk >= num_blocks) bad = true;
     else rec = pool + (blk * hkv + g) * kFp16Rec;
   }
@@ -788,8 +775,8 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   for (int j = 0; j < nw && !bad; ++j) {
     const uint8_t* nrec = nullptr;
     if (j + 1 < nw) {
-      if (((j + 1) & 63) == 0) ids = fetch_ids(j + 1);
-      const long long blk = block_of(j + 1);
+      const long long blk = id_next;
+      if (j + 2 < nw) id_next = bt_row[kWaves * (j + 2)];
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * kFp16Rec;
       else bad = true;
     }
