@@ -51,6 +51,8 @@ def parse():
                    help="also run one device copy of this many MiB (counter calibration)")
     p.add_argument("--no-fp16-decode", action="store_true",
                    help="skip the comparison decode over an unquantised fp16 cache")
+    p.add_argument("--no-multi-decode", action="store_true",
+                   help="skip the several-token (Q = 4) decode measurement")
     return p.parse_args()
 
 
@@ -129,6 +131,46 @@ def fp16_decode_comparison(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np,
     return {"us": round(t16 * 1e6, 2), "gbps": round(b16 / t16 / 1e9, 1),
             "frac_of_peak": round(b16 / t16 / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": b16,
             "packed_speedup": round(t16 / td, 3)}
+
+
+def multi_decode_measure(args, kv, lib, cfg, sp, bt, bt_np, lens, lens_np, R, sm, td, torch,
+                         np, dev, n_query=4):
+    """The several-token decode (query tokens = the last n_query cached tokens of each
+    sequence, causal) over the main run's packed pools, staging tiles and lengths, timed
+    separately after the main loop."""
+    import ctypes
+    from workloads import gen
+    V = ctypes.c_void_p
+    ws_m = kv.decode_multi_workspace_bytes(cfg, sp.batch, sp.hq, n_query, bt_np.shape[1])
+    qm = dev(gen.query_tokens(sp, n_query))
+    om = torch.empty(sp.batch, n_query, sp.hq, D, dtype=torch.float32, device="cuda")
+    wsm = torch.empty(max(ws_m, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    f = lib.kvarn_decode_attention_multi
+    reps = len(R)
+    calls = [(ctypes.byref(cfg), V(qm.data_ptr()), sp.hq, n_query, V(r["pool"].data_ptr()),
+              r["pool"].shape[0], V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()),
+              V(r["sk"].data_ptr()), V(r["sv"].data_ptr()), ctypes.c_float(sm), V(om.data_ptr()),
+              V(wsm.data_ptr()), max(ws_m, 256), sp.batch, V(stream.cuda_stream)) for r in R]
+    steps = max(10, args.steps // 4)
+    for i in range(max(2, args.warmup // 4)):
+        assert f(*calls[i % reps]) == 0
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        assert f(*calls[i % reps]) == 0
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    tm = sum(a.elapsed_time(b) for a, b in evs) / steps * 1e-3
+    bm = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True) + \
+        (n_query - 1) * len(lens_np) * sp.hq * D * (2 + 4)
+    print(f"# {n_query}-token decode {tm * 1e6:.1f} us", file=sys.stderr, flush=True)
+    return {"n_query": n_query, "us": round(tm * 1e6, 2), "gbps": round(bm / tm / 1e9, 1),
+            "frac_of_peak": round(bm / tm / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": bm,
+            "query_tokens_per_s": round(sp.batch * n_query / tm, 1),
+            "time_vs_one_token": round(tm / td, 3)}
 
 
 def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
@@ -300,6 +342,11 @@ def main():
         fp16 = fp16_decode_comparison(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R,
                                       sm, ws_bytes, td, torch, np, dev)
 
+    multi = None
+    if not args.no_multi_decode:
+        multi = multi_decode_measure(args, kv, lib, cfg, sp, bt, bt_np, lens, lens_np, R, sm, td,
+                                     torch, np, dev)
+
     decode_gbps = d_bytes / td / 1e9
     quant_gbps = q_bytes / tq / 1e9
     timings = {"quantise": tq, "append": ta, "decode": td}
@@ -344,6 +391,7 @@ def main():
                      "us": round(tq * 1e6, 2), "algorithmic_bytes": q_bytes},
         "append": {"us": round(ta * 1e6, 2), "algorithmic_bytes": a_bytes},
         "fp16_decode": fp16,
+        "multi_decode": multi,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),

@@ -52,6 +52,11 @@ _SIGNATURES = {
     "kvarn_decode_attention": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P, _P,
                                               ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                               _P]),
+    "kvarn_decode_multi_workspace_bytes": (ctypes.c_int, [_CFG, _I32, _I32, _I32, _I32,
+                                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "kvarn_decode_attention_multi": (ctypes.c_int, [_CFG, _P, _I32, _I32, _P, _I64, _P, _I32, _P,
+                                                    _P, _P, ctypes.c_float, _P, _P,
+                                                    ctypes.c_size_t, _I32, _P]),
     "kvarn_fp16_block_bytes": (ctypes.c_size_t, [_CFG]),
     "kvarn_fp16_write_tiles": (ctypes.c_int, [_CFG, _P, _P, _I64, _I32, _P, _P, _I64, _P]),
     "kvarn_decode_attention_fp16": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P,
@@ -163,6 +168,37 @@ def decode_attention(cfg: Config, q, block_pool, block_table, seq_lens, staging_
                                         _ptr(seq_lens), _ptr(staging_k), _ptr(staging_v),
                                         float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                         batch, _stream(stream)))
+
+
+MAX_QUERY_TOKENS = 16
+
+
+def decode_multi_workspace_bytes(cfg: Config, batch: int, num_q_heads: int, n_query: int,
+                                 max_blocks_per_seq: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("kvarn_decode_multi_workspace_bytes",
+           lib().kvarn_decode_multi_workspace_bytes(ctypes.byref(cfg), batch, num_q_heads,
+                                                    n_query, max_blocks_per_seq,
+                                                    ctypes.byref(out)))
+    return out.value
+
+
+def decode_attention_multi(cfg: Config, q, block_pool, block_table, seq_lens, staging_k,
+                           staging_v, sm_scale, out, workspace, stream=None):
+    """q fp16 [B, Q, Hq, 128]: the last Q tokens of each sequence, query token i at position
+    seq_lens[b] - Q + i, attending causally; out fp32 [B, Q, Hq, 128]; workspace of at least
+    decode_multi_workspace_bytes(...) bytes."""
+    batch, n_query, hq, _ = q.shape
+    max_blocks = block_table.shape[1]
+    num_blocks = block_pool.numel() // block_bytes(cfg)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("kvarn_decode_attention_multi",
+           lib().kvarn_decode_attention_multi(ctypes.byref(cfg), _ptr(q), hq, n_query,
+                                              _ptr(block_pool), num_blocks, _ptr(block_table),
+                                              max_blocks, _ptr(seq_lens), _ptr(staging_k),
+                                              _ptr(staging_v), float(sm_scale), _ptr(out),
+                                              _ptr(workspace), ws_bytes, batch,
+                                              _stream(stream)))
 
 
 # ------------------------------------------------------------------ fp16 cache (comparison path)

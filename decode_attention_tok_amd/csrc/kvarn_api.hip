@@ -88,32 +88,33 @@ kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, cons
       cfg->num_kv_heads, batch, cfg->sinkhorn_iters, static_cast<hipStream_t>(stream)));
 }
 
-kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
-                                          int32_t num_q_heads, int32_t max_blocks_per_seq,
-                                          size_t* bytes) {
+namespace {
+
+kvarn_status multi_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
+                                   int32_t n_query, int32_t max_blocks_per_seq, size_t* bytes) {
   kvarn_status st = check_config(cfg);
   if (st != KVARN_OK) return st;
   if (bytes == nullptr) return KVARN_ERR_NULL_ARG;
   if (batch < 0 || max_blocks_per_seq < 1 || num_q_heads < cfg->num_kv_heads ||
       num_q_heads % cfg->num_kv_heads != 0 ||
-      num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup)
+      num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup || n_query < 1 ||
+      n_query > kvarn::kMaxQuery)
     return KVARN_ERR_BAD_SHAPE;
   const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
-  *bytes = (size_t)batch * (size_t)num_q_heads * (size_t)splits * kvarn::kPartialFloats *
-           sizeof(float);
+  *bytes = (size_t)batch * (size_t)n_query * (size_t)num_q_heads * (size_t)splits *
+           kvarn::kPartialFloats * sizeof(float);
   return KVARN_OK;
 }
 
-kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int32_t num_q_heads,
-                                    const void* block_pool, int64_t num_blocks,
-                                    const int32_t* block_table, int32_t max_blocks_per_seq,
-                                    const int32_t* seq_lens, const void* staging_k,
-                                    const void* staging_v, float sm_scale, float* out,
-                                    void* workspace, size_t workspace_bytes, int32_t batch,
-                                    void* stream) {
+kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_heads,
+                          int32_t n_query, const void* block_pool, int64_t num_blocks,
+                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, const void* staging_k, const void* staging_v,
+                          float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                          int32_t batch, void* stream) {
   size_t need = 0;
-  kvarn_status st = kvarn_decode_workspace_bytes(cfg, batch, num_q_heads, max_blocks_per_seq,
-                                                 &need);
+  kvarn_status st = multi_workspace_bytes(cfg, batch, num_q_heads, n_query, max_blocks_per_seq,
+                                          &need);
   if (st != KVARN_OK) return st;
   if (num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
   if (batch == 0) return KVARN_OK;
@@ -128,11 +129,50 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int3
   const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_decode(
-      static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads,
+      static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads, n_query,
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
       seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
       sm_scale, out, static_cast<float*>(workspace), splits, batch,
       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
+                                          int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          size_t* bytes) {
+  return multi_workspace_bytes(cfg, batch, num_q_heads, 1, max_blocks_per_seq, bytes);
+}
+
+kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int32_t num_q_heads,
+                                    const void* block_pool, int64_t num_blocks,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    const int32_t* seq_lens, const void* staging_k,
+                                    const void* staging_v, float sm_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, int32_t batch,
+                                    void* stream) {
+  return decode_multi(cfg, q, num_q_heads, 1, block_pool, num_blocks, block_table,
+                      max_blocks_per_seq, seq_lens, staging_k, staging_v, sm_scale, out,
+                      workspace, workspace_bytes, batch, stream);
+}
+
+kvarn_status kvarn_decode_multi_workspace_bytes(const kvarn_config* cfg, int32_t batch,
+                                                int32_t num_q_heads, int32_t n_query,
+                                                int32_t max_blocks_per_seq, size_t* bytes) {
+  return multi_workspace_bytes(cfg, batch, num_q_heads, n_query, max_blocks_per_seq, bytes);
+}
+
+kvarn_status kvarn_decode_attention_multi(const kvarn_config* cfg, const void* q,
+                                          int32_t num_q_heads, int32_t n_query,
+                                          const void* block_pool, int64_t num_blocks,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* seq_lens, const void* staging_k,
+                                          const void* staging_v, float sm_scale, float* out,
+                                          void* workspace, size_t workspace_bytes, int32_t batch,
+                                          void* stream) {
+  return decode_multi(cfg, q, num_q_heads, n_query, block_pool, num_blocks, block_table,
+                      max_blocks_per_seq, seq_lens, staging_k, staging_v, sm_scale, out,
+                      workspace, workspace_bytes, batch, stream);
 }
 
 size_t kvarn_fp16_block_bytes(const kvarn_config* cfg) {

@@ -17,9 +17,12 @@
 // the 4 states are merged in LDS. Per tile a wave issues 64 MFMAs (v_mfma_f32_16x16x32_f16):
 //   scores  D[token][col] = codeK[token][ch] x Q[ch][col]   8 token blocks x 4 channel blocks
 //   output  O[row][ch]    = W[row][token] x codeV[token][ch] 4 token blocks x 8 channel blocks
-// Key codes enter the MFMA as normal fp16 halves 1 + code / 16 (the nibble shifted into
-// mantissa bits 6..9 under exponent 0x3C00); the constant 1 contributes sum_j q~_j, which the
-// score needs anyway and subtracts exactly. (The MFMA sums products of subnormal fp16 operands
+// Key codes enter the MFMA as normal fp16 halves (code - 7.5) / 16: the nibble shifted into
+// mantissa bits 6..9 under exponent 0x3C00 gives 1 + code / 16, and one packed fp16 add
+// (exact) centres it; the centring term 7.5 / 16 * sum_j q~_j is added back in fp32. Centred
+// operands keep the products small next to the token-dependent part of the score: the matrix
+// core's accumulation error follows the largest products, and with 1 + code / 16 it reached
+// 2e-3 on outputs of magnitude 250 at 16K tokens, against 5e-4 centred. (The MFMA sums products of subnormal fp16 operands
 // with far less precision than products of normal ones, so raw codes are not used as
 // subnormals; a variant that left nibbles in the low mantissa bits, 1 + code / 1024 with the
 // query scaled to match, was far off as well, so every field sits just below the exponent.) Value codes likewise enter as 1 + code / 4 (the 2-bit
@@ -145,6 +148,11 @@ __device__ __forceinline__ uint32_t hi_or_lo(float a, float b, float negk) {
   return r;
 }
 
+// Both fp16 halves of w plus c (v_pk_add_f16; exact for the centring below).
+__device__ __forceinline__ uint32_t add_h2(uint32_t w, half2v c) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) + c);
+}
+
 // fp16 lo parts of a pair whose packed hi parts are h.
 __device__ __forceinline__ uint32_t lo_of(uint32_t h, float a, float b) {
   uint32_t r;
@@ -226,20 +234,25 @@ __device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int
 }
 
 __global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
+decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     const int32_t* __restrict__ seq_lens, float sm_scale,
                     float* __restrict__ partials) {
   __shared__ TileSmem sm;
   const int split = blockIdx.x, nsplit = gridDim.x;
-  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
+  // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
+  const int group = hq / hkv, vgroup = group * nq;
+  const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
   const int g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
   const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int group = hq / hkv;
-  const int h0 = g * group + hg * kHeadGroup;                 // first query head served
-  const int nh = min(kHeadGroup, group - hg * kHeadGroup);    // heads served (1..8)
+  const int vbase = hg * kHeadGroup;
+  const int nh = min(kHeadGroup, vgroup - vbase);             // rows served (1..8)
+  auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
+    return ((long long)b * nq + v / group) * hq + g * group + v % group;
+  };
   const int len = seq_lens[b];
   bool bad = len < 0 || (len >> 7) > max_blocks;
   const int n_full = bad ? 0 : (len >> 7);
@@ -272,7 +285,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
     const int gg = 2 * wave + k;
     float o0 = 0.0f, o1 = 0.0f;
     if (gg < nh) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h0 + gg) * kD)[lane];
+      const uint32_t w = reinterpret_cast<const uint32_t*>(q + row_of(vbase + gg) * kD)[lane];
       o0 = fp16_bits_to_float(w & 0xFFFFu);
       o1 = fp16_bits_to_float(w >> 16);
     }
@@ -308,6 +321,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   const float negk = colhi ? 0.0f : -1.0f;           // hi parts on columns 0-7, lo on 8-15
   const int ih = colhi ? 0 : 2;                      // this lane's rows of each score block
   const uint32_t vmask_col = colv ? 0xFFFFFFFFu : 0u;
+  // causal limit of this column's query token (position len - nq + i); only tiles that reach
+  // past len - nq are masked, and with nq <= 16 every packed tile keeps >= 112 visible tokens
+  const int qlim = len - nq + (vbase + gq) / group;
   WaveMeta& wm = sm.wm[wave];
   const float* kc = wm.f8;
   const float* ks = wm.f8 + kT;
@@ -319,6 +335,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   uint32_t kmask = 0x03C003C0u, vmask = 0x03000300u;
   asm volatile("" : "+v"(kmask), "+v"(vmask));
   const uint32_t one16 = __builtin_amdgcn_readfirstlane(0x3C003C00u);
+  const half2v kctr = {(_Float16)-1.46875f, (_Float16)-1.46875f};   // 1 + 7.5 / 16
 
   // running state: score-lane view (column n) and output-row view (rows 4 s + i)
   float m_run = -INFINITY, l_run = 0.0f;
@@ -358,6 +375,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       }
     }
     asum = add_xor32(add_xor16(asum));            // over all 128 channels of column n
+    const float asum_c = 0.46875f * asum;          // the centring term, 7.5 / 16 * asum
 
     // ---- scores: 8 token blocks x 4 channel blocks
     float4v sc[8];
@@ -368,19 +386,24 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         // nibble q of the word -> mantissa bits 6..9 of a half under exponent 0x3C00:
-        // the half is 1 + code / 16 (normal, exact); slots (q, q + 4) share a word
+        // 1 + code / 16, then (code - 7.5) / 16 (normal, exact); slots (q, q + 4) share a word
         const uint32_t w = w4[c];
-        const half8 a = as_h8(and_or(w << 6, kmask, one16), and_or(w << 2, kmask, one16),
-                              and_or(w >> 2, kmask, one16), and_or(w >> 6, kmask, one16));
+        const half8 a = as_h8(add_h2(and_or(w << 6, kmask, one16), kctr),
+                              add_h2(and_or(w << 2, kmask, one16), kctr),
+                              add_h2(and_or(w >> 2, kmask, one16), kctr),
+                              add_h2(and_or(w >> 6, kmask, one16), kctr));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], acc, 0, 0, 0);
       }
       sc[mb] = acc;
     }
     if (nrec != nullptr) load_keys(nrec, lo, cur);
     // hi + lo partial scores of this lane's two rows, then the log2-domain score per token:
-    // D = sum_j (1 + code_j / 16) q'_j, so pq <q~, code> = 16 (D - asum)
+    // D = sum_j (code_j - 7.5) / 16 q'_j, so pq <q~, code> = 16 (D + 7.5 / 16 asum)
     float v[8][2];
     float tmax = -INFINITY;
+    const int tpos = kT * (i0 + wave_u + kWaves * j);      // position of this tile's token 0
+    const bool masked = tpos + kT - 1 > len - nq;          // wave-uniform
+    const int tlim = qlim - tpos;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const float snd0 = colhi ? sc[mb][2] : sc[mb][0];
@@ -391,8 +414,12 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
       const int t0 = 16 * mb + 4 * s + ih;
       const float2 ks2 = *reinterpret_cast<const float2*>(ks + t0);
       const float2 kz2 = *reinterpret_cast<const float2*>(kz + t0);
-      v[mb][0] = fmaf(ks2.x, d0 - asum, kz2.x * asum);
-      v[mb][1] = fmaf(ks2.y, d1 - asum, kz2.y * asum);
+      v[mb][0] = fmaf(ks2.x, d0 + asum_c, kz2.x * asum);
+      v[mb][1] = fmaf(ks2.y, d1 + asum_c, kz2.y * asum);
+      if (masked) {
+        v[mb][0] = t0 > tlim ? -INFINITY : v[mb][0];
+        v[mb][1] = t0 + 1 > tlim ? -INFINITY : v[mb][1];
+      }
       tmax = fmaxf(tmax, fmaxf(v[mb][0], v[mb][1]));
     }
     tmax = fmaxf(tmax, dpp_ror8(tmax));
@@ -517,7 +544,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
         oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
       }
     }
-    float* p = partials + (((long long)b * hq + h0 + gg) * nsplit + split) * kPartialFloats;
+    float* p = partials + (row_of(vbase + gg) * nsplit + split) * kPartialFloats;
     if (jj == 0) {
       p[0] = wbad ? NAN : mm;
       p[1] = wbad ? NAN : ll;
@@ -526,7 +553,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
   }
 }
 
-// grid (hq, batch), one wave per (sequence, query head): the staging tokens (exact fp32
+// grid (nq * hq, batch), one wave per (sequence, query token, query head): the staging tokens
+// the query token sees (exact fp32
 // attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
 // / l (the fp16-cache path's partials are not rotated: o + o_raw, / l). Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
 // channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32. Every global load
@@ -554,15 +582,16 @@ __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, co
 
 template <bool kRotated>
 __global__ void __launch_bounds__(kMThreads)
-decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_blocks,
+decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int max_blocks,
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out) {
   __shared__ float qs[kD];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int qi = blockIdx.x / hq, h = blockIdx.x % hq, b = blockIdx.y;   // query token, head
   const int lane = threadIdx.x;
   const int group = hq / hkv, g = h / group;
-  const float* pp = partials + ((long long)b * hq + h) * nsplit * kPartialFloats;
+  const long long row = ((long long)b * nq + qi) * hq + h;              // row in [B][nq][hq]
+  const float* pp = partials + row * nsplit * kPartialFloats;
   // independent loads: this lane's split (m, l), the first splits' o~ pairs, the query pair
   const float msp = lane < nsplit ? pp[lane * kPartialFloats] : -INFINITY;
   const float lsp = lane < nsplit ? pp[lane * kPartialFloats + 1] : 0.0f;
@@ -572,10 +601,11 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
   for (int sp = 0; sp < kMergePreload; ++sp)
     ov[sp] = sp < nsplit ? *reinterpret_cast<const float2*>(col + sp * kPartialFloats)
                          : make_float2(0.0f, 0.0f);
-  const uint32_t qw = reinterpret_cast<const uint32_t*>(q + ((long long)b * hq + h) * kD)[lane];
+  const uint32_t qw = reinterpret_cast<const uint32_t*>(q + row * kD)[lane];
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
-  const int n_stage = bad ? 0 : (len & (kT - 1));
+  // staging tokens this query token sees: positions up to len - nq + qi
+  const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (nq - 1 - qi));
   const float scale2 = sm_scale * kLog2e;
   const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
   const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
@@ -633,7 +663,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int max_block
     res.x = fmaf(o0, kBack, r0) / ls;
     res.y = fmaf(o1, kBack, r1) / ls;
   }
-  reinterpret_cast<float2*>(out + ((long long)b * hq + h) * kD)[lane] = res;
+  reinterpret_cast<float2*>(out + row * kD)[lane] = res;
 }
 
 
@@ -910,20 +940,20 @@ int decode_splits(int batch, int hkv, int max_blocks) {
   return (int)s;
 }
 
-hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
+hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t* pool,
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
                          int splits, int batch, hipStream_t stream) {
-  const int ngroups = (hq / hkv + kHeadGroup - 1) / kHeadGroup;
+  const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   hipLaunchKernelGGL(decode_tiles_kernel, dim3(splits, hkv * ngroups, batch), dim3(kTThreads),
-                     0, stream, q, hq, hkv, pool, num_blocks, block_table, max_blocks, seq_lens,
-                     sm_scale, partials);
+                     0, stream, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
+                     seq_lens, sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq, batch), dim3(kMThreads), 0, stream, q,
-                     hq, hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
-                     splits, out);
+  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq * nq, batch), dim3(kMThreads), 0,
+                     stream, q, hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v,
+                     sm_scale, partials, splits, out);
   return hipGetLastError();
 }
 
@@ -948,7 +978,7 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(kMThreads), 0, stream, q,
-                     hq, hkv, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
+                     hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
                      splits, out);
   return hipGetLastError();
 }

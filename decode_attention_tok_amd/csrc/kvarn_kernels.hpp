@@ -10,6 +10,7 @@ namespace kvarn {
 // Floats per (sequence, query head, split) partial: m, l, rotated output.
 constexpr int kPartialFloats = 2 + 128;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxQuery = 16;        // query tokens per sequence in one multi-token decode
 
 hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
                                  int n_tiles, int hkv, const int32_t* dst_blocks,
@@ -22,7 +23,9 @@ hipError_t launch_append_token(const __half* k_new, const __half* v_new,
                                uint8_t* pool, long long num_blocks, int hkv, int batch,
                                int iters, hipStream_t stream);
 
-hipError_t launch_decode(const __half* q, int hq, int hkv, const uint8_t* pool,
+// nq query tokens per sequence (q, out: [batch][nq][hq][128]); query token i sits at position
+// len - nq + i and attends to positions 0 .. len - nq + i. nq = 1 is the one-token decode.
+hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t* pool,
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,

@@ -167,6 +167,35 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const voi
                                     void* workspace, size_t workspace_bytes, int32_t batch,
                                     void* stream);
 
+/* ---- Several query tokens per sequence (multi-token verification, chunked continuation).
+ * The pages place KVarN beside speculative decoding and multi-token prediction ([GR] "The 2-bit
+ * quantization field"); those steps score Q new tokens per sequence at once. Reading taken
+ * here: the Q tokens are the last Q of the sequence's L = seq_lens[b] tokens, already written
+ * to the cache (kvarn_append_token once per token), and query token i (0-based) sits at
+ * position L - Q + i and attends to positions 0 .. L - Q + i (causal); an empty range gives
+ * zeros. Q = 1 is exactly kvarn_decode_attention. */
+#define KVARN_MAX_QUERY_TOKENS 16
+
+/* Workspace for kvarn_decode_attention_multi (host), as kvarn_decode_workspace_bytes;
+ * KVARN_ERR_BAD_SHAPE unless 1 <= n_query <= KVARN_MAX_QUERY_TOKENS. */
+KVARN_API kvarn_status kvarn_decode_multi_workspace_bytes(const kvarn_config* cfg, int32_t batch,
+                                                int32_t num_q_heads, int32_t n_query,
+                                                int32_t max_blocks_per_seq, size_t* bytes);
+
+/* kvarn_decode_attention for n_query tokens per sequence:
+ *   q    (device) fp16 [batch][n_query][num_q_heads][128]
+ *   out  (device) fp32 [batch][n_query][num_q_heads][128]
+ *   workspace at least kvarn_decode_multi_workspace_bytes bytes, 256-byte aligned
+ * Every other argument, the NaN rules and the errors as kvarn_decode_attention. */
+KVARN_API kvarn_status kvarn_decode_attention_multi(const kvarn_config* cfg, const void* q,
+                                          int32_t num_q_heads, int32_t n_query,
+                                          const void* block_pool, int64_t num_blocks,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* seq_lens, const void* staging_k,
+                                          const void* staging_v, float sm_scale, float* out,
+                                          void* workspace, size_t workspace_bytes, int32_t batch,
+                                          void* stream);
+
 /* ---- Unquantised fp16 paged cache: the comparison path. The pages compare KVarN with FP16
  * serving of the same model ([GR] "Reported benchmarks and the verification gap"); these
  * calls give the same decode over an fp16 cache with the same paging, staging and GQA

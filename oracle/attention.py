@@ -102,6 +102,28 @@ def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_sc
     return out
 
 
+def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+    """Several query tokens per sequence (reading R25): q [B, Q, Hq, 128] holds the last Q of
+    each sequence's L tokens; query token i sits at position L - Q + i and attends to
+    positions 0 .. L - Q + i of the same cache (causal; an empty range gives zeros).
+    Returns [B, Q, Hq, 128] float64; Q = 1 is decode_attention()."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, nq, hq, _ = q.shape
+    hkv = staging_k.shape[1]
+    group = hq // hkv
+    out = np.zeros((bsz, nq, hq, D))
+    for b in range(bsz):
+        length = int(seq_lens[b])
+        for g in range(hkv):
+            keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length)
+            for i in range(nq):
+                n_vis = max(0, length - nq + i + 1)
+                for h in range(g * group, (g + 1) * group):
+                    out[b, i, h] = softmax_attend(q[b, i, h], keys[:n_vis], values[:n_vis],
+                                                  sm_scale)
+    return out
+
+
 def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
     """Folded form: the per-channel key scales and the rotation go into the query, the
     per-token key scale and zero-point into the score, the per-token value scale and

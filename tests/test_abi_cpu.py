@@ -55,6 +55,17 @@ def test_workspace_bytes_depends_only_on_sizes(lib):
     assert kv.decode_workspace_bytes(cfg, 0, 64, 128) == 0
 
 
+def test_multi_workspace_and_query_token_limits(lib):
+    cfg = kv.default_config(8)
+    one = kv.decode_workspace_bytes(cfg, 16, 64, 128)
+    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 1, 128) == one
+    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 4, 128) == 4 * one
+    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, kv.MAX_QUERY_TOKENS, 128) > 0
+    for bad in (0, -1, kv.MAX_QUERY_TOKENS + 1):
+        with pytest.raises(RuntimeError):
+            kv.decode_multi_workspace_bytes(cfg, 16, 64, bad, 128)
+
+
 def _call(lib, name, *args):
     return getattr(lib, name)(*args)
 
@@ -134,6 +145,28 @@ def test_decode_validation(lib):
     assert call(ws=ctypes.c_void_p(0x10010)) == WS  # not 256-byte aligned
     assert call(sm=ctypes.c_float(float("nan"))) == SHAPE
     assert call(q=ctypes.c_void_p(0x1004)) == SHAPE
+
+
+def test_decode_multi_validation(lib):
+    f = "kvarn_decode_attention_multi"
+    cfg = kv.default_config(2)
+    need = kv.decode_multi_workspace_bytes(cfg, 2, 8, 4, 4)
+    names = ["q", "hq", "nq", "pool", "nblk", "bt", "maxb", "lens", "sk", "sv", "sm", "out", "ws",
+             "wsb", "batch", "stream"]
+    good = [FAKE, 8, 4, FAKE, 10, FAKE, 4, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE,
+            ctypes.c_void_p(0x10000), need, 2, None]
+    def call(**over):
+        a = list(good)
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return _call(lib, f, _cfg(), *a)
+    assert call(batch=0) == OK
+    assert call(nq=0) == SHAPE
+    assert call(nq=17) == SHAPE
+    assert call(wsb=need - 4) == WS                  # sized for Q = 4
+    assert call(nq=5) == WS                          # needs more than the Q = 4 workspace
+    assert call(q=None) == NULL
+    assert call(hq=2 * 17) == SHAPE
 
 
 def test_fp16_path_validation(lib):

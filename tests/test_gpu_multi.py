@@ -1,0 +1,127 @@
+"""Parity of the several-token decode (kvarn_decode_attention_multi) with the oracle's
+decode_attention_multi (reading R25: the last Q tokens of each sequence, causal) on seeded
+inputs, through the C ABI. Same bar as the one-token decode: max-abs <= 2e-3."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_tok_amd as kv
+from oracle import attention as oatt
+from oracle import codec
+from workloads import gen
+
+from test_gpu_parity import TOL, _decode_case, _say, dev, gpu_decode
+
+pytestmark = pytest.mark.gpu
+T = D = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kv.lib()
+
+
+def gpu_multi(cfg, q, pool, bt, lens, sk, sv, sm):
+    b, nq, hq, _ = q.shape
+    ws = torch.empty(max(kv.decode_multi_workspace_bytes(cfg, b, hq, nq, bt.shape[1]), 256),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((b, nq, hq, D), -7.0, dtype=torch.float32, device="cuda")
+    pool_d = pool if isinstance(pool, torch.Tensor) else dev(pool)
+    kv.decode_attention_multi(cfg, dev(q), pool_d, dev(bt), dev(lens), dev(sk), dev(sv), sm,
+                              out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,over,tails,nq", [
+    # tails 0: every query token inside the last packed tile; 5 < Q = 8: the tokens straddle
+    # the tile boundary; 127: all in staging
+    ("qwen3-4b", dict(batch=3, ctx=384, hkv=2, hq=8), [0, 5, 127], 2),
+    ("qwen3-4b", dict(batch=3, ctx=384, hkv=2, hq=8), [0, 5, 127], 8),
+    ("qwen3-32b-16k", dict(batch=2, ctx=640, hkv=2, hq=16), [3, 0], 4),
+    ("qwen3-32b-16k", dict(batch=2, ctx=640, hkv=2, hq=16), [100, 9], 16),   # 16 x 8 rows
+    ("qwen3-4b", dict(batch=2, ctx=256, hkv=1, hq=16), [17, 0], 3),          # group 16
+    ("phi4-ragged", dict(batch=4, ragged=(128, 1024), hkv=2, hq=8), [0, 1, 2, 126], 5),
+])
+def test_multi_matches_oracle(name, over, tails, nq):
+    sp = gen.spec(name, **over)
+    pool, bt, lens, sk, sv, _, sm = _decode_case(sp, tails)
+    q = gen.query_tokens(sp, nq)
+    cfg = kv.default_config(sp.hkv)
+    got = gpu_multi(cfg, q, pool, bt, lens, sk, sv, sm)
+    ref = oatt.decode_attention_multi(q, pool, bt, lens, sk, sv, sm)
+    err = np.abs(got - ref).max()
+    _say(f"multi {name} {over} tails={tails} Q={nq}: max abs err {err:.3g}")
+    assert err <= TOL
+
+
+def test_one_query_token_equals_the_one_token_decode():
+    sp = gen.spec("qwen3-4b", batch=3, ctx=384, hkv=2, hq=8)
+    pool, bt, lens, sk, sv, q, sm = _decode_case(sp, [0, 5, 127])
+    cfg = kv.default_config(sp.hkv)
+    a = gpu_multi(cfg, q[:, None], pool, bt, lens, sk, sv, sm)
+    b = gpu_decode(cfg, q, pool, bt, lens, sk, sv, sm)
+    assert np.array_equal(a[:, 0], b)
+
+
+def test_multi_short_sequences_and_invalid_rows():
+    # lengths 0, 1, 2 with Q = 4 (early tokens see nothing: zeros), one valid row, and rows
+    # with a negative length or an out-of-range block id (NaN in every query token)
+    sp = gen.spec("qwen3-4b", batch=6, ctx=256, hkv=2, hq=4)
+    pool, bt, lens, sk, sv, _, sm = _decode_case(sp, [0, 0, 0, 0, 9, 0])
+    lens = lens.copy()
+    lens[:3] = [0, 1, 2]
+    lens[4] = -1
+    bt = bt.copy()
+    bt[5, 0] = pool.shape[0] + 3
+    q = gen.query_tokens(sp, 4)
+    cfg = kv.default_config(sp.hkv)
+    got = gpu_multi(cfg, q, pool, bt, lens, sk, sv, sm)
+    ref = oatt.decode_attention_multi(q[:4], pool, bt[:4], lens[:4], sk[:4], sv[:4], sm)
+    assert np.all(got[0] == 0) and np.all(got[1, :3] == 0) and np.all(got[2, :2] == 0)
+    assert np.abs(got[:4] - ref).max() <= TOL
+    assert np.isnan(got[4:]).all()
+
+
+def test_multi_full_size_sampled():
+    """The 16K workload at full size with Q = 4, launched as the benchmark launches it: one
+    (sequence, KV head) holds oracle records, the rest library-quantised device-generated
+    tiles; that pair's query rows are compared with the oracle."""
+    sp = gen.spec("qwen3-32b-16k")
+    sample_b, sample_g, nq = 5, 2, 4
+    st_s = gen.prefill(sp, sequences=[sample_b])
+    lens = st_s["seq_lens"]
+    bt = st_s["block_table"]
+    cfg = kv.default_config(sp.hkv)
+    pool = torch.zeros(st_s["num_blocks"], sp.hkv, 13312, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(sp.seed + 1)
+    for b in range(sp.batch):
+        n = int(lens[b]) // T
+        kd = (torch.randn(n * T, sp.hkv, D, device="cuda", generator=g) * 4).half()
+        vd = (torch.randn(n * T, sp.hkv, D, device="cuda", generator=g) * 4).half()
+        kv.quantize_tiles(cfg, kd.view(n * T, -1), vd.view(n * T, -1), dev(bt[b, :n]), pool)
+    n_s = int(lens[sample_b]) // T
+    recs = np.stack([codec.encode_record(st_s["k"][T * i:T * i + T, sample_g],
+                                         st_s["v"][T * i:T * i + T, sample_g])
+                     for i in range(n_s)])
+    idx = torch.from_numpy(bt[sample_b, :n_s].astype(np.int64)).cuda()
+    pool[idx, sample_g] = dev(recs)
+    q = gen.query_tokens(sp, nq)
+    sk = np.zeros((sp.batch, sp.hkv, T, D), np.float16)
+    got = gpu_multi(cfg, q, pool, bt, lens, sk, sk, 1 / math.sqrt(D))
+    G = sp.group
+    sub_pool = np.zeros((st_s["num_blocks"], 1, 13312), np.uint8)
+    sub_pool[bt[sample_b, :n_s], 0] = recs
+    ref = oatt.decode_attention_multi(q[sample_b:sample_b + 1, :, sample_g * G:(sample_g + 1) * G],
+                                      sub_pool, bt[sample_b:sample_b + 1],
+                                      lens[sample_b:sample_b + 1], sk[:1, :1], sk[:1, :1],
+                                      1 / math.sqrt(D))
+    err = np.abs(got[sample_b, :, sample_g * G:(sample_g + 1) * G] - ref[0]).max()
+    _say(f"multi full-size Q={nq}: max abs err {err:.3g}")
+    assert err <= TOL
+    assert np.isfinite(got).all()

@@ -14,6 +14,7 @@ step or the queries can be regenerated alone, in any order:
   (seed, 1)           per-sequence context lengths (ragged workload)
   (seed, 2)           block permutation
   (seed, 3)           queries
+  (seed, 6, i)        queries of the earlier tokens of a several-token query (token i)
   (seed, 100 + b)     keys, then values, then per-token drift of sequence b
   (seed, 10**6 + s)   keys then values of append step s
 
@@ -183,6 +184,22 @@ def query(sp: Spec, dense: bool = False) -> np.ndarray:
         scale = np.sqrt(D) / key_rms
         q *= np.repeat(scale, sp.group)[None, :, None].astype(np.float32)
     return q.astype(np.float16)
+
+
+def query_tokens(sp: Spec, n_query: int, dense: bool = False) -> np.ndarray:
+    """Queries of n_query tokens per sequence, fp16 [B, n_query, Hq, 128] (reading R25): the
+    last token's queries are query(sp, dense); the earlier ones are drawn the same way from
+    their own stream."""
+    q = np.empty((sp.batch, n_query, sp.hq, D), np.float16)
+    q[:, -1] = query(sp, dense)
+    for i in range(n_query - 1):
+        x = _rng(sp, 6, i).standard_normal((sp.batch, sp.hq, D), dtype=np.float32)
+        if dense:
+            mult = head_params(sp)
+            key_rms = np.sqrt(np.sum(mult[:, 0, :].astype(np.float64) ** 2, axis=1))
+            x *= np.repeat(np.sqrt(D) / key_rms, sp.group)[None, :, None].astype(np.float32)
+        q[:, i] = x.astype(np.float16)
+    return q
 
 
 def append_tokens(sp: Spec, step: int):
