@@ -364,7 +364,8 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel)",
                            "append": "kvarn_append_token (append_token_kernel)",
-                           "decode": "kvarn_decode_attention (decode_kernel + merge_kernel)"}[dominant],
+                           "decode": "kvarn_decode_attention (decode_tiles_kernel<false> + "
+                                     "decode_merge_kernel<true, false>)"}[dominant],
                 "algorithmic_bytes_per_launch": {"quantise": q_bytes, "append": a_bytes,
                                                  "decode": d_bytes}[dominant],
                 "avg_launch_us": round(timings[dominant] * 1e6, 2)}

@@ -233,6 +233,9 @@ __device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int
                                                               f[1] * fz);
 }
 
+// kCausal: several query tokens per sequence (nq > 1) with the causal mask; a separate
+// instantiation so the one-token decode carries no mask code
+template <bool kCausal>
 __global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
@@ -402,7 +405,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     float v[8][2];
     float tmax = -INFINITY;
     const int tpos = kT * (i0 + wave_u + kWaves * j);      // position of this tile's token 0
-    const bool masked = tpos + kT - 1 > len - nq;          // wave-uniform
+    const bool masked = kCausal && tpos + kT - 1 > len - nq;   // wave-uniform
     const int tlim = qlim - tpos;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -580,7 +583,7 @@ __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, co
   return acc0 + acc1;
 }
 
-template <bool kRotated>
+template <bool kRotated, bool kCausal>
 __global__ void __launch_bounds__(kMThreads)
 decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int max_blocks,
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
@@ -605,7 +608,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
   // staging tokens this query token sees: positions up to len - nq + qi
-  const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (nq - 1 - qi));
+  const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (kCausal ? nq - 1 - qi : 0));
   const float scale2 = sm_scale * kLog2e;
   const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
   const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
@@ -946,14 +949,25 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
                          const __half* staging_v, float sm_scale, float* out, float* partials,
                          int splits, int batch, hipStream_t stream) {
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
-  hipLaunchKernelGGL(decode_tiles_kernel, dim3(splits, hkv * ngroups, batch), dim3(kTThreads),
-                     0, stream, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
-                     seq_lens, sm_scale, partials);
+  const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
+  if (nq == 1)
+    hipLaunchKernelGGL(decode_tiles_kernel<false>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
+                       nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
+                       partials);
+  else
+    hipLaunchKernelGGL(decode_tiles_kernel<true>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
+                       nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
+                       partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(hq * nq, batch), dim3(kMThreads), 0,
-                     stream, q, hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v,
-                     sm_scale, partials, splits, out);
+  if (nq == 1)
+    hipLaunchKernelGGL((decode_merge_kernel<true, false>), mgrid, dim3(kMThreads), 0, stream, q,
+                       hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
+                       partials, splits, out);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<true, true>), mgrid, dim3(kMThreads), 0, stream, q,
+                       hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
+                       partials, splits, out);
   return hipGetLastError();
 }
 
@@ -977,7 +991,7 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
                      max_blocks, seq_lens, sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(hq, batch), dim3(kMThreads), 0, stream, q,
+  hipLaunchKernelGGL((decode_merge_kernel<false, false>), dim3(hq, batch), dim3(kMThreads), 0, stream, q,
                      hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
                      splits, out);
   return hipGetLastError();
