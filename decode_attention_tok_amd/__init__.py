@@ -57,6 +57,7 @@ _SIGNATURES = {
     "kvarn_decode_attention_multi": (ctypes.c_int, [_CFG, _P, _I32, _I32, _P, _I64, _P, _I32, _P,
                                                     _P, _P, ctypes.c_float, _P, _P,
                                                     ctypes.c_size_t, _I32, _P]),
+    "kvarn_dequantize_tiles": (ctypes.c_int, [_CFG, _P, _I64, _P, _I32, _P, _P, _P]),
     "kvarn_fp16_block_bytes": (ctypes.c_size_t, [_CFG]),
     "kvarn_fp16_write_tiles": (ctypes.c_int, [_CFG, _P, _P, _I64, _I32, _P, _P, _I64, _P]),
     "kvarn_decode_attention_fp16": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P,
@@ -168,6 +169,16 @@ def decode_attention(cfg: Config, q, block_pool, block_table, seq_lens, staging_
                                         _ptr(seq_lens), _ptr(staging_k), _ptr(staging_v),
                                         float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                         batch, _stream(stream)))
+
+
+def dequantize_tiles(cfg: Config, block_pool, src_blocks, k_out, v_out, stream=None):
+    """Records of blocks src_blocks (int32 [n_tiles]) back to fp32 tiles in the original
+    space: k_out, v_out fp32 [n_tiles * 128, Hkv, 128]."""
+    num_blocks = block_pool.numel() // block_bytes(cfg)
+    _check("kvarn_dequantize_tiles",
+           lib().kvarn_dequantize_tiles(ctypes.byref(cfg), _ptr(block_pool), num_blocks,
+                                        _ptr(src_blocks), src_blocks.numel(), _ptr(k_out),
+                                        _ptr(v_out), _stream(stream)))
 
 
 MAX_QUERY_TOKENS = 16

@@ -175,6 +175,23 @@ kvarn_status kvarn_decode_attention_multi(const kvarn_config* cfg, const void* q
                       workspace, workspace_bytes, batch, stream);
 }
 
+kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_pool,
+                                    int64_t num_blocks, const int32_t* src_blocks,
+                                    int32_t n_tiles, float* k_out, float* v_out, void* stream) {
+  kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  if (n_tiles < 0 || num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
+  if (n_tiles == 0) return KVARN_OK;
+  if (block_pool == nullptr || src_blocks == nullptr || k_out == nullptr || v_out == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  if (!aligned16(k_out) || !aligned16(v_out)) return KVARN_ERR_BAD_SHAPE;
+  if (2LL * cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
+  return from_hip(kvarn::launch_dequantize_tiles(static_cast<const uint8_t*>(block_pool),
+                                                 num_blocks, src_blocks, n_tiles,
+                                                 cfg->num_kv_heads, k_out, v_out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 size_t kvarn_fp16_block_bytes(const kvarn_config* cfg) {
   return check_config(cfg) == KVARN_OK
              ? (size_t)KVARN_FP16_RECORD_BYTES * (size_t)cfg->num_kv_heads

@@ -670,6 +670,66 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
 }
 
 
+// ------------------------------------------------------------------ dequantisation to memory
+//
+// Stage 4 of [GR] "The four-stage pipeline" written out instead of folded into attention:
+// x_tj = sum_i c-hat_i (s-hat_t code_ti + z-hat_t) H_ij / sqrt(128), the record's tile back in
+// the original channel space (for inspection, export and error measurement). grid: n_tiles *
+// hkv * 2 workgroups (tile, head, K|V) of 4 waves; wave w rebuilds tokens w, w + 4, ..., lane l
+// channels 2 l and 2 l + 1, with the same butterfly as the query rotation.
+
+// Byte offset (in the value section) and bit shift of value code (token t, channel j).
+__device__ __forceinline__ void v_code_pos(int t, int j, uint32_t& byte_off, int& shift) {
+  const int nb = j >> 4, n = j & 15, kb = t >> 5, h = (t >> 4) & 1, s = (t >> 2) & 3, i = t & 3;
+  const int word = 256 * kb + 4 * (16 * s + n) + 2 * h + (i >> 1);
+  const int bit = 2 * nb + 16 * (i & 1);
+  byte_off = 4u * (uint32_t)word + (uint32_t)(bit >> 3);
+  shift = bit & 7;
+}
+
+__global__ void __launch_bounds__(256)
+dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
+                        const int32_t* __restrict__ src_blocks, int n_tiles, int hkv,
+                        float* __restrict__ k_out, float* __restrict__ v_out) {
+  const int id = blockIdx.x;
+  const int is_v = id & 1, head = (id >> 1) % hkv, tile = (id >> 1) / hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (tile >= n_tiles) return;
+  float* out = (is_v ? v_out : k_out) + ((long long)tile * kT * hkv + head) * kD;
+  const long long row_stride = (long long)hkv * kD;
+  const long long blk = src_blocks[tile];
+  if (blk < 0 || blk >= num_blocks) {
+    for (int t = wave; t < kT; t += 4)
+      reinterpret_cast<float2*>(out + t * row_stride)[lane] = make_float2(NAN, NAN);
+    return;
+  }
+  const uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
+  const uint8_t* meta = rec + (is_v ? kVMetaOff : kKMetaOff);
+  const uint32_t cw = *reinterpret_cast<const uint16_t*>(meta + kCRel + 2 * lane);
+  const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false);   // c-hat of 2 l, 2 l + 1
+  uint32_t vb0 = 0, vb1 = 0;
+  int vs0 = 0, vs1 = 0;
+  for (int t = wave; t < kT; t += 4) {
+    const float sh = __builtin_amdgcn_cvt_f32_fp8((int)meta[kSRel + t], 0);
+    const float zh = fp16_bits_to_float(*reinterpret_cast<const uint16_t*>(meta + kZRel + 2 * t));
+    float q0, q1;
+    if (!is_v) {
+      const uint32_t byte = rec[kKCodesOff + 64 * t + lane];          // channels 2 l, 2 l + 1
+      q0 = (float)(byte & 15u);
+      q1 = (float)(byte >> 4);
+    } else {
+      v_code_pos(t, 2 * lane, vb0, vs0);
+      v_code_pos(t, 2 * lane + 1, vb1, vs1);
+      q0 = (float)((rec[kVCodesOff + vb0] >> vs0) & 3u);
+      q1 = (float)((rec[kVCodesOff + vb1] >> vs1) & 3u);
+    }
+    float y0 = c[0] * fmaf(sh, q0, zh), y1 = c[1] * fmaf(sh, q1, zh);
+    fwht_wave(y0, y1, lane);
+    reinterpret_cast<float2*>(out + t * row_stride)[lane] =
+        make_float2(y0 * 0.08838834764831845f, y1 * 0.08838834764831845f);
+  }
+}
+
 // ------------------------------------------------------------------ fp16 cache (comparison path)
 //
 // The unquantised paged cache the packed cache is compared with. Record of one (block, KV
@@ -931,6 +991,15 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 }
 
 }  // namespace
+
+hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
+                                   const int32_t* src_blocks, int n_tiles, int hkv, float* k_out,
+                                   float* v_out, hipStream_t stream) {
+  const long long groups = 2LL * hkv * n_tiles;
+  hipLaunchKernelGGL(dequantize_tiles_kernel, dim3((unsigned)groups), dim3(256), 0, stream, pool,
+                     num_blocks, src_blocks, n_tiles, hkv, k_out, v_out);
+  return hipGetLastError();
+}
 
 int decode_splits(int batch, int hkv, int max_blocks) {
   const long long pairs = (long long)batch * hkv;

@@ -44,6 +44,12 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
                               const __half* staging_v, float sm_scale, float* out,
                               float* partials, int splits, int batch, hipStream_t stream);
 
+// Records of blocks src_blocks[i] back to fp32 tiles in the original space: k_out, v_out
+// [n_tiles * 128][hkv][128]; invalid block ids give NaN rows.
+hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
+                                   const int32_t* src_blocks, int n_tiles, int hkv, float* k_out,
+                                   float* v_out, hipStream_t stream);
+
 // Number of splits of each sequence's tiles for a decode launch (depends on sizes only).
 int decode_splits(int batch, int hkv, int max_blocks);
 

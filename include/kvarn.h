@@ -167,6 +167,19 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const voi
                                     void* workspace, size_t workspace_bytes, int32_t batch,
                                     void* stream);
 
+/* Stage 4 written out ([GR] "The four-stage pipeline": dequantisation restores each element
+ * from its code, the per-token scale and zero-point and the per-channel scale, and the
+ * rotation is undone): the records of blocks src_blocks[i] back to fp32 tiles in the original
+ * channel space, for inspection, export and error measurement (decode attention never does
+ * this; it folds the same arithmetic into the scores and outputs).
+ *   src_blocks  (device) int32 [n_tiles]; an id outside [0, num_blocks) gives NaN rows
+ *   k_out,v_out (device) fp32 [n_tiles * 128][num_kv_heads][128], 16-byte aligned: token
+ *               128 i + t of KV head h from record (src_blocks[i], h)
+ * Errors: NULL_ARG, BAD_SHAPE (negative counts, misaligned outputs, too many tiles). */
+KVARN_API kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_pool,
+                                    int64_t num_blocks, const int32_t* src_blocks,
+                                    int32_t n_tiles, float* k_out, float* v_out, void* stream);
+
 /* ---- Several query tokens per sequence (multi-token verification, chunked continuation).
  * The pages place KVarN beside speculative decoding and multi-token prediction ([GR] "The 2-bit
  * quantization field"); those steps score Q new tokens per sequence at once. Reading taken

@@ -169,6 +169,17 @@ def test_decode_multi_validation(lib):
     assert call(hq=2 * 17) == SHAPE
 
 
+def test_dequantize_validation(lib):
+    f = "kvarn_dequantize_tiles"
+    assert _call(lib, f, _cfg(), FAKE, 4, FAKE, 0, None, None, None) == OK          # no-op
+    assert _call(lib, f, _cfg(), None, 4, FAKE, 1, FAKE, FAKE, None) == NULL
+    assert _call(lib, f, _cfg(), FAKE, 4, FAKE, 1, FAKE, None, None) == NULL
+    assert _call(lib, f, _cfg(), FAKE, 4, FAKE, -1, FAKE, FAKE, None) == SHAPE
+    assert _call(lib, f, _cfg(), FAKE, -4, FAKE, 1, FAKE, FAKE, None) == SHAPE
+    assert _call(lib, f, _cfg(), FAKE, 4, FAKE, 1, ctypes.c_void_p(0x1004), FAKE,
+                 None) == SHAPE                                                   # misaligned
+
+
 def test_fp16_path_validation(lib):
     cfg = kv.default_config(8)
     assert kv.fp16_block_bytes(cfg) == 8 * 65536

@@ -15,6 +15,8 @@ step or the queries can be regenerated alone, in any order:
   (seed, 2)           block permutation
   (seed, 3)           queries
   (seed, 6, i)        queries of the earlier tokens of a several-token query (token i)
+  (seed, 7)           fixed orthogonal maps of the autoregressive error probe
+  (seed, 8, s)        fresh noise of probe step s
   (seed, 100 + b)     keys, then values, then per-token drift of sequence b
   (seed, 10**6 + s)   keys then values of append step s
 
@@ -200,6 +202,26 @@ def query_tokens(sp: Spec, n_query: int, dense: bool = False) -> np.ndarray:
             x *= np.repeat(np.sqrt(D) / key_rms, sp.group)[None, :, None].astype(np.float32)
         q[:, i] = x.astype(np.float16)
     return q
+
+
+def feedback_maps(sp: Spec) -> dict:
+    """Fixed random orthogonal 128 x 128 maps (float32) of the autoregressive error probe: one
+    per KV head for keys and for values, one per query head for queries."""
+    rng = _rng(sp, 7)
+
+    def orth(n):
+        a = rng.standard_normal((n, D, D))
+        qm, r = np.linalg.qr(a)
+        return (qm * np.sign(np.diagonal(r, axis1=1, axis2=2))[:, None, :]).astype(np.float32)
+    return dict(k=orth(sp.hkv), v=orth(sp.hkv), q=orth(sp.hq))
+
+
+def feedback_noise(sp: Spec, step: int) -> dict:
+    """Fresh N(0, 1) noise of probe step `step` (float32): k, v [B, Hkv, 128], q [B, Hq, 128]."""
+    rng = _rng(sp, 8, step)
+    return dict(k=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
+                v=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
+                q=rng.standard_normal((sp.batch, sp.hq, D), dtype=np.float32))
 
 
 def append_tokens(sp: Spec, step: int):
