@@ -107,12 +107,28 @@ __device__ __forceinline__ void fmac_xor2(float* a, float s) {
       : "v"(s));
 }
 
-// Maximum over the 16 lanes of each DPP row (quad pairs, then row rotations by 4 and 8).
+// Maximum of two non-negative finite floats as an integer maximum of their bit patterns (the
+// order is the same): one v_max_u32, where fmaxf would first quiet possible signalling NaNs
+// coming out of a lane exchange.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+
+// Maximum over the 16 lanes of each DPP row (quad pairs, then row rotations by 4 and 8) of a
+// non-negative value.
 __device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(x));
-  x = fmaxf(x, dpp_f<0x4E>(x));
-  x = fmaxf(x, dpp_f<0x124>(x));
-  return fmaxf(x, dpp_f<0x128>(x));
+  x = max_nn(x, dpp_f<0xB1>(x));
+  x = max_nn(x, dpp_f<0x4E>(x));
+  x = max_nn(x, dpp_f<0x124>(x));
+  return max_nn(x, dpp_f<0x128>(x));
+}
+
+// Maximum over lane bits 4 and 5 of a non-negative value (permlane swaps).
+__device__ __forceinline__ float max_xor48_nn(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Chan's merge of two equal-count partials (shifted mean m, centred sum of squares q) held by
@@ -218,7 +234,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   __syncthreads();
   float big = sm.red[0];
 #pragma unroll
-  for (int w = 1; w < kQThreads / 64; ++w) big = fmaxf(big, sm.red[w]);
+  for (int w = 1; w < kQThreads / 64; ++w) big = max_nn(big, sm.red[w]);
   if (big == 0.0f) {                              // uniform across the workgroup
     store_record_zero_tile(rec, is_v, tid);
     return;
@@ -267,7 +283,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     if (it == iters - 1) break;
     float vmax = sm.red[8];
 #pragma unroll
-    for (int w = 1; w < kQThreads / 64; ++w) vmax = fmaxf(vmax, sm.red[8 + w]);
+    for (int w = 1; w < kQThreads / 64; ++w) vmax = max_nn(vmax, sm.red[8 + w]);
     // row step (layout A): std over channels of xt_tj * v_j
     {
       const float* vv = sm.vinv + pbase;
@@ -296,13 +312,13 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
       if ((tid & 3) == 0) sm.u[t & 3][t >> 2] = uinv;
-      const float um = max_xor32(max_xor16(row16_max(uinv)));
+      const float um = max_xor48_nn(row16_max(uinv));
       if (lane == 0) sm.red[16 + wave] = um;
     }
     __syncthreads();
     umax = sm.red[16];
 #pragma unroll
-    for (int w = 1; w < kQThreads / 64; ++w) umax = fmaxf(umax, sm.red[16 + w]);
+    for (int w = 1; w < kQThreads / 64; ++w) umax = max_nn(umax, sm.red[16 + w]);
   }
 
   // ---- gauge (geometric mean of c = 1) and FP8 rounding of c, by wave 0
