@@ -115,12 +115,46 @@ __device__ __forceinline__ float max_nn(float a, float b) {
 }
 
 // Maximum over the 16 lanes of each DPP row (quad pairs, then row rotations by 4 and 8) of a
-// non-negative value.
+// non-negative value: integer maxima with the partner read through DPP in the same
+// instruction (s_nop 1: the two wait states a DPP read needs after a VALU write).
 __device__ __forceinline__ float row16_max(float x) {
-  x = max_nn(x, dpp_f<0xB1>(x));
-  x = max_nn(x, dpp_f<0x4E>(x));
-  x = max_nn(x, dpp_f<0x124>(x));
-  return max_nn(x, dpp_f<0x128>(x));
+  uint32_t v = __float_as_uint(x);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf"
+      : "+v"(v));
+  return __uint_as_float(v);
+}
+
+// (a of the partner lane) + b and (a of the partner lane) - b for the quad partner selected by
+// kCtrl (0xB1: lane ^ 1, 0x4E: lane ^ 2), each one DPP-sourced VALU instruction.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float a, float b) {
+  float r;
+  if constexpr (kCtrl == 0xB1)
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_sub(float a, float b) {
+  float r;
+  if constexpr (kCtrl == 0xB1)
+    asm volatile("s_nop 1\n\tv_sub_f32_dpp %0, %1, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_sub_f32_dpp %0, %1, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                 : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Maximum over lane bits 4 and 5 of a non-negative value (permlane swaps).
@@ -149,9 +183,52 @@ __device__ __forceinline__ void merge_pair(float& m, float& q, float nab) {
 }
 
 // Code = rne(clamp(v, 0, qmax)) written into byte `sel` of `acc`: the conversion rounds to
-// nearest even and clamps below at 0; the upper clamp comes first.
+// nearest even and clamps below at 0. The upper clamp (kClamp) is needed only when the
+// token's scale saturated at the FP8 maximum: otherwise s-hat >= (max - z-hat) / qmax, so
+// v <= qmax up to a few fp32 ulps and rounds to at most qmax.
+template <bool kClamp>
 __device__ __forceinline__ uint32_t put_code(float v, float qmax, uint32_t sel, uint32_t acc) {
-  return __builtin_amdgcn_cvt_pk_u8_f32(fminf(v, qmax), sel, acc);
+  return __builtin_amdgcn_cvt_pk_u8_f32(kClamp ? fminf(v, qmax) : v, sel, acc);
+}
+
+// This thread's codes (token t, its 32 channels) into the LDS staging area (see the callers).
+template <bool kClamp>
+__device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, float qmax,
+                                            int is_v, int t, int q0, int q1, uint32_t* stage) {
+  if (!is_v) {
+    // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
+    // token's 16 words (channel 8 k + e at nibble e of word k)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        lo = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
+        hi = put_code<kClamp>(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
+      }
+      stage[t * 16 + q0 + 2 * m + 8 * q1] = lo | (hi << 4);
+    }
+  } else {
+    // value codes. Byte e of this thread holds the codes of channel n = 8 q0 + e, hf = q1,
+    // nb' = m at bits 2 m; it is staged at byte 2 (t % 2) + hf of LDS word 16 (t / 2) + n,
+    // which makes every LDS word one word of the section.
+    uint8_t* sb = reinterpret_cast<uint8_t*>(stage);
+#pragma unroll
+    for (int eh = 0; eh < 8; eh += 4) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p = put_code<kClamp>(fmaf(x[8 * m + eh + e], ca, cb), qmax, e, p);
+        d |= p << (2 * m);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sb[((t >> 1) * 16 + 8 * q0 + eh + e) * 4 + (t & 1) * 2 + q1] = (uint8_t)(d >> (8 * e));
+    }
+  }
 }
 
 __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, int tid) {
@@ -298,16 +375,15 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       float mh = fmaf(s1, 0.03125f, k0);
       if (flip) mh = -mh;
       float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
-      {
-        const float mo = quad_swap<kDppXor1>(mh), qo = quad_swap<kDppXor1>(qh);
-        const float d = mh - mo;
-        qh = fmaf(16.0f * d, d, qh + qo);
-        mh = 0.5f * (mh + mo);
+      {                                          // Chan merges with quad partners
+        const float d = dpp_sub<kDppXor1>(mh, mh);   // partner - own (only d^2 is used)
+        const float qs = dpp_add<kDppXor1>(qh, qh);
+        mh = 0.5f * dpp_add<kDppXor1>(mh, mh);
+        qh = fmaf(16.0f * d, d, qs);
       }
       {
-        const float mo = quad_swap<kDppXor2>(mh), qo = quad_swap<kDppXor2>(qh);
-        const float d = mh - mo;
-        qh = fmaf(32.0f * d, d, qh + qo);
+        const float d = dpp_sub<kDppXor2>(mh, mh);
+        qh = fmaf(32.0f * d, d, dpp_add<kDppXor2>(qh, qh));
       }
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
@@ -367,40 +443,12 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   }
 
   uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
+  if (scode == 0x7Eu) stage_codes<true>(x, ca, cb, qmax, is_v, t, q0, q1, stage);  // s-hat = 448
+  else stage_codes<false>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
   if (!is_v) {
-    // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
-    // token's 16 words (channel 8 k + e at nibble e of word k)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        lo = put_code(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
-        hi = put_code(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
-      }
-      stage[t * 16 + q0 + 2 * m + 8 * q1] = lo | (hi << 4);
-    }
     __syncthreads();
     reinterpret_cast<uint4*>(rec + kKCodesOff)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
   } else {
-    // value codes. Byte e of this thread holds the codes of channel n = 8 q0 + e, hf = q1,
-    // nb' = m at bits 2 m; it is staged at byte 2 (t % 2) + hf of LDS word 16 (t / 2) + n,
-    // which makes every LDS word one word of the section.
-    uint8_t* sb = reinterpret_cast<uint8_t*>(stage);
-#pragma unroll
-    for (int eh = 0; eh < 8; eh += 4) {
-      uint32_t d = 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t p = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p = put_code(fmaf(x[8 * m + eh + e], ca, cb), qmax, e, p);
-        d |= p << (2 * m);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sb[((t >> 1) * 16 + 8 * q0 + eh + e) * 4 + (t & 1) * 2 + q1] = (uint8_t)(d >> (8 * e));
-    }
     __syncthreads();
     if (tid < 256) {
       uint32_t out[4];
