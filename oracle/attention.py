@@ -27,7 +27,7 @@ D = codec.D
 # ------------------------------------------------------------------ cache-level operations
 
 
-def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS):
+def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS, signs=None):
     """Quantise whole prefill tiles into the block pool, in place.
 
     k, v: [n_tiles * 128, Hkv, 128] fp16 values; tile i holds tokens 128 i .. 128 i + 127 and
@@ -39,11 +39,12 @@ def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS):
     for i in range(n_tiles):
         rows = slice(T * i, T * i + T)
         for h in range(hkv):
-            pool[dst_blocks[i], h] = codec.encode_record(k[rows, h, :], v[rows, h, :], iters)
+            pool[dst_blocks[i], h] = codec.encode_record(k[rows, h, :], v[rows, h, :], iters,
+                                                         signs)
 
 
 def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, pool,
-                 iters: int = codec.DEFAULT_ITERS):
+                 iters: int = codec.DEFAULT_ITERS, signs=None):
     """Write one new token per sequence into its staging tile; when the token is the 128th of
     its tile, quantise the staging tile into block_table[b][position // 128]. In place.
 
@@ -58,15 +59,16 @@ def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, poo
         if slot == T - 1:
             blk = block_table[b, int(pos) // T]
             for h in range(staging_k.shape[1]):
-                pool[blk, h] = codec.encode_record(staging_k[b, h], staging_v[b, h], iters)
+                pool[blk, h] = codec.encode_record(staging_k[b, h], staging_v[b, h], iters,
+                                                   signs)
 
 
-def _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length):
+def _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length, signs=None):
     """Dequantised keys and values (original space) of sequence b, KV head g, length tokens."""
     n_full = length // T
     ks, vs = [], []
     for i in range(n_full):
-        kh, vh = codec.decode_record(pool[block_table[b, i], g])
+        kh, vh = codec.decode_record(pool[block_table[b, i], g], signs)
         ks.append(kh)
         vs.append(vh)
     tail = length % T
@@ -84,7 +86,8 @@ def softmax_attend(q, keys, values, sm_scale):
     return (p @ values) / p.sum()
 
 
-def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale,
+                     signs=None):
     """Plain form: dequantise every packed tile, then exact softmax attention.
 
     q: [B, Hq, 128]; returns [B, Hq, 128] float64. A sequence of length 0 gives zeros."""
@@ -96,13 +99,14 @@ def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_sc
     for b in range(bsz):
         for g in range(hkv):
             keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g,
-                                        int(seq_lens[b]))
+                                        int(seq_lens[b]), signs)
             for h in range(g * group, (g + 1) * group):
                 out[b, h] = softmax_attend(q[b, h], keys, values, sm_scale)
     return out
 
 
-def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale,
+                           signs=None):
     """Several query tokens per sequence (reading R25): q [B, Q, Hq, 128] holds the last Q of
     each sequence's L tokens; query token i sits at position L - Q + i and attends to
     positions 0 .. L - Q + i of the same cache (causal; an empty range gives zeros).
@@ -115,7 +119,8 @@ def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v,
     for b in range(bsz):
         length = int(seq_lens[b])
         for g in range(hkv):
-            keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length)
+            keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length,
+                                        signs)
             for i in range(nq):
                 n_vis = max(0, length - nq + i + 1)
                 for h in range(g * group, (g + 1) * group):
@@ -124,7 +129,8 @@ def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v,
     return out
 
 
-def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale):
+def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale,
+                            signs=None):
     """Folded form: the per-channel key scales and the rotation go into the query, the
     per-token key scale and zero-point into the score, the per-token value scale and
     zero-point into the probabilities, the per-channel value scale into the per-tile partial
@@ -144,7 +150,7 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
             for h in range(g * group, (g + 1) * group):
                 if length == 0:
                     continue
-                q_rot = q[b, h] @ H128
+                q_rot = (q[b, h] if signs is None else q[b, h] * signs) @ H128
                 scores = []
                 for r in recs:
                     qt = q_rot * r["k"]["c_hat"]
@@ -158,7 +164,10 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
                     pt = p[T * i:T * i + T]
                     o_rot += r["v"]["c_hat"] * ((pt * r["v"]["s_hat"]) @ r["v"]["codes"]
                                                 + np.dot(pt, r["v"]["z_hat"]))
-                o = o_rot @ H128 + p[T * n_full:] @ sv
+                o_back = o_rot @ H128
+                if signs is not None:
+                    o_back = o_back * signs
+                o = o_back + p[T * n_full:] @ sv
                 out[b, h] = o / p.sum()
     return out
 

@@ -105,7 +105,7 @@ def normalise(xt: np.ndarray, iters: int = DEFAULT_ITERS, ddof: int = 0):
 # ------------------------------------------------------------------ one tile
 
 
-def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS) -> dict:
+def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS, signs=None) -> dict:
     """Quantise one T x D tile of fp16 values with `bits`-bit codes.
 
     Returns a dict with c_hat, s_hat, z_hat (float64 values), c_code, s_code (E4M3 bytes),
@@ -116,7 +116,7 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS) -> dict:
     if x.shape != (T, D):
         raise ValueError("tile must be 128 x 128")
     qmax = (1 << bits) - 1
-    xt = rotate(x)                                        # stage 1: Hadamard along channels
+    xt = rotate(x, signs)                                 # stage 1: Hadamard along channels
     if np.max(np.abs(xt)) == 0.0:                         # all-zero tile (reading R8)
         one, one_code = e4m3_rne(np.ones(D))
         zero = np.zeros(T)
@@ -148,9 +148,11 @@ def dequantize_rotated(c_hat, s_hat, z_hat, codes) -> np.ndarray:
                                          + np.asarray(z_hat)[:, None])
 
 
-def dequantize(c_hat, s_hat, z_hat, codes) -> np.ndarray:
-    """Dequantised tile in the original space: rotated values times H (H is its own inverse)."""
-    return dequantize_rotated(c_hat, s_hat, z_hat, codes) @ H128
+def dequantize(c_hat, s_hat, z_hat, codes, signs=None) -> np.ndarray:
+    """Dequantised tile in the original space: rotated values times H (H is its own inverse),
+    then the sign flips of the rotation (R27) undone."""
+    out = dequantize_rotated(c_hat, s_hat, z_hat, codes) @ H128
+    return out if signs is None else out * signs
 
 
 # ------------------------------------------------------------------ record pack / unpack
@@ -195,13 +197,14 @@ def unpack_record(rec: np.ndarray) -> dict:
     return out
 
 
-def encode_record(k_tile, v_tile, iters: int = DEFAULT_ITERS) -> np.ndarray:
+def encode_record(k_tile, v_tile, iters: int = DEFAULT_ITERS, signs=None) -> np.ndarray:
     """Quantise the key and value tiles of one (block, KV head) and pack them."""
-    return pack_record(quantize_tile(k_tile, K_BITS, iters), quantize_tile(v_tile, V_BITS, iters))
+    return pack_record(quantize_tile(k_tile, K_BITS, iters, signs),
+                       quantize_tile(v_tile, V_BITS, iters, signs))
 
 
-def decode_record(rec) -> tuple:
+def decode_record(rec, signs=None) -> tuple:
     """Dequantised (K-hat, V-hat) of a record in the original (unrotated) space."""
     u = unpack_record(rec)
-    return tuple(dequantize(u[n]["c_hat"], u[n]["s_hat"], u[n]["z_hat"], u[n]["codes"])
+    return tuple(dequantize(u[n]["c_hat"], u[n]["s_hat"], u[n]["z_hat"], u[n]["codes"], signs)
                  for n in ("k", "v"))

@@ -35,9 +35,22 @@ H128 = hadamard(D)
 SIGNS128 = np.rint(H128 * np.sqrt(float(D)))  # the +-1 matrix, exact
 
 
-def rotate(x: np.ndarray) -> np.ndarray:
-    """x @ H along the last axis (channels), float64.
+def sign_vector(words) -> np.ndarray:
+    """Per-channel signs (+-1, float64) from four 32-bit words: channel j is negated when bit
+    j % 32 of word j // 32 is set (reading R27: the optional sign flips before the rotation;
+    all-zero words give the plain Hadamard of R2)."""
+    w = np.asarray(words, dtype=np.uint64).reshape(4)
+    j = np.arange(D)
+    bits = (w[j // 32] >> (j % 32).astype(np.uint64)) & np.uint64(1)
+    return np.where(bits == 1, -1.0, 1.0)
+
+
+def rotate(x: np.ndarray, signs=None) -> np.ndarray:
+    """(x * signs) @ H along the last axis (channels), float64; signs None means all +1.
 
     The +-1 sums are formed first and scaled once: for fp16 inputs every partial sum is exact
     in float64, so an exactly zero rotated value comes out as exactly zero."""
-    return (np.asarray(x, dtype=np.float64) @ SIGNS128) / np.sqrt(float(D))
+    x = np.asarray(x, dtype=np.float64)
+    if signs is not None:
+        x = x * signs
+    return (x @ SIGNS128) / np.sqrt(float(D))

@@ -17,6 +17,7 @@ step or the queries can be regenerated alone, in any order:
   (seed, 6, i)        queries of the earlier tokens of a several-token query (token i)
   (seed, 7)           fixed orthogonal maps of the autoregressive error probe
   (seed, 8, s)        fresh noise of probe step s
+  (seed, 9)           per-channel rotation sign words (optional sign flips)
   (seed, 100 + b)     keys, then values, then per-token drift of sequence b
   (seed, 10**6 + s)   keys then values of append step s
 
@@ -222,6 +223,12 @@ def feedback_noise(sp: Spec, step: int) -> dict:
     return dict(k=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
                 v=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
                 q=rng.standard_normal((sp.batch, sp.hq, D), dtype=np.float32))
+
+
+def rotation_sign_words(sp: Spec) -> np.ndarray:
+    """Four random 32-bit words (uint32): the optional per-channel sign flips before the
+    rotation, channel j negated when bit j % 32 of word j // 32 is set (reading R27)."""
+    return _rng(sp, 9).integers(0, 2 ** 32, size=4, dtype=np.uint64).astype(np.uint32)
 
 
 def append_tokens(sp: Spec, step: int):
