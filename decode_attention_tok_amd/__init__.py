@@ -30,7 +30,8 @@ class KvarnError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_tokens", ctypes.c_int32), ("k_bits", ctypes.c_int32),
-                ("v_bits", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+                ("v_bits", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
+                ("rotation_signs", ctypes.c_uint32 * 4)]
 
 
 _lib = None
@@ -102,10 +103,15 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def default_config(num_kv_heads: int, sinkhorn_iters: int = 4) -> Config:
+def default_config(num_kv_heads: int, sinkhorn_iters: int = 4, rotation_signs=None) -> Config:
+    """The preset for num_kv_heads heads; rotation_signs: optional four 32-bit words of
+    per-channel sign flips before the rotation (None: the plain Hadamard)."""
     cfg = Config()
     lib().kvarn_default_config(ctypes.byref(cfg), num_kv_heads)
     cfg.sinkhorn_iters = sinkhorn_iters
+    if rotation_signs is not None:
+        for i in range(4):
+            cfg.rotation_signs[i] = int(rotation_signs[i]) & 0xFFFFFFFF
     return cfg
 
 

@@ -35,6 +35,7 @@ void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads) {
   cfg->k_bits = 4;
   cfg->v_bits = 2;
   cfg->sinkhorn_iters = 4;
+  for (int i = 0; i < 4; ++i) cfg->rotation_signs[i] = 0;
 }
 
 size_t kvarn_tile_bytes(const kvarn_config* cfg) {
@@ -63,7 +64,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const 
   return from_hip(kvarn::launch_quantize_tiles(
       static_cast<const __half*>(k), static_cast<const __half*>(v), token_stride, n_tiles,
       cfg->num_kv_heads, dst_blocks, static_cast<uint8_t*>(block_pool), num_blocks,
-      cfg->sinkhorn_iters, static_cast<hipStream_t>(stream)));
+      cfg->sinkhorn_iters, cfg->rotation_signs, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, const void* v_new,
@@ -85,7 +86,8 @@ kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, cons
       static_cast<const __half*>(k_new), static_cast<const __half*>(v_new), positions,
       block_table, max_blocks_per_seq, static_cast<__half*>(staging_k),
       static_cast<__half*>(staging_v), static_cast<uint8_t*>(block_pool), num_blocks,
-      cfg->num_kv_heads, batch, cfg->sinkhorn_iters, static_cast<hipStream_t>(stream)));
+      cfg->num_kv_heads, batch, cfg->sinkhorn_iters, cfg->rotation_signs,
+      static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -132,7 +134,7 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads, n_query,
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
       seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
-      sm_scale, out, static_cast<float*>(workspace), splits, batch,
+      sm_scale, out, static_cast<float*>(workspace), splits, batch, cfg->rotation_signs,
       static_cast<hipStream_t>(stream)));
 }
 
@@ -189,6 +191,7 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_p
   return from_hip(kvarn::launch_dequantize_tiles(static_cast<const uint8_t*>(block_pool),
                                                  num_blocks, src_blocks, n_tiles,
                                                  cfg->num_kv_heads, k_out, v_out,
+                                                 cfg->rotation_signs,
                                                  static_cast<hipStream_t>(stream)));
 }
 

@@ -148,6 +148,14 @@ __device__ __forceinline__ uint32_t hi_or_lo(float a, float b, float negk) {
   return r;
 }
 
+// Sign bits of channels 2 lane and 2 lane + 1 from the four sign words (bit j % 32 of word
+// j / 32 negates channel j), as (bit of 2 lane, bit of 2 lane + 1) in bits 0 and 1.
+__device__ __forceinline__ uint32_t lane_sign_bits(uint4 signs, int lane) {
+  const uint32_t word = lane < 32 ? (lane < 16 ? signs.x : signs.y)
+                                  : (lane < 48 ? signs.z : signs.w);
+  return (word >> (2 * (lane & 15))) & 3u;
+}
+
 // Both fp16 halves of w plus c (v_pk_add_f16; exact for the centring below).
 __device__ __forceinline__ uint32_t add_h2(uint32_t w, half2v c) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) + c);
@@ -241,7 +249,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     const int32_t* __restrict__ seq_lens, float sm_scale,
-                    float* __restrict__ partials) {
+                    float* __restrict__ partials, uint4 signs) {
   __shared__ TileSmem sm;
   const int split = blockIdx.x, nsplit = gridDim.x;
   // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
@@ -288,7 +296,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     const int gg = 2 * wave + k;
     float o0 = 0.0f, o1 = 0.0f;
     if (gg < nh) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(q + row_of(vbase + gg) * kD)[lane];
+      uint32_t w = reinterpret_cast<const uint32_t*>(q + row_of(vbase + gg) * kD)[lane];
+      const uint32_t sb = lane_sign_bits(signs, lane);           // optional sign flips
+      w ^= ((sb & 1u) << 15) | ((sb >> 1) << 31);
       o0 = fp16_bits_to_float(w & 0xFFFFu);
       o1 = fp16_bits_to_float(w >> 16);
     }
@@ -588,7 +598,8 @@ __global__ void __launch_bounds__(kMThreads)
 decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int max_blocks,
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
-                    const float* __restrict__ partials, int nsplit, float* __restrict__ out) {
+                    const float* __restrict__ partials, int nsplit, float* __restrict__ out,
+                    uint4 signs) {
   __shared__ float qs[kD];
   const int qi = blockIdx.x / hq, h = blockIdx.x % hq, b = blockIdx.y;   // query token, head
   const int lane = threadIdx.x;
@@ -647,7 +658,12 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
       o1 = fmaf(w, v.y, o1);
     }
   }
-  if constexpr (kRotated) fwht_wave(o0, o1, lane);
+  if constexpr (kRotated) {
+    fwht_wave(o0, o1, lane);
+    const uint32_t sb = lane_sign_bits(signs, lane);            // optional sign flips
+    o0 = __uint_as_float(__float_as_uint(o0) ^ ((sb & 1u) << 31));
+    o1 = __uint_as_float(__float_as_uint(o1) ^ ((sb >> 1) << 31));
+  }
   constexpr float kBack = kRotated ? 0.08838834764831845f : 1.0f;   // H / sqrt(128) or none
   // raw staging output
   float r0 = 0.0f, r1 = 0.0f;
@@ -690,7 +706,7 @@ __device__ __forceinline__ void v_code_pos(int t, int j, uint32_t& byte_off, int
 __global__ void __launch_bounds__(256)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
                         const int32_t* __restrict__ src_blocks, int n_tiles, int hkv,
-                        float* __restrict__ k_out, float* __restrict__ v_out) {
+                        float* __restrict__ k_out, float* __restrict__ v_out, uint4 signs) {
   const int id = blockIdx.x;
   const int is_v = id & 1, head = (id >> 1) % hkv, tile = (id >> 1) / hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -709,6 +725,7 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
   const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false);   // c-hat of 2 l, 2 l + 1
   uint32_t vb0 = 0, vb1 = 0;
   int vs0 = 0, vs1 = 0;
+  const uint32_t sb = lane_sign_bits(signs, lane);              // optional sign flips
   for (int t = wave; t < kT; t += 4) {
     const float sh = __builtin_amdgcn_cvt_f32_fp8((int)meta[kSRel + t], 0);
     const float zh = fp16_bits_to_float(*reinterpret_cast<const uint16_t*>(meta + kZRel + 2 * t));
@@ -725,8 +742,9 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
     }
     float y0 = c[0] * fmaf(sh, q0, zh), y1 = c[1] * fmaf(sh, q1, zh);
     fwht_wave(y0, y1, lane);
-    reinterpret_cast<float2*>(out + t * row_stride)[lane] =
-        make_float2(y0 * 0.08838834764831845f, y1 * 0.08838834764831845f);
+    y0 = __uint_as_float(__float_as_uint(y0 * 0.08838834764831845f) ^ ((sb & 1u) << 31));
+    y1 = __uint_as_float(__float_as_uint(y1 * 0.08838834764831845f) ^ ((sb >> 1) << 31));
+    reinterpret_cast<float2*>(out + t * row_stride)[lane] = make_float2(y0, y1);
   }
 }
 
@@ -994,10 +1012,11 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 
 hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
                                    const int32_t* src_blocks, int n_tiles, int hkv, float* k_out,
-                                   float* v_out, hipStream_t stream) {
+                                   float* v_out, const uint32_t* signs, hipStream_t stream) {
   const long long groups = 2LL * hkv * n_tiles;
   hipLaunchKernelGGL(dequantize_tiles_kernel, dim3((unsigned)groups), dim3(256), 0, stream, pool,
-                     num_blocks, src_blocks, n_tiles, hkv, k_out, v_out);
+                     num_blocks, src_blocks, n_tiles, hkv, k_out, v_out,
+                     make_uint4(signs[0], signs[1], signs[2], signs[3]));
   return hipGetLastError();
 }
 
@@ -1016,27 +1035,28 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
-                         int splits, int batch, hipStream_t stream) {
+                         int splits, int batch, const uint32_t* signs, hipStream_t stream) {
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
+  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
   if (nq == 1)
     hipLaunchKernelGGL(decode_tiles_kernel<false>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
                        nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
-                       partials);
+                       partials, sg);
   else
     hipLaunchKernelGGL(decode_tiles_kernel<true>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
                        nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
-                       partials);
+                       partials, sg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nq == 1)
     hipLaunchKernelGGL((decode_merge_kernel<true, false>), mgrid, dim3(kMThreads), 0, stream, q,
                        hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                       partials, splits, out);
+                       partials, splits, out, sg);
   else
     hipLaunchKernelGGL((decode_merge_kernel<true, true>), mgrid, dim3(kMThreads), 0, stream, q,
                        hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                       partials, splits, out);
+                       partials, splits, out, sg);
   return hipGetLastError();
 }
 
@@ -1060,9 +1080,9 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
                      max_blocks, seq_lens, sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<false, false>), dim3(hq, batch), dim3(kMThreads), 0, stream, q,
-                     hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials,
-                     splits, out);
+  hipLaunchKernelGGL((decode_merge_kernel<false, false>), dim3(hq, batch), dim3(kMThreads), 0,
+                     stream, q, hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
+                     partials, splits, out, make_uint4(0, 0, 0, 0));
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct QuantSmem {
   uint32_t meta[96];     // staged FP8 s-hat (32 words) and FP16 z-hat (64 words)
   uint32_t chat[32];     // staged FP8 c-hat
   float red[32];
+  alignas(16) uint32_t sgn[64];   // sign-flip masks of channel pairs (2 i, 2 i + 1), fp16 bits
 };
 
 constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
@@ -250,7 +251,7 @@ __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, i
 __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
                                               long long token_stride,
                                               const __half* __restrict__ row127, int is_v,
-                                              int iters, uint8_t* __restrict__ rec,
+                                              int iters, uint4 signs, uint8_t* __restrict__ rec,
                                               QuantSmem& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -270,6 +271,20 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     uint4 w[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) w[m] = r4[2 * m];                // channels cbase + 16 m ..
+    if ((signs.x | signs.y | signs.z | signs.w) != 0u) {        // optional sign flips
+      if (tid < 64) {
+        const uint32_t word = tid < 32 ? (tid < 16 ? signs.x : signs.y)
+                                       : (tid < 48 ? signs.z : signs.w);
+        const uint32_t b2 = (word >> (2 * (tid & 15))) & 3u;
+        sm.sgn[tid] = ((b2 & 1u) << 15) | ((b2 >> 1) << 31);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint4 sg = *reinterpret_cast<const uint4*>(&sm.sgn[(cbase >> 1) + 8 * m]);
+        w[m].x ^= sg.x; w[m].y ^= sg.y; w[m].z ^= sg.z; w[m].w ^= sg.w;
+      }
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) unpack_h8(w[m], x + 8 * m);
   }
@@ -470,7 +485,7 @@ __global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(
 quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v,
                       long long token_stride, int n_tiles, int hkv,
                       const int32_t* __restrict__ dst_blocks, uint8_t* __restrict__ pool,
-                      long long num_blocks, int iters) {
+                      long long num_blocks, int iters, uint4 signs) {
   __shared__ QuantSmem sm;
   const int id = blockIdx.x;
   const int is_v = id & 1;
@@ -481,7 +496,7 @@ quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v
   if (blk < 0 || blk >= num_blocks) return;
   const __half* src = (is_v ? v : k) + (long long)tile * kT * token_stride + head * kD;
   uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
-  quantize_tile(src, token_stride, nullptr, is_v, iters, rec, sm);
+  quantize_tile(src, token_stride, nullptr, is_v, iters, signs, rec, sm);
 }
 
 // grid: 2 * num_kv_heads * batch workgroups; id = (b * Hkv + head) * 2 + kv
@@ -490,7 +505,8 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
                     const int32_t* __restrict__ positions,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     __half* __restrict__ staging_k, __half* __restrict__ staging_v,
-                    uint8_t* __restrict__ pool, long long num_blocks, int hkv, int iters) {
+                    uint8_t* __restrict__ pool, long long num_blocks, int hkv, int iters,
+                    uint4 signs) {
   __shared__ QuantSmem sm;
   const int id = blockIdx.x;
   const int is_v = id & 1;
@@ -512,7 +528,7 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
   if (blk < 0 || blk >= num_blocks) return;
   uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
   // token 127 comes from the new token itself, so no read-after-write through global memory
-  quantize_tile(stg, kD, src_tok, is_v, iters, rec, sm);
+  quantize_tile(stg, kD, src_tok, is_v, iters, signs, rec, sm);
 }
 
 }  // namespace
@@ -520,10 +536,11 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
 hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
                                  int n_tiles, int hkv, const int32_t* dst_blocks,
                                  uint8_t* pool, long long num_blocks, int iters,
-                                 hipStream_t stream) {
+                                 const uint32_t* signs, hipStream_t stream) {
   const long long groups = 2LL * hkv * n_tiles;
+  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
   hipLaunchKernelGGL(quantize_tiles_kernel, dim3((unsigned)groups), dim3(kQThreads), 0, stream,
-                     k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks, iters);
+                     k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks, iters, sg);
   return hipGetLastError();
 }
 
@@ -531,11 +548,12 @@ hipError_t launch_append_token(const __half* k_new, const __half* v_new,
                                const int32_t* positions, const int32_t* block_table,
                                int max_blocks, __half* staging_k, __half* staging_v,
                                uint8_t* pool, long long num_blocks, int hkv, int batch,
-                               int iters, hipStream_t stream) {
+                               int iters, const uint32_t* signs, hipStream_t stream) {
   const long long groups = 2LL * hkv * batch;
+  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
   hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)groups), dim3(kQThreads), 0, stream,
                      k_new, v_new, positions, block_table, max_blocks, staging_k, staging_v,
-                     pool, num_blocks, hkv, iters);
+                     pool, num_blocks, hkv, iters, sg);
   return hipGetLastError();
 }
 

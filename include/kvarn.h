@@ -66,7 +66,7 @@ extern "C" {
 #define KVARN_API
 #endif
 
-#define KVARN_ABI_VERSION 1
+#define KVARN_ABI_VERSION 2
 #define KVARN_TILE_TOKENS 128
 #define KVARN_HEAD_DIM 128
 #define KVARN_TILE_BYTES 13312
@@ -93,9 +93,14 @@ typedef struct {
   int32_t k_bits;         /* must be 4                 */
   int32_t v_bits;         /* must be 2                 */
   int32_t sinkhorn_iters; /* 1..16, default 4          */
+  /* Optional sign flips before the rotation (a randomised-sign Hadamard; not part of the
+   * pages' preset): channel j is negated before H when bit j % 32 of rotation_signs[j / 32]
+   * is set, and again after H on the read path. All zero (the default) is the plain
+   * Hadamard of the preset. Records written with one setting must be read with the same. */
+  uint32_t rotation_signs[4];
 } kvarn_config;
 
-/* Fills *cfg with the preset for num_kv_heads heads (sinkhorn_iters = 4). */
+/* Fills *cfg with the preset for num_kv_heads heads (sinkhorn_iters = 4, no sign flips). */
 KVARN_API void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads);
 
 /* Bytes of one tile record (one KV head of one block, keys and values): 13312, or 0 if the

@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvarn_abi_version() == 1
+    assert lib.kvarn_abi_version() == 2
 
 
 def test_sizes(lib):
