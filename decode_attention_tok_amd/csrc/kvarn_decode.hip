@@ -623,12 +623,34 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   const float scale2 = sm_scale * kLog2e;
   const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
   const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
+  // this lane's staging key row (token lane) is loaded before the length is known: the row
+  // is always inside the staging tile, and used only if the token is live
+  uint4 krow[16];
+  {
+    const uint4* k4 = reinterpret_cast<const uint4*>(sk + lane * kD);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) krow[i] = k4[i];
+  }
+  const uint32_t vpre0 = reinterpret_cast<const uint32_t*>(sv)[lane];
+  const uint32_t vpre1 = reinterpret_cast<const uint32_t*>(sv)[kD / 2 + lane];
   qs[2 * lane] = fp16_bits_to_float(qw & 0xFFFFu);
   qs[2 * lane + 1] = fp16_bits_to_float(qw >> 16);
   __syncthreads();
   // staging scores of tokens lane and lane + 64
   float s0 = -INFINITY, s1 = -INFINITY;
-  if (lane < n_stage) s0 = staging_dot(sk + lane * kD, qs) * scale2;
+  if (lane < n_stage) {
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float kv[8];
+      unpack_h8(krow[k], kv);
+      const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * k);
+      const float4 qc = *reinterpret_cast<const float4*>(qs + 8 * k + 4);
+      acc0 = fmaf(qa.x, kv[0], fmaf(qa.y, kv[1], fmaf(qa.z, kv[2], fmaf(qa.w, kv[3], acc0))));
+      acc1 = fmaf(qc.x, kv[4], fmaf(qc.y, kv[5], fmaf(qc.z, kv[6], fmaf(qc.w, kv[7], acc1))));
+    }
+    s0 = (acc0 + acc1) * scale2;
+  }
   if (lane + 64 < n_stage) s1 = staging_dot(sk + (lane + 64) * kD, qs) * scale2;
   const bool invalid = bad || __any(msp != msp);
   const float mm = wave_max(fmaxf(msp, fmaxf(s0, s1)));
@@ -669,7 +691,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   float r0 = 0.0f, r1 = 0.0f;
   const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
   for (int t = 0; t < n_stage; ++t) {
-    const uint32_t w = vcol[t * (kD / 2)];
+    const uint32_t w = t == 0 ? vpre0 : (t == 1 ? vpre1 : vcol[t * (kD / 2)]);
     const int src = __float_as_int(t < 64 ? p0 : p1);
     const float pt = __int_as_float(__builtin_amdgcn_readlane(src, t & 63));
     r0 = fmaf(pt, fp16_bits_to_float(w & 0xFFFFu), r0);
@@ -1024,8 +1046,11 @@ int decode_splits(int batch, int hkv, int max_blocks) {
   const long long pairs = (long long)batch * hkv;
   // about 512 workgroups (2048 waves: one round at 2 waves per SIMD on 256 CUs)
   long long s = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
-  const long long per_wave = (max_blocks + kWaves - 1) / kWaves;   // >= one tile per wave
-  if (s > per_wave) s = per_wave;
+  // at least two tiles per wave where the table allows it, so a wave's next tile is already
+  // loading while it works on the current one
+  const long long per_wave = (max_blocks + kWaves - 1) / kWaves;
+  const long long cap = per_wave / 2 > 0 ? per_wave / 2 : 1;
+  if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
