@@ -31,16 +31,18 @@ def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS, sig
     """Quantise whole prefill tiles into the block pool, in place.
 
     k, v: [n_tiles * 128, Hkv, 128] fp16 values; tile i holds tokens 128 i .. 128 i + 127 and
-    goes to block dst_blocks[i]; pool: uint8 [num_blocks, Hkv, 13312]."""
+    goes to block dst_blocks[i]; pool: uint8 [num_blocks, Hkv, record bytes] (13312 for 2-bit
+    values, 17408 for 4-bit: the pool's record size selects the preset)."""
     k = np.asarray(k)
     v = np.asarray(v)
     n_tiles = len(dst_blocks)
     hkv = k.shape[1]
+    vb = codec.v_bits_of_record(pool.shape[-1])
     for i in range(n_tiles):
         rows = slice(T * i, T * i + T)
         for h in range(hkv):
             pool[dst_blocks[i], h] = codec.encode_record(k[rows, h, :], v[rows, h, :], iters,
-                                                         signs)
+                                                         signs, vb)
 
 
 def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, pool,
@@ -49,7 +51,9 @@ def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, poo
     its tile, quantise the staging tile into block_table[b][position // 128]. In place.
 
     k_new, v_new: [B, Hkv, 128]; positions: [B] 0-based index of the new token, negative =
-    skip this row; staging_k, staging_v: [B, Hkv, 128, 128]."""
+    skip this row; staging_k, staging_v: [B, Hkv, 128, 128]. The pool's record size selects
+    the preset, as in quantize_tiles()."""
+    vb = codec.v_bits_of_record(pool.shape[-1])
     for b, pos in enumerate(np.asarray(positions)):
         if pos < 0:
             continue
@@ -60,7 +64,7 @@ def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, poo
             blk = block_table[b, int(pos) // T]
             for h in range(staging_k.shape[1]):
                 pool[blk, h] = codec.encode_record(staging_k[b, h], staging_v[b, h], iters,
-                                                   signs)
+                                                   signs, vb)
 
 
 def _sequence_kv(pool, block_table, staging_k, staging_v, b, g, length, signs=None):

@@ -18,7 +18,8 @@ normalised; R9 one asymmetric grid per token over the channel-equalised values; 
 per channel (c-hat) and per token (s-hat), FP16 zero-point per token (z-hat); R13 codes and
 c-hat round to nearest-even, s-hat rounds up and z-hat rounds down so that the grid covers
 every value of its token; R14 codes come from the stored, rounded scales; R15 overflow
-saturates and is flagged.
+saturates and is flagged; R28 a second preset with 4-bit values (kvarn_k4v4_g128) beside the
+pages' kvarn_k4v2_g128, same stages, its own record layout.
 
 Test infrastructure only (see the package header).
 """
@@ -32,24 +33,48 @@ from .hadamard import H128, rotate
 T = 128           # tokens per tile = tokens per cache block
 D = 128           # head dimension = channels per token
 K_BITS = 4
-V_BITS = 2
+V_BITS = 2        # value bits of the default preset kvarn_k4v2_g128
+V_BITS_ALLOWED = (2, 4)
 DEFAULT_ITERS = 4
 
 # ------------------------------------------------------------------ tile record layout
-# One record per (block, KV head), 13312 bytes, little-endian:
-#   [0, 8192)       key codes, token-major: token t at byte 64*t; channel j in byte j//2,
-#                   low nibble for even j, high nibble for odd j
-#   [8192, 12288)   value codes, 2 bits each, at the position given by v_code_position()
-#   [12288, 12416)  key   per-channel scale c-hat, FP8 E4M3, channel j at byte j
-#   [12416, 12544)  key   per-token scale s-hat, FP8 E4M3, token t at byte t
-#   [12544, 12800)  key   per-token zero-point z-hat, FP16, token t at bytes 2t, 2t+1
-#   [12800, 12928)  value c-hat;  [12928, 13056) value s-hat;  [13056, 13312) value z-hat
+# One record per (block, KV head), little-endian. With value bits vb (2 or 4) and
+# V = 2048 vb bytes of value codes:
+#   [0, 8192)            key codes, token-major: token t at byte 64*t; channel j in byte j//2,
+#                        low nibble for even j, high nibble for odd j
+#   [8192, 8192 + V)     value codes, vb bits each, at the position given by
+#                        v_code_position() (vb = 2) or v4_code_position() (vb = 4)
+#   then 512 bytes of key metadata and 512 of value metadata, each:
+#     +0    per-channel scale c-hat, FP8 E4M3, channel j at byte j
+#     +128  per-token scale s-hat, FP8 E4M3, token t at byte t
+#     +256  per-token zero-point z-hat, FP16, token t at bytes 2t, 2t+1
+# vb = 2: 13312 bytes (metadata at 12288 and 12800); vb = 4: 17408 (16384 and 16896).
 K_CODES_OFF = 0
 V_CODES_OFF = 8192
 K_META_OFF = 12288
 V_META_OFF = 12800
 C_REL, S_REL, Z_REL = 0, 128, 256
 TILE_BYTES = 13312
+
+
+def layout(v_bits: int = V_BITS) -> dict:
+    """Byte offsets and size of the record for `v_bits`-bit values."""
+    if v_bits not in V_BITS_ALLOWED:
+        raise ValueError("value bits must be 2 or 4")
+    k_meta = V_CODES_OFF + 2048 * v_bits
+    return dict(k_meta=k_meta, v_meta=k_meta + 512, tile_bytes=k_meta + 1024)
+
+
+def tile_bytes(v_bits: int = V_BITS) -> int:
+    return layout(v_bits)["tile_bytes"]
+
+
+def v_bits_of_record(n_bytes: int) -> int:
+    """The value bits a record of n_bytes bytes holds (13312: 2, 17408: 4)."""
+    for vb in V_BITS_ALLOWED:
+        if tile_bytes(vb) == n_bytes:
+            return vb
+    raise ValueError("record must be 13312 or 17408 bytes")
 
 
 def v_code_position(t, j):
@@ -68,8 +93,24 @@ def v_code_position(t, j):
     return 4 * word + bit // 8, bit % 8
 
 
+def v4_code_position(t, j):
+    """Bit address of the 4-bit value code of token t, channel j (preset kvarn_k4v4_g128).
+
+    The section is 2048 words; the same token grouping as the 2-bit layout, with the channel
+    blocks split into two halves hb = nb // 4 of four nibble fields each:
+        word = 512*kb + 256*hb + 4*(16*s + n) + (2*h + i // 2),   bit = 4*(nb % 4) + 16*(i % 2).
+    Returns (byte offset within the section, bit shift within that byte)."""
+    t = np.asarray(t)
+    j = np.asarray(j)
+    nb, n = j // 16, j % 16
+    kb, h, s, i = t // 32, (t // 16) % 2, (t // 4) % 4, t % 4
+    word = 512 * kb + 256 * (nb // 4) + 4 * (16 * s + n) + (2 * h + i // 2)
+    bit = 4 * (nb % 4) + 16 * (i % 2)
+    return 4 * word + bit // 8, bit % 8
+
+
 _VT, _VJ = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
-_V_BYTE, _V_SHIFT = v_code_position(_VT, _VJ)
+_V_POS = {2: v_code_position(_VT, _VJ), 4: v4_code_position(_VT, _VJ)}
 
 
 # ------------------------------------------------------------------ normalisation
@@ -109,7 +150,7 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS, signs=No
     """Quantise one T x D tile of fp16 values with `bits`-bit codes.
 
     Returns a dict with c_hat, s_hat, z_hat (float64 values), c_code, s_code (E4M3 bytes),
-    z_bits (FP16 patterns), codes (T x D int), and the intermediates xt (rotated tile),
+    z_bits (FP16 patterns), codes (T x D int), bits, and the intermediates xt (rotated tile),
     c (pre-rounding per-channel scale), step (pre-rounding per-token scale), y (xt / c_hat),
     flags (count of saturations)."""
     x = np.asarray(x, dtype=np.float64)
@@ -123,7 +164,7 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS, signs=No
         return dict(c_hat=one, c_code=one_code, s_hat=zero, s_code=np.zeros(T, np.uint8),
                     z_hat=zero.copy(), z_bits=np.zeros(T, np.uint16),
                     codes=np.zeros((T, D), np.int64), xt=xt, c=np.ones(D), step=zero.copy(),
-                    y=np.zeros((T, D)), flags=0)
+                    y=np.zeros((T, D)), flags=0, bits=bits)
     lc, _, _ = normalise(xt, iters)                       # stage 2: variance normalisation
     c = np.exp(lc)
     c_hat, c_code = e4m3_rne(np.clip(c, E4M3_MIN_SUBNORMAL, E4M3_MAX))
@@ -139,7 +180,7 @@ def quantize_tile(x: np.ndarray, bits: int, iters: int = DEFAULT_ITERS, signs=No
         q = np.rint((y - z_hat[:, None]) / s_hat[:, None])
     codes = np.where(s_hat[:, None] > 0, np.clip(q, 0, qmax), 0).astype(np.int64)
     return dict(c_hat=c_hat, c_code=c_code, s_hat=s_hat, s_code=s_code, z_hat=z_hat,
-                z_bits=z_bits, codes=codes, xt=xt, c=c, step=step, y=y, flags=flags)
+                z_bits=z_bits, codes=codes, xt=xt, c=c, step=step, y=y, flags=flags, bits=bits)
 
 
 def dequantize_rotated(c_hat, s_hat, z_hat, codes) -> np.ndarray:
@@ -159,15 +200,21 @@ def dequantize(c_hat, s_hat, z_hat, codes, signs=None) -> np.ndarray:
 
 
 def pack_record(kq: dict, vq: dict) -> np.ndarray:
-    """The 13312-byte record of one (block, KV head) from the key and value tile results."""
-    rec = np.zeros(TILE_BYTES, dtype=np.uint8)
+    """The record of one (block, KV head) from the key and value tile results; its size
+    follows the value bits vq["bits"] (2: 13312 bytes, 4: 17408)."""
+    if kq.get("bits", K_BITS) != K_BITS:
+        raise ValueError("keys are 4-bit in every preset")
+    vb = vq.get("bits", V_BITS)
+    lay = layout(vb)
+    rec = np.zeros(lay["tile_bytes"], dtype=np.uint8)
     kc = np.asarray(kq["codes"], dtype=np.uint8)
     rec[K_CODES_OFF:V_CODES_OFF] = (kc[:, 0::2] | (kc[:, 1::2] << 4)).reshape(-1)
-    vsec = np.zeros(K_META_OFF - V_CODES_OFF, dtype=np.uint8)
+    vsec = np.zeros(lay["k_meta"] - V_CODES_OFF, dtype=np.uint8)
     vc = np.asarray(vq["codes"], dtype=np.uint8)
-    np.bitwise_or.at(vsec, _V_BYTE.reshape(-1), (vc << _V_SHIFT).reshape(-1).astype(np.uint8))
-    rec[V_CODES_OFF:K_META_OFF] = vsec
-    for off, q in ((K_META_OFF, kq), (V_META_OFF, vq)):
+    vbyte, vshift = _V_POS[vb]
+    np.bitwise_or.at(vsec, vbyte.reshape(-1), (vc << vshift).reshape(-1).astype(np.uint8))
+    rec[V_CODES_OFF:lay["k_meta"]] = vsec
+    for off, q in ((lay["k_meta"], kq), (lay["v_meta"], vq)):
         rec[off + C_REL:off + C_REL + D] = q["c_code"]
         rec[off + S_REL:off + S_REL + T] = q["s_code"]
         rec[off + Z_REL:off + Z_REL + 2 * T] = np.asarray(q["z_bits"], "<u2").view(np.uint8)
@@ -176,31 +223,39 @@ def pack_record(kq: dict, vq: dict) -> np.ndarray:
 
 def unpack_record(rec: np.ndarray) -> dict:
     """Codes and scales of both halves of a record: dict(k=..., v=...), each with
-    codes (T x D int), c_code, s_code, z_bits and their float64 values."""
+    codes (T x D int), c_code, s_code, z_bits and their float64 values. The value bits are
+    those of the record's size (13312 bytes: 2, 17408: 4)."""
     rec = np.asarray(rec, dtype=np.uint8)
-    if rec.shape != (TILE_BYTES,):
-        raise ValueError("record must be 13312 bytes")
+    if rec.ndim != 1:
+        raise ValueError("one record at a time")
+    vb = v_bits_of_record(rec.shape[0])
+    lay = layout(vb)
     kb = rec[K_CODES_OFF:V_CODES_OFF].reshape(T, D // 2).astype(np.int64)
     kcodes = np.empty((T, D), np.int64)
     kcodes[:, 0::2] = kb & 0xF
     kcodes[:, 1::2] = kb >> 4
-    vsec = rec[V_CODES_OFF:K_META_OFF].astype(np.int64)
-    vcodes = (vsec[_V_BYTE] >> _V_SHIFT) & 0x3
+    vsec = rec[V_CODES_OFF:lay["k_meta"]].astype(np.int64)
+    vbyte, vshift = _V_POS[vb]
+    vcodes = (vsec[vbyte] >> vshift) & ((1 << vb) - 1)
     out = {}
-    for name, off, codes in (("k", K_META_OFF, kcodes), ("v", V_META_OFF, vcodes)):
+    for name, off, codes in (("k", lay["k_meta"], kcodes), ("v", lay["v_meta"], vcodes)):
         c_code = rec[off + C_REL:off + C_REL + D].copy()
         s_code = rec[off + S_REL:off + S_REL + T].copy()
         z_bits = rec[off + Z_REL:off + Z_REL + 2 * T].copy().view("<u2").astype(np.uint16)
         out[name] = dict(codes=codes, c_code=c_code, s_code=s_code, z_bits=z_bits,
                          c_hat=e4m3_value(c_code), s_hat=e4m3_value(s_code),
                          z_hat=fp16_value(z_bits))
+    out["v_bits"] = vb
     return out
 
 
-def encode_record(k_tile, v_tile, iters: int = DEFAULT_ITERS, signs=None) -> np.ndarray:
+def encode_record(k_tile, v_tile, iters: int = DEFAULT_ITERS, signs=None,
+                  v_bits: int = V_BITS) -> np.ndarray:
     """Quantise the key and value tiles of one (block, KV head) and pack them."""
+    if v_bits not in V_BITS_ALLOWED:
+        raise ValueError("value bits must be 2 or 4")
     return pack_record(quantize_tile(k_tile, K_BITS, iters, signs),
-                       quantize_tile(v_tile, V_BITS, iters, signs))
+                       quantize_tile(v_tile, v_bits, iters, signs))
 
 
 def decode_record(rec, signs=None) -> tuple:
