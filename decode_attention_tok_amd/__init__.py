@@ -1,5 +1,5 @@
-"""Python binding of libkvarn (the KVarN K4V2 g128 codec and paged decode attention on
-MI355X). Argument marshalling only: every step runs in the HIP kernels of libkvarn.so.
+"""Python binding of libkvarn (the KVarN K4V2 g128 codec, a K4V4 variant, and paged decode
+attention on MI355X). Argument marshalling only: every step runs in the HIP kernels of libkvarn.so.
 
 The entry points carry the C names of include/kvarn.h without the ``kvarn_`` prefix and take
 torch tensors (device memory) plus plain integers; torch is used only to own device memory and
@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libkvarn.so")
 
 TILE_TOKENS = 128
 HEAD_DIM = 128
-TILE_BYTES = 13312
+TILE_BYTES = 13312        # record of the default preset kvarn_k4v2_g128
+TILE_BYTES_V4 = 17408     # record with 4-bit values (kvarn_k4v4_g128)
 
 STATUS = {0: "OK", 1: "ERR_NULL_ARG", 2: "ERR_BAD_SHAPE", 3: "ERR_UNSUPPORTED",
           4: "ERR_WORKSPACE", 5: "ERR_HIP"}
@@ -103,12 +104,15 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def default_config(num_kv_heads: int, sinkhorn_iters: int = 4, rotation_signs=None) -> Config:
+def default_config(num_kv_heads: int, sinkhorn_iters: int = 4, rotation_signs=None,
+                   v_bits: int = 2) -> Config:
     """The preset for num_kv_heads heads; rotation_signs: optional four 32-bit words of
-    per-channel sign flips before the rotation (None: the plain Hadamard)."""
+    per-channel sign flips before the rotation (None: the plain Hadamard); v_bits 2
+    (kvarn_k4v2_g128) or 4 (kvarn_k4v4_g128)."""
     cfg = Config()
     lib().kvarn_default_config(ctypes.byref(cfg), num_kv_heads)
     cfg.sinkhorn_iters = sinkhorn_iters
+    cfg.v_bits = v_bits
     if rotation_signs is not None:
         for i in range(4):
             cfg.rotation_signs[i] = int(rotation_signs[i]) & 0xFFFFFFFF
@@ -138,7 +142,7 @@ def decode_workspace_bytes(cfg: Config, batch: int, num_q_heads: int,
 
 def quantize_tiles(cfg: Config, k, v, dst_blocks, block_pool, token_stride=None, stream=None):
     """k, v: fp16 [n_tiles*128, ...] with stride(0) = token_stride; dst_blocks int32 [n_tiles];
-    block_pool uint8 [num_blocks, Hkv, 13312] (or any tensor of num_blocks blocks)."""
+    block_pool uint8 [num_blocks, Hkv, tile_bytes(cfg)] (or any tensor of num_blocks blocks)."""
     n_tiles = dst_blocks.numel()
     stride = k.stride(0) if token_stride is None else token_stride
     num_blocks = block_pool.numel() // block_bytes(cfg)

@@ -13,13 +13,16 @@ kvarn_status check_config(const kvarn_config* cfg) {
   if (cfg == nullptr) return KVARN_ERR_NULL_ARG;
   if (cfg->num_kv_heads < 1) return KVARN_ERR_BAD_SHAPE;
   if (cfg->head_dim != KVARN_HEAD_DIM || cfg->block_tokens != KVARN_TILE_TOKENS ||
-      cfg->k_bits != 4 || cfg->v_bits != 2 || cfg->sinkhorn_iters < 1 ||
+      cfg->k_bits != 4 || (cfg->v_bits != 2 && cfg->v_bits != 4) || cfg->sinkhorn_iters < 1 ||
       cfg->sinkhorn_iters > 16)
     return KVARN_ERR_UNSUPPORTED;
   return KVARN_OK;
 }
 
 kvarn_status from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
+
+// Record bytes of a checked config: 8,192 key-code bytes, 2,048 per value bit, 1,024 metadata.
+size_t record_bytes(const kvarn_config* cfg) { return 8192u + 2048u * cfg->v_bits + 1024u; }
 
 constexpr long long kMaxGrid = 0x7FFFFFFFLL;
 
@@ -39,12 +42,11 @@ void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads) {
 }
 
 size_t kvarn_tile_bytes(const kvarn_config* cfg) {
-  return check_config(cfg) == KVARN_OK ? (size_t)KVARN_TILE_BYTES : 0;
+  return check_config(cfg) == KVARN_OK ? record_bytes(cfg) : 0;
 }
 
 size_t kvarn_block_bytes(const kvarn_config* cfg) {
-  return check_config(cfg) == KVARN_OK ? (size_t)KVARN_TILE_BYTES * (size_t)cfg->num_kv_heads
-                                       : 0;
+  return check_config(cfg) == KVARN_OK ? record_bytes(cfg) * (size_t)cfg->num_kv_heads : 0;
 }
 
 kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const void* v,
@@ -64,7 +66,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const 
   return from_hip(kvarn::launch_quantize_tiles(
       static_cast<const __half*>(k), static_cast<const __half*>(v), token_stride, n_tiles,
       cfg->num_kv_heads, dst_blocks, static_cast<uint8_t*>(block_pool), num_blocks,
-      cfg->sinkhorn_iters, cfg->rotation_signs, static_cast<hipStream_t>(stream)));
+      cfg->sinkhorn_iters, cfg->rotation_signs, cfg->v_bits, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, const void* v_new,
@@ -86,7 +88,7 @@ kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, cons
       static_cast<const __half*>(k_new), static_cast<const __half*>(v_new), positions,
       block_table, max_blocks_per_seq, static_cast<__half*>(staging_k),
       static_cast<__half*>(staging_v), static_cast<uint8_t*>(block_pool), num_blocks,
-      cfg->num_kv_heads, batch, cfg->sinkhorn_iters, cfg->rotation_signs,
+      cfg->num_kv_heads, batch, cfg->sinkhorn_iters, cfg->rotation_signs, cfg->v_bits,
       static_cast<hipStream_t>(stream)));
 }
 
@@ -135,7 +137,7 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
       seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
       sm_scale, out, static_cast<float*>(workspace), splits, batch, cfg->rotation_signs,
-      static_cast<hipStream_t>(stream)));
+      cfg->v_bits, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -191,7 +193,7 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_p
   return from_hip(kvarn::launch_dequantize_tiles(static_cast<const uint8_t*>(block_pool),
                                                  num_blocks, src_blocks, n_tiles,
                                                  cfg->num_kv_heads, k_out, v_out,
-                                                 cfg->rotation_signs,
+                                                 cfg->rotation_signs, cfg->v_bits,
                                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -258,7 +260,8 @@ const char* kvarn_status_string(kvarn_status status) {
     case KVARN_OK: return "ok";
     case KVARN_ERR_NULL_ARG: return "a required pointer is NULL";
     case KVARN_ERR_BAD_SHAPE: return "a size or count is out of range, or a buffer is misaligned";
-    case KVARN_ERR_UNSUPPORTED: return "unsupported config (only kvarn_k4v2_g128, head_dim 128)";
+    case KVARN_ERR_UNSUPPORTED:
+      return "unsupported config (presets kvarn_k4v2_g128 and kvarn_k4v4_g128, head_dim 128)";
     case KVARN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KVARN_ERR_HIP: return "HIP runtime error while launching";
   }

@@ -1,4 +1,4 @@
-// KVarN paged decode attention over packed K4/V2 tiles (read path) for gfx950.
+// KVarN paged decode attention over packed K4/V2 or K4/V4 tiles (read path) for gfx950.
 //
 // [GR] "The four-stage pipeline" (groundy.com, "Huawei's KVarN puts KV-cache quantization
 // inside vLLM's backend"), stage 4: scales are applied when a tile is read for attention;
@@ -26,7 +26,8 @@
 // with far less precision than products of normal ones, so raw codes are not used as
 // subnormals; a variant that left nibbles in the low mantissa bits, 1 + code / 1024 with the
 // query scaled to match, was far off as well, so every field sits just below the exponent.) Value codes likewise enter as 1 + code / 4 (the 2-bit
-// field shifted to mantissa bits 8..9), and sum_t p_t s-hat^V_t removes the constant part.
+// field shifted to mantissa bits 8..9) or 1 + code / 16 (a 4-bit field at bits 6..9), and
+// sum_t p_t s-hat^V_t removes the constant part.
 // fp32-accurate operands are split into fp16 hi + lo parts: query column g holds hi(q~_g),
 // column 8 + g holds lo(q~_g), and one DPP row rotation by 8 adds the two partial scores;
 // the probability operand likewise has rows g (hi) and 8 + g (lo), summed once at the end.
@@ -171,41 +172,48 @@ __device__ __forceinline__ uint32_t lo_of(uint32_t h, float a, float b) {
   return r;
 }
 
+template <int kVBits>
 struct TileRegs {
   uint4 kw[8];        // key codes: token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31
-  uint4 vw[4];        // value codes: section words 256 kb + 4 lane .. + 3
+  uint4 vw[2 * kVBits];   // value codes: section words 256 m + 4 lane .. + 3, m = 0 .. 2 kVBits - 1
   uint2 m8;           // 8 FP8 metadata bytes (see decode_meta)
   uint2 m16;          // 4 fp16 zero-points
 };
 
 // Per-lane byte offsets of the metadata a lane decodes. Lanes 0-15: c-hat^K, 16-31: s-hat^K,
 // 32-47: c-hat^V, 48-63: s-hat^V, 8 bytes each; lanes 0-31: z-hat^K, 32-63: z-hat^V, 4 each.
+template <int kVBits>
 __device__ __forceinline__ int meta8_off(int lane) {
-  return (lane < 32 ? kKMetaOff : kVMetaOff) + ((lane >> 4) & 1) * kSRel + 8 * (lane & 15);
+  using L = RecordLayout<kVBits>;
+  return (lane < 32 ? L::kKMetaOff : L::kVMetaOff) + ((lane >> 4) & 1) * kSRel + 8 * (lane & 15);
 }
+template <int kVBits>
 __device__ __forceinline__ int meta16_off(int lane) {
-  return (lane < 32 ? kKMetaOff : kVMetaOff) + kZRel + 8 * (lane & 31);
+  using L = RecordLayout<kVBits>;
+  return (lane < 32 ? L::kKMetaOff : L::kVMetaOff) + kZRel + 8 * (lane & 31);
 }
 
 // Per-lane byte offsets (unsigned, so a load is a scalar tile base plus a 32-bit lane offset):
 // key codes of token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31 at koff + 1024 mb;
-// value-code section words 4 lane .. + 3 at voff + 1024 kb.
+// value-code section words 256 m + 4 lane .. + 3 at voff + 1024 m.
 struct LaneOffsets {
   uint32_t koff, koff4, voff, off8, off16;
 };
 
+template <int kVBits>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   LaneOffsets o;
   o.koff = kKCodesOff + (uint32_t)(lane & 15) * 64u + 16u * (uint32_t)(lane >> 4);
   o.koff4 = o.koff + 4096u;
   o.voff = kVCodesOff + 16u * (uint32_t)lane;
-  o.off8 = (uint32_t)meta8_off(lane);
-  o.off16 = (uint32_t)meta16_off(lane);
+  o.off8 = (uint32_t)meta8_off<kVBits>(lane);
+  o.off16 = (uint32_t)meta16_off<kVBits>(lane);
   return o;
 }
 
+template <int kVBits>
 __device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, const LaneOffsets& o,
-                                          TileRegs& r) {
+                                          TileRegs<kVBits>& r) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
     r.kw[mb] = *reinterpret_cast<const uint4*>(rec + o.koff + 1024u * mb);
@@ -216,11 +224,12 @@ __device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, const
   r.m16 = *reinterpret_cast<const uint2*>(rec + o.off16);
 }
 
+template <int kVBits>
 __device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, const LaneOffsets& o,
-                                            TileRegs& r) {
+                                            TileRegs<kVBits>& r) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    r.vw[kb] = *reinterpret_cast<const uint4*>(rec + o.voff + 1024u * kb);
+  for (int m = 0; m < 2 * kVBits; ++m)
+    r.vw[m] = *reinterpret_cast<const uint4*>(rec + o.voff + 1024u * m);
 }
 
 // Every lane converts its 8 FP8 bytes and 4 fp16 values (the same instructions on all lanes)
@@ -242,8 +251,9 @@ __device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int
 }
 
 // kCausal: several query tokens per sequence (nq > 1) with the causal mask; a separate
-// instantiation so the one-token decode carries no mask code
-template <bool kCausal>
+// instantiation so the one-token decode carries no mask code. kVBits: 2 or 4 bits per value
+// code (the record layout of that preset).
+template <bool kCausal, int kVBits>
 __global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
@@ -275,8 +285,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
-  const LaneOffsets lo = lane_offsets(lane);
-  TileRegs cur;
+  constexpr long long kTileBytes = RecordLayout<kVBits>::kTileBytes;
+  const LaneOffsets lo = lane_offsets<kVBits>(lane);
+  TileRegs<kVBits> cur;
   int id_next = nw > 1 ? bt_row[kWaves] : 0;        // tile 1
   if (nw > 0) {
     const long long blk = bt_row[0];
@@ -474,8 +485,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     beta = add_xor32(add_xor16(beta));
     wsum = add_xor32(add_xor16(wsum));
     // output rows get D / 8 per tile: D = sum_t W_t (1 + code / 4), W = 32 p s-hat^V, so
-    // sum_t p s-hat^V code = D / 8 - 4 sum_t p s-hat^V = D / 8 - wsum / 8
-    beta = fmaf(-0.125f, wsum, beta);
+    // sum_t p s-hat^V code = D / 8 - 4 sum_t p s-hat^V = D / 8 - wsum / 8; with 4-bit codes
+    // D = sum_t W_t (1 + code / 16) and the sum is D / 2 - wsum / 2
+    constexpr float kVOut = kVBits == 4 ? 0.5f : 0.125f;
+    beta = fmaf(-kVOut, wsum, beta);
     l_run = fmaf(alpha, l_run, psum);
     m_run = mnew;
     if (s == 0) {
@@ -503,21 +516,34 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
         float4v po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
-          // the half is 1 + code / 4 (normal, exact)
-          const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
           uint32_t f[4];
+          if constexpr (kVBits == 2) {
+            // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
+            // the half is 1 + code / 4 (normal, exact)
+            const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
-            f[d] = and_or(x, vmask, one16);
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
+              f[d] = and_or(x, vmask, one16);
+            }
+          } else {
+            // words of channel half nb / 4; field nb % 4 (bits 4 (nb % 4) and 16 + 4 (nb % 4))
+            // -> mantissa bits 6..9: the half is 1 + code / 16 (normal, exact)
+            const uint4 ww = cur.vw[2 * kb + (nb >> 2)];
+            const uint32_t v4[4] = {ww.x, ww.y, ww.z, ww.w};
+            const int kF = nb & 3;                 // a constant once the loop is unrolled
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t x = kF < 2 ? (v4[d] << (6 - 4 * kF)) : (v4[d] >> (4 * kF - 6));
+              f[d] = and_or(x, kmask, one16);
+            }
           }
           po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], as_h8(f[0], f[1], f[2], f[3]),
                                                       po, 0, 0, 0);
         }
         const float cv = vc[16 * nb + n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], 0.125f, br[i]), oacc[nb][i]);
+        for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], kVOut, br[i]), oacc[nb][i]);
       }
     }
     if (nrec != nullptr) load_values(nrec, lo, cur);
@@ -716,15 +742,25 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
 // hkv * 2 workgroups (tile, head, K|V) of 4 waves; wave w rebuilds tokens w, w + 4, ..., lane l
 // channels 2 l and 2 l + 1, with the same butterfly as the query rotation.
 
-// Byte offset (in the value section) and bit shift of value code (token t, channel j).
+// Byte offset (in the value section) and bit shift of value code (token t, channel j), for
+// 2-bit codes (fields of 2 bits, 8 channel blocks per word) or 4-bit codes (fields of 4 bits,
+// the channel blocks split in two halves of 4 with 256 words per half).
+template <int kVBits>
 __device__ __forceinline__ void v_code_pos(int t, int j, uint32_t& byte_off, int& shift) {
   const int nb = j >> 4, n = j & 15, kb = t >> 5, h = (t >> 4) & 1, s = (t >> 2) & 3, i = t & 3;
-  const int word = 256 * kb + 4 * (16 * s + n) + 2 * h + (i >> 1);
-  const int bit = 2 * nb + 16 * (i & 1);
+  int word, bit;
+  if constexpr (kVBits == 2) {
+    word = 256 * kb + 4 * (16 * s + n) + 2 * h + (i >> 1);
+    bit = 2 * nb + 16 * (i & 1);
+  } else {
+    word = 512 * kb + 256 * (nb >> 2) + 4 * (16 * s + n) + 2 * h + (i >> 1);
+    bit = 4 * (nb & 3) + 16 * (i & 1);
+  }
   byte_off = 4u * (uint32_t)word + (uint32_t)(bit >> 3);
   shift = bit & 7;
 }
 
+template <int kVBits>
 __global__ void __launch_bounds__(256)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
                         const int32_t* __restrict__ src_blocks, int n_tiles, int hkv,
@@ -741,8 +777,9 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
       reinterpret_cast<float2*>(out + t * row_stride)[lane] = make_float2(NAN, NAN);
     return;
   }
-  const uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
-  const uint8_t* meta = rec + (is_v ? kVMetaOff : kKMetaOff);
+  using L = RecordLayout<kVBits>;
+  const uint8_t* rec = pool + (blk * hkv + head) * (long long)L::kTileBytes;
+  const uint8_t* meta = rec + (is_v ? L::kVMetaOff : L::kKMetaOff);
   const uint32_t cw = *reinterpret_cast<const uint16_t*>(meta + kCRel + 2 * lane);
   const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false);   // c-hat of 2 l, 2 l + 1
   uint32_t vb0 = 0, vb1 = 0;
@@ -757,10 +794,11 @@ dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
       q0 = (float)(byte & 15u);
       q1 = (float)(byte >> 4);
     } else {
-      v_code_pos(t, 2 * lane, vb0, vs0);
-      v_code_pos(t, 2 * lane + 1, vb1, vs1);
-      q0 = (float)((rec[kVCodesOff + vb0] >> vs0) & 3u);
-      q1 = (float)((rec[kVCodesOff + vb1] >> vs1) & 3u);
+      constexpr uint32_t kVMax = (1u << kVBits) - 1u;
+      v_code_pos<kVBits>(t, 2 * lane, vb0, vs0);
+      v_code_pos<kVBits>(t, 2 * lane + 1, vb1, vs1);
+      q0 = (float)((rec[kVCodesOff + vb0] >> vs0) & kVMax);
+      q1 = (float)((rec[kVCodesOff + vb1] >> vs1) & kVMax);
     }
     float y0 = c[0] * fmaf(sh, q0, zh), y1 = c[1] * fmaf(sh, q1, zh);
     fwht_wave(y0, y1, lane);
@@ -1034,11 +1072,16 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 
 hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
                                    const int32_t* src_blocks, int n_tiles, int hkv, float* k_out,
-                                   float* v_out, const uint32_t* signs, hipStream_t stream) {
+                                   float* v_out, const uint32_t* signs, int v_bits,
+                                   hipStream_t stream) {
   const long long groups = 2LL * hkv * n_tiles;
-  hipLaunchKernelGGL(dequantize_tiles_kernel, dim3((unsigned)groups), dim3(256), 0, stream, pool,
-                     num_blocks, src_blocks, n_tiles, hkv, k_out, v_out,
-                     make_uint4(signs[0], signs[1], signs[2], signs[3]));
+  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
+  if (v_bits == 4)
+    hipLaunchKernelGGL(dequantize_tiles_kernel<4>, dim3((unsigned)groups), dim3(256), 0, stream,
+                       pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg);
+  else
+    hipLaunchKernelGGL(dequantize_tiles_kernel<2>, dim3((unsigned)groups), dim3(256), 0, stream,
+                       pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg);
   return hipGetLastError();
 }
 
@@ -1060,18 +1103,15 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
-                         int splits, int batch, const uint32_t* signs, hipStream_t stream) {
+                         int splits, int batch, const uint32_t* signs, int v_bits,
+                         hipStream_t stream) {
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
   const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  if (nq == 1)
-    hipLaunchKernelGGL(decode_tiles_kernel<false>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
-                       nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
-                       partials, sg);
-  else
-    hipLaunchKernelGGL(decode_tiles_kernel<true>, grid, dim3(kTThreads), 0, stream, q, hq, hkv,
-                       nq, pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale,
-                       partials, sg);
+  auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4> : decode_tiles_kernel<false, 2>)
+                      : (v_bits == 4 ? decode_tiles_kernel<true, 4> : decode_tiles_kernel<true, 2>);
+  hipLaunchKernelGGL(kern, grid, dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool, num_blocks,
+                     block_table, max_blocks, seq_lens, sm_scale, partials, sg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nq == 1)

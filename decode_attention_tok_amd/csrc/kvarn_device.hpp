@@ -14,12 +14,21 @@ namespace kvarn {
 
 constexpr int kT = 128;              // tokens per tile
 constexpr int kD = 128;              // head dimension
-constexpr int kTileBytes = 13312;    // record of one (block, KV head)
-constexpr int kKCodesOff = 0;
-constexpr int kVCodesOff = 8192;
-constexpr int kKMetaOff = 12288;
-constexpr int kVMetaOff = 12800;
-constexpr int kCRel = 0, kSRel = 128, kZRel = 256;
+constexpr int kKCodesOff = 0;        // key codes: 8,192 bytes
+constexpr int kVCodesOff = 8192;     // value codes: 2,048 bytes per value bit
+constexpr int kCRel = 0, kSRel = 128, kZRel = 256;   // c-hat, s-hat, z-hat in a metadata half
+
+// Record of one (block, KV head) for value codes of kVBits bits: key codes, value codes, then
+// 512 bytes of key metadata and 512 of value metadata. kVBits = 2 is the preset
+// kvarn_k4v2_g128 (13,312 bytes), kVBits = 4 the preset kvarn_k4v4_g128 (17,408 bytes).
+template <int kVBits>
+struct RecordLayout {
+  static_assert(kVBits == 2 || kVBits == 4, "value codes are 2 or 4 bits");
+  static constexpr int kVCodeBytes = 2048 * kVBits;
+  static constexpr int kKMetaOff = kVCodesOff + kVCodeBytes;
+  static constexpr int kVMetaOff = kKMetaOff + 512;
+  static constexpr int kTileBytes = kKMetaOff + 1024;
+};
 
 // ------------------------------------------------------------------ FP8 E4M3 (non-negative)
 

@@ -20,7 +20,8 @@
 // channel bits 0-2 and 4-5 live in registers and bits 3 and 6 across the four lanes of a quad.
 // It does the transform (five butterfly stages in registers, two across lanes as DPP-sourced
 // fused multiply-adds), the row statistics and the codes; a thread's eight values of one m are
-// exactly one word of key nibbles, and its four values of one e are one byte of value crumbs.
+// exactly one word of key nibbles, its four values of one e are one byte of 2-bit value codes
+// or one 16-bit half-word of 4-bit value codes.
 // Layout B gives lane (j, th) = (16 wave + lane % 16, lane / 16) the 32 tokens th, th + 4, ...,
 // th + 124 of channel j: the column statistics, read from a copy of the rotated tile kept in LDS
 // for the whole normalisation and merged over the four lanes of a channel with permlane swaps,
@@ -193,10 +194,26 @@ __device__ __forceinline__ uint32_t put_code(float v, float qmax, uint32_t sel, 
 }
 
 // This thread's codes (token t, its 32 channels) into the LDS staging area (see the callers).
-template <bool kClamp>
+template <bool kClamp, int kVBits>
 __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, float qmax,
                                             int is_v, int t, int q0, int q1, uint32_t* stage) {
-  if (!is_v) {
+  if (is_v && kVBits == 4) {
+    // 4-bit value codes, staged as the section itself. Channel 16 nb + n with nb = m + 4 q1,
+    // n = 8 q0 + e: half-word i % 2 of section word 512 kb + 256 q1 + 4 (16 s + n) + 2 h +
+    // i / 2 holds the codes of nb % 4 = m = 0..3 at bits 4 m (t = 32 kb + 16 h + 4 s + i).
+    uint16_t* sh = reinterpret_cast<uint16_t*>(stage);
+    const int kb = t >> 5, h = (t >> 4) & 1, s4 = (t >> 2) & 3, i = t & 3;
+    const int w0 = 512 * kb + 256 * q1 + 4 * (16 * s4 + 8 * q0) + 2 * h + (i >> 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t ev = 0, od = 0;                    // fields m = 0, 2 and m = 1, 3 in bytes 0, 1
+      ev = put_code<kClamp>(fmaf(x[e], ca, cb), qmax, 0, ev);
+      ev = put_code<kClamp>(fmaf(x[16 + e], ca, cb), qmax, 1, ev);
+      od = put_code<kClamp>(fmaf(x[8 + e], ca, cb), qmax, 0, od);
+      od = put_code<kClamp>(fmaf(x[24 + e], ca, cb), qmax, 1, od);
+      sh[2 * (w0 + 4 * e) + (i & 1)] = (uint16_t)(ev | (od << 4));
+    }
+  } else if (!is_v) {
     // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
     // token's 16 words (channel 8 k + e at nibble e of word k)
 #pragma unroll
@@ -232,11 +249,13 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
   }
 }
 
+template <int kVBits>
 __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, int tid) {
   // All-zero rotated tile: c-hat = 1 (E4M3 0x38), s-hat = 0, z-hat = +0, every code 0.
+  using L = RecordLayout<kVBits>;
   const int code_off = is_v ? kVCodesOff : kKCodesOff;
-  const int code_bytes = is_v ? 4096 : 8192;
-  const int meta = is_v ? kVMetaOff : kKMetaOff;
+  const int code_bytes = is_v ? L::kVCodeBytes : 8192;
+  const int meta = is_v ? L::kVMetaOff : L::kKMetaOff;
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int i = tid; i < code_bytes / 16; i += kQThreads)
     reinterpret_cast<uint4*>(rec + code_off)[i] = z;
@@ -247,7 +266,9 @@ __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, i
 
 // Quantise one tile. `src` points at token 0, channel 0 of this KV head; token t starts at
 // src + t * token_stride. If `row127` is not null it replaces token 127 (the append path
-// passes the new token there). Writes the key or value half of the record at `rec`.
+// passes the new token there). Writes the key or value half of the record at `rec` (value
+// codes of kVBits bits).
+template <int kVBits>
 __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
                                               long long token_stride,
                                               const __half* __restrict__ row127, int is_v,
@@ -328,7 +349,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
 #pragma unroll
   for (int w = 1; w < kQThreads / 64; ++w) big = max_nn(big, sm.red[w]);
   if (big == 0.0f) {                              // uniform across the workgroup
-    store_record_zero_tile(rec, is_v, tid);
+    store_record_zero_tile<kVBits>(rec, is_v, tid);
     return;
   }
   const float* xcol = &sm.xt[th][cpos(jj)];       // column jj, tokens th + 4 i, stride 4 kXs
@@ -413,7 +434,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   }
 
   // ---- gauge (geometric mean of c = 1) and FP8 rounding of c, by wave 0
-  const int meta = is_v ? kVMetaOff : kKMetaOff;
+  const int meta = is_v ? RecordLayout<kVBits>::kVMetaOff : RecordLayout<kVBits>::kKMetaOff;
   if (wave == 0) {
     const float c0 = sm.cs[lane], c1 = sm.cs[lane + 64];
     const float lsum = wave_sum(log2f(c0) + log2f(c1));
@@ -429,7 +450,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kCRel)[tid] = sm.chat[tid];
 
   // ---- asymmetric RTN per token (layout A); p = (+-) y, sign `flip`
-  const float qmax = is_v ? 3.0f : 15.0f;
+  const float qmax = is_v ? (float)((1 << kVBits) - 1) : 15.0f;
   float pmin = 3.0e38f, pmax = -3.0e38f;
   {
     const float* rr = sm.rq + pbase;
@@ -458,11 +479,14 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   }
 
   uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
-  if (scode == 0x7Eu) stage_codes<true>(x, ca, cb, qmax, is_v, t, q0, q1, stage);  // s-hat = 448
-  else stage_codes<false>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
-  if (!is_v) {
+  if (scode == 0x7Eu)                                   // s-hat = 448
+    stage_codes<true, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
+  else
+    stage_codes<false, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
+  if (!is_v || kVBits == 4) {                          // staged as the section: 8,192 bytes
     __syncthreads();
-    reinterpret_cast<uint4*>(rec + kKCodesOff)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+    reinterpret_cast<uint4*>(rec + (is_v ? kVCodesOff : kKCodesOff))[tid] =
+        reinterpret_cast<const uint4*>(stage)[tid];
   } else {
     __syncthreads();
     if (tid < 256) {
@@ -481,6 +505,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
 }
 
 // grid: 2 * num_kv_heads * n_tiles workgroups; id = (tile * Hkv + head) * 2 + kv
+template <int kVBits>
 __global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v,
                       long long token_stride, int n_tiles, int hkv,
@@ -495,11 +520,12 @@ quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v
   const long long blk = dst_blocks[tile];
   if (blk < 0 || blk >= num_blocks) return;
   const __half* src = (is_v ? v : k) + (long long)tile * kT * token_stride + head * kD;
-  uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
-  quantize_tile(src, token_stride, nullptr, is_v, iters, signs, rec, sm);
+  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits>::kTileBytes;
+  quantize_tile<kVBits>(src, token_stride, nullptr, is_v, iters, signs, rec, sm);
 }
 
 // grid: 2 * num_kv_heads * batch workgroups; id = (b * Hkv + head) * 2 + kv
+template <int kVBits>
 __global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
 append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                     const int32_t* __restrict__ positions,
@@ -526,9 +552,9 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
   if (bi >= max_blocks) return;
   const long long blk = block_table[(long long)b * max_blocks + bi];
   if (blk < 0 || blk >= num_blocks) return;
-  uint8_t* rec = pool + (blk * hkv + head) * (long long)kTileBytes;
+  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits>::kTileBytes;
   // token 127 comes from the new token itself, so no read-after-write through global memory
-  quantize_tile(stg, kD, src_tok, is_v, iters, signs, rec, sm);
+  quantize_tile<kVBits>(stg, kD, src_tok, is_v, iters, signs, rec, sm);
 }
 
 }  // namespace
@@ -536,11 +562,17 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
 hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
                                  int n_tiles, int hkv, const int32_t* dst_blocks,
                                  uint8_t* pool, long long num_blocks, int iters,
-                                 const uint32_t* signs, hipStream_t stream) {
+                                 const uint32_t* signs, int v_bits, hipStream_t stream) {
   const long long groups = 2LL * hkv * n_tiles;
   const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  hipLaunchKernelGGL(quantize_tiles_kernel, dim3((unsigned)groups), dim3(kQThreads), 0, stream,
-                     k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks, iters, sg);
+  if (v_bits == 4)
+    hipLaunchKernelGGL(quantize_tiles_kernel<4>, dim3((unsigned)groups), dim3(kQThreads), 0,
+                       stream, k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks,
+                       iters, sg);
+  else
+    hipLaunchKernelGGL(quantize_tiles_kernel<2>, dim3((unsigned)groups), dim3(kQThreads), 0,
+                       stream, k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks,
+                       iters, sg);
   return hipGetLastError();
 }
 
@@ -548,12 +580,18 @@ hipError_t launch_append_token(const __half* k_new, const __half* v_new,
                                const int32_t* positions, const int32_t* block_table,
                                int max_blocks, __half* staging_k, __half* staging_v,
                                uint8_t* pool, long long num_blocks, int hkv, int batch,
-                               int iters, const uint32_t* signs, hipStream_t stream) {
+                               int iters, const uint32_t* signs, int v_bits,
+                               hipStream_t stream) {
   const long long groups = 2LL * hkv * batch;
   const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  hipLaunchKernelGGL(append_token_kernel, dim3((unsigned)groups), dim3(kQThreads), 0, stream,
-                     k_new, v_new, positions, block_table, max_blocks, staging_k, staging_v,
-                     pool, num_blocks, hkv, iters, sg);
+  if (v_bits == 4)
+    hipLaunchKernelGGL(append_token_kernel<4>, dim3((unsigned)groups), dim3(kQThreads), 0,
+                       stream, k_new, v_new, positions, block_table, max_blocks, staging_k,
+                       staging_v, pool, num_blocks, hkv, iters, sg);
+  else
+    hipLaunchKernelGGL(append_token_kernel<2>, dim3((unsigned)groups), dim3(kQThreads), 0,
+                       stream, k_new, v_new, positions, block_table, max_blocks, staging_k,
+                       staging_v, pool, num_blocks, hkv, iters, sg);
   return hipGetLastError();
 }
 

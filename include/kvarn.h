@@ -1,6 +1,6 @@
 /*
- * kvarn.h - C ABI of libkvarn: the KVarN K4V2 g128 KV-cache codec and the paged decode
- * attention that reads it, for AMD Instinct MI355X (gfx950).
+ * kvarn.h - C ABI of libkvarn: the KVarN K4V2 g128 KV-cache codec (and a K4V4 variant) and
+ * the paged decode attention that reads it, for AMD Instinct MI355X (gfx950).
  *
  * Sources. The operations follow these pages (cited by title and section):
  *   [GR]  groundy.com, "Huawei's KVarN puts KV-cache quantization inside vLLM's backend":
@@ -29,18 +29,23 @@
  *     out-of-bounds access; see each entry point for the result it then produces.
  *
  * The packed cache. A block holds 128 tokens of every KV head: num_kv_heads tile records of
- * 13312 bytes back to back (record of block b, KV head h at byte (b * num_kv_heads + h) * 13312
- * of the block pool). A record, little-endian:
+ * R = kvarn_tile_bytes() bytes back to back (record of block b, KV head h at byte
+ * (b * num_kv_heads + h) * R of the block pool); R = 13312 for the preset kvarn_k4v2_g128
+ * (v_bits 2) and 17408 for kvarn_k4v4_g128 (v_bits 4). A record, little-endian, with
+ * V = 2048 * v_bits bytes of value codes and M = 8192 + V:
  *   [0, 8192)      key codes (4 bit), token-major: token t at byte 64 t; channel j in byte
  *                  j / 2, low nibble for even j, high nibble for odd j
- *   [8192, 12288)  value codes (2 bit), as 1024 32-bit words. With nb = j / 16, n = j % 16,
- *                  kb = t / 32, h = (t / 16) % 2, s = (t / 4) % 4, i = t % 4, the code of
- *                  token t, channel j is at word 256 kb + 4 (16 s + n) + 2 h + i / 2,
- *                  bits 2 nb + 16 (i % 2) .. +1
- *   [12288, 12416) key per-channel scale c-hat, FP8 E4M3 (OCP), channel j at byte j
- *   [12416, 12544) key per-token scale s-hat, FP8 E4M3, token t at byte t
- *   [12544, 12800) key per-token zero-point z-hat, fp16, token t at bytes 2t, 2t+1
- *   [12800, 13312) the same three arrays for the values
+ *   [8192, M)      value codes, as 32-bit words. With nb = j / 16, n = j % 16, kb = t / 32,
+ *                  h = (t / 16) % 2, s = (t / 4) % 4, i = t % 4, the code of token t,
+ *                  channel j is at
+ *                    v_bits 2: word 256 kb + 4 (16 s + n) + 2 h + i / 2,
+ *                              bits 2 nb + 16 (i % 2) .. +1
+ *                    v_bits 4: word 512 kb + 256 (nb / 4) + 4 (16 s + n) + 2 h + i / 2,
+ *                              bits 4 (nb % 4) + 16 (i % 2) .. +3
+ *   [M, M + 128)       key per-channel scale c-hat, FP8 E4M3 (OCP), channel j at byte j
+ *   [M + 128, M + 256) key per-token scale s-hat, FP8 E4M3, token t at byte t
+ *   [M + 256, M + 512) key per-token zero-point z-hat, fp16, token t at bytes 2t, 2t+1
+ *   [M + 512, M + 1024) the same three arrays for the values
  * A dequantised rotated element is c-hat_j * (s-hat_t * code_tj + z-hat_t); the original
  * element is the rotated row times the 128-point orthonormal Sylvester Hadamard matrix.
  *
@@ -66,32 +71,36 @@ extern "C" {
 #define KVARN_API
 #endif
 
-#define KVARN_ABI_VERSION 2
+#define KVARN_ABI_VERSION 3
 #define KVARN_TILE_TOKENS 128
 #define KVARN_HEAD_DIM 128
-#define KVARN_TILE_BYTES 13312
+#define KVARN_TILE_BYTES 13312        /* record of the default preset (v_bits 2) */
+#define KVARN_TILE_BYTES_V4 17408     /* record with v_bits 4                    */
 #define KVARN_FP16_RECORD_BYTES 65536
 
 typedef enum {
   KVARN_OK = 0,
   KVARN_ERR_NULL_ARG = 1,    /* a required pointer is NULL                               */
   KVARN_ERR_BAD_SHAPE = 2,   /* a size or count is out of range, or a buffer misaligned  */
-  KVARN_ERR_UNSUPPORTED = 3, /* the config is not kvarn_k4v2_g128 with head_dim 128      */
+  KVARN_ERR_UNSUPPORTED = 3, /* the config is not one of the presets below                */
   KVARN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required               */
   KVARN_ERR_HIP = 5          /* the HIP runtime reported an error when launching         */
 } kvarn_status;
 
-/* The codec configuration. Only the preset kvarn_k4v2_g128 exists ([GR], "What KVarN changes
- * in vLLM's serving path" and "Frequently Asked Questions"): head_dim 128, block_tokens 128,
- * k_bits 4, v_bits 2. sinkhorn_iters is the fixed number of column+row normalisation rounds
- * of [GR] "The four-stage pipeline" stage 2, whose value the pages do not give: 4 by default,
- * 1..16 accepted. Prefill and decode must use the same config ([TSM] "Where the bill lands"). */
+/* The codec configuration. The pages ship one preset, kvarn_k4v2_g128 ([GR], "What KVarN
+ * changes in vLLM's serving path" and "Frequently Asked Questions"): head_dim 128,
+ * block_tokens 128, k_bits 4, v_bits 2 (the default). v_bits 4 selects a second preset,
+ * kvarn_k4v4_g128, not on the pages: the same four stages with 4-bit value codes on a grid of
+ * 16 levels ([GR] "The four-stage pipeline", stage 3, at another bit width) and a 17408-byte
+ * record. sinkhorn_iters is the fixed number of column+row normalisation rounds of [GR] "The
+ * four-stage pipeline" stage 2, whose value the pages do not give: 4 by default, 1..16
+ * accepted. Prefill and decode must use the same config ([TSM] "Where the bill lands"). */
 typedef struct {
   int32_t num_kv_heads;   /* >= 1                      */
   int32_t head_dim;       /* must be 128               */
   int32_t block_tokens;   /* must be 128               */
   int32_t k_bits;         /* must be 4                 */
-  int32_t v_bits;         /* must be 2                 */
+  int32_t v_bits;         /* 2 (default) or 4          */
   int32_t sinkhorn_iters; /* 1..16, default 4          */
   /* Optional sign flips before the rotation (a randomised-sign Hadamard; not part of the
    * pages' preset): channel j is negated before H when bit j % 32 of rotation_signs[j / 32]
@@ -103,8 +112,8 @@ typedef struct {
 /* Fills *cfg with the preset for num_kv_heads heads (sinkhorn_iters = 4, no sign flips). */
 KVARN_API void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads);
 
-/* Bytes of one tile record (one KV head of one block, keys and values): 13312, or 0 if the
- * config is invalid. */
+/* Bytes of one tile record (one KV head of one block, keys and values): 13312 (v_bits 2) or
+ * 17408 (v_bits 4), or 0 if the config is invalid. */
 KVARN_API size_t kvarn_tile_bytes(const kvarn_config* cfg);
 
 /* Bytes of one block: num_kv_heads * kvarn_tile_bytes, or 0 if the config is invalid. */

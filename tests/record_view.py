@@ -7,29 +7,36 @@ only decodes the documented byte layout so that records can be compared field by
 import numpy as np
 
 T = D = 128
-K_META, V_META = 12288, 12800
+SIZES = {13312: 2, 17408: 4}          # record bytes -> value bits
 
 
-def _v_index():
+def _v_index(vbits):
     t, j = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
     nb, n = j // 16, j % 16
     kb, h, s, i = t // 32, (t // 16) % 2, (t // 4) % 4, t % 4
-    word = 256 * kb + 4 * (16 * s + n) + 2 * h + i // 2
-    bit = 2 * nb + 16 * (i % 2)
+    if vbits == 2:
+        word = 256 * kb + 4 * (16 * s + n) + 2 * h + i // 2
+        bit = 2 * nb + 16 * (i % 2)
+    else:
+        word = 512 * kb + 256 * (nb // 4) + 4 * (16 * s + n) + 2 * h + i // 2
+        bit = 4 * (nb % 4) + 16 * (i % 2)
     return word, bit
 
 
-_VW, _VB = _v_index()
+_VIDX = {vb: _v_index(vb) for vb in (2, 4)}
 
 
 def parse(rec: np.ndarray) -> dict:
     rec = np.asarray(rec, np.uint8)
+    vbits = SIZES[rec.shape[0]]
+    k_meta = 8192 + 2048 * vbits
     kb = rec[:8192].reshape(T, 64).astype(np.int64)
     kc = np.stack([kb & 15, kb >> 4], axis=-1).reshape(T, D)
-    words = rec[8192:12288].view("<u4").astype(np.int64)
-    vc = (words[_VW] >> _VB) & 3
-    out = dict(k_codes=kc, v_codes=vc)
-    for name, off in (("k", K_META), ("v", V_META)):
+    words = rec[8192:k_meta].view("<u4").astype(np.int64)
+    vw, vbit = _VIDX[vbits]
+    vc = (words[vw] >> vbit) & ((1 << vbits) - 1)
+    out = dict(k_codes=kc, v_codes=vc, v_bits=vbits)
+    for name, off in (("k", k_meta), ("v", k_meta + 512)):
         out[name + "_c"] = rec[off:off + 128].copy()
         out[name + "_s"] = rec[off + 128:off + 256].copy()
         out[name + "_z"] = rec[off + 256:off + 512].view("<u2").copy()

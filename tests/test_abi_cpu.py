@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvarn_abi_version() == 2
+    assert lib.kvarn_abi_version() == 3
 
 
 def test_sizes(lib):
@@ -45,6 +45,24 @@ def test_sizes(lib):
     bad = kv.default_config(8)
     bad.head_dim = 64
     assert kv.tile_bytes(bad) == 0 and kv.block_bytes(bad) == 0
+
+
+def test_value_bit_presets(lib):
+    c4 = kv.default_config(8, v_bits=4)
+    assert kv.tile_bytes(c4) == kv.TILE_BYTES_V4 == 17408
+    assert kv.block_bytes(c4) == 8 * 17408
+    for vb in (0, 1, 3, 8):
+        bad = kv.default_config(8)
+        bad.v_bits = vb
+        assert kv.tile_bytes(bad) == 0
+        assert lib.kvarn_quantize_tiles(ctypes.byref(bad), FAKE, FAKE, 1024, 1, FAKE, FAKE, 1,
+                                        None) == UNSUP
+    bad = kv.default_config(8, v_bits=4)
+    bad.k_bits = 2
+    assert kv.tile_bytes(bad) == 0
+    # the workspace does not depend on the preset
+    assert (kv.decode_workspace_bytes(c4, 16, 64, 128)
+            == kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 128))
 
 
 def test_workspace_bytes_depends_only_on_sizes(lib):
@@ -81,7 +99,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("field,value", [("head_dim", 64), ("block_tokens", 64), ("k_bits", 2),
-                                         ("v_bits", 4), ("sinkhorn_iters", 0),
+                                         ("v_bits", 3), ("v_bits", 8), ("sinkhorn_iters", 0),
                                          ("sinkhorn_iters", 17)])
 def test_unsupported_configs(lib, field, value):
     st = _call(lib, "kvarn_quantize_tiles", _cfg(**{field: value}), FAKE, FAKE, 256, 1, FAKE,
@@ -183,8 +201,9 @@ def test_dequantize_validation(lib):
 def test_fp16_path_validation(lib):
     cfg = kv.default_config(8)
     assert kv.fp16_block_bytes(cfg) == 8 * 65536
+    assert kv.fp16_block_bytes(kv.default_config(8, v_bits=4)) == 8 * 65536   # any preset
     bad = kv.default_config(8)
-    bad.v_bits = 4
+    bad.v_bits = 3
     assert kv.fp16_block_bytes(bad) == 0
     f = "kvarn_fp16_write_tiles"
     assert _call(lib, f, _cfg(), FAKE, FAKE, 256, 0, None, None, 0, None) == OK   # no-op
