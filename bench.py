@@ -53,6 +53,8 @@ def parse():
                    help="skip the comparison decode over an unquantised fp16 cache")
     p.add_argument("--no-multi-decode", action="store_true",
                    help="skip the several-token (Q = 4) decode measurement")
+    p.add_argument("--no-k4v4", action="store_true",
+                   help="skip the measurement of the 4-bit value preset")
     return p.parse_args()
 
 
@@ -171,6 +173,70 @@ def multi_decode_measure(args, kv, lib, cfg, sp, bt, bt_np, lens, lens_np, R, sm
             "frac_of_peak": round(bm / tm / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": bm,
             "query_tokens_per_s": round(sp.batch * n_query / tm, 1),
             "time_vs_one_token": round(tm / td, 3)}
+
+
+def k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch, dev):
+    """The 4-bit value preset (kvarn_k4v4_g128) on the same workload: quantise the same prefill
+    tiles into pools of 17,408-byte records, then the one-token decode over them with the main
+    run's queries, staging tiles and lengths. Each call is timed on its own after the main loop,
+    and the default preset is timed again in the same loops for the ratios."""
+    import ctypes
+    V = ctypes.c_void_p
+    cfg4 = kv.default_config(sp.hkv, v_bits=4)
+    rb = kv.tile_bytes(cfg4)
+    n_tiles = int(st["dst_blocks"].shape[0])
+    tile_heads = n_tiles * sp.hkv
+    dst = dev(st["dst_blocks"])
+    pools4 = [torch.zeros(st["num_blocks"], sp.hkv, rb, dtype=torch.uint8, device="cuda")
+              for _ in R]
+    ws_bytes = kv.decode_workspace_bytes(cfg4, sp.batch, sp.hq, bt_np.shape[1])
+    stream = torch.cuda.current_stream()
+
+    def calls(c, pools):
+        cp = ctypes.byref(c)
+        qc = [(cp, V(r["k"].data_ptr()), V(r["v"].data_ptr()), r["k"].stride(0), n_tiles,
+               V(dst.data_ptr()), V(p.data_ptr()), st["num_blocks"], V(stream.cuda_stream))
+              for r, p in zip(R, pools)]
+        dc = [(cp, V(r["q"].data_ptr()), sp.hq, V(p.data_ptr()), st["num_blocks"],
+               V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()), V(r["sk"].data_ptr()),
+               V(r["sv"].data_ptr()), ctypes.c_float(sm), V(r["out"].data_ptr()),
+               V(r["ws"].data_ptr()), max(ws_bytes, 256), sp.batch, V(stream.cuda_stream))
+              for r, p in zip(R, pools)]
+        return qc, dc
+
+    reps = len(R)
+    steps = max(10, args.steps // 4)
+
+    def timed(f, cl):
+        for i in range(max(reps, args.warmup // 4)):       # every pool is written first
+            assert f(*cl[i % reps]) == 0
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record(stream)
+            assert f(*cl[i % reps]) == 0
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e-3
+
+    res = {}
+    for key, c, pools in (("k4v2", cfg, [r["pool"] for r in R]), ("k4v4", cfg4, pools4)):
+        qc, dc = calls(c, pools)
+        res[key] = (timed(lib.kvarn_quantize_tiles, qc), timed(lib.kvarn_decode_attention, dc))
+    qb = tile_heads * (2 * T * D * 2 + rb)
+    db = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True, tile_bytes=rb)
+    (t2q, t2d), (t4q, t4d) = res["k4v2"], res["k4v4"]
+    print(f"# k4v4: quantise {t4q * 1e6:.1f} us (k4v2 {t2q * 1e6:.1f}), decode "
+          f"{t4d * 1e6:.1f} us (k4v2 {t2d * 1e6:.1f})", file=sys.stderr, flush=True)
+    return {"v_bits": 4, "record_bytes": rb,
+            "quantise": {"us": round(t4q * 1e6, 2), "tiles_per_s": round(tile_heads / t4q, 1),
+                         "gbps": round(qb / t4q / 1e9, 1),
+                         "frac_of_peak": round(qb / t4q / 1e9 / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes": qb, "k4v2_us_same_loop": round(t2q * 1e6, 2)},
+            "decode_attn": {"us": round(t4d * 1e6, 2), "gbps": round(db / t4d / 1e9, 1),
+                            "frac_of_peak": round(db / t4d / 1e9 / HBM_PEAK_GBPS, 4),
+                            "algorithmic_bytes": db, "k4v2_us_same_loop": round(t2d * 1e6, 2)}}
 
 
 def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
@@ -347,6 +413,11 @@ def main():
         multi = multi_decode_measure(args, kv, lib, cfg, sp, bt, bt_np, lens, lens_np, R, sm, td,
                                      torch, np, dev)
 
+    k4v4 = None
+    if not args.no_k4v4:
+        k4v4 = k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch,
+                            dev)
+
     decode_gbps = d_bytes / td / 1e9
     quant_gbps = q_bytes / tq / 1e9
     timings = {"quantise": tq, "append": ta, "decode": td}
@@ -362,9 +433,9 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel)",
-                           "append": "kvarn_append_token (append_token_kernel)",
-                           "decode": "kvarn_decode_attention (decode_tiles_kernel<false> + "
+                "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel<2>)",
+                           "append": "kvarn_append_token (append_token_kernel<2>)",
+                           "decode": "kvarn_decode_attention (decode_tiles_kernel<false, 2> + "
                                      "decode_merge_kernel<true, false>)"}[dominant],
                 "algorithmic_bytes_per_launch": {"quantise": q_bytes, "append": a_bytes,
                                                  "decode": d_bytes}[dominant],
@@ -393,6 +464,7 @@ def main():
         "append": {"us": round(ta * 1e6, 2), "algorithmic_bytes": a_bytes},
         "fp16_decode": fp16,
         "multi_decode": multi,
+        "preset_k4v4": k4v4,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),

@@ -198,12 +198,17 @@ template <bool kClamp, int kVBits>
 __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, float qmax,
                                             int is_v, int t, int q0, int q1, uint32_t* stage) {
   if (is_v && kVBits == 4) {
-    // 4-bit value codes, staged as the section itself. Channel 16 nb + n with nb = m + 4 q1,
-    // n = 8 q0 + e: half-word i % 2 of section word 512 kb + 256 q1 + 4 (16 s + n) + 2 h +
-    // i / 2 holds the codes of nb % 4 = m = 0..3 at bits 4 m (t = 32 kb + 16 h + 4 s + i).
+    // 4-bit value codes. Channel 16 nb + n with nb = m + 4 q1, n = 8 q0 + e: half-word i % 2 of
+    // section word 512 kb + 256 q1 + 4 (16 s + n) + 2 h + i / 2 holds the codes of
+    // nb % 4 = m = 0..3 at bits 4 m (t = 32 kb + 16 h + 4 s + i). The section is staged in
+    // 16-byte chunks (chunk = word / 4 = 128 kb + 64 q1 + 16 s + 8 q0 + e) with the chunk's low
+    // three bits XORed with s + 4 q1, so one instruction's 64 half-word writes spread over
+    // 32 banks instead of 8; the store undoes the swizzle.
     uint16_t* sh = reinterpret_cast<uint16_t*>(stage);
     const int kb = t >> 5, h = (t >> 4) & 1, s4 = (t >> 2) & 3, i = t & 3;
-    const int w0 = 512 * kb + 256 * q1 + 4 * (16 * s4 + 8 * q0) + 2 * h + (i >> 1);
+    const int sw = s4 + 4 * q1;
+    const int c0 = 128 * kb + 64 * q1 + 16 * s4 + 8 * q0;
+    const int lo = 2 * (2 * h + (i >> 1)) + (i & 1);        // half-word within the chunk
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint32_t ev = 0, od = 0;                    // fields m = 0, 2 and m = 1, 3 in bytes 0, 1
@@ -211,7 +216,7 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
       ev = put_code<kClamp>(fmaf(x[16 + e], ca, cb), qmax, 1, ev);
       od = put_code<kClamp>(fmaf(x[8 + e], ca, cb), qmax, 0, od);
       od = put_code<kClamp>(fmaf(x[24 + e], ca, cb), qmax, 1, od);
-      sh[2 * (w0 + 4 * e) + (i & 1)] = (uint16_t)(ev | (od << 4));
+      sh[8 * (c0 + (e ^ sw)) + lo] = (uint16_t)(ev | (od << 4));
     }
   } else if (!is_v) {
     // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
@@ -483,10 +488,14 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     stage_codes<true, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
   else
     stage_codes<false, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
-  if (!is_v || kVBits == 4) {                          // staged as the section: 8,192 bytes
+  if (!is_v) {                                         // staged as the section: 8,192 bytes
     __syncthreads();
-    reinterpret_cast<uint4*>(rec + (is_v ? kVCodesOff : kKCodesOff))[tid] =
-        reinterpret_cast<const uint4*>(stage)[tid];
+    reinterpret_cast<uint4*>(rec + kKCodesOff)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+  } else if (kVBits == 4) {                            // chunk tid sits at tid ^ (s + 4 q1)
+    __syncthreads();
+    const int sw = ((tid >> 4) & 3) + 4 * ((tid >> 6) & 1);
+    reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] =
+        reinterpret_cast<const uint4*>(stage)[tid ^ sw];
   } else {
     __syncthreads();
     if (tid < 256) {
