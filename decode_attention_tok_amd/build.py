@@ -30,7 +30,32 @@ def build(verbose: bool = False) -> str:
     if verbose:
         sys.stderr.write(res.stderr)
     os.replace(LIB + ".tmp", LIB)
+    build_c_client()
     return LIB
+
+
+C_CLIENT_SRC = os.path.join(HERE, "..", "tests", "c", "kvarn_c_client.c")
+C_CLIENT = os.path.join(HERE, "..", "tests", "c", "kvarn_c_client")          # host checks only
+C_CLIENT_GPU = os.path.join(HERE, "..", "tests", "c", "kvarn_c_client_gpu")  # + HIP runtime
+
+
+def build_c_client() -> None:
+    """The plain C99 test client of the C ABI (gcc), once without and once with the HIP
+    runtime's C API; both link libkvarn.so from this directory."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    inc = os.path.join(HERE, "..", "include")
+    common = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-I", inc, C_CLIENT_SRC,
+              "-L", HERE, "-lkvarn", "-Wl,-rpath," + HERE]
+    for out, extra in ((C_CLIENT, ["-pedantic"]),
+                       (C_CLIENT_GPU, ["-DKVARN_C_CLIENT_GPU", "-D__HIP_PLATFORM_AMD__", "-I",
+                                       os.path.join(rocm, "include"), "-L",
+                                       os.path.join(rocm, "lib"), "-lamdhip64",
+                                       "-Wl,-rpath," + os.path.join(rocm, "lib")])):
+        res = subprocess.run(common[:1] + extra[:1] + common[1:] + extra[1:] + ["-o", out],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("gcc failed building " + os.path.basename(out))
 
 
 if __name__ == "__main__":

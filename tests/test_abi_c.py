@@ -1,0 +1,97 @@
+"""The C ABI from a plain C99 program (tests/c/kvarn_c_client.c, built by build()): the header
+compiles as C, the library links, host-side validation answers as documented; on a GPU the
+same program quantises a small prefill and decodes one step through nothing but the C ABI and
+the HIP runtime's C API, and its records and outputs are checked against the oracle."""
+
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from decode_attention_tok_amd import build as kbuild
+
+T = D = 128
+
+
+def _client(path):
+    if not os.path.exists(path):
+        pytest.skip("C client not built (run build())")
+    return path
+
+
+def test_c_client_host_checks():
+    out = subprocess.run([_client(kbuild.C_CLIENT)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    assert "ok" in out.stdout
+
+
+def _write_input(path, st, sp, q, sk, sv, lens, sm, v_bits):
+    hdr = np.array([0x4B56524E, v_bits, len(st["dst_blocks"]), sp.hkv, sp.hq, sp.batch,
+                    st["block_table"].shape[1], st["num_blocks"]], np.int32)
+    with open(path, "wb") as f:
+        for a in (hdr, st["k"].astype(np.float16), st["v"].astype(np.float16),
+                  st["dst_blocks"].astype(np.int32), st["block_table"].astype(np.int32),
+                  lens.astype(np.int32), q.astype(np.float16), sk, sv,
+                  np.array([sm], np.float32)):
+            f.write(np.ascontiguousarray(a).tobytes())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("v_bits", [2, 4])
+def test_c_client_gpu_round_trip(tmp_path, v_bits):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oracle import attention as oatt
+    from oracle import codec
+    from workloads import gen
+    from record_view import Budget, compare_half, parse
+
+    client = _client(kbuild.C_CLIENT_GPU)
+    sp = gen.spec("qwen3-4b", batch=2, ctx=384, hkv=2, hq=8)
+    st = gen.prefill(sp, max_new_tokens=T)
+    lens = st["seq_lens"].astype(np.int32)
+    rng = np.random.default_rng(3)
+    sk = np.zeros((sp.batch, sp.hkv, T, D), np.float16)
+    sv = np.zeros_like(sk)
+    for b, tail in enumerate([0, 40]):
+        sk[b, :, :tail] = rng.standard_normal((sp.hkv, tail, D)).astype(np.float16)
+        sv[b, :, :tail] = rng.standard_normal((sp.hkv, tail, D)).astype(np.float16)
+        lens[b] += tail
+    q = gen.query(sp, dense=True)
+    sm = 1 / math.sqrt(D)
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    _write_input(fin, st, sp, q, sk, sv, lens, sm, v_bits)
+    print(f"C client on the GPU: v_bits={v_bits}", flush=True)
+    res = subprocess.run([client, "run", str(fin), str(fout)], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    raw = np.fromfile(fout, np.uint8)
+    n_out = sp.batch * sp.hq * D * 4
+    got = raw[:n_out].view(np.float32).reshape(sp.batch, sp.hq, D)
+    rb = codec.tile_bytes(v_bits)
+    pool_g = raw[n_out:].reshape(st["num_blocks"], sp.hkv, rb)
+    # the records the C program had the library write, against the oracle's quantisation
+    budget = Budget()
+    for i, blk in enumerate(st["dst_blocks"]):
+        for h in range(sp.hkv):
+            rows = slice(T * i, T * i + T)
+            rec = parse(pool_g[blk, h])
+            compare_half(rec, codec.quantize_tile(st["k"][rows, h].astype(np.float64), 4), "k",
+                         4, budget)
+            compare_half(rec, codec.quantize_tile(st["v"][rows, h].astype(np.float64), v_bits),
+                         "v", v_bits, budget)
+    budget.check(flip_rate=1e-3)
+    # its decode output against the oracle's attention over the oracle's own records of the
+    # same tiles: rounding-boundary flips may move outputs by a fraction of the quantisation
+    # error (the strict decode bar is checked elsewhere on oracle-written records)
+    pool_o = np.zeros((st["num_blocks"], sp.hkv, rb), np.uint8)
+    oatt.quantize_tiles(st["k"], st["v"], st["dst_blocks"], pool_o)
+    ref = oatt.decode_attention(q, pool_o, st["block_table"], lens, sk, sv, sm)
+    err = float(np.abs(got - ref).max())
+    scale = float(np.abs(ref).max())
+    print(f"C client v_bits={v_bits}: {vars(budget)}; decode max abs err {err:.3g} "
+          f"(|o| max {scale:.3g})", flush=True)
+    assert np.isfinite(got).all() and err <= 0.02 * scale
