@@ -125,3 +125,26 @@ def test_multi_full_size_sampled():
     _say(f"multi full-size Q={nq}: max abs err {err:.3g}")
     assert err <= TOL
     assert np.isfinite(got).all()
+
+
+def test_multi_at_the_split_limit():
+    """Sixteen query tokens of eight heads (128 rows per KV head) on one long sequence whose
+    split plan reaches 64 splits, with the last tokens straddling the staging tile."""
+    sp = gen.spec("qwen3-32b-16k", batch=1, ctx=64000, hkv=1, hq=8)
+    st = gen.prefill(sp, max_new_tokens=1200)
+    pool = np.zeros((st["num_blocks"], 1, codec.TILE_BYTES), np.uint8)
+    oatt.quantize_tiles(st["k"], st["v"], st["dst_blocks"], pool)
+    rng = np.random.default_rng(13)
+    sk = np.zeros((1, 1, T, D), np.float16)
+    sv = np.zeros_like(sk)
+    sk[0, 0, :9] = rng.standard_normal((9, D)).astype(np.float16)
+    sv[0, 0, :9] = rng.standard_normal((9, D)).astype(np.float16)
+    lens = st["seq_lens"].astype(np.int32) + 9               # 9 < 16 query tokens
+    q = gen.query_tokens(sp, 16)
+    cfg = kv.default_config(sp.hkv)
+    assert kv.decode_multi_workspace_bytes(cfg, 1, sp.hq, 16, 510) == 16 * sp.hq * 64 * 130 * 4
+    got = gpu_multi(cfg, q, pool, st["block_table"], lens, sk, sv, 1 / math.sqrt(D))
+    ref = oatt.decode_attention_multi(q, pool, st["block_table"], lens, sk, sv, 1 / math.sqrt(D))
+    err = np.abs(got - ref).max()
+    _say(f"multi at 64 splits, Q=16: max abs err {err:.3g}")
+    assert err <= TOL
