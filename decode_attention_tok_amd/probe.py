@@ -19,7 +19,9 @@ feeds the next ([TSM] "Why 2-bit usually breaks"). Without a model, two measurem
 
 Everything on the cache runs through the library's C ABI; torch holds device memory and
 computes the reference trajectory's exact attention and the feedback maps (both outside the
-path). Usage: python -m decode_attention_tok_amd.probe [--steps N] [--out FILE]
+path). Both measurements run for each value width asked for (2: kvarn_k4v2_g128, 4:
+kvarn_k4v4_g128). Usage: python -m decode_attention_tok_amd.probe [--steps N] [--v-bits 2,4]
+[--out FILE]
 """
 
 import argparse
@@ -49,7 +51,7 @@ def summarise(rel):
             "top5_share": top_share(rel)}
 
 
-def per_token_errors(name="qwen3-4b", iters=(1, 4, 8), **over):
+def per_token_errors(name="qwen3-4b", iters=(1, 4, 8), v_bits=2, **over):
     """Relative squared dequantisation error of every token row of a workload's tiles."""
     import torch
     import decode_attention_tok_amd as kv
@@ -62,9 +64,9 @@ def per_token_errors(name="qwen3-4b", iters=(1, 4, 8), **over):
     n = dst.numel()
     out = {}
     for it in iters:
-        cfg = kv.default_config(sp.hkv)
-        cfg.sinkhorn_iters = it
-        pool = torch.zeros(st["num_blocks"], sp.hkv, 13312, dtype=torch.uint8, device="cuda")
+        cfg = kv.default_config(sp.hkv, sinkhorn_iters=it, v_bits=v_bits)
+        pool = torch.zeros(st["num_blocks"], sp.hkv, kv.tile_bytes(cfg), dtype=torch.uint8,
+                           device="cuda")
         kv.quantize_tiles(cfg, k.view(n * T, -1), v.view(n * T, -1), dst, pool)
         ko = torch.empty(n * T, sp.hkv, D, dtype=torch.float32, device="cuda")
         vo = torch.empty_like(ko)
@@ -78,7 +80,7 @@ def per_token_errors(name="qwen3-4b", iters=(1, 4, 8), **over):
     return out
 
 
-def autoregressive(name="qwen3-4b", steps=512, alpha=0.5, **over):
+def autoregressive(name="qwen3-4b", steps=512, alpha=0.5, v_bits=2, **over):
     """The synthetic autoregressive loop (see the module notes); returns per-step series and
     the dequantisation-error summary of the tiles completed during the loop."""
     import torch
@@ -86,7 +88,7 @@ def autoregressive(name="qwen3-4b", steps=512, alpha=0.5, **over):
     from workloads import gen
     sp = gen.spec(name, **over)
     st = gen.prefill(sp, max_new_tokens=steps)
-    cfg = kv.default_config(sp.hkv)
+    cfg = kv.default_config(sp.hkv, v_bits=v_bits)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     B, G, Hkv = sp.batch, sp.group, sp.hkv
     ctx = int(st["seq_lens"][0])
@@ -105,7 +107,8 @@ def autoregressive(name="qwen3-4b", steps=512, alpha=0.5, **over):
     bt = dev(st["block_table"])
 
     def packed_cache():
-        pool = torch.zeros(st["num_blocks"], Hkv, 13312, dtype=torch.uint8, device="cuda")
+        pool = torch.zeros(st["num_blocks"], Hkv, kv.tile_bytes(cfg), dtype=torch.uint8,
+                           device="cuda")
         if n:
             kv.quantize_tiles(cfg, kpre.view(n * T, -1), vpre.view(n * T, -1),
                               dev(st["dst_blocks"]), pool)
@@ -185,7 +188,7 @@ def autoregressive(name="qwen3-4b", steps=512, alpha=0.5, **over):
             tiles[half] = summarise(r.cpu().numpy())
     marks = [t for t in (0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048) if t < steps]
     return {"workload": name, "batch": B, "kv_heads": Hkv, "q_heads": sp.hq, "prefill": ctx,
-            "steps": steps, "alpha": alpha,
+            "steps": steps, "alpha": alpha, "v_bits": v_bits,
             "one_step_rel_err": {"mean": float(np.mean(one_step)),
                                  "p95": float(np.percentile(one_step, 95)),
                                  "max": float(np.max(one_step))},
@@ -200,11 +203,15 @@ def main():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--ctx", type=int, default=1024)
     ap.add_argument("--alpha", type=float, default=0.5)
+    ap.add_argument("--v-bits", default="2", help="comma-separated value widths, e.g. 2,4")
     ap.add_argument("--out", default="")
     a = ap.parse_args()
-    res = {"per_token_dequant_error": per_token_errors("qwen3-4b", batch=2, ctx=1024),
-           "autoregressive": autoregressive("qwen3-4b", steps=a.steps, alpha=a.alpha,
-                                            batch=a.batch, ctx=a.ctx)}
+    res = {}
+    for vb in (int(x) for x in a.v_bits.split(",")):
+        res[f"v_bits={vb}"] = {
+            "per_token_dequant_error": per_token_errors("qwen3-4b", v_bits=vb, batch=2, ctx=1024),
+            "autoregressive": autoregressive("qwen3-4b", steps=a.steps, alpha=a.alpha, v_bits=vb,
+                                             batch=a.batch, ctx=a.ctx)}
     text = json.dumps(res, indent=1)
     print(text)
     if a.out:
