@@ -261,13 +261,32 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const int32_t* __restrict__ seq_lens, float sm_scale,
                     float* __restrict__ partials, uint4 signs) {
   __shared__ TileSmem sm;
-  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int nsplit = gridDim.x;
   // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
   // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
   const int group = hq / hkv, vgroup = group * nq;
   const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
-  const int g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups;
-  const int b = blockIdx.z;
+  int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
+  if (ngroups > 1) {
+    // workgroups that read the same tiles (same split, KV head, sequence; different head
+    // groups) take dispatch ids 8 apart, so they run on the same XCD and share its L2
+    const int L = blockIdx.x + nsplit * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int P = nsplit * hkv * gridDim.z;
+    const int full = P & ~7;
+    int p;
+    if (L < full * ngroups) {
+      const int r = L % (8 * ngroups);
+      hg = r >> 3;
+      p = (L / (8 * ngroups)) * 8 + (r & 7);
+    } else {
+      const int rem = P - full, r = L - full * ngroups;
+      hg = r / rem;
+      p = full + r % rem;
+    }
+    split = p % nsplit;
+    g = (p / nsplit) % hkv;
+    b = p / (nsplit * hkv);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vbase = hg * kHeadGroup;
   const int nh = min(kHeadGroup, vgroup - vbase);             // rows served (1..8)
