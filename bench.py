@@ -55,6 +55,8 @@ def parse():
                    help="skip the several-token (Q = 4) decode measurement")
     p.add_argument("--no-k4v4", action="store_true",
                    help="skip the measurement of the 4-bit value preset")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the copy-bandwidth, layer-stream and write-stream measurements")
     return p.parse_args()
 
 
@@ -239,6 +241,145 @@ def k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, to
                             "algorithmic_bytes": db, "k4v2_us_same_loop": round(t2d * 1e6, 2)}}
 
 
+def hbm_copy_measure(torch, n_bytes=1 << 30, repeats=5):
+    """Achievable HBM bandwidth of a plain device-to-device copy (read + write bytes / time),
+    median of a few repeats: context for the roofline fractions, never their denominator."""
+    a = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[len(ts) // 2]
+    del a, b
+    return {"copy_bytes": n_bytes, "gbps": round(2 * n_bytes / t / 1e9, 1),
+            "frac_of_peak": round(2 * n_bytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def layer_stream_measure(kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch, dev,
+                         layers=36, repeats=5):
+    """Decode of one token through `layers` layers back to back: the same step's decode over
+    `layers` separate packed pools (one per layer, written by the quantiser from the same
+    prefill), launched one after another; per-layer time = stream time / layers (median of
+    repeats). The launch-amortised figure beside the per-launch one."""
+    import ctypes
+    V = ctypes.c_void_p
+    n_tiles = int(st["dst_blocks"].shape[0])
+    dst = dev(st["dst_blocks"])
+    r0 = R[0]
+    pools = []
+    for _ in range(layers):
+        p = torch.zeros(st["num_blocks"], sp.hkv, TILE, dtype=torch.uint8, device="cuda")
+        kv.quantize_tiles(cfg, r0["k"], r0["v"], dst, p)
+        pools.append(p)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    cp = ctypes.byref(cfg)
+    ws_bytes = kv.decode_workspace_bytes(cfg, sp.batch, sp.hq, bt_np.shape[1])
+    calls = [(cp, V(r0["q"].data_ptr()), sp.hq, V(p.data_ptr()), st["num_blocks"],
+              V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()), V(r0["sk"].data_ptr()),
+              V(r0["sv"].data_ptr()), ctypes.c_float(sm), V(r0["out"].data_ptr()),
+              V(r0["ws"].data_ptr()), max(ws_bytes, 256), sp.batch, V(stream.cuda_stream))
+             for p in pools]
+    f = lib.kvarn_decode_attention
+    for c in calls:
+        assert f(*c) == 0
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in calls:
+            assert f(*c) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[len(ts) // 2] / layers
+    db = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True)
+    del pools
+    print(f"# {layers}-layer decode stream: {t * 1e6:.1f} us per layer", file=sys.stderr,
+          flush=True)
+    return {"layers": layers, "us_per_layer": round(t * 1e6, 2), "gbps": round(db / t / 1e9, 1),
+            "frac_of_peak": round(db / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def write_stream_measure(kv, lib, torch, np, dev, steps=None):
+    """The write-path stream workload: batch 64, 8 KV heads, 32 query heads, 1024-token
+    prefill; every step appends one key/value token per sequence into the fp16 staging tile
+    (kvarn_append_token, which quantises the tile when its 128th token arrives) and decodes
+    that token's query over the packed tiles plus staging (kvarn_decode_attention). Each step's
+    append and decode are timed with HIP events; steps whose append completes tiles are the
+    quantisation bursts."""
+    import ctypes
+    from workloads import gen
+    V = ctypes.c_void_p
+    sp = gen.spec("write-stream")
+    steps = steps or sp.steps
+    st = gen.prefill(sp, max_new_tokens=steps)
+    cfg = kv.default_config(sp.hkv)
+    n = len(st["dst_blocks"])
+    pool = torch.zeros(st["num_blocks"], sp.hkv, TILE, dtype=torch.uint8, device="cuda")
+    k0, v0 = dev(st["k"]), dev(st["v"])
+    kv.quantize_tiles(cfg, k0.view(n * T, -1), v0.view(n * T, -1), dev(st["dst_blocks"]), pool)
+    del k0, v0
+    sk = torch.zeros(sp.batch, sp.hkv, T, D, dtype=torch.float16, device="cuda")
+    sv = torch.zeros_like(sk)
+    toks = [gen.append_tokens(sp, i) for i in range(steps)]
+    kn = dev(np.stack([t[0] for t in toks]))
+    vn = dev(np.stack([t[1] for t in toks]))
+    lens0 = st["seq_lens"].astype(np.int32)
+    pos = dev(np.stack([lens0 + i for i in range(steps)]).astype(np.int32))
+    lens = dev(np.stack([lens0 + i + 1 for i in range(steps)]).astype(np.int32))
+    q = dev(gen.query(sp))
+    out = torch.empty(sp.batch, sp.hq, D, dtype=torch.float32, device="cuda")
+    bt_np = st["block_table"]
+    bt = dev(bt_np)
+    ws_bytes = kv.decode_workspace_bytes(cfg, sp.batch, sp.hq, bt_np.shape[1])
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    cp = ctypes.byref(cfg)
+    fa, fd = lib.kvarn_append_token, lib.kvarn_decode_attention
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        assert fa(cp, V(kn[i].data_ptr()), V(vn[i].data_ptr()), V(pos[i].data_ptr()),
+                  V(bt.data_ptr()), bt_np.shape[1], V(sk.data_ptr()), V(sv.data_ptr()),
+                  V(pool.data_ptr()), st["num_blocks"], sp.batch, V(stream.cuda_stream)) == 0
+        evs[i][1].record(stream)
+        assert fd(cp, V(q.data_ptr()), sp.hq, V(pool.data_ptr()), st["num_blocks"],
+                  V(bt.data_ptr()), bt_np.shape[1], V(lens[i].data_ptr()), V(sk.data_ptr()),
+                  V(sv.data_ptr()), ctypes.c_float(1.0 / math.sqrt(D)), V(out.data_ptr()),
+                  V(ws.data_ptr()), max(ws_bytes, 256), sp.batch, V(stream.cuda_stream)) == 0
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    ta = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    td = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    burst = np.array([int(lens0[0] + i) % T == T - 1 for i in range(steps)])
+    dbytes = sum(algorithmic_bytes(lens0 + i + 1, sp.hkv, sp.hq, True) for i in range(steps))
+    tile_heads_burst = sp.batch * sp.hkv
+    print(f"# write stream: {steps} steps, append {ta.mean() * 1e6:.1f} us "
+          f"(bursts {ta[burst].mean() * 1e6:.1f} us), decode {td.mean() * 1e6:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"workload": "write-stream", "batch": sp.batch, "kv_heads": sp.hkv, "q_heads": sp.hq,
+            "start_context": int(lens0[0]), "steps": steps,
+            "step_us_mean": round((ta + td).mean() * 1e6, 2),
+            "append_us_mean": round(ta[~burst].mean() * 1e6, 2),
+            "burst_steps": int(burst.sum()),
+            "burst_append_us_mean": round(ta[burst].mean() * 1e6, 2) if burst.any() else None,
+            "burst_tile_heads_per_s": (round(tile_heads_burst / ta[burst].mean(), 1)
+                                       if burst.any() else None),
+            "decode_us_mean": round(td.mean() * 1e6, 2),
+            "decode_gbps": round(dbytes / td.sum() / 1e9, 1),
+            "decode_frac_of_peak": round(dbytes / td.sum() / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
                  quant_budget_s=12.0, decode_budget_s=8.0):
     """The fp64 oracle, single-threaded, on a time-bounded sample of the same step: tile-head
@@ -418,6 +559,13 @@ def main():
         k4v4 = k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch,
                             dev)
 
+    hbm = layer_stream = wstream = None
+    if not args.no_extras:
+        hbm = hbm_copy_measure(torch)
+        layer_stream = layer_stream_measure(kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R,
+                                            sm, torch, dev)
+        wstream = write_stream_measure(kv, lib, torch, np, dev)
+
     decode_gbps = d_bytes / td / 1e9
     quant_gbps = q_bytes / tq / 1e9
     timings = {"quantise": tq, "append": ta, "decode": td}
@@ -465,6 +613,9 @@ def main():
         "fp16_decode": fp16,
         "multi_decode": multi,
         "preset_k4v4": k4v4,
+        "hbm_copy": hbm,
+        "decode_layer_stream": layer_stream,
+        "write_stream": wstream,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),

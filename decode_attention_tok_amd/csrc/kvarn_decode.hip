@@ -621,6 +621,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 constexpr int kMThreads = 64;
 constexpr int kMaxSplits = 64;
 constexpr int kMergePreload = 8;          // splits whose o~ is loaded before the weights exist
+constexpr int kStageChunk = 16;           // staging value rows loaded per round
 
 // <q, k> over 128 channels: k is one fp16 staging row, q the fp32 query in LDS.
 __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, const float* qs) {
@@ -735,12 +736,23 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   // raw staging output
   float r0 = 0.0f, r1 = 0.0f;
   const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
-  for (int t = 0; t < n_stage; ++t) {
-    const uint32_t w = t == 0 ? vpre0 : (t == 1 ? vpre1 : vcol[t * (kD / 2)]);
-    const int src = __float_as_int(t < 64 ? p0 : p1);
-    const float pt = __int_as_float(__builtin_amdgcn_readlane(src, t & 63));
-    r0 = fmaf(pt, fp16_bits_to_float(w & 0xFFFFu), r0);
-    r1 = fmaf(pt, fp16_bits_to_float(w >> 16), r1);
+  // 16 staging rows per round of loads (rows past n_stage are loaded, always inside the
+  // staging tile, but never used: they may hold anything)
+  for (int t0 = 0; t0 < n_stage; t0 += kStageChunk) {
+    uint32_t w[kStageChunk];
+#pragma unroll
+    for (int i = 0; i < kStageChunk; ++i)
+      w[i] = t0 + i == 0 ? vpre0 : (t0 + i == 1 ? vpre1 : vcol[(t0 + i) * (kD / 2)]);
+#pragma unroll
+    for (int i = 0; i < kStageChunk; ++i) {
+      const int t = t0 + i;
+      if (t < n_stage) {
+        const int src = __float_as_int(t < 64 ? p0 : p1);
+        const float pt = __int_as_float(__builtin_amdgcn_readlane(src, t & 63));
+        r0 = fmaf(pt, fp16_bits_to_float(w[i] & 0xFFFFu), r0);
+        r1 = fmaf(pt, fp16_bits_to_float(w[i] >> 16), r1);
+      }
+    }
   }
   float2 res = make_float2(0.0f, 0.0f);
   if (invalid) {
