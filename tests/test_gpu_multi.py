@@ -47,6 +47,9 @@ def gpu_multi(cfg, q, pool, bt, lens, sk, sv, sm):
     ("qwen3-32b-16k", dict(batch=2, ctx=640, hkv=2, hq=16), [100, 9], 16),   # 16 x 8 rows
     ("qwen3-4b", dict(batch=2, ctx=256, hkv=1, hq=16), [17, 0], 3),          # group 16
     ("phi4-ragged", dict(batch=4, ragged=(128, 1024), hkv=2, hq=8), [0, 1, 2, 126], 5),
+    ("qwen3-4b", dict(batch=2, ctx=384, hkv=2, hq=6), [0, 33], 3),          # 9 rows: 8 + 1
+    ("qwen3-4b", dict(batch=2, ctx=256, hkv=2, hq=24), [90, 1], 2),         # 24 rows: 3 groups
+    ("qwen3-4b", dict(batch=1, ctx=128, hkv=5, hq=10), [127], 16),          # 32 rows, one tile
 ])
 def test_multi_matches_oracle(name, over, tails, nq):
     sp = gen.spec(name, **over)
