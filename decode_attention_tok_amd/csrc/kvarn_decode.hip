@@ -1125,6 +1125,11 @@ int decode_splits(int batch, int hkv, int max_blocks) {
   const long long per_wave = (max_blocks + kWaves - 1) / kWaves;
   const long long cap = per_wave / 2 > 0 ? per_wave / 2 : 1;
   if (s > cap) s = cap;
+  // and at most 32 full tiles per split for the longest table the batch may hold (the last
+  // entry covers the staging tile): in a ragged batch the longest sequences would otherwise
+  // set the kernel's time while the short ones' workgroups sit finished
+  const long long need = (max_blocks - 1 + 31) / 32;
+  if (s < need) s = need;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
