@@ -73,6 +73,20 @@ def test_workspace_bytes_depends_only_on_sizes(lib):
     assert kv.decode_workspace_bytes(cfg, 0, 64, 128) == 0
 
 
+def test_workspace_follows_the_split_plan(lib):
+    """The workspace holds 130 floats per (sequence, query head, split). Splits: about 512
+    workgroups, at least two tiles per wave, and at most 32 full tiles per split for the
+    longest table (its last entry is the staging tile)."""
+    per = 130 * 4
+    # 16K context, batch 16, 8 KV heads: 512 / 128 pairs = 4 splits of 32 tiles
+    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 4 * per
+    # 4K context, batch 8: 8 splits wanted, capped at two tiles per wave (33 entries) -> 4
+    assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 4 * per
+    # ragged batch up to 32K tokens, batch 32, 10 KV heads: 2 splits wanted, 256 full tiles
+    # need 8 splits of at most 32
+    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 8 * per
+
+
 def test_multi_workspace_and_query_token_limits(lib):
     cfg = kv.default_config(8)
     one = kv.decode_workspace_bytes(cfg, 16, 64, 128)
