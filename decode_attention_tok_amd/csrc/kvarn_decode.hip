@@ -647,9 +647,31 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out,
                     uint4 signs) {
   __shared__ float qs[kD];
-  const int qi = blockIdx.x / hq, h = blockIdx.x % hq, b = blockIdx.y;   // query token, head
+  // The group query heads of one (sequence, query token, KV head) read the same staging tile:
+  // they take dispatch ids 8 apart, so the round-robin dispatch runs them on one XCD and the
+  // second and later reads of the tile come from that XCD's L2.
+  const int group = hq / hkv;
+  int qi, h, b;
+  {
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int P = gridDim.y * nq * hkv;                  // (sequence, query token, KV head)
+    const int full = P & ~7;
+    int p, k;
+    if (L < full * group) {
+      const int r = L % (8 * group);
+      k = r >> 3;
+      p = (L / (8 * group)) * 8 + (r & 7);
+    } else {
+      const int rem = P - full, r = L - full * group;
+      k = r / rem;
+      p = full + r % rem;
+    }
+    h = (p % hkv) * group + k;
+    qi = (p / hkv) % nq;
+    b = p / (hkv * nq);
+  }
   const int lane = threadIdx.x;
-  const int group = hq / hkv, g = h / group;
+  const int g = h / group;
   const long long row = ((long long)b * nq + qi) * hq + h;              // row in [B][nq][hq]
   const float* pp = partials + row * nsplit * kPartialFloats;
   // independent loads: this lane's split (m, l), the first splits' o~ pairs, the query pair
