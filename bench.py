@@ -3,17 +3,20 @@
 One step = the whole path on one batch: quantise every full prefill tile of the batch into the
 paged block pool (kvarn_quantize_tiles), append one new key/value token per sequence into the
 fp16 staging tile (kvarn_append_token), and one decode-attention step over the packed tiles plus
-the staging token (kvarn_decode_attention). Default workload: the Qwen3-4B-like layer (8 KV
-heads, 32 query heads, batch 8, 4096-token context = 32 tiles per sequence, then token 4097).
+the staging token (kvarn_decode_attention). Default workload: the Phi-4-14B-like ragged batch
+(10 KV heads, 40 query heads, batch 32, contexts 1K-32K tokens, randomly permuted blocks), the
+largest configuration that fits one GPU.
 
 All inputs are resident in HBM before timing starts. Each step uses the next of several
 identical input/cache replicas so that the 256 MB last-level (Infinity) cache cannot serve a
-step from the previous one.
+step from the previous one. Host-side work that forks processes (drawing the inputs, timing the
+oracle on all host cores) runs before the GPU is first touched.
 
-Printed: one JSON line. value = whole-step effective HBM GB/s (algorithmic bytes of all three
-calls / step time). Also per call: decode-attention GB/s and fraction of the 8 TB/s peak,
-tiles quantised per second; the roofline of the dominant kernel (HIP events around each call
-on the launch stream); the fp64 oracle timed on a bounded sample on the host cores.
+Printed: one JSON line. value = decode-attention effective HBM GB/s (algorithmic bytes of the
+decode call / its time by HIP events on the launch stream); beside it tiles quantised per
+second, each call's fraction of the 8 TB/s peak, the roofline of the dominant kernel, the same
+figures for the Qwen3-32B-like 16K and Qwen3-4B-like workloads, and the fp64 oracle timed on a
+bounded sample on one host core and on all of them.
 """
 
 import argparse
@@ -31,21 +34,16 @@ HBM_PEAK_GBPS = 8000.0
 T = D = 128
 TILE = 13312
 
-WORKLOADS = {
-    # name: (spec name, spec overrides)
-    "qwen3-4b": ("qwen3-4b", {}),
-    "qwen3-32b-16k": ("qwen3-32b-16k", {}),
-    "phi4-ragged": ("phi4-ragged", {}),
-}
+WORKLOADS = ("phi4-ragged", "qwen3-32b-16k", "qwen3-4b")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="qwen3-4b", choices=sorted(WORKLOADS))
-    p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GB")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="phi4-ragged", choices=WORKLOADS)
+    p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1.2 GB")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
@@ -55,8 +53,11 @@ def parse():
                    help="skip the several-token (Q = 4) decode measurement")
     p.add_argument("--no-k4v4", action="store_true",
                    help="skip the measurement of the 4-bit value preset")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the quantise + decode figures of the other two workloads")
     p.add_argument("--no-extras", action="store_true",
-                   help="skip the copy-bandwidth, layer-stream and write-stream measurements")
+                   help="skip the bandwidth probes, warm-cache, rounds sweep, layer-stream and "
+                        "write-stream measurements")
     return p.parse_args()
 
 
@@ -380,92 +381,208 @@ def write_stream_measure(kv, lib, torch, np, dev, steps=None):
             "decode_frac_of_peak": round(dbytes / td.sum() / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def cpu_baseline(sp, st, q, lens, sm, tile_heads_total, pairs_total, step_bytes,
-                 quant_budget_s=12.0, decode_budget_s=8.0):
-    """The fp64 oracle, single-threaded, on a time-bounded sample of the same step: tile-head
-    quantisations in order until all are done or quant_budget_s has passed, then (sequence,
-    KV head) decodes over oracle-built caches until all are done or decode_budget_s has
-    passed; the per-item times are extrapolated to the whole step."""
+def read_probe_measure(torch, lib_path, n_bytes=4 << 30, repeats=5):
+    """Achievable read bandwidth: a streaming read-only kernel (libkvarn_probe.so) over a
+    4 GiB buffer at a few grid sizes, median of repeats at each, the best grid reported.
+    Context for the fractions of peak, never their denominator."""
+    import ctypes
+    if not os.path.exists(lib_path):
+        return None
+    plib = ctypes.CDLL(lib_path)
+    plib.kvarn_probe_read.restype = ctypes.c_int
+    plib.kvarn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_int,
+                                      ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(3)
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = None
+    for per_cu in (2, 4, 8, 16):
+        wg = cus * per_cu
+        call = (buf.data_ptr(), n_bytes, wg, 0x9E3779B9, out.data_ptr(), stream.cuda_stream)
+        assert plib.kvarn_probe_read(*call) == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert plib.kvarn_probe_read(*call) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(ts)[len(ts) // 2]
+        if best is None or t < best[0]:
+            best = (t, wg)
+    del buf
+    t, wg = best
+    print(f"# read probe {n_bytes / t / 1e9:.0f} GB/s ({wg} workgroups)", file=sys.stderr,
+          flush=True)
+    return {"read_bytes": n_bytes, "workgroups": wg, "gbps": round(n_bytes / t / 1e9, 1),
+            "frac_of_peak": round(n_bytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def warm_decode_measure(lib, calls, torch, steps=50):
+    """The decode of the main loop launched back to back on ONE replica: its pool may then be
+    served partly from the 256 MB last-level cache (context, not the metric)."""
+    stream = torch.cuda.current_stream()
+    cd = calls[0][2]
+    f = lib.kvarn_decode_attention
+    for _ in range(5):
+        assert f(*cd) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        assert f(*cd) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def quantise_rounds_measure(kv, lib, sp, st, R, torch, rounds=(1, 2, 4, 8), reps=8):
+    """The quantiser at several normalisation round counts (the config's sinkhorn_iters) on the
+    main workload's prefill: each round is one column step and one row step, so the time is
+    linear in the count and its slope is the cost of one round. A reproducible breakdown of
+    the write path: what the normalisation costs next to rotation, rounding and packing."""
+    import ctypes
     import numpy as np
+    V = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+    n_tiles = int(st["dst_blocks"].shape[0])
+    dst = torch.from_numpy(np.ascontiguousarray(st["dst_blocks"])).cuda()
+    out = {}
+    for it in rounds:
+        cfg = kv.default_config(sp.hkv, sinkhorn_iters=it)
+        cl = [(ctypes.byref(cfg), V(r["k"].data_ptr()), V(r["v"].data_ptr()), r["k"].stride(0),
+               n_tiles, V(dst.data_ptr()), V(r["pool"].data_ptr()), st["num_blocks"],
+               V(stream.cuda_stream)) for r in R]
+        for i in range(2):
+            assert lib.kvarn_quantize_tiles(*cl[i % len(cl)]) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            assert lib.kvarn_quantize_tiles(*cl[i % len(cl)]) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[it] = e0.elapsed_time(e1) * 1e-3 / reps
+    xs = np.array(rounds, float)
+    ys = np.array([out[r] for r in rounds])
+    slope, icpt = np.polyfit(xs, ys, 1)
+    t4 = out.get(4, float(icpt + 4 * slope))
+    print("# quantiser by rounds: " + ", ".join(f"{r}: {out[r] * 1e6:.0f} us" for r in rounds),
+          file=sys.stderr, flush=True)
+    return {"rounds": list(rounds), "us": [round(out[r] * 1e6, 2) for r in rounds],
+            "us_per_round": round(slope * 1e6, 2), "us_at_zero_rounds_fit": round(icpt * 1e6, 2),
+            "normalisation_share_at_4": round(4 * slope / t4, 4)}
+
+
+# ------------------------------------------------------------------ the oracle on the host
+
+
+def _oracle_worker_init():
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
+        pass
+
+
+def _oracle_pairs_job(args):
+    """Encode every tile of the given (sequence, KV head) pairs with the oracle, then decode
+    each pair's queries over those records; stop starting new pairs after `budget` seconds.
+    Returns (tiles encoded, encode seconds, tiles decoded, decode seconds)."""
+    import numpy as np
     from oracle import attention as oatt
     from oracle import codec
-    n_tiles = st["k"].shape[0] // T
-    t0 = time.perf_counter()
-    n_q = 0
-    while n_q < tile_heads_total and time.perf_counter() - t0 < quant_budget_s:
-        tile, head = n_q // sp.hkv, n_q % sp.hkv
-        rows = slice(T * tile, T * tile + T)
-        codec.encode_record(st["k"][rows, head], st["v"][rows, head])
-        n_q += 1
-    tq = (time.perf_counter() - t0) / n_q
-    first = np.concatenate([[0], np.cumsum(st["seq_lens"] // T)])   # first tile of each sequence
-    pool = np.zeros((st["num_blocks"], 1, TILE), np.uint8)
-    td_total, n_d = 0.0, 0
-    while n_d < pairs_total and td_total < decode_budget_s:
-        b, g = n_d // sp.hkv, n_d % sp.hkv
-        n = int(lens[b]) // T
+    pairs, budget = args
+    st, q, sm, group = _ORACLE_STATE
+    first = np.concatenate([[0], np.cumsum(st["seq_lens"] // T)])
+    n_enc = n_dec = 0
+    t_enc = t_dec = 0.0
+    start = time.perf_counter()
+    for b, g in pairs:
+        if time.perf_counter() - start > budget:
+            break
+        n = int(st["seq_lens"][b]) // T
+        if n == 0:
+            continue
+        pool = np.zeros((n, 1, TILE), np.uint8)          # this pair's records, blocks 0..n-1
+        t0 = time.perf_counter()
         for i in range(n):
             rows = slice(T * (first[b] + i), T * (first[b] + i) + T)
-            pool[st["block_table"][b, i], 0] = codec.encode_record(st["k"][rows, g],
-                                                                   st["v"][rows, g])
-        sk = np.zeros((1, 1, T, D), np.float16)
+            pool[i, 0] = codec.encode_record(st["k"][rows, g], st["v"][rows, g])
         t1 = time.perf_counter()
-        oatt.decode_attention(q[b:b + 1, g * sp.group:(g + 1) * sp.group], pool,
-                              st["block_table"][b:b + 1], lens[b:b + 1], sk, sk, sm)
-        td_total += time.perf_counter() - t1
-        n_d += 1
-    td = td_total / n_d
-    est = tq * tile_heads_total + td * pairs_total
-    if limiter is not None:
-        limiter.unregister()
-    return {"value": step_bytes / est / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_q} of {tile_heads_total} tile-head quantisations "
-                      f"({tq * 1e3:.2f} ms each) and {n_d} of {pairs_total} (sequence, KV head) "
-                      f"decodes ({td * 1e3:.1f} ms each) of this step on one host core, "
-                      f"extrapolated to the whole step ({est:.2f} s per step)"}
+        sk = np.zeros((1, 1, T, D), np.float16)         # one (zero) staging token, as in a step
+        lens = np.array([n * T + 1], np.int32)
+        oatt.decode_attention(q[b:b + 1, g * group:(g + 1) * group], pool,
+                              np.arange(n + 1, dtype=np.int32)[None], lens, sk, sk, sm)
+        t2 = time.perf_counter()
+        n_enc += n
+        n_dec += n
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+    return n_enc, t_enc, n_dec, t_dec
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is not built for "
-              "more than one GPU", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
+_ORACLE_STATE = None
 
-    import decode_attention_tok_amd as kv
+
+def cpu_baseline(sp, st, q, sm, d_bytes, tile_heads_total, workers, budget_s=12.0):
+    """The fp64 oracle on a time-bounded sample of the same step, on one host core and then on
+    `workers` cores at once (one process each, BLAS threads = 1): (sequence, KV head) pairs in
+    an order that walks the length mix, every tile of a pair encoded by the oracle and the
+    pair's query heads decoded over those records. Per-tile rates are extrapolated to the whole
+    step: decode GB/s (the metric's unit) and tile-heads quantised per second."""
+    global _ORACLE_STATE
+    import multiprocessing as mp
+    _ORACLE_STATE = (st, q, sm, sp.group)
+    order = [(b, g) for g in range(sp.hkv) for b in range(sp.batch)]
+    _oracle_worker_init()
+    e1, te1, d1, td1 = _oracle_pairs_job((order, budget_s))
+    single = {"value": round(d_bytes / (td1 / d1 * tile_heads_total) / 1e9, 5), "cores": 1,
+              "tiles_per_s": round(e1 / te1, 2), "tiles_encoded": e1, "tiles_decoded": d1}
+    res = None
+    if workers > 1:
+        shares = [order[w::workers] for w in range(workers)]
+        with mp.get_context("fork").Pool(workers, initializer=_oracle_worker_init) as pool:
+            res = pool.map(_oracle_pairs_job, [(sh, budget_s) for sh in shares])
+    if res:
+        enc_rate = sum(e / t for e, t, _, _ in res if t > 0)
+        dec_rate = sum(d / t for _, _, d, t in res if t > 0)
+        n_e = sum(r[0] for r in res)
+        value = d_bytes / (tile_heads_total / dec_rate) / 1e9
+        cores = workers
+    else:
+        enc_rate, dec_rate, n_e = e1 / te1, d1 / td1, e1
+        value, cores = single["value"], 1
+    return {"value": round(value, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "tiles_per_s": round(enc_rate, 2),
+            "sample": f"(sequence, KV head) pairs of this step, every tile of a pair encoded and "
+                      f"its query heads decoded over them: {n_e} tile-heads on {cores} cores at "
+                      f"once ({budget_s:.0f} s budget each), per-tile rates summed over the "
+                      f"cores and extrapolated to the step's {tile_heads_total} tile-heads",
+            "single_core": single}
+
+
+# ------------------------------------------------------------------ one workload on the GPU
+
+
+def setup_workload(kv, lib, sp, st, replicas, torch, np, dev):
+    """Device replicas of one workload's step (prefill tiles, pools, staging, queries, new
+    tokens, outputs, workspaces) and the three calls of each replica's step."""
+    import ctypes
     from workloads import gen
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    spec_name, over = WORKLOADS[args.workload]
-    sp = gen.spec(spec_name, **over)
-    st = gen.prefill(sp, max_new_tokens=1)
     q_np = gen.query(sp)
     k_new_np, v_new_np = gen.append_tokens(sp, 0)
     lens_pre = st["seq_lens"].astype(np.int32)
-    pos_np = lens_pre.copy()
-    lens_np = lens_pre + 1
     bt_np = st["block_table"]
     cfg = kv.default_config(sp.hkv)
     sm = 1.0 / math.sqrt(D)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
     n_tiles = int(st["dst_blocks"].shape[0])
-    tile_heads = n_tiles * sp.hkv
-    q_bytes = tile_heads * (2 * T * D * 2 + TILE)
-    a_bytes = sp.batch * sp.hkv * 4 * D * 2
-    d_bytes = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True)
-    step_bytes = q_bytes + a_bytes + d_bytes
-
     k0, v0 = dev(st["k"]), dev(st["v"])
     per_replica = k0.numel() * 4 + st["num_blocks"] * sp.hkv * TILE
-    reps = args.replicas or max(2, min(16, math.ceil(1.2e9 / per_replica)))
+    reps = replicas or max(2, min(16, math.ceil(1.2e9 / per_replica)))
     ws_bytes = kv.decode_workspace_bytes(cfg, sp.batch, sp.hq, bt_np.shape[1])
     R = []
     for _ in range(reps):
@@ -478,29 +595,43 @@ def main():
             out=torch.empty(sp.batch, sp.hq, D, dtype=torch.float32, device="cuda"),
             ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")))
     del k0, v0
-    dst = dev(st["dst_blocks"])
-    bt = dev(bt_np)
-    pos = dev(pos_np)
-    lens = dev(lens_np)
+    W = dict(sp=sp, st=st, cfg=cfg, sm=sm, q_np=q_np, lens_pre=lens_pre, bt_np=bt_np,
+             lens_np=lens_pre + 1, n_tiles=n_tiles, reps=reps, ws_bytes=ws_bytes, R=R,
+             dst=dev(st["dst_blocks"]), bt=dev(bt_np), pos=dev(lens_pre),
+             lens=dev(lens_pre + 1))
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    import ctypes
-    lib = kv.lib()
     cfgp = ctypes.byref(cfg)
-    V = ctypes.c_void_p
+    Vp = ctypes.c_void_p
     calls = []
     for r in R:
         calls.append((
-            (cfgp, V(r["k"].data_ptr()), V(r["v"].data_ptr()), r["k"].stride(0), n_tiles,
-             V(dst.data_ptr()), V(r["pool"].data_ptr()), st["num_blocks"], V(sptr)),
-            (cfgp, V(r["kn"].data_ptr()), V(r["vn"].data_ptr()), V(pos.data_ptr()),
-             V(bt.data_ptr()), bt_np.shape[1], V(r["sk"].data_ptr()), V(r["sv"].data_ptr()),
-             V(r["pool"].data_ptr()), st["num_blocks"], sp.batch, V(sptr)),
-            (cfgp, V(r["q"].data_ptr()), sp.hq, V(r["pool"].data_ptr()), st["num_blocks"],
-             V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()), V(r["sk"].data_ptr()),
-             V(r["sv"].data_ptr()), ctypes.c_float(sm), V(r["out"].data_ptr()),
-             V(r["ws"].data_ptr()), max(ws_bytes, 256), sp.batch, V(sptr))))
+            (cfgp, Vp(r["k"].data_ptr()), Vp(r["v"].data_ptr()), r["k"].stride(0), n_tiles,
+             Vp(W["dst"].data_ptr()), Vp(r["pool"].data_ptr()), st["num_blocks"], Vp(sptr)),
+            (cfgp, Vp(r["kn"].data_ptr()), Vp(r["vn"].data_ptr()), Vp(W["pos"].data_ptr()),
+             Vp(W["bt"].data_ptr()), bt_np.shape[1], Vp(r["sk"].data_ptr()),
+             Vp(r["sv"].data_ptr()), Vp(r["pool"].data_ptr()), st["num_blocks"], sp.batch,
+             Vp(sptr)),
+            (cfgp, Vp(r["q"].data_ptr()), sp.hq, Vp(r["pool"].data_ptr()), st["num_blocks"],
+             Vp(W["bt"].data_ptr()), bt_np.shape[1], Vp(W["lens"].data_ptr()),
+             Vp(r["sk"].data_ptr()), Vp(r["sv"].data_ptr()), ctypes.c_float(sm),
+             Vp(r["out"].data_ptr()), Vp(r["ws"].data_ptr()), max(ws_bytes, 256), sp.batch,
+             Vp(sptr))))
+    W["calls"] = calls
+    tile_heads = n_tiles * sp.hkv
+    W["tile_heads"] = tile_heads
+    W["q_bytes"] = tile_heads * (2 * T * D * 2 + TILE)
+    W["a_bytes"] = sp.batch * sp.hkv * 4 * D * 2
+    W["d_bytes"] = algorithmic_bytes(W["lens_np"], sp.hkv, sp.hq, True)
+    return W
+
+
+def time_steps(lib, W, steps, warmup, torch, label):
+    """Warm-up steps, then `steps` timed steps (quantise, append, decode on the next replica);
+    HIP events on the launch stream around each call, the wall clock around the whole loop."""
+    stream = torch.cuda.current_stream()
     fq, fa, fd = lib.kvarn_quantize_tiles, lib.kvarn_append_token, lib.kvarn_decode_attention
+    calls, reps = W["calls"], W["reps"]
 
     def step(i, ev=None):
         cq, ca, cd = calls[i % reps]
@@ -516,25 +647,89 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    print(f"# workload {args.workload}: {tile_heads} tile-heads, batch {sp.batch}, "
-          f"{reps} replicas, warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
-          flush=True)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for i in range(steps):
+        step(warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    tq = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
-    ta = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
-    td = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
-    ms = elapsed / args.steps * 1e3
-    print(f"# step {ms:.4f} ms: quantise {tq * 1e6:.1f} us, append {ta * 1e6:.1f} us, "
-          f"decode {td * 1e6:.1f} us", file=sys.stderr, flush=True)
+    tq = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
+    ta = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
+    td = sum(e[2].elapsed_time(e[3]) for e in evs) / steps * 1e-3
+    print(f"# {label}: step {elapsed / steps * 1e3:.4f} ms: quantise {tq * 1e6:.1f} us, append "
+          f"{ta * 1e6:.1f} us, decode {td * 1e6:.1f} us", file=sys.stderr, flush=True)
+    return dict(tq=tq, ta=ta, td=td, elapsed=elapsed, steps=steps)
+
+
+def summary(W, tm):
+    sp = W["sp"]
+    dg = W["d_bytes"] / tm["td"] / 1e9
+    qg = W["q_bytes"] / tm["tq"] / 1e9
+    return {"batch": sp.batch, "kv_heads": sp.hkv, "q_heads": sp.hq,
+            "context_max": int(W["lens_pre"].max()),
+            "decode_attn": {"gbps": round(dg, 1), "frac_of_peak": round(dg / HBM_PEAK_GBPS, 4),
+                            "us": round(tm["td"] * 1e6, 2), "algorithmic_bytes": W["d_bytes"]},
+            "quantise": {"tiles_per_s": round(W["tile_heads"] / tm["tq"], 1),
+                         "gbps": round(qg, 1), "frac_of_peak": round(qg / HBM_PEAK_GBPS, 4),
+                         "us": round(tm["tq"] * 1e6, 2), "algorithmic_bytes": W["q_bytes"],
+                         "tile_heads": W["tile_heads"]},
+            "append": {"us": round(tm["ta"] * 1e6, 2), "algorithmic_bytes": W["a_bytes"]},
+            "replicas": W["reps"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path is not built for "
+              "more than one GPU", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import decode_attention_tok_amd as kv
+    from decode_attention_tok_amd import build as kbuild
+    from workloads import gen
+
+    assert torch.cuda.device_count() >= 1, "bench.py needs a GPU"   # does not initialise it
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    # ---- host phase (forks processes; the GPU is not initialised yet)
+    sp = gen.spec(args.workload)
+    t0 = time.perf_counter()
+    st = gen.prefill(sp, max_new_tokens=1, workers=workers)
+    others = {}
+    if not args.no_other_workloads:
+        for name in WORKLOADS:
+            if name != args.workload:
+                osp = gen.spec(name)
+                others[name] = (osp, gen.prefill(osp, max_new_tokens=1, workers=workers))
+    print(f"# inputs drawn in {time.perf_counter() - t0:.1f} s on {workers} host cores",
+          file=sys.stderr, flush=True)
+    lens_np = st["seq_lens"].astype(np.int32) + 1
+    d_bytes = algorithmic_bytes(lens_np, sp.hkv, sp.hq, True)
+    tile_heads = int(st["dst_blocks"].shape[0]) * sp.hkv
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(sp, st, gen.query(sp), 1.0 / math.sqrt(D), d_bytes, tile_heads,
+                           workers)
+
+    # ---- GPU phase
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    lib = kv.lib()
+    W = setup_workload(kv, lib, sp, st, args.replicas, torch, np, dev)
+    print(f"# workload {args.workload}: {W['tile_heads']} tile-heads, batch {sp.batch}, "
+          f"{W['reps']} replicas, warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    tm = time_steps(lib, W, args.steps, args.warmup, torch, args.workload)
+    tq, ta, td = tm["tq"], tm["ta"], tm["td"]
+    ms = tm["elapsed"] / args.steps * 1e3
+    main_sum = summary(W, tm)
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
@@ -543,34 +738,46 @@ def main():
         torch.cuda.synchronize()
         b_.copy_(a)
         torch.cuda.synchronize()
+        del a, b_
 
-    fp16 = None
+    cfg, bt, bt_np, lens, R, sm = W["cfg"], W["bt"], W["bt_np"], W["lens"], W["R"], W["sm"]
+    fp16 = multi = k4v4 = None
     if not args.no_fp16_decode:
         fp16 = fp16_decode_comparison(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R,
-                                      sm, ws_bytes, td, torch, np, dev)
-
-    multi = None
+                                      sm, W["ws_bytes"], td, torch, np, dev)
     if not args.no_multi_decode:
         multi = multi_decode_measure(args, kv, lib, cfg, sp, bt, bt_np, lens, lens_np, R, sm, td,
                                      torch, np, dev)
-
-    k4v4 = None
     if not args.no_k4v4:
         k4v4 = k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch,
                             dev)
 
-    hbm = layer_stream = wstream = None
+    hbm = rprobe = warm = rounds = layer_stream = wstream = None
     if not args.no_extras:
         hbm = hbm_copy_measure(torch)
+        rprobe = read_probe_measure(torch, kbuild.PROBE_LIB)
+        tw = warm_decode_measure(lib, W["calls"], torch)
+        warm = {"us": round(tw * 1e6, 2), "gbps": round(d_bytes / tw / 1e9, 1),
+                "pool_bytes": st["num_blocks"] * sp.hkv * TILE}
+        rounds = quantise_rounds_measure(kv, lib, sp, st, R, torch)
         layer_stream = layer_stream_measure(kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R,
                                             sm, torch, dev)
         wstream = write_stream_measure(kv, lib, torch, np, dev)
+    del W, R
 
-    decode_gbps = d_bytes / td / 1e9
-    quant_gbps = q_bytes / tq / 1e9
+    other_res = {}
+    for name, (osp, ost) in others.items():
+        OW = setup_workload(kv, lib, osp, ost, 0, torch, np, dev)
+        otm = time_steps(lib, OW, max(10, args.steps // 2), max(2, args.warmup), torch, name)
+        other_res[name] = summary(OW, otm)
+        del OW
+        torch.cuda.empty_cache()
+
     timings = {"quantise": tq, "append": ta, "decode": td}
     dominant = max(timings, key=timings.get)
-    ach = {"quantise": quant_gbps, "append": a_bytes / ta / 1e9, "decode": decode_gbps}[dominant]
+    byts = {"quantise": main_sum["quantise"]["algorithmic_bytes"],
+            "append": main_sum["append"]["algorithmic_bytes"], "decode": d_bytes}
+    ach = byts[dominant] / timings[dominant] / 1e9
     # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by what those
     # counters read for a device copy of known size; null once the kernels have changed
     traffic = None
@@ -585,35 +792,29 @@ def main():
                            "append": "kvarn_append_token (append_token_kernel<2>)",
                            "decode": "kvarn_decode_attention (decode_tiles_kernel<false, 2> + "
                                      "decode_merge_kernel<true, false>)"}[dominant],
-                "algorithmic_bytes_per_launch": {"quantise": q_bytes, "append": a_bytes,
-                                                 "decode": d_bytes}[dominant],
+                "algorithmic_bytes_per_launch": byts[dominant],
                 "avg_launch_us": round(timings[dominant] * 1e6, 2)}
-    value = step_bytes / (elapsed / args.steps) / 1e9
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("# timing the oracle on a bounded sample", file=sys.stderr, flush=True)
-        pairs = sp.batch * sp.hkv
-        cpu = cpu_baseline(sp, st, q_np, lens_np, sm, tile_heads, pairs, step_bytes)
+    decode_gbps = d_bytes / td / 1e9
     line = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + tiles quantised/s, K4V2 g128",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "value": round(decode_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16-in/fp32-acc, u4/u2 codes",
         "data": "synthetic (seeded generators; no model weights)",
         "config": {"workload": args.workload, "batch": sp.batch, "kv_heads": sp.hkv,
-                   "q_heads": sp.hq, "context": int(lens_pre.max()),
-                   "tile_heads_quantised_per_step": tile_heads, "replicas": reps},
-        "decode_attn": {"gbps": round(decode_gbps, 1),
-                        "frac_of_peak": round(decode_gbps / HBM_PEAK_GBPS, 4),
-                        "us": round(td * 1e6, 2), "algorithmic_bytes": d_bytes},
-        "quantise": {"tiles_per_s": round(tile_heads / tq, 1), "gbps": round(quant_gbps, 1),
-                     "frac_of_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                     "us": round(tq * 1e6, 2), "algorithmic_bytes": q_bytes},
-        "append": {"us": round(ta * 1e6, 2), "algorithmic_bytes": a_bytes},
+                   "q_heads": sp.hq, "context_max": int(W_lens_max(st)),
+                   "tile_heads_quantised_per_step": tile_heads, "replicas": main_sum["replicas"]},
+        "decode_attn": main_sum["decode_attn"],
+        "quantise": main_sum["quantise"],
+        "append": main_sum["append"],
+        "workloads": other_res or None,
         "fp16_decode": fp16,
         "multi_decode": multi,
         "preset_k4v4": k4v4,
         "hbm_copy": hbm,
+        "hbm_read_probe": rprobe,
+        "decode_warm": warm,
+        "quantise_rounds": rounds,
         "decode_layer_stream": layer_stream,
         "write_stream": wstream,
         "roofline": roofline,
@@ -621,6 +822,10 @@ def main():
         "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)
+
+
+def W_lens_max(st):
+    return max(int(x) for x in st["seq_lens"])
 
 
 if __name__ == "__main__":

@@ -60,7 +60,7 @@ kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const 
   if (k == nullptr || v == nullptr || dst_blocks == nullptr || block_pool == nullptr)
     return KVARN_ERR_NULL_ARG;
   if (token_stride < (int64_t)cfg->num_kv_heads * KVARN_HEAD_DIM || token_stride % 8 != 0 ||
-      !aligned16(k) || !aligned16(v))
+      !aligned16(k) || !aligned16(v) || !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (2LL * cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_quantize_tiles(
@@ -81,7 +81,8 @@ kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, cons
   if (k_new == nullptr || v_new == nullptr || positions == nullptr || block_table == nullptr ||
       staging_k == nullptr || staging_v == nullptr || block_pool == nullptr)
     return KVARN_ERR_NULL_ARG;
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(staging_k) || !aligned16(staging_v))
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(staging_k) || !aligned16(staging_v) ||
+      !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (2LL * cfg->num_kv_heads * batch > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_append_token(
@@ -127,7 +128,8 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
     return KVARN_ERR_NULL_ARG;
   if (workspace == nullptr || workspace_bytes < need) return KVARN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KVARN_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(staging_k) || !aligned16(staging_v) || !aligned16(out))
+  if (!aligned16(q) || !aligned16(staging_k) || !aligned16(staging_v) || !aligned16(out) ||
+      !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
   const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
@@ -188,7 +190,7 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_p
   if (n_tiles == 0) return KVARN_OK;
   if (block_pool == nullptr || src_blocks == nullptr || k_out == nullptr || v_out == nullptr)
     return KVARN_ERR_NULL_ARG;
-  if (!aligned16(k_out) || !aligned16(v_out)) return KVARN_ERR_BAD_SHAPE;
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(block_pool)) return KVARN_ERR_BAD_SHAPE;
   if (2LL * cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_dequantize_tiles(static_cast<const uint8_t*>(block_pool),
                                                  num_blocks, src_blocks, n_tiles,

@@ -42,6 +42,8 @@
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
 
+#include <atomic>
+
 namespace kvarn {
 
 namespace {
@@ -1138,15 +1140,40 @@ hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
   return hipGetLastError();
 }
 
+// Compute units of the current device, read once per device and cached. A host without a
+// usable device (argument checks only; nothing is launched there) plans for 256, the MI355X count.
+int device_compute_units() {
+  constexpr int kDefaultCUs = 256, kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();                    // leave no error behind for a later launch
+    return kDefaultCUs;
+  }
+  const int cached = cache[dev].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = kDefaultCUs;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 int decode_splits(int batch, int hkv, int max_blocks) {
-  const long long pairs = (long long)batch * hkv;
-  // about 512 workgroups (2048 waves: one round at 2 waves per SIMD on 256 CUs)
-  long long s = (512 + pairs - 1) / (pairs > 0 ? pairs : 1);
+  const long long pairs = (long long)batch * hkv > 0 ? (long long)batch * hkv : 1;
+  // two workgroups per compute unit (2 waves per SIMD)
+  const long long target = 2LL * device_compute_units();
+  long long s = (target + pairs - 1) / pairs;
   // at least two tiles per wave where the table allows it, so a wave's next tile is already
-  // loading while it works on the current one
+  // loading while it works on the current one; one tile per wave when two per wave would
+  // leave the grid short of two workgroups per compute unit
   const long long per_wave = (max_blocks + kWaves - 1) / kWaves;
-  const long long cap = per_wave / 2 > 0 ? per_wave / 2 : 1;
-  if (s > cap) s = cap;
+  const long long cap2 = per_wave / 2 > 0 ? per_wave / 2 : 1;
+  const long long cap1 = per_wave > 0 ? per_wave : 1;
+  s = pairs * (s < cap2 ? s : cap2) >= target ? (s < cap2 ? s : cap2) : (s < cap1 ? s : cap1);
   // and at most 32 full tiles per split for the longest table the batch may hold (the last
   // entry covers the staging tile): in a ragged batch the longest sequences would otherwise
   // set the kernel's time while the short ones' workgroups sit finished

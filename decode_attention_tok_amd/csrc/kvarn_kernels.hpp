@@ -56,7 +56,9 @@ hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
                                    float* v_out, const uint32_t* signs, int v_bits,
                                    hipStream_t stream);
 
-// Number of splits of each sequence's tiles for a decode launch (depends on sizes only).
+// Number of splits of each sequence's tiles for a decode launch: depends on the sizes and on
+// the compute-unit count of the current device (read once per device and cached).
 int decode_splits(int batch, int hkv, int max_blocks);
+int device_compute_units();
 
 }  // namespace kvarn

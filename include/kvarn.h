@@ -18,7 +18,8 @@
  *
  * Conventions shared by every entry point.
  *   - Pointers marked (device) are HIP device pointers; (host) are host pointers.
- *   - fp16 means IEEE binary16, little-endian. All fp16 buffers must be 16-byte aligned.
+ *   - fp16 means IEEE binary16, little-endian. All fp16 buffers and every block pool must be
+ *     16-byte aligned (a misaligned one gives KVARN_ERR_BAD_SHAPE).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream. Every call
  *     validates its arguments on the host, then enqueues its kernels on `stream` and returns
  *     without synchronising. On a validation error nothing is enqueued.
@@ -134,8 +135,8 @@ KVARN_API kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void*
                                   const int32_t* dst_blocks, void* block_pool,
                                   int64_t num_blocks, void* stream);
 
-/* Write path, one decode step ([GR] "The four-stage pipeline", stage 4: the per-step write
- * stays cheap). For each sequence b with positions[b] >= 0, writes its new key and value
+/* Write path, one decode step ([GR] "The four-stage pipeline", stage 4: a token's write does
+ * no dequantisation work). For each sequence b with positions[b] >= 0, writes its new key and value
  * token into staging slot positions[b] % 128; when that slot is 127 the staging tile now
  * holds 128 tokens and is quantised into block block_table[b][positions[b] / 128].
  *   k_new, v_new      (device) fp16 [batch][num_kv_heads][128]
@@ -152,7 +153,9 @@ KVARN_API kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k
                                 void* stream);
 
 /* Size of the workspace kvarn_decode_attention needs for these sizes, into *bytes (host).
- * It depends only on the arguments. */
+ * It depends on the arguments and on the compute-unit count of the current HIP device (the
+ * split plan fills the device; 256 compute units are assumed when no device is usable), so
+ * query it with the device current that will run the decode. */
 KVARN_API kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
                                           int32_t num_q_heads, int32_t max_blocks_per_seq,
                                           size_t* bytes);
@@ -189,7 +192,7 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const voi
  *   src_blocks  (device) int32 [n_tiles]; an id outside [0, num_blocks) gives NaN rows
  *   k_out,v_out (device) fp32 [n_tiles * 128][num_kv_heads][128], 16-byte aligned: token
  *               128 i + t of KV head h from record (src_blocks[i], h)
- * Errors: NULL_ARG, BAD_SHAPE (negative counts, misaligned outputs, too many tiles). */
+ * Errors: NULL_ARG, BAD_SHAPE (negative counts, misaligned outputs or pool, too many tiles). */
 KVARN_API kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_pool,
                                     int64_t num_blocks, const int32_t* src_blocks,
                                     int32_t n_tiles, float* k_out, float* v_out, void* stream);

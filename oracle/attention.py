@@ -1,7 +1,7 @@
 """Exact decode attention over a paged KVarN cache, and the three cache-level operations.
 
-[GR] "The four-stage pipeline", stage 4: scales are applied when a tile is loaded for the
-attention computation, not when it is written, so the per-step write path stays cheap.
+[GR] "The four-stage pipeline", stage 4: the stored scales meet the codes again only inside
+attention, at read time; writing a token involves no dequantisation.
 [GR] "What KVarN changes in vLLM's serving path": the cache lives in fixed-size paged blocks,
 one 128-token tile per block. [GR] stage 1: the rotation is orthonormal and does not change
 attention scores, which is what lets the folded form below equal the plain one.

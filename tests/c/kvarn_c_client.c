@@ -50,6 +50,31 @@ static int host_checks(void) {
   CHECK(kvarn_decode_attention(&cfg, fake, 32, fake, 1, fake, 8, fake, fake, fake, 0.1f,
                                (float*)fake, fake, 0, 4, NULL) == KVARN_ERR_WORKSPACE, 23);
   CHECK(strlen(kvarn_status_string(KVARN_ERR_UNSUPPORTED)) > 0, 24);
+  /* every entry point's validation, including misaligned block pools */
+  void* odd = (void*)(uintptr_t)0x1004;
+  CHECK(kvarn_quantize_tiles(&cfg, fake, fake, 1024, 1, fake, odd, 1, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 25);
+  CHECK(kvarn_append_token(&cfg, fake, fake, fake, fake, 4, fake, fake, odd, 8, 2, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 26);
+  CHECK(kvarn_append_token(&cfg, fake, fake, fake, fake, 0, fake, fake, fake, 8, 2, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 27);
+  CHECK(kvarn_decode_workspace_bytes(&cfg, 4, 32, 8, &ws) == KVARN_OK, 28);
+  CHECK(kvarn_decode_attention(&cfg, fake, 32, odd, 1, fake, 8, fake, fake, fake, 0.1f,
+                               (float*)fake, (void*)(uintptr_t)0x10000, ws, 4, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 29);
+  size_t wsm = 0;
+  CHECK(kvarn_decode_multi_workspace_bytes(&cfg, 4, 32, 4, 8, &wsm) == KVARN_OK && wsm > ws, 30);
+  CHECK(kvarn_decode_multi_workspace_bytes(&cfg, 4, 32, KVARN_MAX_QUERY_TOKENS + 1, 8, &wsm) ==
+            KVARN_ERR_BAD_SHAPE, 31);
+  CHECK(kvarn_dequantize_tiles(&cfg, odd, 4, fake, 1, (float*)fake, (float*)fake, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 32);
+  CHECK(kvarn_dequantize_tiles(&cfg, fake, 4, fake, 0, NULL, NULL, NULL) == KVARN_OK, 33);
+  CHECK(kvarn_fp16_block_bytes(&cfg) == 8u * KVARN_FP16_RECORD_BYTES, 34);
+  CHECK(kvarn_fp16_write_tiles(&cfg, fake, fake, 1024, 1, fake, odd, 1, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 35);
+  CHECK(kvarn_decode_attention_fp16(&cfg, fake, 32, fake, 1, fake, 8, fake, fake, fake, 0.1f,
+                                    (float*)fake, fake, 0, 4, NULL) == KVARN_ERR_WORKSPACE, 36);
+  for (int st = 0; st <= 6; ++st) CHECK(kvarn_status_string((kvarn_status)st) != NULL, 37);
   return 0;
 }
 

@@ -27,6 +27,16 @@ def test_c_client_host_checks():
     assert "ok" in out.stdout
 
 
+def test_c_client_host_checks_under_address_sanitizer():
+    """The same host checks against a copy of the library whose host code is built with
+    AddressSanitizer: every validation path runs without an invalid access or a leak."""
+    exe = _client(kbuild.C_CLIENT_ASAN)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:exitcode=99")
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0, out.stderr[-4000:]
+    assert "ok" in out.stdout and "AddressSanitizer" not in out.stderr
+
+
 def _write_input(path, st, sp, q, sk, sv, lens, sm, v_bits):
     hdr = np.array([0x4B56524E, v_bits, len(st["dst_blocks"]), sp.hkv, sp.hq, sp.batch,
                     st["block_table"].shape[1], st["num_blocks"]], np.int32)
@@ -83,10 +93,11 @@ def test_c_client_gpu_round_trip(tmp_path, v_bits):
                          4, budget)
             compare_half(rec, codec.quantize_tile(st["v"][rows, h].astype(np.float64), v_bits),
                          "v", v_bits, budget)
-    budget.check(flip_rate=1e-3)
+    budget.check()
     # its decode output against the oracle's attention over the oracle's own records of the
-    # same tiles: rounding-boundary flips may move outputs by a fraction of the quantisation
-    # error (the strict decode bar is checked elsewhere on oracle-written records)
+    # same tiles. When every record matches the oracle's exactly (no rounding-boundary flip,
+    # the measured case), the two caches are byte-identical and the decode bar of 2e-3 holds;
+    # a tolerated flip may move outputs by a fraction of the quantisation error instead
     pool_o = np.zeros((st["num_blocks"], sp.hkv, rb), np.uint8)
     oatt.quantize_tiles(st["k"], st["v"], st["dst_blocks"], pool_o)
     ref = oatt.decode_attention(q, pool_o, st["block_table"], lens, sk, sv, sm)
@@ -94,4 +105,9 @@ def test_c_client_gpu_round_trip(tmp_path, v_bits):
     scale = float(np.abs(ref).max())
     print(f"C client v_bits={v_bits}: {vars(budget)}; decode max abs err {err:.3g} "
           f"(|o| max {scale:.3g})", flush=True)
-    assert np.isfinite(got).all() and err <= 0.02 * scale
+    assert np.isfinite(got).all()
+    if budget.exact():
+        assert np.array_equal(pool_g, pool_o)
+        assert err <= 2e-3
+    else:
+        assert err <= 0.02 * scale

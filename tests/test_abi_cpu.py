@@ -65,7 +65,7 @@ def test_value_bit_presets(lib):
             == kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 128))
 
 
-def test_workspace_bytes_depends_only_on_sizes(lib):
+def test_workspace_bytes_depends_only_on_sizes_and_device(lib):
     cfg = kv.default_config(8)
     a = kv.decode_workspace_bytes(cfg, 16, 64, 128)
     b = kv.decode_workspace_bytes(cfg, 16, 64, 128)
@@ -74,14 +74,19 @@ def test_workspace_bytes_depends_only_on_sizes(lib):
 
 
 def test_workspace_follows_the_split_plan(lib):
-    """The workspace holds 130 floats per (sequence, query head, split). Splits: about 512
-    workgroups, at least two tiles per wave, and at most 32 full tiles per split for the
-    longest table (its last entry is the staging tile)."""
+    """The workspace holds 130 floats per (sequence, query head, split). Splits: two workgroups
+    per compute unit (this host has no GPU: the plan assumes 256 compute units), at least two
+    tiles per wave unless that leaves fewer than two workgroups per compute unit (then one),
+    and at most 32 full tiles per split for the longest table (its last entry is the staging
+    tile)."""
     per = 130 * 4
     # 16K context, batch 16, 8 KV heads: 512 / 128 pairs = 4 splits of 32 tiles
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 4 * per
-    # 4K context, batch 8: 8 splits wanted, capped at two tiles per wave (33 entries) -> 4
-    assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 4 * per
+    # 4K context, batch 8 (33 entries): 8 splits wanted; two tiles per wave would allow 4, or
+    # 256 workgroups (one per compute unit), so one tile per wave is allowed: 8
+    assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
+    # 4K context, batch 64: 512 (sequence, KV head) pairs fill the device with one split
+    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 1 * per
     # ragged batch up to 32K tokens, batch 32, 10 KV heads: 2 splits wanted, 256 full tiles
     # need 8 splits of at most 32
     assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 8 * per
@@ -137,6 +142,8 @@ def test_quantize_validation(lib):
     assert _call(lib, f, _cfg(), ctypes.c_void_p(0x1002), FAKE, 256, 1, FAKE, FAKE, 1,
                  None) == SHAPE                                                  # misaligned
     assert _call(lib, f, _cfg(hkv=0), FAKE, FAKE, 256, 1, FAKE, FAKE, 1, None) == SHAPE
+    assert _call(lib, f, _cfg(), FAKE, FAKE, 256, 1, FAKE, ctypes.c_void_p(0x1004), 1,
+                 None) == SHAPE                                                  # pool
 
 
 def test_append_validation(lib):
@@ -151,6 +158,9 @@ def test_append_validation(lib):
     bad = list(args)
     bad[5] = ctypes.c_void_p(0x1008)
     assert _call(lib, f, _cfg(), *bad, 2, None) == SHAPE                         # misaligned
+    bad = list(args)
+    bad[7] = ctypes.c_void_p(0x1001)
+    assert _call(lib, f, _cfg(), *bad, 2, None) == SHAPE                         # pool
 
 
 def test_decode_validation(lib):
@@ -177,6 +187,7 @@ def test_decode_validation(lib):
     assert call(ws=ctypes.c_void_p(0x10010)) == WS  # not 256-byte aligned
     assert call(sm=ctypes.c_float(float("nan"))) == SHAPE
     assert call(q=ctypes.c_void_p(0x1004)) == SHAPE
+    assert call(pool=ctypes.c_void_p(0x1008)) == SHAPE
 
 
 def test_decode_multi_validation(lib):
@@ -199,6 +210,7 @@ def test_decode_multi_validation(lib):
     assert call(nq=5) == WS                          # needs more than the Q = 4 workspace
     assert call(q=None) == NULL
     assert call(hq=2 * 17) == SHAPE
+    assert call(pool=ctypes.c_void_p(0x1002)) == SHAPE
 
 
 def test_dequantize_validation(lib):
@@ -210,6 +222,8 @@ def test_dequantize_validation(lib):
     assert _call(lib, f, _cfg(), FAKE, -4, FAKE, 1, FAKE, FAKE, None) == SHAPE
     assert _call(lib, f, _cfg(), FAKE, 4, FAKE, 1, ctypes.c_void_p(0x1004), FAKE,
                  None) == SHAPE                                                   # misaligned
+    assert _call(lib, f, _cfg(), ctypes.c_void_p(0x1004), 4, FAKE, 1, FAKE, FAKE,
+                 None) == SHAPE                                                   # pool
 
 
 def test_fp16_path_validation(lib):

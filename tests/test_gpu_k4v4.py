@@ -57,7 +57,7 @@ def test_quantize_special_tiles():
     pool = gpu_quantize(cfg, k, v, dst, n, 1).cpu().numpy()
     for i in range(n):
         b = compare_records(pool, k, v, dst, 1, tiles=[i], v_bits=4)
-        b.check(flip_rate=1e-2)
+        b.check()
 
 
 def test_key_half_equals_the_default_preset():

@@ -68,6 +68,69 @@ def test_closed_form_one_nonzero_per_row(seed):
         assert np.array_equal(q["codes"], codes_exp)
 
 
+def floor_tile():
+    """A tile on which both standard-deviation floors (reading R8) decide the column scales.
+
+    Token 2k (k < 64) is m_k * (row 2k - row 2k+1 of the +-1 Sylvester matrix) with m_k = 2^-6
+    for k < 32 and 2^-4 for k >= 32; every odd token is zero. fp16-exact."""
+    pm1 = hadamard.H128 * np.sqrt(128.0)
+    x = np.zeros((T, D))
+    for k in range(64):
+        x[2 * k] = (2.0 ** -6 if k < 32 else 2.0 ** -4) * (pm1[2 * k] - pm1[2 * k + 1])
+    return x
+
+
+def test_closed_form_floor_tile():
+    # Worked by hand (s = sqrt(128), kappa = sqrt(127/128); a column or row with one nonzero w
+    # among 128 entries has standard deviation |w| kappa / s; two entries +-w have w sqrt(2)/s).
+    # Rotated: token 2k holds +m_k s at channel 2k and -m_k s at channel 2k+1, nothing else;
+    # max |rotated| = 2^-4 s.
+    # Round 1 columns (u = 1): channel of token k: std m_k kappa; floor 2^-16 * 2^-4 s * 1 is
+    #   far below. Rows: token rows see +-s / kappa -> std sqrt(2) / kappa; zero rows sit at the
+    #   row floor 2^-16 * 2^-4 s * max(v), max(v) = 1 / (2^-6 kappa), so their multiplier
+    #   u0 = 2^-6 kappa / (2^-16 * 2^-4 s) is the largest of all multipliers.
+    # Later column steps: the column floor is 2^-16 * 2^-4 s * u0 = 2^-6 kappa, while a small
+    #   channel's std is 2^-6 kappa^2 / sqrt(2) below it: every small channel (64 of them) sits
+    #   at the floor 2^-6 kappa from round 2 on. A large channel's row multiplier shrinks by
+    #   kappa / sqrt(2) per round: in units of 2^-6 its std is 4 kappa^2 / sqrt(2), 2 kappa^3
+    #   and sqrt(2) kappa^4 in rounds 2 to 4.
+    # Round 4 (the last column step) and the gauge (geometric mean of c = 1):
+    #   small channels c = kappa / (2^(1/4) kappa^(5/2)) = 2^(-1/4) kappa^(-3/2) = 0.845857...
+    #   large channels c = 2^(1/4) kappa^(3/2) = 1.182232...
+    #   E4M3 nearest: 0.845857 -> 0.875 (midpoint 0.84375); 1.182232 -> 1.125 (midpoint 1.1875).
+    # Rounding per token (y = rotated / c-hat; zero rows give z = 0, s = 0, codes 0):
+    #   small rows: y = +-s / 56 = +-0.2020305; z = FP16 round-down = -1656 * 2^-13;
+    #     K: (0.2020305 + 0.2021484) / 15 -> E4M3 round-up 14 * 2^-9; codes 15 (+), 0 (-), 7
+    #     V: (...) / 3 -> 9 * 2^-6; codes 3 (+), 0 (-), 1
+    #   large rows: y = +-s / 18 = +-0.6285394; z = -1288 * 2^-11;
+    #     K: (0.6285394 + 0.6289063) / 15 -> 11 * 2^-7; codes 15, 0, 7
+    #     V: (...) / 3 -> 14 * 2^-5; codes 3, 0, 1 (0.62890625 / 0.4375 = 1.4375 -> 1)
+    # A floor twice as large, half as large, or without its multiplier factor, in either step,
+    # moves every c-hat off these values.
+    x = floor_tile()
+    assert np.array_equal(x.astype(np.float16).astype(np.float64), x)
+    kappa = np.sqrt(127.0 / 128.0)
+    small = np.arange(D) < 64
+    c_pre = np.where(small, 2 ** -0.25 * kappa ** -1.5, 2 ** 0.25 * kappa ** 1.5)
+    live = np.arange(T) % 2 == 0
+    big_row = np.arange(T) >= 64
+    for bits, s_small, s_big, mid in ((4, 14 * 2.0 ** -9, 11 * 2.0 ** -7, 7),
+                                      (2, 9 * 2.0 ** -6, 14 * 2.0 ** -5, 1)):
+        top = 2 ** bits - 1
+        q = codec.quantize_tile(x, bits)
+        assert np.allclose(q["c"], c_pre, rtol=1e-12, atol=0)
+        assert np.array_equal(q["c_hat"], np.where(small, 0.875, 1.125))
+        assert np.array_equal(q["z_hat"], np.where(~live, 0.0,
+                                                   np.where(big_row, -1288 * 2.0 ** -11,
+                                                            -1656 * 2.0 ** -13)))
+        assert np.array_equal(q["s_hat"], np.where(~live, 0.0, np.where(big_row, s_big, s_small)))
+        codes = np.where(live[:, None], mid, 0) * np.ones((T, D), int)
+        for t in np.flatnonzero(live):
+            codes[t, t] = top              # +m s at channel 2k = t
+            codes[t, t + 1] = 0            # -m s at channel 2k + 1
+        assert np.array_equal(q["codes"], codes)
+
+
 # ------------------------------------------------------------------ normalisation invariants
 
 

@@ -124,7 +124,12 @@ def _sequence_kv(sp: Spec, b: int, length: int, mult: np.ndarray):
     return k16, v16
 
 
-def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None) -> dict:
+def _sequence_job(args):
+    sp, b, length = args
+    return _sequence_kv(sp, b, length, head_params(sp))
+
+
+def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None, workers: int = 1) -> dict:
     """Prefill state of the workload.
 
     Returns a dict with
@@ -135,7 +140,9 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None) -> dict:
       block_table   int32 [B, max_blocks] (room for max_new_tokens more tokens per sequence)
       seq_lens      int32 [B]
       num_blocks    int
-      sequences     the sequence indices included in k/v (default: all)."""
+      sequences     the sequence indices included in k/v (default: all).
+    workers > 1 draws the sequences in that many forked processes (same values: every
+    sequence has its own stream); call it before the process initialises a GPU."""
     lens = seq_lens(sp)
     max_blocks = int(max((int(l) + max_new_tokens + T - 1) // T for l in lens))
     max_blocks = max(max_blocks, 1)
@@ -147,9 +154,14 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None) -> dict:
     mult = head_params(sp)
     chosen = range(sp.batch) if sequences is None else list(sequences)
     ks, vs, dst, tk, tv = [], [], [], [], []
-    for b in chosen:
+    if workers > 1 and len(chosen) > 1:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(min(workers, len(chosen))) as pool:
+            drawn = pool.map(_sequence_job, [(sp, b, int(lens[b])) for b in chosen])
+    else:
+        drawn = [_sequence_kv(sp, b, int(lens[b]), mult) for b in chosen]
+    for b, (k, v) in zip(chosen, drawn):
         length = int(lens[b])
-        k, v = _sequence_kv(sp, b, length, mult)
         n_full = length // T
         ks.append(k[:n_full * T])
         vs.append(v[:n_full * T])
