@@ -19,7 +19,7 @@ TILE_BYTES = 13312        # record of the default preset kvarn_k4v2_g128
 TILE_BYTES_V4 = 17408     # record with 4-bit values (kvarn_k4v4_g128)
 
 STATUS = {0: "OK", 1: "ERR_NULL_ARG", 2: "ERR_BAD_SHAPE", 3: "ERR_UNSUPPORTED",
-          4: "ERR_WORKSPACE", 5: "ERR_HIP"}
+          4: "ERR_WORKSPACE", 5: "ERR_HIP", 6: "ERR_SCRATCH_LIMIT"}
 
 
 class KvarnError(RuntimeError):
@@ -54,6 +54,8 @@ _SIGNATURES = {
     "kvarn_decode_attention": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P, _P, _P,
                                               ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                               _P]),
+    "kvarn_decode_attention_noalloc": (ctypes.c_int, [_CFG, _P, _I32, _P, _I64, _P, _I32, _P,
+                                                      _P, _P, ctypes.c_float, _P, _I32, _P]),
     "kvarn_decode_multi_workspace_bytes": (ctypes.c_int, [_CFG, _I32, _I32, _I32, _I32,
                                                           ctypes.POINTER(ctypes.c_size_t)]),
     "kvarn_decode_attention_multi": (ctypes.c_int, [_CFG, _P, _I32, _I32, _P, _I64, _P, _I32, _P,
@@ -179,6 +181,24 @@ def decode_attention(cfg: Config, q, block_pool, block_table, seq_lens, staging_
                                         _ptr(seq_lens), _ptr(staging_k), _ptr(staging_v),
                                         float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                         batch, _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_attention_noalloc(cfg: Config, q, block_pool, block_table, seq_lens, staging_k,
+                             staging_v, sm_scale, out, stream=None):
+    """decode_attention() with the library's static per-device scratch instead of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    batch, hq, _ = q.shape
+    max_blocks = block_table.shape[1]
+    num_blocks = block_pool.numel() // block_bytes(cfg)
+    _check("kvarn_decode_attention_noalloc",
+           lib().kvarn_decode_attention_noalloc(ctypes.byref(cfg), _ptr(q), hq, _ptr(block_pool),
+                                                num_blocks, _ptr(block_table), max_blocks,
+                                                _ptr(seq_lens), _ptr(staging_k),
+                                                _ptr(staging_v), float(sm_scale), _ptr(out),
+                                                batch, _stream(stream)))
 
 
 def dequantize_tiles(cfg: Config, block_pool, src_blocks, k_out, v_out, stream=None):

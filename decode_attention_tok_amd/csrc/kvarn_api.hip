@@ -5,7 +5,39 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
+
+// Decode scratch for callers that cannot allocate (kvarn_decode_attention_noalloc): one array
+// of KVARN_STATIC_SCRATCH_BYTES on every device the library runs on, held until the process
+// ends. In host code the array's name is only a stand-in; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept per device.
+__device__ __align__(256) unsigned char scratch[KVARN_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+kvarn_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVARN_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KVARN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return KVARN_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVARN_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -162,6 +194,31 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, int3
                       workspace, workspace_bytes, batch, stream);
 }
 
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_config* cfg, const void* q,
+                                            int32_t num_q_heads, const void* block_pool,
+                                            int64_t num_blocks, const int32_t* block_table,
+                                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                            const void* staging_k, const void* staging_v,
+                                            float sm_scale, float* out, int32_t batch,
+                                            void* stream) {
+  size_t need = 0;
+  kvarn_status st = multi_workspace_bytes(cfg, batch, num_q_heads, 1, max_blocks_per_seq, &need);
+  if (st != KVARN_OK) return st;
+  if (batch == 0) return KVARN_OK;
+  if (need > (size_t)KVARN_STATIC_SCRATCH_BYTES) return KVARN_ERR_SCRATCH_LIMIT;
+  // every other argument is checked by the shared path before anything is launched; the
+  // scratch address is only resolved once they have passed
+  if (q == nullptr || block_pool == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      staging_k == nullptr || staging_v == nullptr || out == nullptr)
+    return KVARN_ERR_NULL_ARG;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != KVARN_OK) return st;
+  return decode_multi(cfg, q, num_q_heads, 1, block_pool, num_blocks, block_table,
+                      max_blocks_per_seq, seq_lens, staging_k, staging_v, sm_scale, out, ws,
+                      (size_t)KVARN_STATIC_SCRATCH_BYTES, batch, stream);
+}
+
 kvarn_status kvarn_decode_multi_workspace_bytes(const kvarn_config* cfg, int32_t batch,
                                                 int32_t num_q_heads, int32_t n_query,
                                                 int32_t max_blocks_per_seq, size_t* bytes) {
@@ -266,6 +323,9 @@ const char* kvarn_status_string(kvarn_status status) {
       return "unsupported config (presets kvarn_k4v2_g128 and kvarn_k4v4_g128, head_dim 128)";
     case KVARN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KVARN_ERR_HIP: return "HIP runtime error while launching";
+    case KVARN_ERR_SCRATCH_LIMIT:
+      return "the decode needs more scratch than the library's static array "
+             "(KVARN_STATIC_SCRATCH_BYTES); use kvarn_decode_attention with a workspace";
   }
   return "unknown status";
 }

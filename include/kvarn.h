@@ -72,7 +72,7 @@ extern "C" {
 #define KVARN_API
 #endif
 
-#define KVARN_ABI_VERSION 3
+#define KVARN_ABI_VERSION 4
 #define KVARN_TILE_TOKENS 128
 #define KVARN_HEAD_DIM 128
 #define KVARN_TILE_BYTES 13312        /* record of the default preset (v_bits 2) */
@@ -85,7 +85,8 @@ typedef enum {
   KVARN_ERR_BAD_SHAPE = 2,   /* a size or count is out of range, or a buffer misaligned  */
   KVARN_ERR_UNSUPPORTED = 3, /* the config is not one of the presets below                */
   KVARN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required               */
-  KVARN_ERR_HIP = 5          /* the HIP runtime reported an error when launching         */
+  KVARN_ERR_HIP = 5,         /* the HIP runtime reported an error when launching         */
+  KVARN_ERR_SCRATCH_LIMIT = 6 /* kvarn_decode_attention_noalloc: sizes beyond its scratch  */
 } kvarn_status;
 
 /* The codec configuration. The pages ship one preset, kvarn_k4v2_g128 ([GR], "What KVarN
@@ -196,6 +197,27 @@ KVARN_API kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const voi
 KVARN_API kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_pool,
                                     int64_t num_blocks, const int32_t* src_blocks,
                                     int32_t n_tiles, float* k_out, float* v_out, void* stream);
+
+/* ---- Decode without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The library keeps
+ * one static device array of KVARN_STATIC_SCRATCH_BYTES per GPU it runs on (held until the
+ * process ends) and uses it as the workspace of kvarn_decode_attention; the call itself
+ * allocates nothing. Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (different streams, or different threads) race and must not be issued; the array
+ * needs no clearing (the decode writes every partial it reads). Arguments, results, NaN rules
+ * and errors are those of kvarn_decode_attention without the workspace, plus
+ * KVARN_ERR_SCRATCH_LIMIT when kvarn_decode_workspace_bytes for these sizes exceeds
+ * KVARN_STATIC_SCRATCH_BYTES (nothing is launched then), and KVARN_ERR_HIP if the array's
+ * device address cannot be obtained. */
+#define KVARN_STATIC_SCRATCH_BYTES (16u << 20)
+
+KVARN_API kvarn_status kvarn_decode_attention_noalloc(const kvarn_config* cfg, const void* q,
+                                            int32_t num_q_heads, const void* block_pool,
+                                            int64_t num_blocks, const int32_t* block_table,
+                                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                            const void* staging_k, const void* staging_v,
+                                            float sm_scale, float* out, int32_t batch,
+                                            void* stream);
 
 /* ---- Several query tokens per sequence (multi-token verification, chunked continuation).
  * The pages place KVarN beside speculative decoding and multi-token prediction ([GR] "The 2-bit

@@ -35,7 +35,7 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvarn_abi_version() == 3
+    assert lib.kvarn_abi_version() == 4
 
 
 def test_sizes(lib):
@@ -211,6 +211,26 @@ def test_decode_multi_validation(lib):
     assert call(q=None) == NULL
     assert call(hq=2 * 17) == SHAPE
     assert call(pool=ctypes.c_void_p(0x1002)) == SHAPE
+
+
+def test_decode_noalloc_validation(lib):
+    f = "kvarn_decode_attention_noalloc"
+    names = ["q", "hq", "pool", "nblk", "bt", "maxb", "lens", "sk", "sv", "sm", "out", "batch",
+             "stream"]
+    good = [FAKE, 8, FAKE, 10, FAKE, 4, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, 2, None]
+    def call(hkv=2, **over):
+        a = list(good)
+        for k, v in over.items():
+            a[names.index(k)] = v
+        return _call(lib, f, _cfg(hkv=hkv), *a)
+    assert call(batch=0) == OK
+    assert call(q=None) == NULL
+    assert call(hq=7) == SHAPE
+    assert call(maxb=0) == SHAPE
+    # sizes whose workspace would exceed the static scratch are rejected before any HIP call
+    assert kv.decode_workspace_bytes(kv.default_config(8), 4096, 64, 8) > kv.STATIC_SCRATCH_BYTES
+    assert call(hkv=8, hq=64, maxb=8, batch=4096) == 6
+    assert b"scratch" in lib.kvarn_status_string(6)
 
 
 def test_dequantize_validation(lib):
