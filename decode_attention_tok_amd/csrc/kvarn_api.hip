@@ -137,7 +137,10 @@ kvarn_status multi_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32
       num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup || n_query < 1 ||
       n_query > kvarn::kMaxQuery)
     return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  const int splits = kvarn::decode_splits(
+      batch, cfg->num_kv_heads, max_blocks_per_seq,
+      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, batch,
+                        cfg->num_kv_heads, max_blocks_per_seq));
   *bytes = (size_t)batch * (size_t)n_query * (size_t)num_q_heads * (size_t)splits *
            kvarn::kPartialFloats * sizeof(float);
   return KVARN_OK;
@@ -164,7 +167,10 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
       !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  const int splits = kvarn::decode_splits(
+      batch, cfg->num_kv_heads, max_blocks_per_seq,
+      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, batch,
+                        cfg->num_kv_heads, max_blocks_per_seq));
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_decode(
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads, n_query,
@@ -305,7 +311,7 @@ kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
     return KVARN_ERR_BAD_SHAPE;
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
+  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq, false);
   return from_hip(kvarn::launch_decode_fp16(
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads,
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,

@@ -17,12 +17,13 @@
 // the 4 states are merged in LDS. Per tile a wave issues 64 MFMAs (v_mfma_f32_16x16x32_f16):
 //   scores  D[token][col] = codeK[token][ch] x Q[ch][col]   8 token blocks x 4 channel blocks
 //   output  O[row][ch]    = W[row][token] x codeV[token][ch] 4 token blocks x 8 channel blocks
-// Key codes enter the MFMA as normal fp16 halves (code - 7.5) / 16: the nibble shifted into
-// mantissa bits 6..9 under exponent 0x3C00 gives 1 + code / 16, and one packed fp16 add
-// (exact) centres it; the centring term 7.5 / 16 * sum_j q~_j is added back in fp32. Centred
-// operands keep the products small next to the token-dependent part of the score: the matrix
-// core's accumulation error follows the largest products, and with 1 + code / 16 it reached
-// 2e-3 on outputs of magnitude 250 at 16K tokens, against 5e-4 centred. (The MFMA sums products of subnormal fp16 operands
+// Key codes enter the MFMA as normal fp16 halves (code - 8) / 64: a nibble at bits 0..3 of a
+// half goes under exponent 16 (16 + code / 64), a nibble at bits 4..7 under exponent 1
+// (1 + code / 64), so one shift by 8 serves the upper two nibbles of each half, and one packed
+// fp16 add (exact) centres each pair; the centring term 8 / 64 * sum_j q~_j is added back in
+// fp32. Centred operands keep the products small next to the token-dependent part of the
+// score: the matrix core's accumulation error follows the largest products, and uncentred
+// 1 + code / 16 reached 2e-3 on outputs of magnitude 250 at 16K tokens, against 5e-4 centred. (The MFMA sums products of subnormal fp16 operands
 // with far less precision than products of normal ones, so raw codes are not used as
 // subnormals; a variant that left nibbles in the low mantissa bits, 1 + code / 1024 with the
 // query scaled to match, was far off as well, so every field sits just below the exponent.) Value codes likewise enter as 1 + code / 4 (the 2-bit
@@ -164,6 +165,33 @@ __device__ __forceinline__ uint32_t add_h2(uint32_t w, half2v c) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, w) + c);
 }
 
+// Per-lane constants of the key-code operand (masks in VGPRs, exponent words in SGPRs: a VOP3
+// instruction takes one literal at most).
+struct KeyConsts {
+  uint32_t m_lo, m_hi, e16, e1;
+};
+
+__device__ __forceinline__ KeyConsts key_consts() {
+  KeyConsts k;
+  k.m_lo = 0x000F000Fu;
+  k.m_hi = 0x00F000F0u;
+  asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi));
+  k.e16 = __builtin_amdgcn_readfirstlane(0x4C004C00u);   // 16.0 in both halves
+  k.e1 = __builtin_amdgcn_readfirstlane(0x3C003C00u);    // 1.0 in both halves
+  return k;
+}
+
+// The eight key codes of one 32-bit word (channels 8 d .. 8 d + 7 of a token; channel 8 d + 2 b
+// in the low nibble of byte b) as the operand halves of channels 8 d + {0, 4, 1, 5, 2, 6, 3, 7},
+// each (code - 8) / 64 exactly.
+__device__ __forceinline__ half8 key_operand(uint32_t w, const KeyConsts& k) {
+  const half2v c16 = {(_Float16)-16.125f, (_Float16)-16.125f};   // 16 + 8 / 64
+  const half2v c1 = {(_Float16)-1.125f, (_Float16)-1.125f};      // 1 + 8 / 64
+  const uint32_t w8 = w >> 8;
+  return as_h8(add_h2(and_or(w, k.m_lo, k.e16), c16), add_h2(and_or(w, k.m_hi, k.e1), c1),
+               add_h2(and_or(w8, k.m_lo, k.e16), c16), add_h2(and_or(w8, k.m_hi, k.e1), c1));
+}
+
 // fp16 lo parts of a pair whose packed hi parts are h.
 __device__ __forceinline__ uint32_t lo_of(uint32_t h, float a, float b) {
   uint32_t r;
@@ -181,6 +209,34 @@ struct TileRegs {
   uint2 m8;           // 8 FP8 metadata bytes (see decode_meta)
   uint2 m16;          // 4 fp16 zero-points
 };
+
+// Value codes of channel block nb (channel 16 nb + lane % 16) and token block kb as the B
+// operand of the output product: 2-bit codes as 1 + code / 4 (field nb of the section words
+// moved to mantissa bits 8..9 under exponent 1), 4-bit codes as 1 + code / 16 (field nb % 4 of
+// the words of channel half nb / 4 moved to bits 6..9). Normal and exact.
+template <int kVBits>
+__device__ __forceinline__ half8 value_operand(const uint4 (&vw)[2 * kVBits], int nb, int kb,
+                                               uint32_t vmask, uint32_t kmask, uint32_t one16) {
+  uint32_t f[4];
+  if constexpr (kVBits == 2) {
+    const uint32_t v4[4] = {vw[kb].x, vw[kb].y, vw[kb].z, vw[kb].w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
+      f[d] = and_or(x, vmask, one16);
+    }
+  } else {
+    const uint4 ww = vw[2 * kb + (nb >> 2)];
+    const uint32_t v4[4] = {ww.x, ww.y, ww.z, ww.w};
+    const int kF = nb & 3;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = kF < 2 ? (v4[d] << (6 - 4 * kF)) : (v4[d] >> (4 * kF - 6));
+      f[d] = and_or(x, kmask, one16);
+    }
+  }
+  return as_h8(f[0], f[1], f[2], f[3]);
+}
 
 // Per-lane byte offsets of the metadata a lane decodes. Lanes 0-15: c-hat^K, 16-31: s-hat^K,
 // 32-47: c-hat^V, 48-63: s-hat^V, 8 bytes each; lanes 0-31: z-hat^K, 32-63: z-hat^V, 4 each.
@@ -238,18 +294,19 @@ __device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, con
 // and stores them, times per-lane factors, at 8 lane and 4 lane of the wave's tables.
 // FP8 goes through the hardware E4M3 conversion (exact for every finite code).
 __device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int lane,
-                                            WaveMeta& wm, float fm, float fz) {
+                                            float* __restrict__ f8, float* __restrict__ h16,
+                                            float fm, float fz) {
   const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, false);
   const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, true);
   const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, false);
   const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, true);
-  float4* dst = reinterpret_cast<float4*>(wm.f8 + 8 * lane);
+  float4* dst = reinterpret_cast<float4*>(f8 + 8 * lane);
   dst[0] = make_float4(a[0] * fm, a[1] * fm, b[0] * fm, b[1] * fm);
   dst[1] = make_float4(c[0] * fm, c[1] * fm, d[0] * fm, d[1] * fm);
   const float2v e = __builtin_convertvector(__builtin_bit_cast(half2v, m16.x), float2v);
   const float2v f = __builtin_convertvector(__builtin_bit_cast(half2v, m16.y), float2v);
-  *reinterpret_cast<float4*>(wm.h16 + 4 * lane) = make_float4(e[0] * fz, e[1] * fz, f[0] * fz,
-                                                              f[1] * fz);
+  *reinterpret_cast<float4*>(h16 + 4 * lane) = make_float4(e[0] * fz, e[1] * fz, f[0] * fz,
+                                                           f[1] * fz);
 }
 
 // kCausal: several query tokens per sequence (nq > 1) with the causal mask; a separate
@@ -350,7 +407,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   frexpf(fmaxf(qmax, 1e-30f) * 448.0f, &qe);
   const float pq = ldexpf(1.0f, 14 - qe);
   const float scale2 = sm_scale * kLog2e;
-  const float kfac = scale2 * 16.0f / pq;          // undoes the code / 16 encoding and pq
+  const float kfac = scale2 * 64.0f / pq;          // undoes the code / 64 encoding and pq
   const float kzfac = scale2 / pq;                 // multiplies pq * sum_j q~_j
   // per-lane metadata factors (see decode_meta): pq on c-hat^K, kfac on s-hat^K, 1 on
   // c-hat^V, 32 on s-hat^V; kzfac on z-hat^K, 1 on z-hat^V
@@ -380,7 +437,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   uint32_t kmask = 0x03C003C0u, vmask = 0x03000300u;
   asm volatile("" : "+v"(kmask), "+v"(vmask));
   const uint32_t one16 = __builtin_amdgcn_readfirstlane(0x3C003C00u);
-  const half2v kctr = {(_Float16)-1.46875f, (_Float16)-1.46875f};   // 1 + 7.5 / 16
+  const KeyConsts kcon = key_consts();
 
   // running state: score-lane view (column n) and output-row view (rows 4 s + i)
   float m_run = -INFINITY, l_run = 0.0f;
@@ -399,7 +456,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
       else bad = true;                             // finishes this tile, then stops
     }
-    decode_meta(cur.m8, cur.m16, lane, wm, fm, fz);   // wave-local LDS tables
+    decode_meta(cur.m8, cur.m16, lane, wm.f8, wm.h16, fm, fz);   // wave-local LDS tables
 
     // ---- query operand for this tile: q' = pq * q_rot * c-hat^K, hi (cols 0-7) or lo (8-15);
     // element e of channel block c is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
@@ -420,7 +477,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       }
     }
     asum = add_xor32(add_xor16(asum));            // over all 128 channels of column n
-    const float asum_c = 0.46875f * asum;          // the centring term, 7.5 / 16 * asum
+    const float asum_c = 0.125f * asum;            // the centring term, 8 / 64 * asum
 
     // ---- scores: 8 token blocks x 4 channel blocks
     float4v sc[8];
@@ -429,21 +486,13 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
       float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // nibble q of the word -> mantissa bits 6..9 of a half under exponent 0x3C00:
-        // 1 + code / 16, then (code - 7.5) / 16 (normal, exact); slots (q, q + 4) share a word
-        const uint32_t w = w4[c];
-        const half8 a = as_h8(add_h2(and_or(w << 6, kmask, one16), kctr),
-                              add_h2(and_or(w << 2, kmask, one16), kctr),
-                              add_h2(and_or(w >> 2, kmask, one16), kctr),
-                              add_h2(and_or(w >> 6, kmask, one16), kctr));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], acc, 0, 0, 0);
-      }
+      for (int c = 0; c < 4; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(w4[c], kcon), qb[c], acc, 0, 0, 0);
       sc[mb] = acc;
     }
     if (nrec != nullptr) load_keys(nrec, lo, cur);
     // hi + lo partial scores of this lane's two rows, then the log2-domain score per token:
-    // D = sum_j (code_j - 7.5) / 16 q'_j, so pq <q~, code> = 16 (D + 7.5 / 16 asum)
+    // D = sum_j (code_j - 8) / 64 q'_j, so pq <q~, code> = 64 (D + 8 / 64 asum)
     float v[8][2];
     float tmax = -INFINITY;
     const int tpos = kT * (i0 + wave_u + kWaves * j);      // position of this tile's token 0
@@ -613,6 +662,360 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   }
 }
 
+// ------------------------------------------------------------------ paired tiles (<= 4 heads)
+//
+// With at most four virtual heads per KV head (G * nq <= 4) one tile fills only half of the 16
+// MFMA columns (a hi and a lo part per head), so a wave takes its tiles two at a time and the
+// products carry both: columns (score product) and rows (output product) 0..7 belong to the
+// first tile of the pair, 8..15 to the second, and within each half position h holds head h's
+// hi part and position 7 - h its lo part (DPP row_half_mirror pairs the two). Each tile's
+// operand is zero in the other tile's half, so the two tiles' MFMAs accumulate into one set of
+// accumulators and everything between and after them (combining the score parts, the softmax,
+// the probability operand, folding the output scales) runs once per pair.
+//
+// One wave per workgroup, one chunk of `chunk` consecutive tiles of one (sequence, KV head) per
+// wave (grid: chunks x KV heads x sequences); each wave writes its own partial (m, l, o~) per
+// virtual head, so waves never wait for each other and a short sequence simply has fewer
+// chunks (the waves past its end write an empty partial and leave). Only a chunk's last pair
+// can be single: its second tile's products are then skipped and its columns carry no
+// probability.
+
+struct PairSmem {
+  float qrot[4][kD + 4];           // rotated queries of the virtual heads (fp32)
+  float f8[2][4 * kD];             // per tile: c-hat^K * pq | s-hat^K * kfac | c-hat^V | 32 s-hat^V
+  float h16[2][2 * kT];            // per tile: z-hat^K * kzfac | z-hat^V
+  float alpha[16], beta[16];       // per column / row of the pair layout
+};
+
+__device__ __forceinline__ float dpp_half_mirror(float v) {   // lane (l & ~7) | (7 - (l & 7))
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t dpp_half_mirror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+}
+
+template <bool kCausal, int kVBits>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
+                    const uint8_t* __restrict__ pool, long long num_blocks,
+                    const int32_t* __restrict__ block_table, int max_blocks,
+                    const int32_t* __restrict__ seq_lens, float sm_scale,
+                    float* __restrict__ partials, uint4 signs, int chunk) {
+  __shared__ PairSmem sm;
+  const int nsplit = gridDim.x;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int group = hq / hkv, nh = group * nq;                // virtual heads served (1..4)
+  const int lane = threadIdx.x;
+  auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
+    return ((long long)b * nq + v / group) * hq + g * group + v % group;
+  };
+  const int len = seq_lens[b];
+  bool bad = len < 0 || (len >> 7) > max_blocks;
+  const int n_full = bad ? 0 : (len >> 7);
+  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  const int ntile = i1 - i0;
+  if (ntile == 0) {                                // nothing here: an empty partial per head
+    for (int idx = lane; idx < nh * kPartialFloats; idx += 64) {
+      const int gg = idx / kPartialFloats, k = idx % kPartialFloats;
+      float* pp = partials + (row_of(gg) * nsplit + split) * kPartialFloats;
+      pp[k] = k == 0 ? (bad ? NAN : -INFINITY) : (k == 1 && bad ? NAN : 0.0f);
+    }
+    return;
+  }
+  const int npair = (ntile + 1) >> 1;              // pair p: tiles i0 + 2 p, i0 + 2 p + 1
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0;
+  constexpr long long kTileBytes = RecordLayout<kVBits>::kTileBytes;
+  const LaneOffsets lo = lane_offsets<kVBits>(lane);
+  TileRegs<kVBits> cx, cy;
+  // block ids are scalar loads issued one pair before the pair that needs them
+  int idx_next = 0, idy_next = 0;
+  if (npair > 1) {
+    idx_next = bt_row[2];
+    if (3 < ntile) idy_next = bt_row[3];
+  }
+  {
+    const long long bx = bt_row[0];
+    const bool y0 = 1 < ntile;
+    const long long by = y0 ? bt_row[1] : 0;
+    if (bx < 0 || bx >= num_blocks || (y0 && (by < 0 || by >= num_blocks))) {
+      bad = true;
+    } else {
+      const uint8_t* rx = pool + (bx * hkv + g) * kTileBytes;
+      load_keys(rx, lo, cx);
+      load_values(rx, lo, cx);
+      if (y0) {
+        const uint8_t* ry = pool + (by * hkv + g) * kTileBytes;
+        load_keys(ry, lo, cy);
+        load_values(ry, lo, cy);
+      }
+    }
+  }
+
+  // ---- rotated queries in LDS (channels 2 lane, 2 lane + 1 of each virtual head)
+  float qmax = 0.0f;
+  const uint32_t sb = lane_sign_bits(signs, lane);              // optional sign flips
+  for (int k = 0; k < 4; ++k) {
+    float o0 = 0.0f, o1 = 0.0f;
+    if (k < nh) {
+      uint32_t w = reinterpret_cast<const uint32_t*>(q + row_of(k) * kD)[lane];
+      w ^= ((sb & 1u) << 15) | ((sb >> 1) << 31);
+      o0 = fp16_bits_to_float(w & 0xFFFFu);
+      o1 = fp16_bits_to_float(w >> 16);
+      fwht_wave(o0, o1, lane);
+      o0 *= 0.08838834764831845f;
+      o1 *= 0.08838834764831845f;
+    }
+    *reinterpret_cast<float2*>(&sm.qrot[k][2 * lane]) = make_float2(o0, o1);
+    qmax = fmaxf(qmax, fmaxf(fabsf(o0), fabsf(o1)));
+  }
+  qmax = wave_max_nonneg(qmax);
+  int qe = 0;
+  frexpf(fmaxf(qmax, 1e-30f) * 448.0f, &qe);
+  const float pq = ldexpf(1.0f, 14 - qe);          // |q~ * pq| <= 2^14: hi parts stay finite
+  const float scale2 = sm_scale * kLog2e;
+  const float kfac = scale2 * 64.0f / pq;          // undoes the code / 64 encoding and pq
+  const float kzfac = scale2 / pq;
+  const int mgrp = lane >> 4;
+  const float fm = mgrp == 0 ? pq : (mgrp == 1 ? kfac : (mgrp == 2 ? 1.0f : 32.0f));
+  const float fz = lane < 32 ? kzfac : 1.0f;
+
+  // lane roles: column / row n of the pair layout, score rows and output k groups s
+  const int n = lane & 15, s = lane >> 4;
+  const int tsel = n >> 3;                         // first or second tile of the pair
+  const int pos = n & 7;
+  const bool colhi = pos < 4;
+  const int hh = colhi ? pos : 7 - pos;            // virtual head of this column / row
+  const bool colv = hh < nh;
+  const float negk = colhi ? 0.0f : -1.0f;         // hi parts at positions 0-3, lo at 4-7
+  const int ih = colhi ? 0 : 2;                    // this lane's rows of each score block
+  const uint32_t mask_x = (colv && tsel == 0) ? 0xFFFFFFFFu : 0u;
+  const uint32_t mask_y = (colv && tsel == 1) ? 0xFFFFFFFFu : 0u;
+  // causal limit of this column's query token (position len - nq + i); with nq <= 16 every
+  // packed tile keeps >= 112 visible tokens
+  const int qlim = len - nq + hh / group;
+  uint32_t vmask = 0x03000300u, kmask = 0x03C003C0u;
+  asm volatile("" : "+v"(vmask), "+v"(kmask));
+  const uint32_t one16 = __builtin_amdgcn_readfirstlane(0x3C003C00u);
+  const KeyConsts kcon = key_consts();
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  for (int p = 0; p < npair && !bad; ++p) {
+    const bool has_y = 2 * p + 1 < ntile;          // wave-uniform
+    const uint8_t* nrx = nullptr;
+    const uint8_t* nry = nullptr;
+    if (p + 1 < npair) {
+      const bool ny = 2 * p + 3 < ntile;
+      const long long bx = idx_next, by = idy_next;
+      if (p + 2 < npair) {
+        idx_next = bt_row[2 * p + 4];
+        idy_next = 2 * p + 5 < ntile ? bt_row[2 * p + 5] : 0;
+      }
+      if (bx >= 0 && bx < num_blocks && (!ny || (by >= 0 && by < num_blocks))) {
+        nrx = pool + (bx * hkv + g) * kTileBytes;
+        if (ny) nry = pool + (by * hkv + g) * kTileBytes;
+      } else {
+        bad = true;                                // finishes this pair, then stops
+      }
+    }
+    decode_meta(cx.m8, cx.m16, lane, sm.f8[0], sm.h16[0], fm, fz);
+    if (has_y) decode_meta(cy.m8, cy.m16, lane, sm.f8[1], sm.h16[1], fm, fz);
+    // tables this lane reads: its column's tile (the first tile's when the pair is single; the
+    // second tile's columns are then masked), and its output rows' tile
+    const int tcol = has_y ? tsel : 0;
+    const int trow = has_y ? (s >> 1) : 0;
+    const bool col_live = tsel == 0 || has_y;
+
+    // ---- query operands: q' = pq * q_rot * c-hat^K of this column's tile, hi or lo part;
+    // element e of channel block c is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
+    half8 qx[4], qy[4];
+    float asum = 0.0f;
+    {
+      const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[colv ? hh : 0] + 32 * s);
+      const float4* kc4 = reinterpret_cast<const float4*>(sm.f8[tcol] + 32 * s);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
+        const float4 ka = kc4[2 * c], kk = kc4[2 * c + 1];
+        const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
+        const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
+        asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
+        const uint32_t h0 = hi_or_lo(x0, x4, negk), h1 = hi_or_lo(x1, x5, negk);
+        const uint32_t h2 = hi_or_lo(x2, x6, negk), h3 = hi_or_lo(x3, x7, negk);
+        qx[c] = as_h8(h0 & mask_x, h1 & mask_x, h2 & mask_x, h3 & mask_x);
+        qy[c] = as_h8(h0 & mask_y, h1 & mask_y, h2 & mask_y, h3 & mask_y);
+      }
+    }
+    asum = add_xor32(add_xor16(asum));             // over all 128 channels of column n
+    const float asum_c = 0.125f * asum;            // the centring term, 8 / 64 * asum
+
+    // ---- scores: 8 token blocks x (4 channel blocks of the first tile, 4 of the second)
+    float4v sc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t wx[4] = {cx.kw[mb].x, cx.kw[mb].y, cx.kw[mb].z, cx.kw[mb].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(wx[c], kcon), qx[c], acc, 0, 0, 0);
+      if (has_y) {
+        const uint32_t wy[4] = {cy.kw[mb].x, cy.kw[mb].y, cy.kw[mb].z, cy.kw[mb].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(wy[c], kcon), qy[c], acc, 0, 0, 0);
+      }
+      sc[mb] = acc;
+    }
+    if (nrx != nullptr) load_keys(nrx, lo, cx);
+    if (nry != nullptr) load_keys(nry, lo, cy);
+    // hi + lo partial scores of this lane's two rows, then the log2-domain score per token
+    const float* ks = sm.f8[tcol] + kT;
+    const float* kz = sm.h16[tcol];
+    float v[8][2];
+    float tmax = -INFINITY;
+    const int tpos = kT * (i0 + 2 * p + tsel);     // position of token 0 of this column's tile
+    const bool masked = kCausal && tpos + kT - 1 > len - nq;
+    const int tlim = qlim - tpos;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const float snd0 = colhi ? sc[mb][2] : sc[mb][0];
+      const float snd1 = colhi ? sc[mb][3] : sc[mb][1];
+      const float own0 = colhi ? sc[mb][0] : sc[mb][2];
+      const float own1 = colhi ? sc[mb][1] : sc[mb][3];
+      const float d0 = own0 + dpp_half_mirror(snd0), d1 = own1 + dpp_half_mirror(snd1);
+      const int t0 = 16 * mb + 4 * s + ih;
+      const float2 ks2 = *reinterpret_cast<const float2*>(ks + t0);
+      const float2 kz2 = *reinterpret_cast<const float2*>(kz + t0);
+      v[mb][0] = fmaf(ks2.x, d0 + asum_c, kz2.x * asum);
+      v[mb][1] = fmaf(ks2.y, d1 + asum_c, kz2.y * asum);
+      if (masked) {
+        v[mb][0] = t0 > tlim ? -INFINITY : v[mb][0];
+        v[mb][1] = t0 + 1 > tlim ? -INFINITY : v[mb][1];
+      }
+      if (!col_live) {
+        v[mb][0] = -INFINITY;
+        v[mb][1] = -INFINITY;
+      }
+      tmax = fmaxf(tmax, fmaxf(v[mb][0], v[mb][1]));
+    }
+    tmax = fmaxf(tmax, dpp_half_mirror(tmax));     // hi and lo columns of the head
+    tmax = fmaxf(tmax, dpp_ror8(tmax));            // the head's columns of the other tile
+    tmax = max_xor32(max_xor16(tmax));             // all score rows
+    const bool upd = tmax > m_run + kLazy;         // also true on the first pair
+    const float mnew = upd ? tmax : m_run;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+    const bool rescale = __any(upd) && p > 0;      // wave-uniform
+    float psum = 0.0f, beta = 0.0f, wsum = 0.0f;
+    // probabilities -> operand rows: row n holds hi(32 p s-hat^V) (positions 0-3) or lo
+    // (positions 4-7) of its tile's tokens; element e of token block kb is token
+    // 32 kb + 16 (e / 4) + 4 s + e % 4
+    const float* vs = sm.f8[tcol] + 3 * kT;
+    const float* vz = sm.h16[tcol] + kT;
+    half8 wx[4], wy[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t u[4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mb = 2 * kb + h2, t0 = 16 * mb + 4 * s + ih;
+        const float2 vs2 = *reinterpret_cast<const float2*>(vs + t0);
+        const float2 vz2 = *reinterpret_cast<const float2*>(vz + t0);
+        const float p0 = __builtin_amdgcn_exp2f(v[mb][0] - mnew);
+        const float p1 = __builtin_amdgcn_exp2f(v[mb][1] - mnew);
+        psum += p0 + p1;
+        beta = fmaf(p0, vz2.x, fmaf(p1, vz2.y, beta));
+        const float w0 = p0 * vs2.x, w1 = p1 * vs2.y;
+        wsum += w0 + w1;
+        const uint32_t hp = pack_h2(w0, w1);
+        const uint32_t lp = lo_of(hp, w0, w1);
+        const uint32_t rcv = dpp_half_mirror_u(colhi ? lp : hp);
+        u[2 * h2] = colhi ? hp : rcv;              // rows 0, 1 of block mb
+        u[2 * h2 + 1] = colhi ? rcv : lp;          // rows 2, 3
+      }
+      wx[kb] = as_h8(u[0] & mask_x, u[1] & mask_x, u[2] & mask_x, u[3] & mask_x);
+      wy[kb] = as_h8(u[0] & mask_y, u[1] & mask_y, u[2] & mask_y, u[3] & mask_y);
+    }
+    // per tile and head: hi and lo columns, all score rows; psum also over both tiles
+    psum += dpp_half_mirror(psum);
+    beta += dpp_half_mirror(beta);
+    wsum += dpp_half_mirror(wsum);
+    psum += dpp_ror8(psum);
+    psum = add_xor32(add_xor16(psum));
+    beta = add_xor32(add_xor16(beta));
+    wsum = add_xor32(add_xor16(wsum));
+    constexpr float kVOut = kVBits == 4 ? 0.5f : 0.125f;
+    beta = fmaf(-kVOut, wsum, beta);
+    l_run = fmaf(alpha, l_run, psum);
+    m_run = mnew;
+    if (s == 0) {
+      sm.alpha[n] = alpha;
+      sm.beta[n] = colhi ? beta : 0.0f;            // the zero-point term enters the hi row once
+    }
+
+    // ---- output: 8 channel blocks x (4 token blocks of each tile); rows 4 s + i of channel
+    // 16 nb + n; each block's accumulator is folded with the c-hat^V of its rows' tile
+    {
+      const float4 b4 = *reinterpret_cast<const float4*>(sm.beta + 4 * s);
+      const float br[4] = {b4.x, b4.y, b4.z, b4.w};
+      if (rescale) {
+        const float4 a4 = *reinterpret_cast<const float4*>(sm.alpha + 4 * s);
+        const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[nb][i] *= ar[i];
+        }
+      }
+      const float* vc = sm.f8[trow] + 2 * kT;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float4v po = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              wx[kb], value_operand<kVBits>(cx.vw, nb, kb, vmask, kmask, one16), po, 0, 0, 0);
+        if (has_y) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            po = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                wy[kb], value_operand<kVBits>(cy.vw, nb, kb, vmask, kmask, one16), po, 0, 0, 0);
+        }
+        const float cv = vc[16 * nb + n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], kVOut, br[i]), oacc[nb][i]);
+      }
+    }
+    if (nrx != nullptr) load_values(nrx, lo, cx);
+    if (nry != nullptr) load_values(nry, lo, cy);
+  }
+
+  // ---- partial per virtual head: rows h (first tile, hi), 7 - h (first, lo), 8 + h and
+  // 15 - h (second tile) sit in lane groups s = 0, 1, 2, 3 at register h, 3 - h, h, 3 - h
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = add_xor32(oacc[nb][i]);     // + the other tile's row
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = (s & 1) ? x[3 - i] : x[i];   // lo rows in head order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float both = add_xor16(y[i]);                           // + the lo part
+      if (s == 0 && i < nh)
+        partials[(row_of(i) * nsplit + split) * kPartialFloats + 2 + 16 * nb + n] = both;
+    }
+  }
+  if (s == 0 && colhi && tsel == 0 && colv) {
+    float* pp = partials + (row_of(hh) * nsplit + split) * kPartialFloats;
+    pp[0] = bad ? NAN : m_run;
+    pp[1] = bad ? NAN : l_run;
+  }
+}
+
 // grid (nq * hq, batch), one wave per (sequence, query token, query head): the staging tokens
 // the query token sees (exact fp32
 // attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
@@ -622,6 +1025,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 // are broadcast from the lane that computed them.
 constexpr int kMThreads = 64;
 constexpr int kMaxSplits = 64;
+#ifndef KVARN_PAIR_MIN_TILES_PER_CU
+#define KVARN_PAIR_MIN_TILES_PER_CU 64
+#endif
+constexpr int kPairMinTilesPerCU = KVARN_PAIR_MIN_TILES_PER_CU;
 constexpr int kMergePreload = 8;          // splits whose o~ is loaded before the weights exist
 constexpr int kStageChunk = 16;           // staging value rows loaded per round
 
@@ -1162,7 +1569,36 @@ int device_compute_units() {
   return cus;
 }
 
-int decode_splits(int batch, int hkv, int max_blocks) {
+// The paired-tile kernel serves at most four virtual heads per KV head with 2-bit values, and
+// only when the table holds enough tiles for about four one-wave chunks per SIMD slot: with fewer
+// tiles than that, one tile per wave of four-wave workgroups fills the device better.
+bool pairs_mode(int virtual_heads, int v_bits, int batch, int hkv, int max_blocks) {
+  const long long tiles = (long long)batch * hkv * max_blocks;
+  return virtual_heads <= 4 && v_bits == 2 && tiles >= kPairMinTilesPerCU * device_compute_units();
+}
+
+// Tiles per chunk of the paired-tile kernel for a plan of `splits` chunks (even, so only a
+// chunk's last pair can be single).
+int pairs_chunk(int max_blocks, int splits) {
+  const int c = (max_blocks + splits - 1) / splits;
+  return c + (c & 1);
+}
+
+int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel) {
+  if (pair_kernel) {
+    // one wave per chunk: about four waves per SIMD slot in all (two slots per SIMD) for the
+    // table width, chunks of an even number of tiles, at most kMaxSplits chunks per sequence
+    const long long work = (long long)batch * hkv * max_blocks;
+    const long long waves = 32LL * device_compute_units();
+    long long c = (work + waves - 1) / waves;
+    const long long cmin = (max_blocks + kMaxSplits - 1) / kMaxSplits;
+    if (c < cmin) c = cmin;
+    if (c < 2) c = 2;
+    c += c & 1;
+    long long s = (max_blocks + c - 1) / c;
+    if (s < 1) s = 1;
+    return (int)s;
+  }
   const long long pairs = (long long)batch * hkv > 0 ? (long long)batch * hkv : 1;
   // two workgroups per compute unit (2 waves per SIMD)
   const long long target = 2LL * device_compute_units();
@@ -1193,10 +1629,19 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
   const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4> : decode_tiles_kernel<false, 2>)
-                      : (v_bits == 4 ? decode_tiles_kernel<true, 4> : decode_tiles_kernel<true, 2>);
-  hipLaunchKernelGGL(kern, grid, dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool, num_blocks,
-                     block_table, max_blocks, seq_lens, sm_scale, partials, sg);
+  if (pairs_mode(hq / hkv * nq, v_bits, batch, hkv, max_blocks)) {   // decode_pairs_kernel
+    auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
+    const int chunk = pairs_chunk(max_blocks, splits);
+    hipLaunchKernelGGL(kern, dim3(splits, hkv, batch), dim3(64), 0, stream, q, hq, hkv, nq,
+                       pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale, partials,
+                       sg, chunk);
+  } else {
+    auto kern = nq == 1
+        ? (v_bits == 4 ? decode_tiles_kernel<false, 4> : decode_tiles_kernel<false, 2>)
+        : (v_bits == 4 ? decode_tiles_kernel<true, 4> : decode_tiles_kernel<true, 2>);
+    hipLaunchKernelGGL(kern, grid, dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool, num_blocks,
+                       block_table, max_blocks, seq_lens, sm_scale, partials, sg);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nq == 1)

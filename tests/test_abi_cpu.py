@@ -60,7 +60,8 @@ def test_value_bit_presets(lib):
     bad = kv.default_config(8, v_bits=4)
     bad.k_bits = 2
     assert kv.tile_bytes(bad) == 0
-    # the workspace does not depend on the preset
+    # with more than four virtual heads per KV head the workspace does not depend on the
+    # preset (both use the four-wave tile kernel)
     assert (kv.decode_workspace_bytes(c4, 16, 64, 128)
             == kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 128))
 
@@ -74,22 +75,31 @@ def test_workspace_bytes_depends_only_on_sizes_and_device(lib):
 
 
 def test_workspace_follows_the_split_plan(lib):
-    """The workspace holds 130 floats per (sequence, query head, split). Splits: two workgroups
-    per compute unit (this host has no GPU: the plan assumes 256 compute units), at least two
-    tiles per wave unless that leaves fewer than two workgroups per compute unit (then one),
-    and at most 32 full tiles per split for the longest table (its last entry is the staging
-    tile)."""
+    """The workspace holds 130 floats per (sequence, query head, split). This host has no GPU:
+    the plan assumes 256 compute units.
+    Four-wave tile kernel (more than four virtual heads per KV head, 4-bit values, or fewer
+    than 64 table entries x KV heads x sequences per compute unit): two workgroups per compute
+    unit, at least two tiles per wave unless that leaves fewer than two workgroups per compute
+    unit (then one), at most 32 full tiles per split for the longest table (its last entry is
+    the staging tile).
+    Paired-tile kernel (otherwise): one wave per chunk of an even number of tiles, about 32
+    chunks per compute unit for the table's entries, at most 64 chunks per sequence."""
     per = 130 * 4
-    # 16K context, batch 16, 8 KV heads: 512 / 128 pairs = 4 splits of 32 tiles
+    # 16K context, batch 16, 8 KV heads, group 8: 512 / 128 pairs = 4 splits of 32 tiles
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 4 * per
-    # 4K context, batch 8 (33 entries): 8 splits wanted; two tiles per wave would allow 4, or
-    # 256 workgroups (one per compute unit), so one tile per wave is allowed: 8
+    # 4K context, batch 8 (33 entries; 2,112 < 16,384): 8 splits wanted; two tiles per wave
+    # would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
     assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
-    # 4K context, batch 64: 512 (sequence, KV head) pairs fill the device with one split
-    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 1 * per
-    # ragged batch up to 32K tokens, batch 32, 10 KV heads: 2 splits wanted, 256 full tiles
-    # need 8 splits of at most 32
-    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 8 * per
+    # 4K context, batch 64 (16,896 entries), group 4: paired tiles, chunks of
+    # ceil(16,896 / 8,192) = 3 -> 4 tiles, 9 chunks per sequence
+    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 9 * per
+    # the same with 4-bit values: tile kernel, 512 pairs fill the device with one split
+    assert kv.decode_workspace_bytes(kv.default_config(8, v_bits=4), 64, 32, 33) == 64 * 32 * per
+    # ragged batch up to 32K tokens, batch 32, 10 KV heads, group 4 (82,240 entries): paired
+    # tiles, chunks of ceil(82,240 / 8,192) = 11 -> 12 tiles, 22 chunks per sequence
+    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 22 * per
+    # the same batch with group 8: tile kernel, 2 splits wanted, 256 full tiles need 8
+    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 80, 257) == 32 * 80 * 8 * per
 
 
 def test_multi_workspace_and_query_token_limits(lib):

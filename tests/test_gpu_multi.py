@@ -151,3 +151,23 @@ def test_multi_at_the_split_limit():
     err = np.abs(got - ref).max()
     _say(f"multi at 64 splits, Q=16: max abs err {err:.3g}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("name,over,tails,nq", [
+    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=4), [0, 5, 127], 2),      # 2 x 2 rows
+    ("qwen3-4b", dict(batch=2, ctx=640, hkv=2, hq=2), [100, 9], 4),          # 1 x 4 rows
+    ("qwen3-4b", dict(batch=2, ctx=768, hkv=2, hq=2), [0, 1], 3),            # 1 x 3 rows
+])
+def test_multi_pair_kernel_matches_oracle(name, over, tails, nq):
+    """Several query tokens with at most four virtual heads per KV head in the paired-tile
+    kernel (a wide block table selects it), causal masks included."""
+    from test_gpu_parity import widen
+    sp = gen.spec(name, **over)
+    pool, bt, lens, sk, sv, _, sm = _decode_case(sp, tails)
+    q = gen.query_tokens(sp, nq)
+    cfg = kv.default_config(sp.hkv)
+    got = gpu_multi(cfg, q, pool, widen(bt, sp.hkv), lens, sk, sv, sm)
+    ref = oatt.decode_attention_multi(q, pool, bt, lens, sk, sv, sm)
+    err = np.abs(got - ref).max()
+    _say(f"multi pair kernel {name} {over} tails={tails} nq={nq}: max abs err {err:.3g}")
+    assert err <= TOL
