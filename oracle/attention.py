@@ -18,10 +18,10 @@ Test infrastructure only (see the package header).
 import numpy as np
 
 from . import codec
-from .hadamard import H128
+from .hadamard import H_OF
 
 T = codec.T
-D = codec.D
+D = codec.D   # the pages' head dimension; every function takes D from its arguments
 
 
 # ------------------------------------------------------------------ cache-level operations
@@ -30,14 +30,17 @@ D = codec.D
 def quantize_tiles(k, v, dst_blocks, pool, iters: int = codec.DEFAULT_ITERS, signs=None):
     """Quantise whole prefill tiles into the block pool, in place.
 
-    k, v: [n_tiles * 128, Hkv, 128] fp16 values; tile i holds tokens 128 i .. 128 i + 127 and
-    goes to block dst_blocks[i]; pool: uint8 [num_blocks, Hkv, record bytes] (13312 for 2-bit
-    values, 17408 for 4-bit: the pool's record size selects the preset)."""
+    k, v: [n_tiles * 128, Hkv, D] fp16 values (D = 64, 128 or 256); tile i holds tokens
+    128 i .. 128 i + 127 and goes to block dst_blocks[i]; pool: uint8 [num_blocks, Hkv, record
+    bytes] (with D = 128: 13312 for 2-bit values, 17408 for 4-bit; the pool's record size
+    selects the preset and must match D)."""
     k = np.asarray(k)
     v = np.asarray(v)
     n_tiles = len(dst_blocks)
     hkv = k.shape[1]
-    vb = codec.v_bits_of_record(pool.shape[-1])
+    d, vb = codec.geometry_of_record(pool.shape[-1])
+    if k.shape[2] != d or v.shape[2] != d:
+        raise ValueError("record size does not match the head dimension")
     for i in range(n_tiles):
         rows = slice(T * i, T * i + T)
         for h in range(hkv):
@@ -50,10 +53,12 @@ def append_token(k_new, v_new, positions, block_table, staging_k, staging_v, poo
     """Write one new token per sequence into its staging tile; when the token is the 128th of
     its tile, quantise the staging tile into block_table[b][position // 128]. In place.
 
-    k_new, v_new: [B, Hkv, 128]; positions: [B] 0-based index of the new token, negative =
-    skip this row; staging_k, staging_v: [B, Hkv, 128, 128]. The pool's record size selects
-    the preset, as in quantize_tiles()."""
-    vb = codec.v_bits_of_record(pool.shape[-1])
+    k_new, v_new: [B, Hkv, D]; positions: [B] 0-based index of the new token, negative =
+    skip this row; staging_k, staging_v: [B, Hkv, 128, D]. The pool's record size selects
+    the preset and must match D, as in quantize_tiles()."""
+    d, vb = codec.geometry_of_record(pool.shape[-1])
+    if staging_k.shape[-1] != d:
+        raise ValueError("record size does not match the head dimension")
     for b, pos in enumerate(np.asarray(positions)):
         if pos < 0:
             continue
@@ -94,12 +99,12 @@ def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_sc
                      signs=None):
     """Plain form: dequantise every packed tile, then exact softmax attention.
 
-    q: [B, Hq, 128]; returns [B, Hq, 128] float64. A sequence of length 0 gives zeros."""
+    q: [B, Hq, D]; returns [B, Hq, D] float64. A sequence of length 0 gives zeros."""
     q = np.asarray(q, dtype=np.float64)
-    bsz, hq, _ = q.shape
+    bsz, hq, d = q.shape
     hkv = staging_k.shape[1]
     group = hq // hkv
-    out = np.zeros((bsz, hq, D))
+    out = np.zeros((bsz, hq, d))
     for b in range(bsz):
         for g in range(hkv):
             keys, values = _sequence_kv(pool, block_table, staging_k, staging_v, b, g,
@@ -111,15 +116,15 @@ def decode_attention(q, pool, block_table, seq_lens, staging_k, staging_v, sm_sc
 
 def decode_attention_multi(q, pool, block_table, seq_lens, staging_k, staging_v, sm_scale,
                            signs=None):
-    """Several query tokens per sequence (reading R25): q [B, Q, Hq, 128] holds the last Q of
+    """Several query tokens per sequence (reading R25): q [B, Q, Hq, D] holds the last Q of
     each sequence's L tokens; query token i sits at position L - Q + i and attends to
     positions 0 .. L - Q + i of the same cache (causal; an empty range gives zeros).
-    Returns [B, Q, Hq, 128] float64; Q = 1 is decode_attention()."""
+    Returns [B, Q, Hq, D] float64; Q = 1 is decode_attention()."""
     q = np.asarray(q, dtype=np.float64)
-    bsz, nq, hq, _ = q.shape
+    bsz, nq, hq, d = q.shape
     hkv = staging_k.shape[1]
     group = hq // hkv
-    out = np.zeros((bsz, nq, hq, D))
+    out = np.zeros((bsz, nq, hq, d))
     for b in range(bsz):
         length = int(seq_lens[b])
         for g in range(hkv):
@@ -140,10 +145,10 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
     zero-point into the probabilities, the per-channel value scale into the per-tile partial
     output, and the rotation back onto the summed output. Must equal decode_attention()."""
     q = np.asarray(q, dtype=np.float64)
-    bsz, hq, _ = q.shape
+    bsz, hq, d = q.shape
     hkv = staging_k.shape[1]
     group = hq // hkv
-    out = np.zeros((bsz, hq, D))
+    out = np.zeros((bsz, hq, d))
     for b in range(bsz):
         length = int(seq_lens[b])
         n_full, tail = length // T, length % T
@@ -154,7 +159,7 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
             for h in range(g * group, (g + 1) * group):
                 if length == 0:
                     continue
-                q_rot = (q[b, h] if signs is None else q[b, h] * signs) @ H128
+                q_rot = (q[b, h] if signs is None else q[b, h] * signs) @ H_OF[d]
                 scores = []
                 for r in recs:
                     qt = q_rot * r["k"]["c_hat"]
@@ -163,12 +168,12 @@ def decode_attention_folded(q, pool, block_table, seq_lens, staging_k, staging_v
                 scores.append(sm_scale * (sk @ q[b, h]))
                 s = np.concatenate(scores)
                 p = np.exp(s - s.max())
-                o_rot = np.zeros(D)
+                o_rot = np.zeros(d)
                 for i, r in enumerate(recs):
                     pt = p[T * i:T * i + T]
                     o_rot += r["v"]["c_hat"] * ((pt * r["v"]["s_hat"]) @ r["v"]["codes"]
                                                 + np.dot(pt, r["v"]["z_hat"]))
-                o_back = o_rot @ H128
+                o_back = o_rot @ H_OF[d]
                 if signs is not None:
                     o_back = o_back * signs
                 o = o_back + p[T * n_full:] @ sv
@@ -189,10 +194,10 @@ def decode_attention_fp16(q, k_tiles, v_tiles, block_table, seq_lens, staging_k,
     channel); block_table, seq_lens, staging and q as in decode_attention(). The same cache
     model: floor(L/128) blocks, then L mod 128 staging tokens. Returns [B, Hq, 128] float64."""
     q = np.asarray(q, dtype=np.float64)
-    bsz, hq, _ = q.shape
+    bsz, hq, d = q.shape
     hkv = staging_k.shape[1]
     group = hq // hkv
-    out = np.zeros((bsz, hq, D))
+    out = np.zeros((bsz, hq, d))
     for b in range(bsz):
         length = int(seq_lens[b])
         n_full, tail = length // T, length % T

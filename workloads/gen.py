@@ -49,6 +49,7 @@ class Spec:
     ragged: tuple = ()            # (lo, hi) context range, rounded to a multiple of 128
     steps: int = 0                # append steps (write-stream workload)
     extra: dict = field(default_factory=dict)
+    head_dim: int = D             # channels per head: 128 (the pages' preset), 64 or 256
 
     @property
     def group(self) -> int:
@@ -85,17 +86,18 @@ def _rng(sp: Spec, *key) -> np.random.Generator:
 
 
 def head_params(sp: Spec) -> np.ndarray:
-    """Per-(KV head, K|V, channel) multipliers, float32 [Hkv, 2, 128]."""
+    """Per-(KV head, K|V, channel) multipliers, float32 [Hkv, 2, head_dim]."""
     rng = _rng(sp, 0)
-    mult = np.ones((sp.hkv, 2, D), np.float32)
+    d = sp.head_dim
+    mult = np.ones((sp.hkv, 2, d), np.float32)
     if sp.lognormal:
-        mult *= np.exp(rng.standard_normal((sp.hkv, 2, D))).astype(np.float32)
+        mult *= np.exp(rng.standard_normal((sp.hkv, 2, d))).astype(np.float32)
     for h in range(sp.hkv):
         for kv in range(2):
             if sp.outlier_channels:
                 picks = np.array(sp.outlier_channels)
             elif sp.outlier_count:
-                picks = rng.choice(D, size=sp.outlier_count, replace=False)
+                picks = rng.choice(d, size=sp.outlier_count, replace=False)
             else:
                 picks = np.array([], dtype=np.int64)
             mult[h, kv, picks] *= sp.outlier_gain
@@ -113,8 +115,8 @@ def seq_lens(sp: Spec) -> np.ndarray:
 
 def _sequence_kv(sp: Spec, b: int, length: int, mult: np.ndarray):
     rng = _rng(sp, 100 + b)
-    k = rng.standard_normal((length, sp.hkv, D), dtype=np.float32) * mult[None, :, 0, :]
-    v = rng.standard_normal((length, sp.hkv, D), dtype=np.float32) * mult[None, :, 1, :]
+    k = rng.standard_normal((length, sp.hkv, sp.head_dim), dtype=np.float32) * mult[None, :, 0, :]
+    v = rng.standard_normal((length, sp.hkv, sp.head_dim), dtype=np.float32) * mult[None, :, 1, :]
     if sp.drift_sigma:
         k *= np.exp(sp.drift_sigma * rng.standard_normal((length, sp.hkv, 1), dtype=np.float32))
         v *= np.exp(sp.drift_sigma * rng.standard_normal((length, sp.hkv, 1), dtype=np.float32))
@@ -133,10 +135,10 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None, workers: int = 1)
     """Prefill state of the workload.
 
     Returns a dict with
-      k, v          fp16 [n_tiles * 128, Hkv, 128]: the full tiles of the chosen sequences,
+      k, v          fp16 [n_tiles * 128, Hkv, head_dim]: the full tiles of the chosen sequences,
                     concatenated sequence after sequence (what kvarn_quantize_tiles reads)
       dst_blocks    int32 [n_tiles]: destination block of each of those tiles
-      tail_k/tail_v list (per chosen sequence) of fp16 [len % 128, Hkv, 128] staging tokens
+      tail_k/tail_v list (per chosen sequence) of fp16 [len % 128, Hkv, head_dim] staging tokens
       block_table   int32 [B, max_blocks] (room for max_new_tokens more tokens per sequence)
       seq_lens      int32 [B]
       num_blocks    int
@@ -168,7 +170,7 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None, workers: int = 1)
         dst.append(block_table[b, :n_full])
         tk.append(k[n_full * T:])
         tv.append(v[n_full * T:])
-    empty = np.zeros((0, sp.hkv, D), np.float16)
+    empty = np.zeros((0, sp.hkv, sp.head_dim), np.float16)
     return dict(k=np.concatenate(ks) if ks else empty, v=np.concatenate(vs) if vs else empty,
                 dst_blocks=np.concatenate(dst).astype(np.int32) if dst else np.zeros(0, np.int32),
                 tail_k=tk, tail_v=tv, block_table=block_table, seq_lens=lens,
@@ -177,9 +179,9 @@ def prefill(sp: Spec, max_new_tokens: int = 0, sequences=None, workers: int = 1)
 
 def tiles_by_block(st: dict, hkv: int) -> tuple:
     """The prefill tiles of a prefill() state as block-indexed arrays [num_blocks, Hkv, 128,
-    128] fp16 (K and V; blocks that hold no prefill tile are zero): the logical content of an
-    unquantised paged cache."""
-    kt = np.zeros((st["num_blocks"], hkv, T, D), np.float16)
+    head_dim] fp16 (K and V; blocks that hold no prefill tile are zero): the logical content
+    of an unquantised paged cache."""
+    kt = np.zeros((st["num_blocks"], hkv, T, st["k"].shape[2]), np.float16)
     vt = np.zeros_like(kt)
     for i, blk in enumerate(st["dst_blocks"]):
         kt[blk] = np.transpose(st["k"][T * i:T * (i + 1)], (1, 0, 2))
@@ -188,65 +190,69 @@ def tiles_by_block(st: dict, hkv: int) -> tuple:
 
 
 def query(sp: Spec, dense: bool = False) -> np.ndarray:
-    """Decode queries fp16 [B, Hq, 128], N(0, 1) (reading R21).
+    """Decode queries fp16 [B, Hq, head_dim], N(0, 1) (reading R21).
 
     dense=True scales each query head so that its scores against a typical key have a
-    standard deviation near 1 under the default 1/sqrt(128) softmax scale."""
-    q = _rng(sp, 3).standard_normal((sp.batch, sp.hq, D), dtype=np.float32)
+    standard deviation near 1 under the default 1/sqrt(head_dim) softmax scale."""
+    q = _rng(sp, 3).standard_normal((sp.batch, sp.hq, sp.head_dim), dtype=np.float32)
     if dense:
         mult = head_params(sp)
         key_rms = np.sqrt(np.sum(mult[:, 0, :].astype(np.float64) ** 2, axis=1))  # [Hkv]
-        scale = np.sqrt(D) / key_rms
+        scale = np.sqrt(sp.head_dim) / key_rms
         q *= np.repeat(scale, sp.group)[None, :, None].astype(np.float32)
     return q.astype(np.float16)
 
 
 def query_tokens(sp: Spec, n_query: int, dense: bool = False) -> np.ndarray:
-    """Queries of n_query tokens per sequence, fp16 [B, n_query, Hq, 128] (reading R25): the
+    """Queries of n_query tokens per sequence, fp16 [B, n_query, Hq, head_dim] (R25): the
     last token's queries are query(sp, dense); the earlier ones are drawn the same way from
     their own stream."""
-    q = np.empty((sp.batch, n_query, sp.hq, D), np.float16)
+    q = np.empty((sp.batch, n_query, sp.hq, sp.head_dim), np.float16)
     q[:, -1] = query(sp, dense)
     for i in range(n_query - 1):
-        x = _rng(sp, 6, i).standard_normal((sp.batch, sp.hq, D), dtype=np.float32)
+        x = _rng(sp, 6, i).standard_normal((sp.batch, sp.hq, sp.head_dim), dtype=np.float32)
         if dense:
             mult = head_params(sp)
             key_rms = np.sqrt(np.sum(mult[:, 0, :].astype(np.float64) ** 2, axis=1))
-            x *= np.repeat(np.sqrt(D) / key_rms, sp.group)[None, :, None].astype(np.float32)
+            x *= np.repeat(np.sqrt(sp.head_dim) / key_rms, sp.group)[None, :, None].astype(np.float32)
         q[:, i] = x.astype(np.float16)
     return q
 
 
 def feedback_maps(sp: Spec) -> dict:
-    """Fixed random orthogonal 128 x 128 maps (float32) of the autoregressive error probe: one
+    """Fixed random orthogonal head_dim x head_dim maps (float32) of the autoregressive error probe: one
     per KV head for keys and for values, one per query head for queries."""
     rng = _rng(sp, 7)
 
     def orth(n):
-        a = rng.standard_normal((n, D, D))
+        a = rng.standard_normal((n, sp.head_dim, sp.head_dim))
         qm, r = np.linalg.qr(a)
         return (qm * np.sign(np.diagonal(r, axis1=1, axis2=2))[:, None, :]).astype(np.float32)
     return dict(k=orth(sp.hkv), v=orth(sp.hkv), q=orth(sp.hq))
 
 
 def feedback_noise(sp: Spec, step: int) -> dict:
-    """Fresh N(0, 1) noise of probe step `step` (float32): k, v [B, Hkv, 128], q [B, Hq, 128]."""
+    """Fresh N(0, 1) noise of probe step `step` (float32): k, v [B, Hkv, head_dim], q [B, Hq,
+    head_dim]."""
     rng = _rng(sp, 8, step)
-    return dict(k=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
-                v=rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32),
-                q=rng.standard_normal((sp.batch, sp.hq, D), dtype=np.float32))
+    d = sp.head_dim
+    return dict(k=rng.standard_normal((sp.batch, sp.hkv, d), dtype=np.float32),
+                v=rng.standard_normal((sp.batch, sp.hkv, d), dtype=np.float32),
+                q=rng.standard_normal((sp.batch, sp.hq, d), dtype=np.float32))
 
 
 def rotation_sign_words(sp: Spec) -> np.ndarray:
-    """Four random 32-bit words (uint32): the optional per-channel sign flips before the
-    rotation, channel j negated when bit j % 32 of word j // 32 is set (reading R27)."""
-    return _rng(sp, 9).integers(0, 2 ** 32, size=4, dtype=np.uint64).astype(np.uint32)
+    """head_dim / 32 random 32-bit words (uint32): the optional per-channel sign flips before
+    the rotation, channel j negated when bit j % 32 of word j // 32 is set (reading R27)."""
+    return _rng(sp, 9).integers(0, 2 ** 32, size=sp.head_dim // 32,
+                                dtype=np.uint64).astype(np.uint32)
 
 
 def append_tokens(sp: Spec, step: int):
-    """New keys and values of append step `step`: fp16 [B, Hkv, 128] each."""
+    """New keys and values of append step `step`: fp16 [B, Hkv, head_dim] each."""
     mult = head_params(sp)
     rng = _rng(sp, 10 ** 6 + step)
-    k = rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32) * mult[None, :, 0, :]
-    v = rng.standard_normal((sp.batch, sp.hkv, D), dtype=np.float32) * mult[None, :, 1, :]
+    d = sp.head_dim
+    k = rng.standard_normal((sp.batch, sp.hkv, d), dtype=np.float32) * mult[None, :, 0, :]
+    v = rng.standard_normal((sp.batch, sp.hkv, d), dtype=np.float32) * mult[None, :, 1, :]
     return k.astype(np.float16), v.astype(np.float16)
