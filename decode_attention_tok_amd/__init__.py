@@ -14,7 +14,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvarn.so")
 
 TILE_TOKENS = 128
-HEAD_DIM = 128
+HEAD_DIM = 128            # the preset's head dimension; 64 and 256 are accepted too
+HEAD_DIMS = (64, 128, 256)
+SIGN_WORDS = 8
 TILE_BYTES = 13312        # record of the default preset kvarn_k4v2_g128
 TILE_BYTES_V4 = 17408     # record with 4-bit values (kvarn_k4v4_g128)
 
@@ -32,7 +34,7 @@ class Config(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_tokens", ctypes.c_int32), ("k_bits", ctypes.c_int32),
                 ("v_bits", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
-                ("rotation_signs", ctypes.c_uint32 * 4)]
+                ("rotation_signs", ctypes.c_uint32 * SIGN_WORDS)]
 
 
 _lib = None
@@ -107,17 +109,21 @@ def _stream(stream):
 
 
 def default_config(num_kv_heads: int, sinkhorn_iters: int = 4, rotation_signs=None,
-                   v_bits: int = 2) -> Config:
-    """The preset for num_kv_heads heads; rotation_signs: optional four 32-bit words of
-    per-channel sign flips before the rotation (None: the plain Hadamard); v_bits 2
-    (kvarn_k4v2_g128) or 4 (kvarn_k4v4_g128)."""
+                   v_bits: int = 2, head_dim: int = HEAD_DIM) -> Config:
+    """The preset for num_kv_heads heads; rotation_signs: optional head_dim / 32 32-bit words
+    of per-channel sign flips before the rotation (None: the plain Hadamard); v_bits 2
+    (kvarn_k4v2_g128) or 4 (kvarn_k4v4_g128); head_dim 64, 128 or 256."""
     cfg = Config()
     lib().kvarn_default_config(ctypes.byref(cfg), num_kv_heads)
     cfg.sinkhorn_iters = sinkhorn_iters
     cfg.v_bits = v_bits
+    cfg.head_dim = head_dim
     if rotation_signs is not None:
-        for i in range(4):
-            cfg.rotation_signs[i] = int(rotation_signs[i]) & 0xFFFFFFFF
+        words = list(rotation_signs)
+        if len(words) > SIGN_WORDS:
+            raise ValueError("at most 8 sign words")
+        for i, w in enumerate(words):
+            cfg.rotation_signs[i] = int(w) & 0xFFFFFFFF
     return cfg
 
 
@@ -156,8 +162,8 @@ def quantize_tiles(cfg: Config, k, v, dst_blocks, block_pool, token_stride=None,
 
 def append_token(cfg: Config, k_new, v_new, positions, block_table, staging_k, staging_v,
                  block_pool, stream=None):
-    """k_new, v_new fp16 [B, Hkv, 128]; positions int32 [B]; block_table int32 [B, max_blocks];
-    staging_k/v fp16 [B, Hkv, 128, 128]; block_pool uint8 blocks."""
+    """k_new, v_new fp16 [B, Hkv, D]; positions int32 [B]; block_table int32 [B, max_blocks];
+    staging_k/v fp16 [B, Hkv, 128, D]; block_pool uint8 blocks (D = cfg.head_dim)."""
     batch, max_blocks = block_table.shape
     num_blocks = block_pool.numel() // block_bytes(cfg)
     _check("kvarn_append_token",
@@ -169,7 +175,7 @@ def append_token(cfg: Config, k_new, v_new, positions, block_table, staging_k, s
 
 def decode_attention(cfg: Config, q, block_pool, block_table, seq_lens, staging_k, staging_v,
                      sm_scale, out, workspace, stream=None):
-    """q fp16 [B, Hq, 128]; out fp32 [B, Hq, 128]; workspace: a device tensor of at least
+    """q fp16 [B, Hq, D]; out fp32 [B, Hq, D]; workspace: a device tensor of at least
     decode_workspace_bytes(...) bytes."""
     batch, hq, _ = q.shape
     max_blocks = block_table.shape[1]
@@ -203,7 +209,7 @@ def decode_attention_noalloc(cfg: Config, q, block_pool, block_table, seq_lens, 
 
 def dequantize_tiles(cfg: Config, block_pool, src_blocks, k_out, v_out, stream=None):
     """Records of blocks src_blocks (int32 [n_tiles]) back to fp32 tiles in the original
-    space: k_out, v_out fp32 [n_tiles * 128, Hkv, 128]."""
+    space: k_out, v_out fp32 [n_tiles * 128, Hkv, D]."""
     num_blocks = block_pool.numel() // block_bytes(cfg)
     _check("kvarn_dequantize_tiles",
            lib().kvarn_dequantize_tiles(ctypes.byref(cfg), _ptr(block_pool), num_blocks,
@@ -226,8 +232,8 @@ def decode_multi_workspace_bytes(cfg: Config, batch: int, num_q_heads: int, n_qu
 
 def decode_attention_multi(cfg: Config, q, block_pool, block_table, seq_lens, staging_k,
                            staging_v, sm_scale, out, workspace, stream=None):
-    """q fp16 [B, Q, Hq, 128]: the last Q tokens of each sequence, query token i at position
-    seq_lens[b] - Q + i, attending causally; out fp32 [B, Q, Hq, 128]; workspace of at least
+    """q fp16 [B, Q, Hq, D]: the last Q tokens of each sequence, query token i at position
+    seq_lens[b] - Q + i, attending causally; out fp32 [B, Q, Hq, D]; workspace of at least
     decode_multi_workspace_bytes(...) bytes."""
     batch, n_query, hq, _ = q.shape
     max_blocks = block_table.shape[1]

@@ -44,17 +44,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 kvarn_status check_config(const kvarn_config* cfg) {
   if (cfg == nullptr) return KVARN_ERR_NULL_ARG;
   if (cfg->num_kv_heads < 1) return KVARN_ERR_BAD_SHAPE;
-  if (cfg->head_dim != KVARN_HEAD_DIM || cfg->block_tokens != KVARN_TILE_TOKENS ||
-      cfg->k_bits != 4 || (cfg->v_bits != 2 && cfg->v_bits != 4) || cfg->sinkhorn_iters < 1 ||
+  if ((cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256) ||
+      cfg->block_tokens != KVARN_TILE_TOKENS || cfg->k_bits != 4 ||
+      (cfg->v_bits != 2 && cfg->v_bits != 4) || cfg->sinkhorn_iters < 1 ||
       cfg->sinkhorn_iters > 16)
     return KVARN_ERR_UNSUPPORTED;
+  for (int i = cfg->head_dim / 32; i < KVARN_SIGN_WORDS; ++i)   // words past the channels
+    if (cfg->rotation_signs[i] != 0) return KVARN_ERR_UNSUPPORTED;
   return KVARN_OK;
 }
 
 kvarn_status from_hip(hipError_t e) { return e == hipSuccess ? KVARN_OK : KVARN_ERR_HIP; }
 
-// Record bytes of a checked config: 8,192 key-code bytes, 2,048 per value bit, 1,024 metadata.
-size_t record_bytes(const kvarn_config* cfg) { return 8192u + 2048u * cfg->v_bits + 1024u; }
+// Record bytes of a checked config (head dimension D): 64 D key-code bytes, 16 D per value
+// bit, two metadata halves of D + 384 bytes.
+size_t record_bytes(const kvarn_config* cfg) {
+  const size_t d = (size_t)cfg->head_dim;
+  return 64u * d + 16u * d * (size_t)cfg->v_bits + 2u * (d + 384u);
+}
 
 constexpr long long kMaxGrid = 0x7FFFFFFFLL;
 
@@ -70,7 +77,7 @@ void kvarn_default_config(kvarn_config* cfg, int32_t num_kv_heads) {
   cfg->k_bits = 4;
   cfg->v_bits = 2;
   cfg->sinkhorn_iters = 4;
-  for (int i = 0; i < 4; ++i) cfg->rotation_signs[i] = 0;
+  for (int i = 0; i < KVARN_SIGN_WORDS; ++i) cfg->rotation_signs[i] = 0;
 }
 
 size_t kvarn_tile_bytes(const kvarn_config* cfg) {
@@ -91,14 +98,15 @@ kvarn_status kvarn_quantize_tiles(const kvarn_config* cfg, const void* k, const 
   if (n_tiles == 0) return KVARN_OK;
   if (k == nullptr || v == nullptr || dst_blocks == nullptr || block_pool == nullptr)
     return KVARN_ERR_NULL_ARG;
-  if (token_stride < (int64_t)cfg->num_kv_heads * KVARN_HEAD_DIM || token_stride % 8 != 0 ||
+  if (token_stride < (int64_t)cfg->num_kv_heads * cfg->head_dim || token_stride % 8 != 0 ||
       !aligned16(k) || !aligned16(v) || !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (2LL * cfg->num_kv_heads * n_tiles > kMaxGrid) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_quantize_tiles(
       static_cast<const __half*>(k), static_cast<const __half*>(v), token_stride, n_tiles,
       cfg->num_kv_heads, dst_blocks, static_cast<uint8_t*>(block_pool), num_blocks,
-      cfg->sinkhorn_iters, cfg->rotation_signs, cfg->v_bits, static_cast<hipStream_t>(stream)));
+      cfg->sinkhorn_iters, cfg->rotation_signs, cfg->v_bits, cfg->head_dim,
+      static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, const void* v_new,
@@ -122,7 +130,7 @@ kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k_new, cons
       block_table, max_blocks_per_seq, static_cast<__half*>(staging_k),
       static_cast<__half*>(staging_v), static_cast<uint8_t*>(block_pool), num_blocks,
       cfg->num_kv_heads, batch, cfg->sinkhorn_iters, cfg->rotation_signs, cfg->v_bits,
-      static_cast<hipStream_t>(stream)));
+      cfg->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
@@ -139,10 +147,10 @@ kvarn_status multi_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32
     return KVARN_ERR_BAD_SHAPE;
   const int splits = kvarn::decode_splits(
       batch, cfg->num_kv_heads, max_blocks_per_seq,
-      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, batch,
-                        cfg->num_kv_heads, max_blocks_per_seq));
+      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, cfg->head_dim,
+                        batch, cfg->num_kv_heads, max_blocks_per_seq));
   *bytes = (size_t)batch * (size_t)n_query * (size_t)num_q_heads * (size_t)splits *
-           kvarn::kPartialFloats * sizeof(float);
+           (size_t)kvarn::partial_floats(cfg->head_dim) * sizeof(float);
   return KVARN_OK;
 }
 
@@ -169,15 +177,15 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
   const int splits = kvarn::decode_splits(
       batch, cfg->num_kv_heads, max_blocks_per_seq,
-      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, batch,
-                        cfg->num_kv_heads, max_blocks_per_seq));
+      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, cfg->head_dim,
+                        batch, cfg->num_kv_heads, max_blocks_per_seq));
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_decode(
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads, n_query,
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,
       seq_lens, static_cast<const __half*>(staging_k), static_cast<const __half*>(staging_v),
       sm_scale, out, static_cast<float*>(workspace), splits, batch, cfg->rotation_signs,
-      cfg->v_bits, static_cast<hipStream_t>(stream)));
+      cfg->v_bits, cfg->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -259,11 +267,18 @@ kvarn_status kvarn_dequantize_tiles(const kvarn_config* cfg, const void* block_p
                                                  num_blocks, src_blocks, n_tiles,
                                                  cfg->num_kv_heads, k_out, v_out,
                                                  cfg->rotation_signs, cfg->v_bits,
-                                                 static_cast<hipStream_t>(stream)));
+                                                 cfg->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+// The unquantised comparison cache exists at head dimension 128 only.
+static kvarn_status check_fp16_config(const kvarn_config* cfg) {
+  const kvarn_status st = check_config(cfg);
+  if (st != KVARN_OK) return st;
+  return cfg->head_dim == KVARN_HEAD_DIM ? KVARN_OK : KVARN_ERR_UNSUPPORTED;
 }
 
 size_t kvarn_fp16_block_bytes(const kvarn_config* cfg) {
-  return check_config(cfg) == KVARN_OK
+  return check_fp16_config(cfg) == KVARN_OK
              ? (size_t)KVARN_FP16_RECORD_BYTES * (size_t)cfg->num_kv_heads
              : 0;
 }
@@ -272,7 +287,7 @@ kvarn_status kvarn_fp16_write_tiles(const kvarn_config* cfg, const void* k, cons
                                     int64_t token_stride, int32_t n_tiles,
                                     const int32_t* dst_blocks, void* block_pool,
                                     int64_t num_blocks, void* stream) {
-  kvarn_status st = check_config(cfg);
+  kvarn_status st = check_fp16_config(cfg);
   if (st != KVARN_OK) return st;
   if (n_tiles < 0 || num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
   if (n_tiles == 0) return KVARN_OK;
@@ -295,9 +310,10 @@ kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
                                          const void* staging_k, const void* staging_v,
                                          float sm_scale, float* out, void* workspace,
                                          size_t workspace_bytes, int32_t batch, void* stream) {
+  kvarn_status st = check_fp16_config(cfg);
+  if (st != KVARN_OK) return st;
   size_t need = 0;
-  kvarn_status st = kvarn_decode_workspace_bytes(cfg, batch, num_q_heads, max_blocks_per_seq,
-                                                 &need);
+  st = kvarn_decode_workspace_bytes(cfg, batch, num_q_heads, max_blocks_per_seq, &need);
   if (st != KVARN_OK) return st;
   if (num_blocks < 0) return KVARN_ERR_BAD_SHAPE;
   if (batch == 0) return KVARN_OK;
@@ -326,7 +342,8 @@ const char* kvarn_status_string(kvarn_status status) {
     case KVARN_ERR_NULL_ARG: return "a required pointer is NULL";
     case KVARN_ERR_BAD_SHAPE: return "a size or count is out of range, or a buffer is misaligned";
     case KVARN_ERR_UNSUPPORTED:
-      return "unsupported config (presets kvarn_k4v2_g128 and kvarn_k4v4_g128, head_dim 128)";
+      return "unsupported config (k_bits 4, v_bits 2 or 4, block_tokens 128, head_dim 64, 128 "
+             "or 256, sign words past head_dim / 32 zero; the fp16 cache: head_dim 128)";
     case KVARN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KVARN_ERR_HIP: return "HIP runtime error while launching";
     case KVARN_ERR_SCRATCH_LIMIT:

@@ -60,18 +60,22 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
+template <int kDim = 128>
 struct WaveMeta {                  // per-wave, per-tile metadata (fp32, factors folded in)
-  float f8[4 * kD];                // c-hat^K_j * pq | s-hat^K_t * kfac | c-hat^V_j | 32 s-hat^V_t
+  // c-hat^K_j * pq | s-hat^K_t * kfac | c-hat^V_j | 32 s-hat^V_t (2 kDim + 256 floats; the
+  // rest takes the writes of lanes that hold no metadata chunk)
+  float f8[kDim == 256 ? 1024 : 512];
   float h16[2 * kT];               // z-hat^K_t * kzfac | z-hat^V_t
   float alpha[16], beta[16];       // per-row rescale and zero-point term of the last tile
 };
 
+template <int kDim = 128>
 struct TileSmem {
-  float qrot[kHeadGroup][kD + 4];  // rotated queries (fp32); rows padded so the 8 heads read
-                                   // by one instruction start on different banks
-  WaveMeta wm[kWaves];
+  float qrot[kHeadGroup][kDim + 4];  // rotated queries (fp32); rows padded so the 8 heads
+                                     // read by one instruction start on different banks
+  WaveMeta<kDim> wm[kWaves];
   float comb_m[kWaves][kHeadGroup], comb_l[kWaves][kHeadGroup];
-  float comb_o[kWaves][kHeadGroup][kD];
+  float comb_o[kWaves][kHeadGroup][kDim];
   float red[kWaves];
 };
 
@@ -202,124 +206,247 @@ __device__ __forceinline__ uint32_t lo_of(uint32_t h, float a, float b) {
   return r;
 }
 
-template <int kVBits>
+// Code registers of one tile, per lane. Key words: token 16 mb + (lane % 16), channels
+// (kDim / 4)(lane / 16) + 8 c .. + 7 in word c. Value words of 32-token block kb: 2-bit codes,
+// the kDim / 32 section words (kDim / 32)(16 s + n) .. of the block (lane = 16 s + n); 4-bit
+// codes, the four words 4 lane .. of each 256-word quarter hb of the block (word 4 hb + d).
+template <int kVBits, int kDim = 128>
 struct TileRegs {
-  uint4 kw[8];        // key codes: token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31
-  uint4 vw[2 * kVBits];   // value codes: section words 256 m + 4 lane .. + 3, m = 0 .. 2 kVBits - 1
-  uint2 m8;           // 8 FP8 metadata bytes (see decode_meta)
+  static constexpr int kKW = kDim / 32;                            // key words per token block
+  static constexpr int kVW = kVBits == 2 ? kDim / 32 : kDim / 16;  // value words per 32 tokens
+  static constexpr int kM8 = kDim == 256 ? 2 : 1;                  // metadata chunks per lane
+  uint32_t kw[8][kKW];
+  uint32_t vw[4][kVW];
+  uint2 m8[kM8];      // 8 FP8 metadata bytes per chunk (see meta_chunk)
   uint2 m16;          // 4 fp16 zero-points
 };
 
 // Value codes of channel block nb (channel 16 nb + lane % 16) and token block kb as the B
-// operand of the output product: 2-bit codes as 1 + code / 4 (field nb of the section words
-// moved to mantissa bits 8..9 under exponent 1), 4-bit codes as 1 + code / 16 (field nb % 4 of
-// the words of channel half nb / 4 moved to bits 6..9). Normal and exact.
-template <int kVBits>
-__device__ __forceinline__ half8 value_operand(const uint4 (&vw)[2 * kVBits], int nb, int kb,
-                                               uint32_t vmask, uint32_t kmask, uint32_t one16) {
+// operand of the output product: 2-bit codes as 1 + code / 4 (the code's field moved to
+// mantissa bits 8..9 under exponent 1), 4-bit codes as 1 + code / 16 (field nb % 4 of the
+// words of quarter nb / 4 moved to bits 6..9). Normal and exact. Element pair d holds the
+// tokens 16 (d / 2) + 4 s + 2 (d % 2) + {0, 1} of the block.
+template <int kVBits, int kDim = 128>
+__device__ __forceinline__ half8 value_operand(const uint32_t (&vw)[4][TileRegs<kVBits, kDim>::kVW],
+                                               int nb, int kb, uint32_t vmask, uint32_t kmask,
+                                               uint32_t one16) {
   uint32_t f[4];
-  if constexpr (kVBits == 2) {
-    const uint32_t v4[4] = {vw[kb].x, vw[kb].y, vw[kb].z, vw[kb].w};
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (kVBits == 2 && kDim >= 128) {
+      // field nb % 8 (bits 2 (nb % 8) and 16 + 2 (nb % 8)) of word 4 (nb / 8) + d
+      const uint32_t w = vw[kb][4 * (nb >> 3) + d];
+      const int f8 = nb & 7;
+      const uint32_t x = f8 < 4 ? (w << (8 - 2 * f8)) : (w >> (2 * f8 - 8));
       f[d] = and_or(x, vmask, one16);
-    }
-  } else {
-    const uint4 ww = vw[2 * kb + (nb >> 2)];
-    const uint32_t v4[4] = {ww.x, ww.y, ww.z, ww.w};
-    const int kF = nb & 3;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t x = kF < 2 ? (v4[d] << (6 - 4 * kF)) : (v4[d] >> (4 * kF - 6));
+    } else if constexpr (kVBits == 2) {
+      // kDim = 64: word d / 2 holds the pair at bits 2 nb + 8 (d % 2) and 16 above
+      const uint32_t w = vw[kb][d >> 1];
+      const int bit = 2 * nb + 8 * (d & 1);
+      const uint32_t x = bit <= 8 ? (w << (8 - bit)) : (w >> (bit - 8));
+      f[d] = and_or(x, vmask, one16);
+    } else {
+      const uint32_t w = vw[kb][4 * (nb >> 2) + d];
+      const int kF = nb & 3;
+      const uint32_t x = kF < 2 ? (w << (6 - 4 * kF)) : (w >> (4 * kF - 6));
       f[d] = and_or(x, kmask, one16);
     }
   }
   return as_h8(f[0], f[1], f[2], f[3]);
 }
 
-// Per-lane byte offsets of the metadata a lane decodes. Lanes 0-15: c-hat^K, 16-31: s-hat^K,
-// 32-47: c-hat^V, 48-63: s-hat^V, 8 bytes each; lanes 0-31: z-hat^K, 32-63: z-hat^V, 4 each.
-template <int kVBits>
-__device__ __forceinline__ int meta8_off(int lane) {
-  using L = RecordLayout<kVBits>;
-  return (lane < 32 ? L::kKMetaOff : L::kVMetaOff) + ((lane >> 4) & 1) * kSRel + 8 * (lane & 15);
+// FP8 metadata chunk ci (8 bytes) of a record, and the factor its values are scaled by. The
+// FP8 bytes of a metadata half (c-hat: kDim, s-hat: 128) are contiguous, so chunk ci of the
+// table [c-hat^K | s-hat^K | c-hat^V | s-hat^V] is record byte kmeta + 8 ci in the key half
+// and vmeta + 8 ci' (ci' = ci - (kDim + 128) / 8) in the value half. Chunks past the table
+// (lanes without one) read chunk 0 and write into the unused tail of the table.
+template <int kVBits, int kDim>
+__device__ __forceinline__ uint32_t meta_chunk_off(int ci) {
+  using L = RecordLayout<kVBits, kDim>;
+  constexpr int kHalf = (kDim + 128) / 8;
+  if (ci >= 2 * kHalf) ci = 0;
+  return (uint32_t)(ci < kHalf ? L::kKMetaOff + 8 * ci : L::kVMetaOff + 8 * (ci - kHalf));
 }
-template <int kVBits>
-__device__ __forceinline__ int meta16_off(int lane) {
-  using L = RecordLayout<kVBits>;
-  return (lane < 32 ? L::kKMetaOff : L::kVMetaOff) + kZRel + 8 * (lane & 31);
+template <int kDim>
+__device__ __forceinline__ float meta_chunk_factor(int ci, float pq, float kfac) {
+  return ci < kDim / 8 ? pq : (ci < (kDim + 128) / 8 ? kfac : (ci < (2 * kDim + 128) / 8 ? 1.0f : 32.0f));
 }
 
 // Per-lane byte offsets (unsigned, so a load is a scalar tile base plus a 32-bit lane offset):
-// key codes of token 16 mb + (lane % 16), channels 32 (lane / 16) .. + 31 at koff + 1024 mb;
-// value-code section words 256 m + 4 lane .. + 3 at voff + 1024 m.
+// key codes of token 16 mb + (lane % 16) at koff + 8 kDim mb (koff4 = koff + 4096 serves
+// mb >= 4 at kDim = 128, within the 12-bit immediate); value-code words of token block kb at
+// voff + 8 kDim kb (2-bit) or voff + 1024 ((kDim / 64) kb + hb) (4-bit); metadata chunks at
+// off8[], zero-points at off16 (lanes 0-31 z-hat^K, 32-63 z-hat^V, 8 bytes each).
+template <int kDim>
 struct LaneOffsets {
-  uint32_t koff, koff4, voff, off8, off16;
+  uint32_t koff, koff4, voff, off8[kDim == 256 ? 2 : 1], off16;
 };
 
-template <int kVBits>
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-  LaneOffsets o;
-  o.koff = kKCodesOff + (uint32_t)(lane & 15) * 64u + 16u * (uint32_t)(lane >> 4);
+template <int kVBits, int kDim = 128>
+__device__ __forceinline__ LaneOffsets<kDim> lane_offsets(int lane) {
+  using L = RecordLayout<kVBits, kDim>;
+  LaneOffsets<kDim> o;
+  o.koff = (uint32_t)(lane & 15) * (kDim / 2) + (kDim / 8) * (uint32_t)(lane >> 4);
   o.koff4 = o.koff + 4096u;
-  o.voff = kVCodesOff + 16u * (uint32_t)lane;
-  o.off8 = (uint32_t)meta8_off<kVBits>(lane);
-  o.off16 = (uint32_t)meta16_off<kVBits>(lane);
+  o.voff = L::kVCodes + (kVBits == 2 ? (kDim / 8) : 16) * (uint32_t)lane;
+  o.off8[0] = meta_chunk_off<kVBits, kDim>(lane);
+  if constexpr (kDim == 256) o.off8[1] = meta_chunk_off<kVBits, kDim>(lane + 64);
+  o.off16 = (uint32_t)((lane < 32 ? L::kKMetaOff : L::kVMetaOff) + L::kZ + 8 * (lane & 31));
   return o;
 }
 
-template <int kVBits>
-__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, const LaneOffsets& o,
-                                          TileRegs<kVBits>& r) {
+// n consecutive words at p (n = 2, 4 or 8; 8- or 16-byte aligned) into w.
+template <int kN>
+__device__ __forceinline__ void load_words(const uint8_t* __restrict__ p, uint32_t* w) {
+  if constexpr (kN == 2) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    w[0] = a.x; w[1] = a.y;
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + o.koff + 1024u * mb);
+    for (int i = 0; i < kN; i += 4) {
+      const uint4 a = *reinterpret_cast<const uint4*>(p + 4 * i);
+      w[i] = a.x; w[i + 1] = a.y; w[i + 2] = a.z; w[i + 3] = a.w;
+    }
+  }
+}
+
+template <int kVBits, int kDim>
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec,
+                                          const LaneOffsets<kDim>& o,
+                                          TileRegs<kVBits, kDim>& r) {
+  constexpr int kKW = TileRegs<kVBits, kDim>::kKW;
+  if constexpr (kDim == 128) {
 #pragma unroll
-  for (int mb = 4; mb < 8; ++mb)
-    r.kw[mb] = *reinterpret_cast<const uint4*>(rec + o.koff4 + 1024u * (mb - 4));
-  r.m8 = *reinterpret_cast<const uint2*>(rec + o.off8);
+    for (int mb = 0; mb < 4; ++mb) load_words<4>(rec + o.koff + 1024u * mb, r.kw[mb]);
+#pragma unroll
+    for (int mb = 4; mb < 8; ++mb) load_words<4>(rec + o.koff4 + 1024u * (mb - 4), r.kw[mb]);
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) load_words<kKW>(rec + o.koff + 8u * kDim * mb, r.kw[mb]);
+  }
+#pragma unroll
+  for (int k = 0; k < TileRegs<kVBits, kDim>::kM8; ++k)
+    r.m8[k] = *reinterpret_cast<const uint2*>(rec + o.off8[k]);
   r.m16 = *reinterpret_cast<const uint2*>(rec + o.off16);
 }
 
-template <int kVBits>
-__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, const LaneOffsets& o,
-                                            TileRegs<kVBits>& r) {
+template <int kVBits, int kDim>
+__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec,
+                                            const LaneOffsets<kDim>& o,
+                                            TileRegs<kVBits, kDim>& r) {
+  if constexpr (kVBits == 2) {
 #pragma unroll
-  for (int m = 0; m < 2 * kVBits; ++m)
-    r.vw[m] = *reinterpret_cast<const uint4*>(rec + o.voff + 1024u * m);
+    for (int kb = 0; kb < 4; ++kb)
+      load_words<kDim / 32>(rec + o.voff + 8u * kDim * kb, r.vw[kb]);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int hb = 0; hb < kDim / 64; ++hb)
+        load_words<4>(rec + o.voff + 1024u * ((kDim / 64) * kb + hb), r.vw[kb] + 4 * hb);
+    }
+  }
 }
 
-// Every lane converts its 8 FP8 bytes and 4 fp16 values (the same instructions on all lanes)
-// and stores them, times per-lane factors, at 8 lane and 4 lane of the wave's tables.
-// FP8 goes through the hardware E4M3 conversion (exact for every finite code).
-__device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int lane,
-                                            float* __restrict__ f8, float* __restrict__ h16,
-                                            float fm, float fz) {
+// A lane converts its 8 FP8 bytes (one metadata chunk) and stores them, times a factor, at
+// f8[0..7]; the FP8 conversion is the hardware E4M3 one (exact for every finite code).
+__device__ __forceinline__ void decode_meta8(const uint2 m8, float* __restrict__ f8, float fm) {
   const float2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, false);
   const float2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.x, true);
   const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, false);
   const float2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)m8.y, true);
-  float4* dst = reinterpret_cast<float4*>(f8 + 8 * lane);
+  float4* dst = reinterpret_cast<float4*>(f8);
   dst[0] = make_float4(a[0] * fm, a[1] * fm, b[0] * fm, b[1] * fm);
   dst[1] = make_float4(c[0] * fm, c[1] * fm, d[0] * fm, d[1] * fm);
+}
+
+// ... and its 4 fp16 zero-points, times fz, at h16[0..3].
+__device__ __forceinline__ void decode_meta16(const uint2 m16, float* __restrict__ h16, float fz) {
   const float2v e = __builtin_convertvector(__builtin_bit_cast(half2v, m16.x), float2v);
   const float2v f = __builtin_convertvector(__builtin_bit_cast(half2v, m16.y), float2v);
-  *reinterpret_cast<float4*>(h16 + 4 * lane) = make_float4(e[0] * fz, e[1] * fz, f[0] * fz,
-                                                           f[1] * fz);
+  *reinterpret_cast<float4*>(h16) = make_float4(e[0] * fz, e[1] * fz, f[0] * fz, f[1] * fz);
+}
+
+// Every lane converts its metadata (the same instructions on all lanes) and stores it, times
+// per-lane factors, at 8 lane and 4 lane of the wave's tables (head dimension 128).
+__device__ __forceinline__ void decode_meta(const uint2 m8, const uint2 m16, int lane,
+                                            float* __restrict__ f8, float* __restrict__ h16,
+                                            float fm, float fz) {
+  decode_meta8(m8, f8 + 8 * lane, fm);
+  decode_meta16(m16, h16 + 4 * lane, fz);
+}
+
+// Walsh-Hadamard transform (unscaled) of a vector of 64 kPer channels held kPer per lane:
+// channel kPer lane + i in v[i]. Butterflies on the channel bits inside a lane first, then on
+// the lane bits.
+template <int kPer>
+__device__ __forceinline__ void fwht_lanes(float (&v)[kPer], int lane) {
+#pragma unroll
+  for (int h = 1; h < kPer; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    v[i] = fwht_lane_stage<1>(v[i], lane);
+    v[i] = fwht_lane_stage<2>(v[i], lane);
+    v[i] = fwht_lane_stage<4>(v[i], lane);
+    v[i] = fwht_lane_stage<8>(v[i], lane);
+    v[i] = fwht_lane_stage<16>(v[i], lane);
+    v[i] = fwht_lane_stage<32>(v[i], lane);
+  }
+}
+
+// Sign bits of channels kPer lane .. + kPer - 1 (bit i = channel kPer lane + i).
+template <int kPer>
+__device__ __forceinline__ uint32_t lane_sign_bits_d(const SignWords& signs, int lane) {
+  const int c0 = kPer * lane;
+  return (sign_word(signs, c0 >> 5) >> (c0 & 31)) & ((1u << kPer) - 1u);
+}
+
+// This lane's kPer fp16 values at p (kPer = 1, 2 or 4) as floats.
+template <int kPer>
+__device__ __forceinline__ void load_h(const __half* __restrict__ p, float (&v)[kPer]) {
+  if constexpr (kPer == 1) {
+    v[0] = __half2float(p[0]);
+  } else if constexpr (kPer == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = fp16_bits_to_float(w & 0xFFFFu);
+    v[1] = fp16_bits_to_float(w >> 16);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = fp16_bits_to_float(w.x & 0xFFFFu);
+    v[1] = fp16_bits_to_float(w.x >> 16);
+    v[2] = fp16_bits_to_float(w.y & 0xFFFFu);
+    v[3] = fp16_bits_to_float(w.y >> 16);
+  }
 }
 
 // kCausal: several query tokens per sequence (nq > 1) with the causal mask; a separate
 // instantiation so the one-token decode carries no mask code. kVBits: 2 or 4 bits per value
-// code (the record layout of that preset).
-template <bool kCausal, int kVBits>
-__global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// code; kDim: head dimension 64, 128 or 256 (the record layout of that preset). At kDim = 256
+// the score products run channel block by channel block (one query operand live at a time),
+// and the tile's codes and 16 output accumulators need more than the 256 registers of two
+// waves per SIMD, so that instantiation runs one wave per SIMD.
+template <bool kCausal, int kVBits, int kDim>
+__global__ void __launch_bounds__(kTThreads)
+__attribute__((amdgpu_waves_per_eu(kDim == 256 ? 1 : 2, kDim == 256 ? 1 : 2)))
 decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     const int32_t* __restrict__ seq_lens, float sm_scale,
-                    float* __restrict__ partials, uint4 signs) {
-  __shared__ TileSmem sm;
+                    float* __restrict__ partials, SignWords signs) {
+  constexpr int kKW = kDim / 32;        // key words per lane and token block = channel blocks
+  constexpr int kNB = kDim / 16;        // output channel blocks
+  constexpr int kPer = kDim / 64;       // channels per lane in the query rotation
+  constexpr int kPF = 2 + kDim;         // floats per partial
+  __shared__ TileSmem<kDim> sm;
   const int nsplit = gridDim.x;
   // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
   // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
@@ -363,9 +490,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
-  constexpr long long kTileBytes = RecordLayout<kVBits>::kTileBytes;
-  const LaneOffsets lo = lane_offsets<kVBits>(lane);
-  TileRegs<kVBits> cur;
+  constexpr long long kTileBytes = RecordLayout<kVBits, kDim>::kTileBytes;
+  const LaneOffsets<kDim> lo = lane_offsets<kVBits, kDim>(lane);
+  TileRegs<kVBits, kDim> cur;
   int id_next = nw > 1 ? bt_row[kWaves] : 0;        // tile 1
   if (nw > 0) {
     const long long blk = bt_row[0];
@@ -378,24 +505,29 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     }
   }
 
-  // ---- rotated queries in LDS: wave w rotates heads 2 w and 2 w + 1 (channels 2 lane, +1)
+  // ---- rotated queries in LDS: wave w rotates heads 2 w and 2 w + 1 (channels kPer lane ..)
   float qmax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int gg = 2 * wave + k;
-    float o0 = 0.0f, o1 = 0.0f;
+    float o[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) o[i] = 0.0f;
     if (gg < nh) {
-      uint32_t w = reinterpret_cast<const uint32_t*>(q + row_of(vbase + gg) * kD)[lane];
-      const uint32_t sb = lane_sign_bits(signs, lane);           // optional sign flips
-      w ^= ((sb & 1u) << 15) | ((sb >> 1) << 31);
-      o0 = fp16_bits_to_float(w & 0xFFFFu);
-      o1 = fp16_bits_to_float(w >> 16);
+      load_h<kPer>(q + row_of(vbase + gg) * kDim + kPer * lane, o);
+      const uint32_t sb = lane_sign_bits_d<kPer>(signs, lane);   // optional sign flips
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) o[i] = (sb >> i) & 1u ? -o[i] : o[i];
     }
-    fwht_wave(o0, o1, lane);
-    o0 *= 0.08838834764831845f;
-    o1 *= 0.08838834764831845f;
-    *reinterpret_cast<float2*>(&sm.qrot[gg][2 * lane]) = make_float2(o0, o1);
-    qmax = fmaxf(qmax, fmaxf(fabsf(o0), fabsf(o1)));
+    fwht_lanes<kPer>(o, lane);
+    constexpr float kInvSqrt = kDim == 64 ? 0.125f
+                             : (kDim == 128 ? 0.08838834764831845f : 0.0625f);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      o[i] *= kInvSqrt;
+      sm.qrot[gg][kPer * lane + i] = o[i];
+      qmax = fmaxf(qmax, fabsf(o[i]));
+    }
   }
   qmax = wave_max_nonneg(qmax);
   if (lane == 0) sm.red[wave] = qmax;
@@ -409,10 +541,12 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const float scale2 = sm_scale * kLog2e;
   const float kfac = scale2 * 64.0f / pq;          // undoes the code / 64 encoding and pq
   const float kzfac = scale2 / pq;                 // multiplies pq * sum_j q~_j
-  // per-lane metadata factors (see decode_meta): pq on c-hat^K, kfac on s-hat^K, 1 on
-  // c-hat^V, 32 on s-hat^V; kzfac on z-hat^K, 1 on z-hat^V
-  const int mgrp = lane >> 4;
-  const float fm = mgrp == 0 ? pq : (mgrp == 1 ? kfac : (mgrp == 2 ? 1.0f : 32.0f));
+  // per-lane metadata factors: pq on c-hat^K, kfac on s-hat^K, 1 on c-hat^V, 32 on s-hat^V
+  // (by chunk, meta_chunk_factor); kzfac on z-hat^K, 1 on z-hat^V
+  float fm[TileRegs<kVBits, kDim>::kM8];
+#pragma unroll
+  for (int k = 0; k < TileRegs<kVBits, kDim>::kM8; ++k)
+    fm[k] = meta_chunk_factor<kDim>(lane + 64 * k, pq, kfac);
   const float fz = lane < 32 ? kzfac : 1.0f;
 
   // lane roles: m / s for operand rows and k groups, n for columns
@@ -426,11 +560,11 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   // causal limit of this column's query token (position len - nq + i); only tiles that reach
   // past len - nq are masked, and with nq <= 16 every packed tile keeps >= 112 visible tokens
   const int qlim = len - nq + (vbase + gq) / group;
-  WaveMeta& wm = sm.wm[wave];
+  WaveMeta<kDim>& wm = sm.wm[wave];
   const float* kc = wm.f8;
-  const float* ks = wm.f8 + kT;
-  const float* vc = wm.f8 + 2 * kT;
-  const float* vs = wm.f8 + 3 * kT;
+  const float* ks = wm.f8 + kDim;
+  const float* vc = wm.f8 + kDim + kT;
+  const float* vs = wm.f8 + 2 * kDim + kT;
   const float* kz = wm.h16;
   const float* vz = wm.h16 + kT;
   // per-lane copies of the code masks (kept in VGPRs) and the wave-uniform exponent word
@@ -441,9 +575,9 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 
   // running state: score-lane view (column n) and output-row view (rows 4 s + i)
   float m_run = -INFINITY, l_run = 0.0f;
-  float4v oacc[8];
+  float4v oacc[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kNB; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   // Tile pipeline without extra registers: the next tile's key codes (and metadata) are
   // loaded into the key registers once the score products have consumed them, and the next
@@ -456,39 +590,57 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
       else bad = true;                             // finishes this tile, then stops
     }
-    decode_meta(cur.m8, cur.m16, lane, wm.f8, wm.h16, fm, fz);   // wave-local LDS tables
+#pragma unroll
+    for (int k = 0; k < TileRegs<kVBits, kDim>::kM8; ++k)   // wave-local LDS tables
+      decode_meta8(cur.m8[k], wm.f8 + 8 * (lane + 64 * k), fm[k]);
+    decode_meta16(cur.m16, wm.h16 + 4 * lane, fz);
 
-    // ---- query operand for this tile: q' = pq * q_rot * c-hat^K, hi (cols 0-7) or lo (8-15);
-    // element e of channel block c is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
-    half8 qb[4];
+    // ---- query operand of channel block c: q' = pq * q_rot * c-hat^K, hi (cols 0-7) or lo
+    // (8-15); element e is channel (kDim / 4) s + 8 c + {0,4,1,5,2,6,3,7}[e]
     float asum = 0.0f;                            // sum_j q'_j over this lane's channels
-    {
-      const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[gq] + 32 * s);
-      const float4* kc4 = reinterpret_cast<const float4*>(kc + 32 * s);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
-        const float4 ka = kc4[2 * c], kk = kc4[2 * c + 1];
-        const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
-        const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
-        asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
-        qb[c] = as_h8(hi_or_lo(x0, x4, negk) & vmask_col, hi_or_lo(x1, x5, negk) & vmask_col,
-                      hi_or_lo(x2, x6, negk) & vmask_col, hi_or_lo(x3, x7, negk) & vmask_col);
-      }
-    }
-    asum = add_xor32(add_xor16(asum));            // over all 128 channels of column n
-    const float asum_c = 0.125f * asum;            // the centring term, 8 / 64 * asum
+    const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[gq] + (kDim / 4) * s);
+    const float4* kc4 = reinterpret_cast<const float4*>(kc + (kDim / 4) * s);
+    auto q_operand = [&](int c) -> half8 {
+      const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
+      const float4 ka = kc4[2 * c], kk = kc4[2 * c + 1];
+      const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
+      const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
+      asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
+      return as_h8(hi_or_lo(x0, x4, negk) & vmask_col, hi_or_lo(x1, x5, negk) & vmask_col,
+                   hi_or_lo(x2, x6, negk) & vmask_col, hi_or_lo(x3, x7, negk) & vmask_col);
+    };
 
-    // ---- scores: 8 token blocks x 4 channel blocks
+    // ---- scores: 8 token blocks x kDim / 32 channel blocks
     float4v sc[8];
+    float asum_c;
+    if constexpr (kDim <= 128) {
+      half8 qb[kKW];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < kKW; ++c) qb[c] = q_operand(c);
+      asum = add_xor32(add_xor16(asum));          // over all kDim channels of column n
+      asum_c = 0.125f * asum;                     // the centring term, 8 / 64 * asum
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(w4[c], kcon), qb[c], acc, 0, 0, 0);
-      sc[mb] = acc;
+      for (int mb = 0; mb < 8; ++mb) {
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kKW; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(cur.kw[mb][c], kcon), qb[c],
+                                                       acc, 0, 0, 0);
+        sc[mb] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) sc[mb] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kKW; ++c) {
+        const half8 qc = q_operand(c);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+          sc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(cur.kw[mb][c], kcon), qc,
+                                                          sc[mb], 0, 0, 0);
+      }
+      asum = add_xor32(add_xor16(asum));
+      asum_c = 0.125f * asum;
     }
     if (nrec != nullptr) load_keys(nrec, lo, cur);
     // hi + lo partial scores of this lane's two rows, then the log2-domain score per token:
@@ -566,8 +718,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       wm.beta[n] = colhi ? beta : 0.0f;           // the zero-point term enters the hi row once
     }
 
-    // ---- output: 8 channel blocks x 4 token blocks; each channel block's accumulator is
-    // folded into o~ as soon as its 4 products are done (rows 4 s + i: beta of their head,
+    // ---- output: kDim / 16 channel blocks x 4 token blocks; each channel block's accumulator
+    // is folded into o~ as soon as its 4 products are done (rows 4 s + i: beta of their head,
     // c-hat^V of column 16 nb + n); rows are rescaled first when a running maximum moved
     {
       const float4 b4 = *reinterpret_cast<const float4*>(wm.beta + 4 * s);
@@ -576,41 +728,19 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
         const float4 a4 = *reinterpret_cast<const float4*>(wm.alpha + ((4 * s) & 7));
         const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+        for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) oacc[nb][i] *= ar[i];
         }
       }
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
+      for (int nb = 0; nb < kNB; ++nb) {
         float4v po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          uint32_t f[4];
-          if constexpr (kVBits == 2) {
-            // field nb (bits 2 nb and 16 + 2 nb) -> mantissa bits 8..9 under exponent 0x3C00:
-            // the half is 1 + code / 4 (normal, exact)
-            const uint32_t v4[4] = {cur.vw[kb].x, cur.vw[kb].y, cur.vw[kb].z, cur.vw[kb].w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const uint32_t x = nb < 4 ? (v4[d] << (8 - 2 * nb)) : (v4[d] >> (2 * nb - 8));
-              f[d] = and_or(x, vmask, one16);
-            }
-          } else {
-            // words of channel half nb / 4; field nb % 4 (bits 4 (nb % 4) and 16 + 4 (nb % 4))
-            // -> mantissa bits 6..9: the half is 1 + code / 16 (normal, exact)
-            const uint4 ww = cur.vw[2 * kb + (nb >> 2)];
-            const uint32_t v4[4] = {ww.x, ww.y, ww.z, ww.w};
-            const int kF = nb & 3;                 // a constant once the loop is unrolled
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const uint32_t x = kF < 2 ? (v4[d] << (6 - 4 * kF)) : (v4[d] >> (4 * kF - 6));
-              f[d] = and_or(x, kmask, one16);
-            }
-          }
-          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[kb], as_h8(f[0], f[1], f[2], f[3]),
-                                                      po, 0, 0, 0);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              wa[kb], value_operand<kVBits, kDim>(cur.vw, nb, kb, vmask, kmask, one16), po,
+              0, 0, 0);
         const float cv = vc[16 * nb + n];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], kVOut, br[i]), oacc[nb][i]);
@@ -629,7 +759,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   {
     // add the lo rows (lanes 32..63) into the hi rows (lanes 0..31)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float both = add_xor32(oacc[nb][i]);
@@ -639,8 +769,8 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   }
   __syncthreads();
   const int wbad = __syncthreads_or(bad ? 1 : 0);
-  for (int idx = tid; idx < nh * kD; idx += kTThreads) {
-    const int gg = idx >> 7, jj = idx & (kD - 1);
+  for (int idx = tid; idx < nh * kDim; idx += kTThreads) {
+    const int gg = idx / kDim, jj = idx % kDim;
     float mm = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm.comb_m[w][gg]);
@@ -653,7 +783,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
         oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
       }
     }
-    float* p = partials + (row_of(vbase + gg) * nsplit + split) * kPartialFloats;
+    float* p = partials + (row_of(vbase + gg) * nsplit + split) * kPF;
     if (jj == 0) {
       p[0] = wbad ? NAN : mm;
       p[1] = wbad ? NAN : ll;
@@ -700,7 +830,7 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const uint8_t* __restrict__ pool, long long num_blocks,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     const int32_t* __restrict__ seq_lens, float sm_scale,
-                    float* __restrict__ partials, uint4 signs, int chunk) {
+                    float* __restrict__ partials, SignWords signs, int chunk) {
   __shared__ PairSmem sm;
   const int nsplit = gridDim.x;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -725,8 +855,8 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const int npair = (ntile + 1) >> 1;              // pair p: tiles i0 + 2 p, i0 + 2 p + 1
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0;
   constexpr long long kTileBytes = RecordLayout<kVBits>::kTileBytes;
-  const LaneOffsets lo = lane_offsets<kVBits>(lane);
-  TileRegs<kVBits> cx, cy;
+  const LaneOffsets<kD> lo = lane_offsets<kVBits, kD>(lane);
+  TileRegs<kVBits, kD> cx, cy;
   // block ids are scalar loads issued one pair before the pair that needs them
   int idx_next = 0, idy_next = 0;
   if (npair > 1) {
@@ -753,7 +883,7 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 
   // ---- rotated queries in LDS (channels 2 lane, 2 lane + 1 of each virtual head)
   float qmax = 0.0f;
-  const uint32_t sb = lane_sign_bits(signs, lane);              // optional sign flips
+  const uint32_t sb = lane_sign_bits(signs.lo, lane);           // optional sign flips
   for (int k = 0; k < 4; ++k) {
     float o0 = 0.0f, o1 = 0.0f;
     if (k < nh) {
@@ -821,8 +951,8 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
         bad = true;                                // finishes this pair, then stops
       }
     }
-    decode_meta(cx.m8, cx.m16, lane, sm.f8[0], sm.h16[0], fm, fz);
-    if (has_y) decode_meta(cy.m8, cy.m16, lane, sm.f8[1], sm.h16[1], fm, fz);
+    decode_meta(cx.m8[0], cx.m16, lane, sm.f8[0], sm.h16[0], fm, fz);
+    if (has_y) decode_meta(cy.m8[0], cy.m16, lane, sm.f8[1], sm.h16[1], fm, fz);
     // tables this lane reads: its column's tile (the first tile's when the pair is single; the
     // second tile's columns are then masked), and its output rows' tile
     const int tcol = has_y ? tsel : 0;
@@ -857,12 +987,12 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       float4v acc = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t wx[4] = {cx.kw[mb].x, cx.kw[mb].y, cx.kw[mb].z, cx.kw[mb].w};
+      const uint32_t* wx = cx.kw[mb];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(wx[c], kcon), qx[c], acc, 0, 0, 0);
       if (has_y) {
-        const uint32_t wy[4] = {cy.kw[mb].x, cy.kw[mb].y, cy.kw[mb].z, cy.kw[mb].w};
+        const uint32_t* wy = cy.kw[mb];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand(wy[c], kcon), qy[c], acc, 0, 0, 0);
@@ -1019,8 +1149,10 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 // grid (nq * hq, batch), one wave per (sequence, query token, query head): the staging tokens
 // the query token sees (exact fp32
 // attention with the unrotated query), the log-sum-exp merge of the tile splits, o~ H + o_raw,
-// / l (the fp16-cache path's partials are not rotated: o + o_raw, / l). Lane l owns output channels 2 l and 2 l + 1; the inverse rotation is a butterfly on
-// channel bit 0 in registers and on bits 1..6 across lanes l ^ 1 .. l ^ 32. Every global load
+// / l (the fp16-cache path's partials are not rotated: o + o_raw, / l). Lane l owns output
+// channels kPer l .. kPer l + kPer - 1 (kPer = head dimension / 64); the inverse rotation is a
+// butterfly on the channel bits inside a lane in registers and on the lane bits across lanes
+// l ^ 1 .. l ^ 32. Every global load
 // that does not depend on another is issued first; split weights and staging probabilities
 // are broadcast from the lane that computed them.
 constexpr int kMThreads = 64;
@@ -1032,12 +1164,13 @@ constexpr int kPairMinTilesPerCU = KVARN_PAIR_MIN_TILES_PER_CU;
 constexpr int kMergePreload = 8;          // splits whose o~ is loaded before the weights exist
 constexpr int kStageChunk = 16;           // staging value rows loaded per round
 
-// <q, k> over 128 channels: k is one fp16 staging row, q the fp32 query in LDS.
+// <q, k> over kDim channels: k is one fp16 staging row, q the fp32 query in LDS.
+template <int kDim>
 __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, const float* qs) {
   const uint4* k4 = reinterpret_cast<const uint4*>(krow);
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < kDim / 8; ++k) {
     float kv[8];
     unpack_h8(k4[k], kv);
     const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * k);
@@ -1048,14 +1181,48 @@ __device__ __forceinline__ float staging_dot(const __half* __restrict__ krow, co
   return acc0 + acc1;
 }
 
-template <bool kRotated, bool kCausal>
+// kPer consecutive floats at p (kPer = 1, 2 or 4) into v. p is 8-byte aligned for kPer >= 2
+// (a partial holds 2 + D floats, so at D = 256 its rows are not 16-byte aligned): pairs.
+template <int kPer>
+__device__ __forceinline__ void load_f(const float* __restrict__ p, float (&v)[kPer]) {
+  if constexpr (kPer == 1) {
+    v[0] = p[0];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; i += 2) {
+      const float2 a = *reinterpret_cast<const float2*>(p + i);
+      v[i] = a.x; v[i + 1] = a.y;
+    }
+  }
+}
+
+// This lane's kPer fp16 bit patterns at p, kept packed (one 16-bit pattern per element).
+template <int kPer>
+struct HalfBits {
+  uint32_t w[(kPer + 1) / 2];
+  __device__ __forceinline__ void load(const __half* __restrict__ p) {
+    if constexpr (kPer == 1) w[0] = *reinterpret_cast<const uint16_t*>(p);
+    else if constexpr (kPer == 2) w[0] = *reinterpret_cast<const uint32_t*>(p);
+    else {
+      const uint2 a = *reinterpret_cast<const uint2*>(p);
+      w[0] = a.x; w[1] = a.y;
+    }
+  }
+  __device__ __forceinline__ float at(int i) const {
+    return fp16_bits_to_float((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+  }
+};
+
+template <bool kRotated, bool kCausal, int kDim>
 __global__ void __launch_bounds__(kMThreads)
 decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int max_blocks,
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out,
-                    uint4 signs) {
-  __shared__ float qs[kD];
+                    SignWords signs) {
+  constexpr int kPer = kDim / 64;      // output channels per lane: kPer lane .. + kPer - 1
+  constexpr int kPF = 2 + kDim;        // floats per partial
+  __shared__ float qs[kDim];
   // The group query heads of one (sequence, query token, KV head) read the same staging tile:
   // they take dispatch ids 8 apart, so the round-robin dispatch runs them on one XCD and the
   // second and later reads of the tile come from that XCD's L2.
@@ -1082,53 +1249,66 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   const int lane = threadIdx.x;
   const int g = h / group;
   const long long row = ((long long)b * nq + qi) * hq + h;              // row in [B][nq][hq]
-  const float* pp = partials + row * nsplit * kPartialFloats;
-  // independent loads: this lane's split (m, l), the first splits' o~ pairs, the query pair
-  const float msp = lane < nsplit ? pp[lane * kPartialFloats] : -INFINITY;
-  const float lsp = lane < nsplit ? pp[lane * kPartialFloats + 1] : 0.0f;
-  const float* col = pp + 2 + 2 * lane;
-  float2 ov[kMergePreload];
+  const float* pp = partials + row * nsplit * kPF;
+  // independent loads: this lane's split (m, l), the first splits' o~ values, the query values
+  const float msp = lane < nsplit ? pp[lane * kPF] : -INFINITY;
+  const float lsp = lane < nsplit ? pp[lane * kPF + 1] : 0.0f;
+  const float* col = pp + 2 + kPer * lane;
+  float ov[kMergePreload][kPer];
 #pragma unroll
-  for (int sp = 0; sp < kMergePreload; ++sp)
-    ov[sp] = sp < nsplit ? *reinterpret_cast<const float2*>(col + sp * kPartialFloats)
-                         : make_float2(0.0f, 0.0f);
-  const uint32_t qw = reinterpret_cast<const uint32_t*>(q + row * kD)[lane];
+  for (int sp = 0; sp < kMergePreload; ++sp) {
+    if (sp < nsplit) {
+      load_f<kPer>(col + sp * kPF, ov[sp]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) ov[sp][i] = 0.0f;
+    }
+  }
+  HalfBits<kPer> qw;
+  qw.load(q + row * kDim + kPer * lane);
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
   // staging tokens this query token sees: positions up to len - nq + qi
   const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (kCausal ? nq - 1 - qi : 0));
   const float scale2 = sm_scale * kLog2e;
-  const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kD;
-  const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kD;
-  // this lane's staging key row (token lane) is loaded before the length is known: the row
-  // is always inside the staging tile, and used only if the token is live
-  uint4 krow[16];
-  {
-    const uint4* k4 = reinterpret_cast<const uint4*>(sk + lane * kD);
+  const __half* sk = staging_k + ((long long)b * hkv + g) * kT * kDim;
+  const __half* sv = staging_v + ((long long)b * hkv + g) * kT * kDim;
+  // this lane's staging key row (token lane) is loaded before the length is known when it
+  // fits in registers (kDim <= 128): the row is always inside the staging tile, and used only
+  // if the token is live
+  constexpr int kPre = kDim <= 128 ? kDim / 8 : 1;
+  uint4 krow[kPre];
+  if constexpr (kDim <= 128) {
+    const uint4* k4 = reinterpret_cast<const uint4*>(sk + lane * kDim);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) krow[i] = k4[i];
+    for (int i = 0; i < kPre; ++i) krow[i] = k4[i];
   }
-  const uint32_t vpre0 = reinterpret_cast<const uint32_t*>(sv)[lane];
-  const uint32_t vpre1 = reinterpret_cast<const uint32_t*>(sv)[kD / 2 + lane];
-  qs[2 * lane] = fp16_bits_to_float(qw & 0xFFFFu);
-  qs[2 * lane + 1] = fp16_bits_to_float(qw >> 16);
+  HalfBits<kPer> vpre0, vpre1;
+  vpre0.load(sv + kPer * lane);
+  vpre1.load(sv + kDim + kPer * lane);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) qs[kPer * lane + i] = qw.at(i);
   __syncthreads();
   // staging scores of tokens lane and lane + 64
   float s0 = -INFINITY, s1 = -INFINITY;
   if (lane < n_stage) {
-    float acc0 = 0.0f, acc1 = 0.0f;
+    if constexpr (kDim <= 128) {
+      float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float kv[8];
-      unpack_h8(krow[k], kv);
-      const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * k);
-      const float4 qc = *reinterpret_cast<const float4*>(qs + 8 * k + 4);
-      acc0 = fmaf(qa.x, kv[0], fmaf(qa.y, kv[1], fmaf(qa.z, kv[2], fmaf(qa.w, kv[3], acc0))));
-      acc1 = fmaf(qc.x, kv[4], fmaf(qc.y, kv[5], fmaf(qc.z, kv[6], fmaf(qc.w, kv[7], acc1))));
+      for (int k = 0; k < kPre; ++k) {
+        float kv[8];
+        unpack_h8(krow[k], kv);
+        const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * k);
+        const float4 qc = *reinterpret_cast<const float4*>(qs + 8 * k + 4);
+        acc0 = fmaf(qa.x, kv[0], fmaf(qa.y, kv[1], fmaf(qa.z, kv[2], fmaf(qa.w, kv[3], acc0))));
+        acc1 = fmaf(qc.x, kv[4], fmaf(qc.y, kv[5], fmaf(qc.z, kv[6], fmaf(qc.w, kv[7], acc1))));
+      }
+      s0 = (acc0 + acc1) * scale2;
+    } else {
+      s0 = staging_dot<kDim>(sk + lane * kDim, qs) * scale2;
     }
-    s0 = (acc0 + acc1) * scale2;
   }
-  if (lane + 64 < n_stage) s1 = staging_dot(sk + (lane + 64) * kD, qs) * scale2;
+  if (lane + 64 < n_stage) s1 = staging_dot<kDim>(sk + (lane + 64) * kDim, qs) * scale2;
   const bool invalid = bad || __any(msp != msp);
   const float mm = wave_max(fmaxf(msp, fmaxf(s0, s1)));
   float ls = 0.0f, wsp = 0.0f, p0 = 0.0f, p1 = 0.0f;
@@ -1139,134 +1319,144 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
     ls = fmaf(wsp, lsp, p0 + p1);
   }
   ls = wave_sum(ls);
-  // merged rotated output o~ of channels 2 lane, 2 lane + 1
-  float o0 = 0.0f, o1 = 0.0f;
+  // merged rotated output o~ of this lane's channels
+  float o[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) o[i] = 0.0f;
   if (mm != -INFINITY && !invalid) {
 #pragma unroll
     for (int sp = 0; sp < kMergePreload; ++sp) {
       if (sp < nsplit) {
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
-        o0 = fmaf(w, ov[sp].x, o0);
-        o1 = fmaf(w, ov[sp].y, o1);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, ov[sp][i], o[i]);
       }
     }
     for (int sp = kMergePreload; sp < nsplit; ++sp) {
-      const float2 v = *reinterpret_cast<const float2*>(col + sp * kPartialFloats);
+      float v[kPer];
+      load_f<kPer>(col + sp * kPF, v);
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
-      o0 = fmaf(w, v.x, o0);
-      o1 = fmaf(w, v.y, o1);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, v[i], o[i]);
     }
   }
   if constexpr (kRotated) {
-    fwht_wave(o0, o1, lane);
-    const uint32_t sb = lane_sign_bits(signs, lane);            // optional sign flips
-    o0 = __uint_as_float(__float_as_uint(o0) ^ ((sb & 1u) << 31));
-    o1 = __uint_as_float(__float_as_uint(o1) ^ ((sb >> 1) << 31));
+    fwht_lanes<kPer>(o, lane);
+    const uint32_t sb = lane_sign_bits_d<kPer>(signs, lane);     // optional sign flips
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      o[i] = __uint_as_float(__float_as_uint(o[i]) ^ (((sb >> i) & 1u) << 31));
   }
-  constexpr float kBack = kRotated ? 0.08838834764831845f : 1.0f;   // H / sqrt(128) or none
+  // H / sqrt(kDim) or none
+  constexpr float kBack = !kRotated ? 1.0f
+                        : (kDim == 64 ? 0.125f : (kDim == 128 ? 0.08838834764831845f : 0.0625f));
   // raw staging output
-  float r0 = 0.0f, r1 = 0.0f;
-  const uint32_t* vcol = reinterpret_cast<const uint32_t*>(sv) + lane;
+  float r[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) r[i] = 0.0f;
+  const __half* vcol = sv + kPer * lane;
   // 16 staging rows per round of loads (rows past n_stage are loaded, always inside the
   // staging tile, but never used: they may hold anything)
   for (int t0 = 0; t0 < n_stage; t0 += kStageChunk) {
-    uint32_t w[kStageChunk];
+    HalfBits<kPer> w[kStageChunk];
 #pragma unroll
-    for (int i = 0; i < kStageChunk; ++i)
-      w[i] = t0 + i == 0 ? vpre0 : (t0 + i == 1 ? vpre1 : vcol[(t0 + i) * (kD / 2)]);
+    for (int i = 0; i < kStageChunk; ++i) {
+      if (t0 + i == 0) w[i] = vpre0;
+      else if (t0 + i == 1) w[i] = vpre1;
+      else w[i].load(vcol + (t0 + i) * kDim);
+    }
 #pragma unroll
     for (int i = 0; i < kStageChunk; ++i) {
       const int t = t0 + i;
       if (t < n_stage) {
         const int src = __float_as_int(t < 64 ? p0 : p1);
         const float pt = __int_as_float(__builtin_amdgcn_readlane(src, t & 63));
-        r0 = fmaf(pt, fp16_bits_to_float(w[i] & 0xFFFFu), r0);
-        r1 = fmaf(pt, fp16_bits_to_float(w[i] >> 16), r1);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) r[e] = fmaf(pt, w[i].at(e), r[e]);
       }
     }
   }
-  float2 res = make_float2(0.0f, 0.0f);
-  if (invalid) {
-    res = make_float2(NAN, NAN);
-  } else if (ls > 0.0f) {
-    res.x = fmaf(o0, kBack, r0) / ls;
-    res.y = fmaf(o1, kBack, r1) / ls;
+  float res[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    res[i] = 0.0f;
+    if (invalid) res[i] = NAN;
+    else if (ls > 0.0f) res[i] = fmaf(o[i], kBack, r[i]) / ls;
   }
-  reinterpret_cast<float2*>(out + row * kD)[lane] = res;
+  float* dst = out + row * kDim + kPer * lane;
+  if constexpr (kPer == 1) {
+    dst[0] = res[0];
+  } else if constexpr (kPer == 2) {
+    *reinterpret_cast<float2*>(dst) = make_float2(res[0], res[1]);
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(res[0], res[1], res[2], res[3]);
+  }
 }
 
 
 // ------------------------------------------------------------------ dequantisation to memory
 //
 // Stage 4 of [GR] "The four-stage pipeline" written out instead of folded into attention:
-// x_tj = sum_i c-hat_i (s-hat_t code_ti + z-hat_t) H_ij / sqrt(128), the record's tile back in
+// x_tj = sum_i c-hat_i (s-hat_t code_ti + z-hat_t) H_ij / sqrt(D), the record's tile back in
 // the original channel space (for inspection, export and error measurement). grid: n_tiles *
 // hkv * 2 workgroups (tile, head, K|V) of 4 waves; wave w rebuilds tokens w, w + 4, ..., lane l
-// channels 2 l and 2 l + 1, with the same butterfly as the query rotation.
+// channels kPer l .. kPer l + kPer - 1 (kPer = D / 64), with the same butterfly as the query
+// rotation.
 
-// Byte offset (in the value section) and bit shift of value code (token t, channel j), for
-// 2-bit codes (fields of 2 bits, 8 channel blocks per word) or 4-bit codes (fields of 4 bits,
-// the channel blocks split in two halves of 4 with 256 words per half).
-template <int kVBits>
-__device__ __forceinline__ void v_code_pos(int t, int j, uint32_t& byte_off, int& shift) {
-  const int nb = j >> 4, n = j & 15, kb = t >> 5, h = (t >> 4) & 1, s = (t >> 2) & 3, i = t & 3;
-  int word, bit;
-  if constexpr (kVBits == 2) {
-    word = 256 * kb + 4 * (16 * s + n) + 2 * h + (i >> 1);
-    bit = 2 * nb + 16 * (i & 1);
-  } else {
-    word = 512 * kb + 256 * (nb >> 2) + 4 * (16 * s + n) + 2 * h + (i >> 1);
-    bit = 4 * (nb & 3) + 16 * (i & 1);
-  }
-  byte_off = 4u * (uint32_t)word + (uint32_t)(bit >> 3);
-  shift = bit & 7;
-}
-
-template <int kVBits>
+template <int kVBits, int kDim>
 __global__ void __launch_bounds__(256)
 dequantize_tiles_kernel(const uint8_t* __restrict__ pool, long long num_blocks,
                         const int32_t* __restrict__ src_blocks, int n_tiles, int hkv,
-                        float* __restrict__ k_out, float* __restrict__ v_out, uint4 signs) {
+                        float* __restrict__ k_out, float* __restrict__ v_out, SignWords signs) {
+  constexpr int kPer = kDim / 64;
   const int id = blockIdx.x;
   const int is_v = id & 1, head = (id >> 1) % hkv, tile = (id >> 1) / hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (tile >= n_tiles) return;
-  float* out = (is_v ? v_out : k_out) + ((long long)tile * kT * hkv + head) * kD;
-  const long long row_stride = (long long)hkv * kD;
+  float* out = (is_v ? v_out : k_out) + ((long long)tile * kT * hkv + head) * kDim + kPer * lane;
+  const long long row_stride = (long long)hkv * kDim;
   const long long blk = src_blocks[tile];
   if (blk < 0 || blk >= num_blocks) {
-    for (int t = wave; t < kT; t += 4)
-      reinterpret_cast<float2*>(out + t * row_stride)[lane] = make_float2(NAN, NAN);
+    for (int t = wave; t < kT; t += 4) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) out[t * row_stride + i] = NAN;
+    }
     return;
   }
-  using L = RecordLayout<kVBits>;
+  using L = RecordLayout<kVBits, kDim>;
   const uint8_t* rec = pool + (blk * hkv + head) * (long long)L::kTileBytes;
   const uint8_t* meta = rec + (is_v ? L::kVMetaOff : L::kKMetaOff);
-  const uint32_t cw = *reinterpret_cast<const uint16_t*>(meta + kCRel + 2 * lane);
-  const float2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false);   // c-hat of 2 l, 2 l + 1
-  uint32_t vb0 = 0, vb1 = 0;
-  int vs0 = 0, vs1 = 0;
-  const uint32_t sb = lane_sign_bits(signs, lane);              // optional sign flips
+  float c[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    c[i] = __builtin_amdgcn_cvt_f32_fp8((int)meta[L::kC + kPer * lane + i], 0);
+  const uint32_t sb = lane_sign_bits_d<kPer>(signs, lane);     // optional sign flips
+  constexpr float kInvSqrt = kDim == 64 ? 0.125f : (kDim == 128 ? 0.08838834764831845f : 0.0625f);
+  constexpr uint32_t kVMax = (1u << kVBits) - 1u;
   for (int t = wave; t < kT; t += 4) {
-    const float sh = __builtin_amdgcn_cvt_f32_fp8((int)meta[kSRel + t], 0);
-    const float zh = fp16_bits_to_float(*reinterpret_cast<const uint16_t*>(meta + kZRel + 2 * t));
-    float q0, q1;
-    if (!is_v) {
-      const uint32_t byte = rec[kKCodesOff + 64 * t + lane];          // channels 2 l, 2 l + 1
-      q0 = (float)(byte & 15u);
-      q1 = (float)(byte >> 4);
-    } else {
-      constexpr uint32_t kVMax = (1u << kVBits) - 1u;
-      v_code_pos<kVBits>(t, 2 * lane, vb0, vs0);
-      v_code_pos<kVBits>(t, 2 * lane + 1, vb1, vs1);
-      q0 = (float)((rec[kVCodesOff + vb0] >> vs0) & kVMax);
-      q1 = (float)((rec[kVCodesOff + vb1] >> vs1) & kVMax);
+    const float sh = __builtin_amdgcn_cvt_f32_fp8((int)meta[L::kS + t], 0);
+    const float zh = fp16_bits_to_float(*reinterpret_cast<const uint16_t*>(meta + L::kZ + 2 * t));
+    float y[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ch = kPer * lane + i;
+      uint32_t code;
+      if (!is_v) {
+        const uint32_t byte = rec[L::kKCodes + (kDim / 2) * t + (ch >> 1)];
+        code = (ch & 1) ? (byte >> 4) : (byte & 15u);
+      } else {
+        uint32_t off;
+        int shift;
+        value_code_pos<kVBits, kDim>(t, ch, off, shift);
+        code = (rec[L::kVCodes + off] >> shift) & kVMax;
+      }
+      y[i] = c[i] * fmaf(sh, (float)code, zh);
     }
-    float y0 = c[0] * fmaf(sh, q0, zh), y1 = c[1] * fmaf(sh, q1, zh);
-    fwht_wave(y0, y1, lane);
-    y0 = __uint_as_float(__float_as_uint(y0 * 0.08838834764831845f) ^ ((sb & 1u) << 31));
-    y1 = __uint_as_float(__float_as_uint(y1 * 0.08838834764831845f) ^ ((sb >> 1) << 31));
-    reinterpret_cast<float2*>(out + t * row_stride)[lane] = make_float2(y0, y1);
+    fwht_lanes<kPer>(y, lane);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      out[t * row_stride + i] =
+          __uint_as_float(__float_as_uint(y[i] * kInvSqrt) ^ (((sb >> i) & 1u) << 31));
   }
 }
 
@@ -1532,18 +1722,38 @@ decode_fp16_tiles_kernel(const __half* __restrict__ q, int hq, int hkv,
 
 }  // namespace
 
+namespace {
+
+SignWords sign_words(const uint32_t* signs) {
+  SignWords s;
+  s.lo = make_uint4(signs[0], signs[1], signs[2], signs[3]);
+  s.hi = make_uint4(signs[4], signs[5], signs[6], signs[7]);
+  return s;
+}
+
+template <int kDim>
+void launch_dequantize_t(const uint8_t* pool, long long num_blocks, const int32_t* src_blocks,
+                         int n_tiles, int hkv, float* k_out, float* v_out, SignWords sg,
+                         int v_bits, hipStream_t stream) {
+  const long long groups = 2LL * hkv * n_tiles;
+  auto kern = v_bits == 4 ? dequantize_tiles_kernel<4, kDim> : dequantize_tiles_kernel<2, kDim>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)groups), dim3(256), 0, stream, pool, num_blocks,
+                     src_blocks, n_tiles, hkv, k_out, v_out, sg);
+}
+
+}  // namespace
+
 hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
                                    const int32_t* src_blocks, int n_tiles, int hkv, float* k_out,
-                                   float* v_out, const uint32_t* signs, int v_bits,
+                                   float* v_out, const uint32_t* signs, int v_bits, int head_dim,
                                    hipStream_t stream) {
-  const long long groups = 2LL * hkv * n_tiles;
-  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  if (v_bits == 4)
-    hipLaunchKernelGGL(dequantize_tiles_kernel<4>, dim3((unsigned)groups), dim3(256), 0, stream,
-                       pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg);
+  const SignWords sg = sign_words(signs);
+  if (head_dim == 64)
+    launch_dequantize_t<64>(pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg, v_bits, stream);
+  else if (head_dim == 256)
+    launch_dequantize_t<256>(pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg, v_bits, stream);
   else
-    hipLaunchKernelGGL(dequantize_tiles_kernel<2>, dim3((unsigned)groups), dim3(256), 0, stream,
-                       pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg);
+    launch_dequantize_t<128>(pool, num_blocks, src_blocks, n_tiles, hkv, k_out, v_out, sg, v_bits, stream);
   return hipGetLastError();
 }
 
@@ -1569,12 +1779,14 @@ int device_compute_units() {
   return cus;
 }
 
-// The paired-tile kernel serves at most four virtual heads per KV head with 2-bit values, and
-// only when the table holds enough tiles for about four one-wave chunks per SIMD slot: with fewer
+// The paired-tile kernel serves at most four virtual heads per KV head with 2-bit values at
+// head dimension 128, and only when the table holds enough tiles for about four one-wave chunks per SIMD slot: with fewer
 // tiles than that, one tile per wave of four-wave workgroups fills the device better.
-bool pairs_mode(int virtual_heads, int v_bits, int batch, int hkv, int max_blocks) {
+bool pairs_mode(int virtual_heads, int v_bits, int head_dim, int batch, int hkv,
+                int max_blocks) {
   const long long tiles = (long long)batch * hkv * max_blocks;
-  return virtual_heads <= 4 && v_bits == 2 && tiles >= kPairMinTilesPerCU * device_compute_units();
+  return virtual_heads <= 4 && v_bits == 2 && head_dim == 128 &&
+         tiles >= kPairMinTilesPerCU * device_compute_units();
 }
 
 // Tiles per chunk of the paired-tile kernel for a plan of `splits` chunks (even, so only a
@@ -1620,39 +1832,55 @@ int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel) {
   return (int)s;
 }
 
-hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t* pool,
-                         long long num_blocks, const int32_t* block_table, int max_blocks,
-                         const int32_t* seq_lens, const __half* staging_k,
-                         const __half* staging_v, float sm_scale, float* out, float* partials,
-                         int splits, int batch, const uint32_t* signs, int v_bits,
-                         hipStream_t stream) {
+namespace {
+
+template <int kDim>
+hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8_t* pool,
+                           long long num_blocks, const int32_t* block_table, int max_blocks,
+                           const int32_t* seq_lens, const __half* staging_k,
+                           const __half* staging_v, float sm_scale, float* out, float* partials,
+                           int splits, int batch, SignWords sg, int v_bits, hipStream_t stream) {
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
-  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  if (pairs_mode(hq / hkv * nq, v_bits, batch, hkv, max_blocks)) {   // decode_pairs_kernel
+  if (kDim == 128 && pairs_mode(hq / hkv * nq, v_bits, kDim, batch, hkv, max_blocks)) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
     const int chunk = pairs_chunk(max_blocks, splits);
     hipLaunchKernelGGL(kern, dim3(splits, hkv, batch), dim3(64), 0, stream, q, hq, hkv, nq,
                        pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale, partials,
                        sg, chunk);
   } else {
-    auto kern = nq == 1
-        ? (v_bits == 4 ? decode_tiles_kernel<false, 4> : decode_tiles_kernel<false, 2>)
-        : (v_bits == 4 ? decode_tiles_kernel<true, 4> : decode_tiles_kernel<true, 2>);
+    auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4, kDim>
+                                       : decode_tiles_kernel<false, 2, kDim>)
+                        : (v_bits == 4 ? decode_tiles_kernel<true, 4, kDim>
+                                       : decode_tiles_kernel<true, 2, kDim>);
     hipLaunchKernelGGL(kern, grid, dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool, num_blocks,
                        block_table, max_blocks, seq_lens, sm_scale, partials, sg);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (nq == 1)
-    hipLaunchKernelGGL((decode_merge_kernel<true, false>), mgrid, dim3(kMThreads), 0, stream, q,
-                       hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                       partials, splits, out, sg);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<true, true>), mgrid, dim3(kMThreads), 0, stream, q,
-                       hq, hkv, nq, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                       partials, splits, out, sg);
+  auto merge = nq == 1 ? decode_merge_kernel<true, false, kDim> : decode_merge_kernel<true, true, kDim>;
+  hipLaunchKernelGGL(merge, mgrid, dim3(kMThreads), 0, stream, q, hq, hkv, nq, max_blocks,
+                     seq_lens, staging_k, staging_v, sm_scale, partials, splits, out, sg);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t* pool,
+                         long long num_blocks, const int32_t* block_table, int max_blocks,
+                         const int32_t* seq_lens, const __half* staging_k,
+                         const __half* staging_v, float sm_scale, float* out, float* partials,
+                         int splits, int batch, const uint32_t* signs, int v_bits, int head_dim,
+                         hipStream_t stream) {
+  const SignWords sg = sign_words(signs);
+#define KVARN_D(DIM)                                                                         \
+  launch_decode_t<DIM>(q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks, seq_lens,   \
+                       staging_k, staging_v, sm_scale, out, partials, splits, batch, sg,       \
+                       v_bits, stream)
+  if (head_dim == 64) return KVARN_D(64);
+  if (head_dim == 256) return KVARN_D(256);
+  return KVARN_D(128);
+#undef KVARN_D
 }
 
 hipError_t launch_fp16_write_tiles(const __half* k, const __half* v, long long token_stride,
@@ -1675,9 +1903,12 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
                      max_blocks, seq_lens, sm_scale, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<false, false>), dim3(hq, batch), dim3(kMThreads), 0,
+  SignWords none;
+  none.lo = make_uint4(0, 0, 0, 0);
+  none.hi = none.lo;
+  hipLaunchKernelGGL((decode_merge_kernel<false, false, kD>), dim3(hq, batch), dim3(kMThreads), 0,
                      stream, q, hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                     partials, splits, out, make_uint4(0, 0, 0, 0));
+                     partials, splits, out, none);
   return hipGetLastError();
 }
 

@@ -13,22 +13,70 @@
 namespace kvarn {
 
 constexpr int kT = 128;              // tokens per tile
-constexpr int kD = 128;              // head dimension
-constexpr int kKCodesOff = 0;        // key codes: 8,192 bytes
-constexpr int kVCodesOff = 8192;     // value codes: 2,048 bytes per value bit
+constexpr int kD = 128;              // head dimension of the preset
+constexpr int kKCodesOff = 0;        // key codes: 8,192 bytes (head dimension 128)
+constexpr int kVCodesOff = 8192;     // value codes: 2,048 bytes per value bit (head dimension 128)
 constexpr int kCRel = 0, kSRel = 128, kZRel = 256;   // c-hat, s-hat, z-hat in a metadata half
 
-// Record of one (block, KV head) for value codes of kVBits bits: key codes, value codes, then
-// 512 bytes of key metadata and 512 of value metadata. kVBits = 2 is the preset
-// kvarn_k4v2_g128 (13,312 bytes), kVBits = 4 the preset kvarn_k4v4_g128 (17,408 bytes).
-template <int kVBits>
+// Record of one (block, KV head) for value codes of kVBits bits and head dimension kDim:
+// 64 kDim bytes of key codes, 16 kDim kVBits of value codes, then kDim + 384 bytes of key
+// metadata and as many of value metadata (c-hat: kDim bytes, s-hat: 128, z-hat: 256).
+// kDim = 128, kVBits = 2 is the preset kvarn_k4v2_g128 (13,312 bytes); kVBits = 4 the preset
+// kvarn_k4v4_g128 (17,408 bytes); head dimensions 64 and 256 scale the same sections.
+template <int kVBits, int kDim = 128>
 struct RecordLayout {
   static_assert(kVBits == 2 || kVBits == 4, "value codes are 2 or 4 bits");
-  static constexpr int kVCodeBytes = 2048 * kVBits;
-  static constexpr int kKMetaOff = kVCodesOff + kVCodeBytes;
-  static constexpr int kVMetaOff = kKMetaOff + 512;
-  static constexpr int kTileBytes = kKMetaOff + 1024;
+  static_assert(kDim == 64 || kDim == 128 || kDim == 256, "head dimension 64, 128 or 256");
+  static constexpr int kKCodes = 0;
+  static constexpr int kVCodes = 64 * kDim;
+  static constexpr int kVCodeBytes = 16 * kDim * kVBits;
+  static constexpr int kMetaHalf = kDim + 384;
+  static constexpr int kKMetaOff = kVCodes + kVCodeBytes;
+  static constexpr int kVMetaOff = kKMetaOff + kMetaHalf;
+  static constexpr int kTileBytes = kKMetaOff + 2 * kMetaHalf;
+  static constexpr int kC = 0, kS = kDim, kZ = kDim + 128;   // inside a metadata half
 };
+
+// Optional per-channel sign flips before the rotation: channel j is negated when bit j % 32 of
+// word j / 32 is set (words 0-3 in lo, 4-7 in hi; a head dimension d uses the first d / 32).
+struct SignWords {
+  uint4 lo, hi;
+};
+
+__device__ __forceinline__ uint32_t sign_word(const SignWords& s, int i) {
+  const uint4 q = i < 4 ? s.lo : s.hi;
+  const int k = i & 3;
+  return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
+}
+
+// Byte offset (in the value-code section) and bit shift of the value code of token t, channel
+// j. With nb = j / 16, n = j % 16, kb = t / 32, h = (t / 16) % 2, s = (t / 4) % 4, i = t % 4 and
+// e = 2 h + i / 2, in 32-bit words:
+//   2-bit, kDim >= 128: word 2 kDim kb + (kDim / 32)(16 s + n) + 4 (nb / 8) + e,
+//                       bit 2 (nb % 8) + 16 (i % 2)
+//   2-bit, kDim = 64:   word 128 kb + 2 (16 s + n) + e / 2, bit 2 nb + 8 (e % 2) + 16 (i % 2)
+//   4-bit:              word 4 kDim kb + 256 (nb / 4) + 4 (16 s + n) + e,
+//                       bit 4 (nb % 4) + 16 (i % 2)
+// A lane (n, s) of a value product thus finds the codes of its eight tokens of block kb in
+// kDim / 32 (2-bit) or kDim / 16 (4-bit) consecutive words.
+template <int kVBits, int kDim>
+__device__ __forceinline__ void value_code_pos(int t, int j, uint32_t& byte_off, int& shift) {
+  const int nb = j >> 4, n = j & 15, kb = t >> 5, h = (t >> 4) & 1, s = (t >> 2) & 3, i = t & 3;
+  const int e = 2 * h + (i >> 1);
+  int word, bit;
+  if constexpr (kVBits == 2 && kDim >= 128) {
+    word = 2 * kDim * kb + (kDim / 32) * (16 * s + n) + 4 * (nb >> 3) + e;
+    bit = 2 * (nb & 7) + 16 * (i & 1);
+  } else if constexpr (kVBits == 2) {
+    word = 128 * kb + 2 * (16 * s + n) + (e >> 1);
+    bit = 2 * nb + 8 * (e & 1) + 16 * (i & 1);
+  } else {
+    word = 4 * kDim * kb + 256 * (nb >> 2) + 4 * (16 * s + n) + e;
+    bit = 4 * (nb & 3) + 16 * (i & 1);
+  }
+  byte_off = 4u * (uint32_t)word + (uint32_t)(bit >> 3);
+  shift = bit & 7;
+}
 
 // ------------------------------------------------------------------ FP8 E4M3 (non-negative)
 

@@ -1,6 +1,8 @@
 // KVarN tile quantiser (write path) for gfx950.
 //
-// One workgroup of 512 threads quantises one 128-token x 128-channel tile of one KV head,
+// One workgroup of 4 D threads quantises one 128-token x D-channel tile of one KV head (D, the
+// head dimension, is 128 in the preset; 64 and 256 are built the same way, described after the
+// D = 128 layout below),
 // keys or values, through the write-path stages of [GR] "The four-stage pipeline" (groundy.com,
 // "Huawei's KVarN puts KV-cache quantization inside vLLM's backend"):
 //   1. Hadamard rotation along channels: a 128-point fast Walsh-Hadamard transform.
@@ -37,6 +39,15 @@
 //
 // Variances use shifted one-pass sums (shift = the thread's first value), merged between the
 // threads sharing a row or column with Chan et al.'s pairwise update.
+//
+// Other head dimensions. A token has D / 32 threads (lane bits 0 .. log2(D / 32) - 1): channel
+// c = e + 8 q0 + 16 m + 64 q1 + 128 q2 with q2 = lane bit 2 at D = 256, and no q1 at D = 64.
+// The butterfly on channel bit 7 (D = 256) crosses lanes through ds_swizzle and computes the
+// difference on the upper lane exactly (partner - own), so it adds no sign. Layout B keeps 16
+// channels per wave (D / 16 waves). A row's statistics merge over D / 32 threads; the gauge and
+// the per-channel rounding factor use 1 / D and 1 / sqrt(D). Key codes are staged token-major
+// as at D = 128; value codes are ORed into an LDS copy of the section at the positions of
+// value_code_pos() and then stored.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -45,25 +56,36 @@ namespace kvarn {
 
 namespace {
 
-constexpr int kQThreads = 512;
-constexpr int kXs = 144;                             // LDS row stride of the rotated tile
-constexpr int kCp = kD + 4;                          // padded per-channel array length
-constexpr float kInvSqrtD = 0.08838834764831845f;   // 2^-3.5
+// Sizes of the quantiser for head dimension kDim.
+template <int kDim>
+struct QGeom {
+  static constexpr int kThreads = 4 * kDim;                 // 4 kDim / 128 x 128 tokens
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kTPT = kDim / 32;                    // threads per token (layout A)
+  // LDS row stride of the rotated tile: the row plus the cpos padding, rounded so that the
+  // four token rows th = 0..3 read by one layout-B instruction start 16 banks apart
+  static constexpr int kXs = kDim == 64 ? 80 : (kDim == 128 ? 144 : 272);
+  static constexpr int kCp = kDim + 4 * (kDim / 64);        // padded per-channel array length
+  static constexpr float kInvSqrt = kDim == 64 ? 0.125f
+                                  : (kDim == 128 ? 0.08838834764831845f : 0.0625f);
+};
 
-// Position of channel c in an LDS row or per-channel array: channels 64..127 sit 4 floats
+// Position of channel c in an LDS row or per-channel array: each 64-channel block sits 4 floats
 // further on, so the quad lanes holding channel bit 6 = 0 and 1 use different banks.
 __device__ __forceinline__ int cpos(int c) { return c + ((c >> 6) << 2); }
 
+template <int kDim>
 struct QuantSmem {
-  alignas(16) float xt[kT][kXs];   // rotated tile, layout A -> B; reused to stage the packed codes
+  using G = QGeom<kDim>;
+  alignas(16) float xt[kT][G::kXs];   // rotated tile, layout A -> B; reused to stage the codes
   float u[4][kT / 4];    // per-token multipliers 1 / r_t, token t at [t % 4][t / 4]
-  float cs[kD];          // per-channel standard deviations (unrounded c before the gauge)
-  float vinv[kCp];       // per-channel multipliers 1 / c_j (at cpos)
-  float rq[kCp];         // per-channel rounding factor 2^-3.5 / c-hat_j (at cpos)
+  float cs[kDim];        // per-channel standard deviations (unrounded c before the gauge)
+  float vinv[G::kCp];    // per-channel multipliers 1 / c_j (at cpos)
+  float rq[G::kCp];      // per-channel rounding factor (1 / sqrt(D)) / c-hat_j (at cpos)
   uint32_t meta[96];     // staged FP8 s-hat (32 words) and FP16 z-hat (64 words)
-  uint32_t chat[32];     // staged FP8 c-hat
-  float red[32];
-  alignas(16) uint32_t sgn[64];   // sign-flip masks of channel pairs (2 i, 2 i + 1), fp16 bits
+  uint32_t chat[kDim / 4];   // staged FP8 c-hat
+  float red[3 * G::kWaves];  // per-wave maxima: |rotated|, column multipliers, row multipliers
+  alignas(16) uint32_t sgn[kDim / 2];   // sign-flip masks of channel pairs (2 i, 2 i + 1)
 };
 
 constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
@@ -194,10 +216,40 @@ __device__ __forceinline__ uint32_t put_code(float v, float qmax, uint32_t sel, 
 }
 
 // This thread's codes (token t, its 32 channels) into the LDS staging area (see the callers).
-template <bool kClamp, int kVBits>
+// q2 is used at kDim = 256 only, q1 at kDim >= 128 only.
+template <bool kClamp, int kVBits, int kDim>
 __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, float qmax,
-                                            int is_v, int t, int q0, int q1, uint32_t* stage) {
-  if (is_v && kVBits == 4) {
+                                            int is_v, int t, int q0, int q1, int q2,
+                                            uint32_t* stage) {
+  if (!is_v) {
+    // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 + 16 q2
+    // of the token's kDim / 8 words (channel 8 k + e at nibble e of word k)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        lo = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
+        hi = put_code<kClamp>(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
+      }
+      stage[t * (kDim / 8) + q0 + 2 * m + 8 * q1 + 16 * q2] = lo | (hi << 4);
+    }
+  } else if constexpr (kDim != 128) {
+    // value codes of the other head dimensions: each code ORed into its word of an LDS copy of
+    // the section (cleared by the caller)
+    const int cbase = 8 * q0 + 64 * q1 + 128 * q2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t code = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, 0, 0);
+        uint32_t byte_off;
+        int shift;
+        value_code_pos<kVBits, kDim>(t, cbase + 16 * m + e, byte_off, shift);
+        atomicOr(&stage[byte_off >> 2], code << (8 * (byte_off & 3u) + shift));
+      }
+    }
+  } else if constexpr (kVBits == 4) {
     // 4-bit value codes. Channel 16 nb + n with nb = m + 4 q1, n = 8 q0 + e: half-word i % 2 of
     // section word 512 kb + 256 q1 + 4 (16 s + n) + 2 h + i / 2 holds the codes of
     // nb % 4 = m = 0..3 at bits 4 m (t = 32 kb + 16 h + 4 s + i). The section is staged in
@@ -217,19 +269,6 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
       od = put_code<kClamp>(fmaf(x[8 + e], ca, cb), qmax, 0, od);
       od = put_code<kClamp>(fmaf(x[24 + e], ca, cb), qmax, 1, od);
       sh[8 * (c0 + (e ^ sw)) + lo] = (uint16_t)(ev | (od << 4));
-    }
-  } else if (!is_v) {
-    // key codes: token-major nibbles; group m of this thread is word q0 + 2 m + 8 q1 of the
-    // token's 16 words (channel 8 k + e at nibble e of word k)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        lo = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
-        hi = put_code<kClamp>(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
-      }
-      stage[t * 16 + q0 + 2 * m + 8 * q1] = lo | (hi << 4);
     }
   } else {
     // value codes. Byte e of this thread holds the codes of channel n = 8 q0 + e, hf = q1,
@@ -254,37 +293,47 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
   }
 }
 
-template <int kVBits>
+template <int kVBits, int kDim>
 __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, int tid) {
   // All-zero rotated tile: c-hat = 1 (E4M3 0x38), s-hat = 0, z-hat = +0, every code 0.
-  using L = RecordLayout<kVBits>;
-  const int code_off = is_v ? kVCodesOff : kKCodesOff;
-  const int code_bytes = is_v ? L::kVCodeBytes : 8192;
+  using L = RecordLayout<kVBits, kDim>;
+  const int code_off = is_v ? L::kVCodes : L::kKCodes;
+  const int code_bytes = is_v ? L::kVCodeBytes : 64 * kDim;
   const int meta = is_v ? L::kVMetaOff : L::kKMetaOff;
   const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int i = tid; i < code_bytes / 16; i += kQThreads)
+  for (int i = tid; i < code_bytes / 16; i += QGeom<kDim>::kThreads)
     reinterpret_cast<uint4*>(rec + code_off)[i] = z;
-  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kCRel)[tid] = 0x38383838u;
-  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kSRel)[tid] = 0u;
-  if (tid < 64) reinterpret_cast<uint32_t*>(rec + meta + kZRel)[tid] = 0u;
+  if (tid < kDim / 4) reinterpret_cast<uint32_t*>(rec + meta + L::kC)[tid] = 0x38383838u;
+  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + L::kS)[tid] = 0u;
+  if (tid < 64) reinterpret_cast<uint32_t*>(rec + meta + L::kZ)[tid] = 0u;
+}
+
+// ds_swizzle across lane bit 2 (bit-mask mode: and 0x1F, xor 4, within 32 lanes).
+__device__ __forceinline__ float swz_xor4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (4 << 10) | 0x1F));
 }
 
 // Quantise one tile. `src` points at token 0, channel 0 of this KV head; token t starts at
 // src + t * token_stride. If `row127` is not null it replaces token 127 (the append path
 // passes the new token there). Writes the key or value half of the record at `rec` (value
-// codes of kVBits bits).
-template <int kVBits>
+// codes of kVBits bits, head dimension kDim).
+template <int kVBits, int kDim>
 __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
                                               long long token_stride,
                                               const __half* __restrict__ row127, int is_v,
-                                              int iters, uint4 signs, uint8_t* __restrict__ rec,
-                                              QuantSmem& sm) {
+                                              int iters, SignWords signs,
+                                              uint8_t* __restrict__ rec, QuantSmem<kDim>& sm) {
+  using G = QGeom<kDim>;
+  using L = RecordLayout<kVBits, kDim>;
+  constexpr int kXs = G::kXs, kQW = G::kWaves, kTPT = G::kTPT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t = tid >> 2, q0 = tid & 1, q1 = (tid >> 1) & 1;   // layout A
+  const int t = tid / kTPT, q0 = tid & 1;                       // layout A
+  const int q1 = kDim >= 128 ? (tid >> 1) & 1 : 0;
+  const int q2 = kDim == 256 ? (tid >> 2) & 1 : 0;
   const int jj = 16 * wave + (lane & 15), th = lane >> 4;     // layout B
-  const int cbase = 8 * q0 + 64 * q1;                           // channel of x[0]
+  const int cbase = 8 * q0 + 64 * q1 + 128 * q2;                // channel of x[0]
   const int pbase = cpos(cbase);                                // its LDS position
   const bool flip = (q0 ^ q1) != 0;                             // values carry a factor -1
 
@@ -297,10 +346,12 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     uint4 w[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) w[m] = r4[2 * m];                // channels cbase + 16 m ..
-    if ((signs.x | signs.y | signs.z | signs.w) != 0u) {        // optional sign flips
-      if (tid < 64) {
-        const uint32_t word = tid < 32 ? (tid < 16 ? signs.x : signs.y)
-                                       : (tid < 48 ? signs.z : signs.w);
+    uint32_t any = 0;
+#pragma unroll
+    for (int i = 0; i < kDim / 32; ++i) any |= sign_word(signs, i);
+    if (any != 0u) {                                            // optional sign flips
+      if (tid < kDim / 2) {
+        const uint32_t word = sign_word(signs, tid >> 4);
         const uint32_t b2 = (word >> (2 * (tid & 15))) & 3u;
         sm.sgn[tid] = ((b2 & 1u) << 15) | ((b2 >> 1) << 31);
       }
@@ -329,8 +380,15 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     const float s1 = q0 ? -1.0f : 1.0f, s2 = q1 ? -1.0f : 1.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) fmac_xor1(x + 8 * g, s1);      // channel bit 3
+    if constexpr (kDim >= 128) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) fmac_xor2(x + 8 * g, s2);      // channel bit 6
+      for (int g = 0; g < 4; ++g) fmac_xor2(x + 8 * g, s2);    // channel bit 6
+    }
+    if constexpr (kDim == 256) {                                // channel bit 7, exact
+      const float s4 = q2 ? -1.0f : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = fmaf(s4, x[i], swz_xor4(x[i]));
+    }
   }
   float amax = 0.0f;
 #pragma unroll
@@ -352,15 +410,16 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   __syncthreads();
   float big = sm.red[0];
 #pragma unroll
-  for (int w = 1; w < kQThreads / 64; ++w) big = max_nn(big, sm.red[w]);
+  for (int w = 1; w < kQW; ++w) big = max_nn(big, sm.red[w]);
   if (big == 0.0f) {                              // uniform across the workgroup
-    store_record_zero_tile<kVBits>(rec, is_v, tid);
+    store_record_zero_tile<kVBits, kDim>(rec, is_v, tid);
     return;
   }
   const float* xcol = &sm.xt[th][cpos(jj)];       // column jj, tokens th + 4 i, stride 4 kXs
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
+  constexpr float kInvD = 1.0f / kDim;
   float umax = 1.0f;
   for (int it = 0; it < iters; ++it) {
     // column step (layout B): std over tokens of xt_tj * u_t
@@ -394,14 +453,14 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
         const float vi = __builtin_amdgcn_rcpf(sd);
         if (th == 0) sm.vinv[cpos(jj)] = vi;
         const float vm = row16_max(vi);           // the wave's 16 channels are one DPP row
-        if (lane == 0) sm.red[8 + wave] = vm;
+        if (lane == 0) sm.red[kQW + wave] = vm;
       }
     }
     __syncthreads();
     if (it == iters - 1) break;
-    float vmax = sm.red[8];
+    float vmax = sm.red[kQW];
 #pragma unroll
-    for (int w = 1; w < kQThreads / 64; ++w) vmax = max_nn(vmax, sm.red[8 + w]);
+    for (int w = 1; w < kQW; ++w) vmax = max_nn(vmax, sm.red[kQW + w]);
     // row step (layout A): std over channels of xt_tj * v_j
     {
       const float* vv = sm.vinv + pbase;
@@ -422,37 +481,57 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
         mh = 0.5f * dpp_add<kDppXor1>(mh, mh);
         qh = fmaf(16.0f * d, d, qs);
       }
-      {
+      if constexpr (kDim >= 128) {
         const float d = dpp_sub<kDppXor2>(mh, mh);
-        qh = fmaf(32.0f * d, d, dpp_add<kDppXor2>(qh, qh));
+        const float qs = dpp_add<kDppXor2>(qh, qh);
+        if constexpr (kDim == 256) mh = 0.5f * dpp_add<kDppXor2>(mh, mh);
+        qh = fmaf(32.0f * d, d, qs);
       }
-      const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * vmax);
+      if constexpr (kDim == 256) {               // and across lane bit 2 (128 channels each)
+        const float d = swz_xor4(mh) - mh;
+        qh = fmaf(64.0f * d, d, qh + swz_xor4(qh));
+      }
+      const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * kInvD), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
-      if ((tid & 3) == 0) sm.u[t & 3][t >> 2] = uinv;
+      if ((tid & (kTPT - 1)) == 0) sm.u[t & 3][t >> 2] = uinv;
       const float um = max_xor48_nn(row16_max(uinv));
-      if (lane == 0) sm.red[16 + wave] = um;
+      if (lane == 0) sm.red[2 * kQW + wave] = um;
     }
     __syncthreads();
-    umax = sm.red[16];
+    umax = sm.red[2 * kQW];
 #pragma unroll
-    for (int w = 1; w < kQThreads / 64; ++w) umax = max_nn(umax, sm.red[16 + w]);
+    for (int w = 1; w < kQW; ++w) umax = max_nn(umax, sm.red[2 * kQW + w]);
   }
 
-  // ---- gauge (geometric mean of c = 1) and FP8 rounding of c, by wave 0
-  const int meta = is_v ? RecordLayout<kVBits>::kVMetaOff : RecordLayout<kVBits>::kKMetaOff;
+  // ---- gauge (geometric mean of c = 1) and FP8 rounding of c, by wave 0 (lane: channels
+  // lane + 64 k)
+  const int meta = is_v ? L::kVMetaOff : L::kKMetaOff;
   if (wave == 0) {
-    const float c0 = sm.cs[lane], c1 = sm.cs[lane + 64];
-    const float lsum = wave_sum(log2f(c0) + log2f(c1));
-    const float g = exp2f(-lsum * 0.0078125f);
-    const uint32_t e0 = e4m3_rne(fminf(fmaxf(c0 * g, 0.001953125f), 448.0f));
-    const uint32_t e1 = e4m3_rne(fminf(fmaxf(c1 * g, 0.001953125f), 448.0f));
-    sm.rq[cpos(lane)] = kInvSqrtD / e4m3_to_float(e0);
-    sm.rq[cpos(lane + 64)] = kInvSqrtD / e4m3_to_float(e1);
-    reinterpret_cast<uint8_t*>(sm.chat)[lane] = (uint8_t)e0;
-    reinterpret_cast<uint8_t*>(sm.chat)[lane + 64] = (uint8_t)e1;
+    float cl[kDim / 64];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kDim / 64; ++k) {
+      cl[k] = sm.cs[lane + 64 * k];
+      lsum += log2f(cl[k]);
+    }
+    lsum = wave_sum(lsum);
+    const float g = exp2f(-lsum * kInvD);
+#pragma unroll
+    for (int k = 0; k < kDim / 64; ++k) {
+      const uint32_t e = e4m3_rne(fminf(fmaxf(cl[k] * g, 0.001953125f), 448.0f));
+      sm.rq[cpos(lane + 64 * k)] = G::kInvSqrt / e4m3_to_float(e);
+      reinterpret_cast<uint8_t*>(sm.chat)[lane + 64 * k] = (uint8_t)e;
+    }
   }
   __syncthreads();   // also: every read of sm.xt is done, so it may hold the packed codes
-  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kCRel)[tid] = sm.chat[tid];
+  if (tid < kDim / 4) reinterpret_cast<uint32_t*>(rec + meta + L::kC)[tid] = sm.chat[tid];
+  uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
+  if constexpr (kDim != 128) {                      // cleared LDS copy of the value section
+    if (is_v) {
+      for (int i = tid; i < L::kVCodeBytes / 16; i += G::kThreads)
+        reinterpret_cast<uint4*>(stage)[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
 
   // ---- asymmetric RTN per token (layout A); p = (+-) y, sign `flip`
   const float qmax = is_v ? (float)((1 << kVBits) - 1) : 15.0f;
@@ -469,8 +548,14 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   float mn = flip ? -pmax : pmin, mx = flip ? -pmin : pmax;
   mn = fminf(mn, quad_swap<kDppXor1>(mn));
   mx = fmaxf(mx, quad_swap<kDppXor1>(mx));
-  mn = fminf(mn, quad_swap<kDppXor2>(mn));
-  mx = fmaxf(mx, quad_swap<kDppXor2>(mx));
+  if constexpr (kDim >= 128) {
+    mn = fminf(mn, quad_swap<kDppXor2>(mn));
+    mx = fmaxf(mx, quad_swap<kDppXor2>(mx));
+  }
+  if constexpr (kDim == 256) {
+    mn = fminf(mn, swz_xor4(mn));
+    mx = fmaxf(mx, swz_xor4(mx));
+  }
   const uint32_t zbits = fp16_rd(fmaxf(mn, -65504.0f));
   const float zf = fp16_bits_to_float(zbits);
   const uint32_t scode = e4m3_ru((mx - zf) / qmax);
@@ -478,20 +563,26 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   const float inv_s = sf > 0.0f ? 1.0f / sf : 0.0f;
   const float ca = flip ? -inv_s : inv_s;          // (y - z) / s = p * ca + cb
   const float cb = -zf * inv_s;
-  if ((tid & 3) == 0) {
+  if ((tid & (kTPT - 1)) == 0) {
     reinterpret_cast<uint8_t*>(sm.meta)[t] = (uint8_t)scode;
     reinterpret_cast<uint16_t*>(sm.meta + 32)[t] = (uint16_t)zbits;
   }
+  if constexpr (kDim != 128) {
+    if (is_v) __syncthreads();                      // the cleared section before the ORs
+  }
 
-  uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
   if (scode == 0x7Eu)                                   // s-hat = 448
-    stage_codes<true, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
+    stage_codes<true, kVBits, kDim>(x, ca, cb, qmax, is_v, t, q0, q1, q2, stage);
   else
-    stage_codes<false, kVBits>(x, ca, cb, qmax, is_v, t, q0, q1, stage);
-  if (!is_v) {                                         // staged as the section: 8,192 bytes
+    stage_codes<false, kVBits, kDim>(x, ca, cb, qmax, is_v, t, q0, q1, q2, stage);
+  if (!is_v) {                                         // staged as the section: 64 kDim bytes
     __syncthreads();
-    reinterpret_cast<uint4*>(rec + kKCodesOff)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
-  } else if (kVBits == 4) {                            // chunk tid sits at tid ^ (s + 4 q1)
+    reinterpret_cast<uint4*>(rec + L::kKCodes)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+  } else if constexpr (kDim != 128) {
+    __syncthreads();
+    if (tid < L::kVCodeBytes / 16)
+      reinterpret_cast<uint4*>(rec + L::kVCodes)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+  } else if constexpr (kVBits == 4) {                  // chunk tid sits at tid ^ (s + 4 q1)
     __syncthreads();
     const int sw = ((tid >> 4) & 3) + 4 * ((tid >> 6) & 1);
     reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] =
@@ -509,18 +600,18 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] = make_uint4(out[0], out[1], out[2], out[3]);
     }
   }
-  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + kSRel)[tid] = sm.meta[tid];
-  else if (tid < 96) reinterpret_cast<uint32_t*>(rec + meta + kZRel)[tid - 32] = sm.meta[tid];
+  if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + L::kS)[tid] = sm.meta[tid];
+  else if (tid < 96) reinterpret_cast<uint32_t*>(rec + meta + L::kZ)[tid - 32] = sm.meta[tid];
 }
 
 // grid: 2 * num_kv_heads * n_tiles workgroups; id = (tile * Hkv + head) * 2 + kv
-template <int kVBits>
-__global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <int kVBits, int kDim>
+__global__ void __launch_bounds__(4 * kDim) __attribute__((amdgpu_waves_per_eu(4, 4)))
 quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v,
                       long long token_stride, int n_tiles, int hkv,
                       const int32_t* __restrict__ dst_blocks, uint8_t* __restrict__ pool,
-                      long long num_blocks, int iters, uint4 signs) {
-  __shared__ QuantSmem sm;
+                      long long num_blocks, int iters, SignWords signs) {
+  __shared__ QuantSmem<kDim> sm;
   const int id = blockIdx.x;
   const int is_v = id & 1;
   const int head = (id >> 1) % hkv;
@@ -528,21 +619,21 @@ quantize_tiles_kernel(const __half* __restrict__ k, const __half* __restrict__ v
   if (tile >= n_tiles) return;
   const long long blk = dst_blocks[tile];
   if (blk < 0 || blk >= num_blocks) return;
-  const __half* src = (is_v ? v : k) + (long long)tile * kT * token_stride + head * kD;
-  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits>::kTileBytes;
-  quantize_tile<kVBits>(src, token_stride, nullptr, is_v, iters, signs, rec, sm);
+  const __half* src = (is_v ? v : k) + (long long)tile * kT * token_stride + head * kDim;
+  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits, kDim>::kTileBytes;
+  quantize_tile<kVBits, kDim>(src, token_stride, nullptr, is_v, iters, signs, rec, sm);
 }
 
 // grid: 2 * num_kv_heads * batch workgroups; id = (b * Hkv + head) * 2 + kv
-template <int kVBits>
-__global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <int kVBits, int kDim>
+__global__ void __launch_bounds__(4 * kDim) __attribute__((amdgpu_waves_per_eu(4, 4)))
 append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__ v_new,
                     const int32_t* __restrict__ positions,
                     const int32_t* __restrict__ block_table, int max_blocks,
                     __half* __restrict__ staging_k, __half* __restrict__ staging_v,
                     uint8_t* __restrict__ pool, long long num_blocks, int hkv, int iters,
-                    uint4 signs) {
-  __shared__ QuantSmem sm;
+                    SignWords signs) {
+  __shared__ QuantSmem<kDim> sm;
   const int id = blockIdx.x;
   const int is_v = id & 1;
   const int head = (id >> 1) % hkv;
@@ -550,10 +641,10 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
   const int pos = positions[b];
   if (pos < 0) return;
   const int slot = pos & (kT - 1);
-  const __half* src_tok = (is_v ? v_new : k_new) + ((long long)b * hkv + head) * kD;
-  __half* stg = (is_v ? staging_v : staging_k) + ((long long)b * hkv + head) * kT * kD;
-  if (threadIdx.x < 16) {
-    reinterpret_cast<uint4*>(stg + slot * kD)[threadIdx.x] =
+  const __half* src_tok = (is_v ? v_new : k_new) + ((long long)b * hkv + head) * kDim;
+  __half* stg = (is_v ? staging_v : staging_k) + ((long long)b * hkv + head) * kT * kDim;
+  if (threadIdx.x < kDim / 8) {
+    reinterpret_cast<uint4*>(stg + slot * kDim)[threadIdx.x] =
         reinterpret_cast<const uint4*>(src_tok)[threadIdx.x];
   }
   if (slot != kT - 1) return;
@@ -561,9 +652,37 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
   if (bi >= max_blocks) return;
   const long long blk = block_table[(long long)b * max_blocks + bi];
   if (blk < 0 || blk >= num_blocks) return;
-  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits>::kTileBytes;
+  uint8_t* rec = pool + (blk * hkv + head) * (long long)RecordLayout<kVBits, kDim>::kTileBytes;
   // token 127 comes from the new token itself, so no read-after-write through global memory
-  quantize_tile<kVBits>(stg, kD, src_tok, is_v, iters, signs, rec, sm);
+  quantize_tile<kVBits, kDim>(stg, kDim, src_tok, is_v, iters, signs, rec, sm);
+}
+
+SignWords sign_words(const uint32_t* signs) {
+  SignWords s;
+  s.lo = make_uint4(signs[0], signs[1], signs[2], signs[3]);
+  s.hi = make_uint4(signs[4], signs[5], signs[6], signs[7]);
+  return s;
+}
+
+template <int kVBits, int kDim>
+void launch_quantize_t(const __half* k, const __half* v, long long token_stride, int n_tiles,
+                       int hkv, const int32_t* dst_blocks, uint8_t* pool, long long num_blocks,
+                       int iters, SignWords sg, hipStream_t stream) {
+  const long long groups = 2LL * hkv * n_tiles;
+  hipLaunchKernelGGL((quantize_tiles_kernel<kVBits, kDim>), dim3((unsigned)groups),
+                     dim3(4 * kDim), 0, stream, k, v, token_stride, n_tiles, hkv, dst_blocks,
+                     pool, num_blocks, iters, sg);
+}
+
+template <int kVBits, int kDim>
+void launch_append_t(const __half* k_new, const __half* v_new, const int32_t* positions,
+                     const int32_t* block_table, int max_blocks, __half* staging_k,
+                     __half* staging_v, uint8_t* pool, long long num_blocks, int hkv, int batch,
+                     int iters, SignWords sg, hipStream_t stream) {
+  const long long groups = 2LL * hkv * batch;
+  hipLaunchKernelGGL((append_token_kernel<kVBits, kDim>), dim3((unsigned)groups),
+                     dim3(4 * kDim), 0, stream, k_new, v_new, positions, block_table,
+                     max_blocks, staging_k, staging_v, pool, num_blocks, hkv, iters, sg);
 }
 
 }  // namespace
@@ -571,17 +690,20 @@ append_token_kernel(const __half* __restrict__ k_new, const __half* __restrict__
 hipError_t launch_quantize_tiles(const __half* k, const __half* v, long long token_stride,
                                  int n_tiles, int hkv, const int32_t* dst_blocks,
                                  uint8_t* pool, long long num_blocks, int iters,
-                                 const uint32_t* signs, int v_bits, hipStream_t stream) {
-  const long long groups = 2LL * hkv * n_tiles;
-  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  if (v_bits == 4)
-    hipLaunchKernelGGL(quantize_tiles_kernel<4>, dim3((unsigned)groups), dim3(kQThreads), 0,
-                       stream, k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks,
-                       iters, sg);
-  else
-    hipLaunchKernelGGL(quantize_tiles_kernel<2>, dim3((unsigned)groups), dim3(kQThreads), 0,
-                       stream, k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks,
-                       iters, sg);
+                                 const uint32_t* signs, int v_bits, int head_dim,
+                                 hipStream_t stream) {
+  const SignWords sg = sign_words(signs);
+#define KVARN_Q(VB, DIM)                                                                    \
+  launch_quantize_t<VB, DIM>(k, v, token_stride, n_tiles, hkv, dst_blocks, pool, num_blocks, \
+                             iters, sg, stream)
+  if (head_dim == 64) {
+    if (v_bits == 4) KVARN_Q(4, 64); else KVARN_Q(2, 64);
+  } else if (head_dim == 256) {
+    if (v_bits == 4) KVARN_Q(4, 256); else KVARN_Q(2, 256);
+  } else {
+    if (v_bits == 4) KVARN_Q(4, 128); else KVARN_Q(2, 128);
+  }
+#undef KVARN_Q
   return hipGetLastError();
 }
 
@@ -589,18 +711,20 @@ hipError_t launch_append_token(const __half* k_new, const __half* v_new,
                                const int32_t* positions, const int32_t* block_table,
                                int max_blocks, __half* staging_k, __half* staging_v,
                                uint8_t* pool, long long num_blocks, int hkv, int batch,
-                               int iters, const uint32_t* signs, int v_bits,
+                               int iters, const uint32_t* signs, int v_bits, int head_dim,
                                hipStream_t stream) {
-  const long long groups = 2LL * hkv * batch;
-  const uint4 sg = make_uint4(signs[0], signs[1], signs[2], signs[3]);
-  if (v_bits == 4)
-    hipLaunchKernelGGL(append_token_kernel<4>, dim3((unsigned)groups), dim3(kQThreads), 0,
-                       stream, k_new, v_new, positions, block_table, max_blocks, staging_k,
-                       staging_v, pool, num_blocks, hkv, iters, sg);
-  else
-    hipLaunchKernelGGL(append_token_kernel<2>, dim3((unsigned)groups), dim3(kQThreads), 0,
-                       stream, k_new, v_new, positions, block_table, max_blocks, staging_k,
-                       staging_v, pool, num_blocks, hkv, iters, sg);
+  const SignWords sg = sign_words(signs);
+#define KVARN_A(VB, DIM)                                                                      \
+  launch_append_t<VB, DIM>(k_new, v_new, positions, block_table, max_blocks, staging_k,       \
+                           staging_v, pool, num_blocks, hkv, batch, iters, sg, stream)
+  if (head_dim == 64) {
+    if (v_bits == 4) KVARN_A(4, 64); else KVARN_A(2, 64);
+  } else if (head_dim == 256) {
+    if (v_bits == 4) KVARN_A(4, 256); else KVARN_A(2, 256);
+  } else {
+    if (v_bits == 4) KVARN_A(4, 128); else KVARN_A(2, 128);
+  }
+#undef KVARN_A
   return hipGetLastError();
 }
 

@@ -6,40 +6,47 @@ only decodes the documented byte layout so that records can be compared field by
 
 import numpy as np
 
-T = D = 128
-SIZES = {13312: 2, 17408: 4}          # record bytes -> value bits
+T = 128
+# record bytes -> (head dimension D, value bits): 64 D key-code bytes, 16 D vbits value-code
+# bytes, two metadata halves of D + 384 bytes
+SIZES = {64 * d + 16 * d * vb + 2 * (d + 384): (d, vb) for d in (64, 128, 256) for vb in (2, 4)}
 
 
-def _v_index(vbits):
-    t, j = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
+def _v_index(vbits, d):
+    t, j = np.meshgrid(np.arange(T), np.arange(d), indexing="ij")
     nb, n = j // 16, j % 16
     kb, h, s, i = t // 32, (t // 16) % 2, (t // 4) % 4, t % 4
-    if vbits == 2:
-        word = 256 * kb + 4 * (16 * s + n) + 2 * h + i // 2
-        bit = 2 * nb + 16 * (i % 2)
+    e = 2 * h + i // 2
+    if vbits == 2 and d >= 128:
+        word = 2 * d * kb + (d // 32) * (16 * s + n) + 4 * (nb // 8) + e
+        bit = 2 * (nb % 8) + 16 * (i % 2)
+    elif vbits == 2:
+        word = 128 * kb + 2 * (16 * s + n) + e // 2
+        bit = 2 * nb + 8 * (e % 2) + 16 * (i % 2)
     else:
-        word = 512 * kb + 256 * (nb // 4) + 4 * (16 * s + n) + 2 * h + i // 2
+        word = 4 * d * kb + 256 * (nb // 4) + 4 * (16 * s + n) + e
         bit = 4 * (nb % 4) + 16 * (i % 2)
     return word, bit
 
 
-_VIDX = {vb: _v_index(vb) for vb in (2, 4)}
+_VIDX = {(vb, d): _v_index(vb, d) for vb in (2, 4) for d in (64, 128, 256)}
 
 
 def parse(rec: np.ndarray) -> dict:
     rec = np.asarray(rec, np.uint8)
-    vbits = SIZES[rec.shape[0]]
-    k_meta = 8192 + 2048 * vbits
-    kb = rec[:8192].reshape(T, 64).astype(np.int64)
-    kc = np.stack([kb & 15, kb >> 4], axis=-1).reshape(T, D)
-    words = rec[8192:k_meta].view("<u4").astype(np.int64)
-    vw, vbit = _VIDX[vbits]
+    d, vbits = SIZES[rec.shape[0]]
+    kcode = 64 * d
+    k_meta = kcode + 16 * d * vbits
+    kb = rec[:kcode].reshape(T, d // 2).astype(np.int64)
+    kc = np.stack([kb & 15, kb >> 4], axis=-1).reshape(T, d)
+    words = rec[kcode:k_meta].view("<u4").astype(np.int64)
+    vw, vbit = _VIDX[(vbits, d)]
     vc = (words[vw] >> vbit) & ((1 << vbits) - 1)
-    out = dict(k_codes=kc, v_codes=vc, v_bits=vbits)
-    for name, off in (("k", k_meta), ("v", k_meta + 512)):
-        out[name + "_c"] = rec[off:off + 128].copy()
-        out[name + "_s"] = rec[off + 128:off + 256].copy()
-        out[name + "_z"] = rec[off + 256:off + 512].view("<u2").copy()
+    out = dict(k_codes=kc, v_codes=vc, v_bits=vbits, head_dim=d)
+    for name, off in (("k", k_meta), ("v", k_meta + d + 384)):
+        out[name + "_c"] = rec[off:off + d].copy()
+        out[name + "_s"] = rec[off + d:off + d + 128].copy()
+        out[name + "_z"] = rec[off + d + 128:off + d + 384].view("<u2").copy()
     return out
 
 
@@ -66,7 +73,7 @@ class Budget:
 
     def check(self, flip_rate=1e-4, code_rate=1e-4):
         # at most 1e-4 of the scale values and of the codes, and never more than one of each
-        # when fewer than 10,000 were compared (a single tile holds 768 scale values)
+        # when fewer than 10,000 were compared (a tile holds 2 (D + 256) scale values)
         assert self.scale_flips <= max(1, int(flip_rate * self.values)), vars(self)
         assert self.code_off_by_one <= max(1, int(code_rate * self.elements)), vars(self)
 
@@ -87,7 +94,7 @@ def compare_half(gpu: dict, ora: dict, name: str, bits: int, budget: Budget):
     qmax = 2 ** bits - 1
     gc, gs, gz = gpu[name + "_c"].astype(np.int64), gpu[name + "_s"].astype(np.int64), gpu[name + "_z"]
     oc, os_, oz = ora["c_code"].astype(np.int64), ora["s_code"].astype(np.int64), ora["z_bits"]
-    budget.values += 3 * 128
+    budget.values += len(gc) + 2 * 128
     # per-channel scale (round to nearest): boundary = midpoint of the two codes
     dc = gc != oc
     if dc.any():

@@ -35,16 +35,50 @@ def test_header_and_binding_agree():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvarn_abi_version() == 4
+    assert lib.kvarn_abi_version() == 5
 
 
 def test_sizes(lib):
     cfg = kv.default_config(8)
     assert kv.tile_bytes(cfg) == 13312
     assert kv.block_bytes(cfg) == 8 * 13312
-    bad = kv.default_config(8)
-    bad.head_dim = 64
-    assert kv.tile_bytes(bad) == 0 and kv.block_bytes(bad) == 0
+    for d in (32, 96, 512):
+        bad = kv.default_config(8)
+        bad.head_dim = d
+        assert kv.tile_bytes(bad) == 0 and kv.block_bytes(bad) == 0
+
+
+@pytest.mark.parametrize("d,vb,size", [(64, 2, 7040), (64, 4, 9088), (128, 2, 13312),
+                                       (128, 4, 17408), (256, 2, 25856), (256, 4, 34048)])
+def test_head_dim_record_sizes_match_the_layout(lib, d, vb, size):
+    cfg = kv.default_config(4, v_bits=vb, head_dim=d)
+    assert kv.tile_bytes(cfg) == size == 64 * d + 16 * d * vb + 2 * (d + 384)
+    assert kv.block_bytes(cfg) == 4 * size
+
+
+def test_head_dim_rules(lib):
+    # token_stride must cover num_kv_heads * head_dim
+    c64 = kv.default_config(8, head_dim=64)
+    assert lib.kvarn_quantize_tiles(ctypes.byref(c64), FAKE, FAKE, 8 * 64 - 8, 1, FAKE, FAKE, 1,
+                                    None) == SHAPE
+    c256 = kv.default_config(8, head_dim=256)
+    assert lib.kvarn_quantize_tiles(ctypes.byref(c256), FAKE, FAKE, 8 * 128, 1, FAKE, FAKE, 1,
+                                    None) == SHAPE
+    # sign words past head_dim / 32 must be zero: word 2 is channel 64.. at head_dim 64
+    assert kv.tile_bytes(kv.default_config(8, head_dim=64, rotation_signs=[1, 1])) == 7040
+    assert kv.tile_bytes(kv.default_config(8, head_dim=64, rotation_signs=[0, 0, 1])) == 0
+    assert kv.tile_bytes(kv.default_config(8, rotation_signs=[0, 0, 0, 0, 1])) == 0
+    assert kv.tile_bytes(kv.default_config(8, head_dim=256, rotation_signs=[0] * 7 + [1])) > 0
+    # the fp16 comparison cache exists at head_dim 128 only
+    assert kv.fp16_block_bytes(c64) == 0 and kv.fp16_block_bytes(c256) == 0
+    assert lib.kvarn_fp16_write_tiles(ctypes.byref(c64), FAKE, FAKE, 1024, 1, FAKE, FAKE, 1,
+                                      None) == UNSUP
+    # the workspace holds one partial of 2 + head_dim floats per query head and split; these
+    # sizes take the four-wave tile kernel at every head dimension (eight query heads per KV
+    # head), so the split plan is the same
+    ws = {d: kv.decode_workspace_bytes(kv.default_config(8, head_dim=d), 16, 64, 128)
+          for d in (64, 128, 256)}
+    assert ws[64] * 130 == ws[128] * 66 and ws[256] * 130 == ws[128] * 258
 
 
 def test_value_bit_presets(lib):
@@ -127,9 +161,9 @@ def _cfg(**kw):
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
-@pytest.mark.parametrize("field,value", [("head_dim", 64), ("block_tokens", 64), ("k_bits", 2),
-                                         ("v_bits", 3), ("v_bits", 8), ("sinkhorn_iters", 0),
-                                         ("sinkhorn_iters", 17)])
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("head_dim", 32), ("block_tokens", 64),
+                                         ("k_bits", 2), ("v_bits", 3), ("v_bits", 8),
+                                         ("sinkhorn_iters", 0), ("sinkhorn_iters", 17)])
 def test_unsupported_configs(lib, field, value):
     st = _call(lib, "kvarn_quantize_tiles", _cfg(**{field: value}), FAKE, FAKE, 256, 1, FAKE,
                FAKE, 1, None)
@@ -297,7 +331,7 @@ def test_status_strings(lib):
 
 def test_binding_raises_on_error(lib):
     cfg = kv.default_config(2)
-    cfg.head_dim = 64
+    cfg.head_dim = 96
     with pytest.raises(kv.KvarnError) as e:
         kv.decode_workspace_bytes(cfg, 1, 2, 1)
     assert e.value.code == UNSUP
