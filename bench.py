@@ -58,6 +58,11 @@ def parse():
     p.add_argument("--no-extras", action="store_true",
                    help="skip the bandwidth probes, warm-cache, rounds sweep, layer-stream and "
                         "write-stream measurements")
+    p.add_argument("--no-head-dims", action="store_true",
+                   help="skip the 16K workload at head dimensions 64 and 256")
+    p.add_argument("--host-workers", type=int, default=0,
+                   help="processes for the host phase (0 = the usable cores, at most 16); use 1 "
+                        "under a profiler that initialises the GPU before the program starts")
     return p.parse_args()
 
 
@@ -79,14 +84,15 @@ def source_digest(part=None):
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(lens, hkv, hq, appended, tile_bytes=TILE):
+def algorithmic_bytes(lens, hkv, hq, appended, tile_bytes=TILE, head_dim=D):
     """Bytes the method must move (not what an implementation happens to move); tile_bytes is
-    the size of one (block, KV head) record: 13,312 packed, 65,536 for the fp16 cache."""
+    the size of one (block, KV head) record: 13,312 packed, 65,536 for the fp16 cache (head
+    dimension 128; the record scales with head_dim)."""
     n_full = [int(l) // T for l in lens]
     n_stage = [int(l) % T for l in lens]
-    decode = sum(n * hkv * tile_bytes + s * hkv * 2 * D * 2 + 4 * n + 4
+    decode = sum(n * hkv * tile_bytes + s * hkv * 2 * head_dim * 2 + 4 * n + 4
                  for n, s in zip(n_full, n_stage))
-    decode += len(lens) * hq * D * (2 + 4)                       # q in (fp16), out (fp32)
+    decode += len(lens) * hq * head_dim * (2 + 4)                # q in (fp16), out (fp32)
     return decode
 
 
@@ -192,19 +198,23 @@ def k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, to
     dst = dev(st["dst_blocks"])
     pools4 = [torch.zeros(st["num_blocks"], sp.hkv, rb, dtype=torch.uint8, device="cuda")
               for _ in R]
-    ws_bytes = kv.decode_workspace_bytes(cfg4, sp.batch, sp.hq, bt_np.shape[1])
     stream = torch.cuda.current_stream()
+    keep = []
 
     def calls(c, pools):
         cp = ctypes.byref(c)
+        # each preset's decode has its own split plan, so its own workspace
+        ws_bytes = max(kv.decode_workspace_bytes(c, sp.batch, sp.hq, bt_np.shape[1]), 256)
+        wss = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in R]
+        keep.append(wss)
         qc = [(cp, V(r["k"].data_ptr()), V(r["v"].data_ptr()), r["k"].stride(0), n_tiles,
                V(dst.data_ptr()), V(p.data_ptr()), st["num_blocks"], V(stream.cuda_stream))
               for r, p in zip(R, pools)]
         dc = [(cp, V(r["q"].data_ptr()), sp.hq, V(p.data_ptr()), st["num_blocks"],
                V(bt.data_ptr()), bt_np.shape[1], V(lens.data_ptr()), V(r["sk"].data_ptr()),
                V(r["sv"].data_ptr()), ctypes.c_float(sm), V(r["out"].data_ptr()),
-               V(r["ws"].data_ptr()), max(ws_bytes, 256), sp.batch, V(stream.cuda_stream))
-              for r, p in zip(R, pools)]
+               V(w.data_ptr()), ws_bytes, sp.batch, V(stream.cuda_stream))
+              for r, p, w in zip(R, pools, wss)]
         return qc, dc
 
     reps = len(R)
@@ -577,22 +587,24 @@ def setup_workload(kv, lib, sp, st, replicas, torch, np, dev):
     k_new_np, v_new_np = gen.append_tokens(sp, 0)
     lens_pre = st["seq_lens"].astype(np.int32)
     bt_np = st["block_table"]
-    cfg = kv.default_config(sp.hkv)
-    sm = 1.0 / math.sqrt(D)
+    hd = sp.head_dim
+    cfg = kv.default_config(sp.hkv, head_dim=hd)
+    tile = kv.tile_bytes(cfg)
+    sm = 1.0 / math.sqrt(hd)
     n_tiles = int(st["dst_blocks"].shape[0])
     k0, v0 = dev(st["k"]), dev(st["v"])
-    per_replica = k0.numel() * 4 + st["num_blocks"] * sp.hkv * TILE
+    per_replica = k0.numel() * 4 + st["num_blocks"] * sp.hkv * tile
     reps = replicas or max(2, min(16, math.ceil(1.2e9 / per_replica)))
     ws_bytes = kv.decode_workspace_bytes(cfg, sp.batch, sp.hq, bt_np.shape[1])
     R = []
     for _ in range(reps):
         R.append(dict(
             k=k0.clone().view(k0.shape[0], -1), v=v0.clone().view(v0.shape[0], -1),
-            pool=torch.zeros(st["num_blocks"], sp.hkv, TILE, dtype=torch.uint8, device="cuda"),
-            sk=torch.zeros(sp.batch, sp.hkv, T, D, dtype=torch.float16, device="cuda"),
-            sv=torch.zeros(sp.batch, sp.hkv, T, D, dtype=torch.float16, device="cuda"),
+            pool=torch.zeros(st["num_blocks"], sp.hkv, tile, dtype=torch.uint8, device="cuda"),
+            sk=torch.zeros(sp.batch, sp.hkv, T, hd, dtype=torch.float16, device="cuda"),
+            sv=torch.zeros(sp.batch, sp.hkv, T, hd, dtype=torch.float16, device="cuda"),
             q=dev(q_np), kn=dev(k_new_np), vn=dev(v_new_np),
-            out=torch.empty(sp.batch, sp.hq, D, dtype=torch.float32, device="cuda"),
+            out=torch.empty(sp.batch, sp.hq, hd, dtype=torch.float32, device="cuda"),
             ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")))
     del k0, v0
     W = dict(sp=sp, st=st, cfg=cfg, sm=sm, q_np=q_np, lens_pre=lens_pre, bt_np=bt_np,
@@ -620,9 +632,10 @@ def setup_workload(kv, lib, sp, st, replicas, torch, np, dev):
     W["calls"] = calls
     tile_heads = n_tiles * sp.hkv
     W["tile_heads"] = tile_heads
-    W["q_bytes"] = tile_heads * (2 * T * D * 2 + TILE)
-    W["a_bytes"] = sp.batch * sp.hkv * 4 * D * 2
-    W["d_bytes"] = algorithmic_bytes(W["lens_np"], sp.hkv, sp.hq, True)
+    W["q_bytes"] = tile_heads * (2 * T * hd * 2 + tile)
+    W["a_bytes"] = sp.batch * sp.hkv * 4 * hd * 2
+    W["d_bytes"] = algorithmic_bytes(W["lens_np"], sp.hkv, sp.hq, True, tile, hd)
+    W["tile_bytes"] = tile
     return W
 
 
@@ -669,8 +682,8 @@ def summary(W, tm):
     sp = W["sp"]
     dg = W["d_bytes"] / tm["td"] / 1e9
     qg = W["q_bytes"] / tm["tq"] / 1e9
-    return {"batch": sp.batch, "kv_heads": sp.hkv, "q_heads": sp.hq,
-            "context_max": int(W["lens_pre"].max()),
+    return {"batch": sp.batch, "kv_heads": sp.hkv, "q_heads": sp.hq, "head_dim": sp.head_dim,
+            "tile_bytes": W["tile_bytes"], "context_max": int(W["lens_pre"].max()),
             "decode_attn": {"gbps": round(dg, 1), "frac_of_peak": round(dg / HBM_PEAK_GBPS, 4),
                             "us": round(tm["td"] * 1e6, 2), "algorithmic_bytes": W["d_bytes"]},
             "quantise": {"tiles_per_s": round(W["tile_heads"] / tm["tq"], 1),
@@ -695,7 +708,7 @@ def main():
     from workloads import gen
 
     assert torch.cuda.device_count() >= 1, "bench.py needs a GPU"   # does not initialise it
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = args.host_workers or max(1, min(16, len(os.sched_getaffinity(0))))
 
     # ---- host phase (forks processes; the GPU is not initialised yet)
     sp = gen.spec(args.workload)
@@ -707,6 +720,12 @@ def main():
             if name != args.workload:
                 osp = gen.spec(name)
                 others[name] = (osp, gen.prefill(osp, max_new_tokens=1, workers=workers))
+    heads = {}
+    if not args.no_head_dims:
+        # the 16K GQA-8 workload at head dimensions 64 and 256 (reading R29)
+        for hd in (64, 256):
+            hsp = gen.spec("qwen3-32b-16k", head_dim=hd)
+            heads[hd] = (hsp, gen.prefill(hsp, max_new_tokens=1, workers=workers))
     print(f"# inputs drawn in {time.perf_counter() - t0:.1f} s on {workers} host cores",
           file=sys.stderr, flush=True)
     lens_np = st["seq_lens"].astype(np.int32) + 1
@@ -772,6 +791,14 @@ def main():
         other_res[name] = summary(OW, otm)
         del OW
         torch.cuda.empty_cache()
+    head_res = {}
+    for hd, (hsp, hst) in heads.items():
+        HW = setup_workload(kv, lib, hsp, hst, 0, torch, np, dev)
+        htm = time_steps(lib, HW, max(10, args.steps // 2), max(2, args.warmup), torch,
+                         f"qwen3-32b-16k head_dim {hd}")
+        head_res[str(hd)] = summary(HW, htm)
+        del HW
+        torch.cuda.empty_cache()
 
     timings = {"quantise": tq, "append": ta, "decode": td}
     dominant = max(timings, key=timings.get)
@@ -788,10 +815,12 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel<2>)",
-                           "append": "kvarn_append_token (append_token_kernel<2>)",
-                           "decode": "kvarn_decode_attention (decode_tiles_kernel<false, 2> + "
-                                     "decode_merge_kernel<true, false>)"}[dominant],
+                "kernel": {"quantise": "kvarn_quantize_tiles (quantize_tiles_kernel<2, 128>)",
+                           "append": "kvarn_append_token (append_token_kernel<2, 128>)",
+                           "decode": "kvarn_decode_attention (decode_pairs_kernel<false, 2> on "
+                                     "large tables with at most 4 query heads per KV head, else "
+                                     "decode_tiles_kernel<false, 2, 128>; then "
+                                     "decode_merge_kernel<true, false, 128>)"}[dominant],
                 "algorithmic_bytes_per_launch": byts[dominant],
                 "avg_launch_us": round(timings[dominant] * 1e6, 2)}
     decode_gbps = d_bytes / td / 1e9
@@ -808,6 +837,7 @@ def main():
         "quantise": main_sum["quantise"],
         "append": main_sum["append"],
         "workloads": other_res or None,
+        "head_dims": head_res or None,
         "fp16_decode": fp16,
         "multi_decode": multi,
         "preset_k4v4": k4v4,

@@ -5,6 +5,7 @@
 
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace {
@@ -145,10 +146,15 @@ kvarn_status multi_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32
       num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup || n_query < 1 ||
       n_query > kvarn::kMaxQuery)
     return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(
-      batch, cfg->num_kv_heads, max_blocks_per_seq,
-      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, cfg->head_dim,
-                        batch, cfg->num_kv_heads, max_blocks_per_seq));
+  const bool pairs = kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits,
+                                       cfg->head_dim, batch, cfg->num_kv_heads,
+                                       max_blocks_per_seq);
+  int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq, pairs);
+  // the fp16 comparison decode of the same sizes runs the four-wave tile plan: the size
+  // covers both plans, so one workspace serves either call
+  if (pairs)
+    splits = std::max(splits, kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq,
+                                                   false));
   *bytes = (size_t)batch * (size_t)n_query * (size_t)num_q_heads * (size_t)splits *
            (size_t)kvarn::partial_floats(cfg->head_dim) * sizeof(float);
   return KVARN_OK;
@@ -328,6 +334,9 @@ kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
   const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq, false);
+  if (workspace_bytes < (size_t)batch * (size_t)num_q_heads * (size_t)splits *
+                            (size_t)kvarn::kPartialFloats * sizeof(float))
+    return KVARN_ERR_WORKSPACE;                 // covered by the size above; checked anyway
   return from_hip(kvarn::launch_decode_fp16(
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads,
       static_cast<const uint8_t*>(block_pool), num_blocks, block_table, max_blocks_per_seq,

@@ -169,7 +169,8 @@ KVARN_API kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k
  * It depends on the arguments and on the compute-unit count of the current HIP device (the
  * split plan fills the device; 256 compute units are assumed when no device is usable), so
  * query it with the device current that will run the decode. It grows with head_dim (one
- * partial of 2 + head_dim floats per query head and split). */
+ * partial of 2 + head_dim floats per query head and split). The same size also serves
+ * kvarn_decode_attention_fp16 at these sizes. */
 KVARN_API kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
                                           int32_t num_q_heads, int32_t max_blocks_per_seq,
                                           size_t* bytes);

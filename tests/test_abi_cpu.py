@@ -134,6 +134,10 @@ def test_workspace_follows_the_split_plan(lib):
     assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 22 * per
     # the same batch with group 8: tile kernel, 2 splits wanted, 256 full tiles need 8
     assert kv.decode_workspace_bytes(kv.default_config(10), 32, 80, 257) == 32 * 80 * 8 * per
+    # 128K context, batch 64, 8 KV heads, group 4 (524,800 entries): paired tiles in chunks of
+    # ceil(524,800 / 8,192) = 65 -> 66 tiles, 16 chunks; the fp16 comparison decode of the same
+    # sizes runs the tile plan, whose 1,024 full tiles need 32 splits: the size covers both
+    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 1025) == 64 * 32 * 32 * per
 
 
 def test_multi_workspace_and_query_token_limits(lib):
