@@ -1332,12 +1332,28 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
         for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, ov[sp][i], o[i]);
       }
     }
-    for (int sp = kMergePreload; sp < nsplit; ++sp) {
-      float v[kPer];
-      load_f<kPer>(col + sp * kPF, v);
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
+    // the remaining splits kMergePreload at a time, every load of a chunk issued before its
+    // values are used
+    for (int sp0 = kMergePreload; sp0 < nsplit; sp0 += kMergePreload) {
+      float v[kMergePreload][kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, v[i], o[i]);
+      for (int k = 0; k < kMergePreload; ++k) {
+        if (sp0 + k < nsplit) {
+          load_f<kPer>(col + (sp0 + k) * kPF, v[k]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) v[k][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kMergePreload; ++k) {
+        if (sp0 + k < nsplit) {
+          const float w =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp0 + k));
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, v[k][i], o[i]);
+        }
+      }
     }
   }
   if constexpr (kRotated) {

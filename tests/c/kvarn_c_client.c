@@ -4,9 +4,9 @@
  * runtime's C API, reading its inputs from <in> and writing the fp32 outputs to <out>.
  *
  * <in>: int32 header {magic 0x4B56524E, v_bits, n_tiles, hkv, hq, batch, max_blocks,
- * num_blocks}, then fp16 k[n_tiles*128][hkv][128], fp16 v (same), int32 dst_blocks[n_tiles],
- * int32 block_table[batch][max_blocks], int32 seq_lens[batch], fp16 q[batch][hq][128],
- * fp16 staging_k[batch][hkv][128][128], fp16 staging_v (same), float sm_scale. */
+ * num_blocks, head_dim D}, then fp16 k[n_tiles*128][hkv][D], fp16 v (same), int32
+ * dst_blocks[n_tiles], int32 block_table[batch][max_blocks], int32 seq_lens[batch], fp16
+ * q[batch][hq][D], fp16 staging_k[batch][hkv][128][D], fp16 staging_v (same), float sm_scale. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -75,6 +75,30 @@ static int host_checks(void) {
   CHECK(kvarn_decode_attention_fp16(&cfg, fake, 32, fake, 1, fake, 8, fake, fake, fake, 0.1f,
                                     (float*)fake, fake, 0, 4, NULL) == KVARN_ERR_WORKSPACE, 36);
   for (int st = 0; st <= 6; ++st) CHECK(kvarn_status_string((kvarn_status)st) != NULL, 37);
+  /* head dimensions: record sizes 64 D + 16 D v_bits + 2 (D + 384), token stride >= hkv * D,
+   * sign words past D / 32 rejected, the fp16 cache at 128 only */
+  kvarn_default_config(&cfg, 8);
+  cfg.head_dim = 64;
+  CHECK(kvarn_tile_bytes(&cfg) == 7040u, 51);
+  cfg.v_bits = 4;
+  CHECK(kvarn_tile_bytes(&cfg) == 9088u, 52);
+  cfg.head_dim = 256;
+  CHECK(kvarn_tile_bytes(&cfg) == 34048u, 53);
+  cfg.v_bits = 2;
+  CHECK(kvarn_tile_bytes(&cfg) == 25856u, 54);
+  CHECK(kvarn_quantize_tiles(&cfg, fake, fake, 8 * 128, 1, fake, fake, 1, NULL) ==
+            KVARN_ERR_BAD_SHAPE, 55);
+  cfg.rotation_signs[7] = 1u;
+  CHECK(kvarn_tile_bytes(&cfg) > 0, 56);
+  cfg.head_dim = 64;
+  CHECK(kvarn_tile_bytes(&cfg) == 0, 57);
+  cfg.rotation_signs[7] = 0u;
+  CHECK(kvarn_fp16_block_bytes(&cfg) == 0, 58);
+  CHECK(kvarn_decode_attention_fp16(&cfg, fake, 32, fake, 1, fake, 8, fake, fake, fake, 0.1f,
+                                    (float*)fake, fake, 0, 4, NULL) == KVARN_ERR_UNSUPPORTED, 59);
+  cfg.head_dim = 96;
+  CHECK(kvarn_tile_bytes(&cfg) == 0 && kvarn_decode_workspace_bytes(&cfg, 4, 32, 8, &ws) ==
+            KVARN_ERR_UNSUPPORTED, 60);
   return 0;
 }
 
@@ -91,15 +115,16 @@ static void* upload(const void* host, size_t n) {
 static int gpu_run(const char* in_path, const char* out_path) {
   FILE* f = fopen(in_path, "rb");
   CHECK(f != NULL, 30);
-  int32_t h[8];
+  int32_t h[9];
   CHECK(fread(h, sizeof h, 1, f) == 1 && h[0] == 0x4B56524E, 31);
   const int v_bits = h[1], n_tiles = h[2], hkv = h[3], hq = h[4], batch = h[5];
-  const int max_blocks = h[6], num_blocks = h[7];
-  CHECK(n_tiles >= 0 && hkv > 0 && hq > 0 && batch > 0 && max_blocks > 0 && num_blocks > 0, 32);
-  const size_t kv_n = (size_t)n_tiles * 128 * hkv * 128 * 2;
+  const int max_blocks = h[6], num_blocks = h[7], d = h[8];
+  CHECK(n_tiles >= 0 && hkv > 0 && hq > 0 && batch > 0 && max_blocks > 0 && num_blocks > 0 &&
+            (d == 64 || d == 128 || d == 256), 32);
+  const size_t kv_n = (size_t)n_tiles * 128 * hkv * d * 2;
   const size_t bt_n = (size_t)batch * max_blocks * 4;
-  const size_t q_n = (size_t)batch * hq * 128 * 2;
-  const size_t st_n = (size_t)batch * hkv * 128 * 128 * 2;
+  const size_t q_n = (size_t)batch * hq * d * 2;
+  const size_t st_n = (size_t)batch * hkv * 128 * d * 2;
   char* buf = (char*)malloc(2 * kv_n + n_tiles * 4 + bt_n + batch * 4 + q_n + 2 * st_n + 4);
   CHECK(buf != NULL, 33);
   char* p = buf;
@@ -109,6 +134,7 @@ static int gpu_run(const char* in_path, const char* out_path) {
   kvarn_config cfg;
   kvarn_default_config(&cfg, hkv);
   cfg.v_bits = v_bits;
+  cfg.head_dim = d;
   const size_t pool_n = (size_t)num_blocks * kvarn_block_bytes(&cfg);
   CHECK(pool_n > 0, 35);
   void* k = upload(p, kv_n); p += kv_n;
@@ -129,23 +155,23 @@ static int gpu_run(const char* in_path, const char* out_path) {
   CHECK(hipMalloc(&pool, pool_n) == hipSuccess && hipMemset(pool, 0, pool_n) == hipSuccess, 37);
   CHECK(kvarn_decode_workspace_bytes(&cfg, batch, hq, max_blocks, &ws) == KVARN_OK, 38);
   CHECK(hipMalloc(&work, ws) == hipSuccess, 39);
-  CHECK(hipMalloc(&out, (size_t)batch * hq * 128 * 4) == hipSuccess, 40);
-  CHECK(kvarn_quantize_tiles(&cfg, k, v, (int64_t)hkv * 128, n_tiles, (const int32_t*)dst, pool,
+  CHECK(hipMalloc(&out, (size_t)batch * hq * d * 4) == hipSuccess, 40);
+  CHECK(kvarn_quantize_tiles(&cfg, k, v, (int64_t)hkv * d, n_tiles, (const int32_t*)dst, pool,
                              num_blocks, NULL) == KVARN_OK, 41);
   CHECK(kvarn_decode_attention(&cfg, q, hq, pool, num_blocks, (const int32_t*)bt, max_blocks,
                                (const int32_t*)lens, sk, sv, sm, (float*)out, work, ws, batch,
                                NULL) == KVARN_OK, 42);
   CHECK(hipDeviceSynchronize() == hipSuccess, 43);
-  float* host_out = (float*)malloc((size_t)batch * hq * 128 * 4);
+  float* host_out = (float*)malloc((size_t)batch * hq * d * 4);
   CHECK(host_out != NULL, 44);
-  CHECK(hipMemcpy(host_out, out, (size_t)batch * hq * 128 * 4, hipMemcpyDeviceToHost) ==
+  CHECK(hipMemcpy(host_out, out, (size_t)batch * hq * d * 4, hipMemcpyDeviceToHost) ==
             hipSuccess, 45);
   unsigned char* host_pool = (unsigned char*)malloc(pool_n);
   CHECK(host_pool != NULL, 46);
   CHECK(hipMemcpy(host_pool, pool, pool_n, hipMemcpyDeviceToHost) == hipSuccess, 47);
   FILE* o = fopen(out_path, "wb");
   CHECK(o != NULL, 48);
-  CHECK(fwrite(host_out, 4, (size_t)batch * hq * 128, o) == (size_t)batch * hq * 128, 49);
+  CHECK(fwrite(host_out, 4, (size_t)batch * hq * d, o) == (size_t)batch * hq * d, 49);
   CHECK(fwrite(host_pool, 1, pool_n, o) == pool_n, 50);
   fclose(o);
   hipFree(k); hipFree(v); hipFree(dst); hipFree(bt); hipFree(lens); hipFree(q); hipFree(sk);

@@ -39,7 +39,7 @@ def test_c_client_host_checks_under_address_sanitizer():
 
 def _write_input(path, st, sp, q, sk, sv, lens, sm, v_bits):
     hdr = np.array([0x4B56524E, v_bits, len(st["dst_blocks"]), sp.hkv, sp.hq, sp.batch,
-                    st["block_table"].shape[1], st["num_blocks"]], np.int32)
+                    st["block_table"].shape[1], st["num_blocks"], sp.head_dim], np.int32)
     with open(path, "wb") as f:
         for a in (hdr, st["k"].astype(np.float16), st["v"].astype(np.float16),
                   st["dst_blocks"].astype(np.int32), st["block_table"].astype(np.int32),
@@ -49,8 +49,8 @@ def _write_input(path, st, sp, q, sk, sv, lens, sm, v_bits):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("v_bits", [2, 4])
-def test_c_client_gpu_round_trip(tmp_path, v_bits):
+@pytest.mark.parametrize("v_bits,d", [(2, 128), (4, 128), (2, 64), (4, 256)])
+def test_c_client_gpu_round_trip(tmp_path, v_bits, d):
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -60,28 +60,28 @@ def test_c_client_gpu_round_trip(tmp_path, v_bits):
     from record_view import Budget, compare_half, parse
 
     client = _client(kbuild.C_CLIENT_GPU)
-    sp = gen.spec("qwen3-4b", batch=2, ctx=384, hkv=2, hq=8)
+    sp = gen.spec("qwen3-4b", batch=2, ctx=384, hkv=2, hq=8, head_dim=d)
     st = gen.prefill(sp, max_new_tokens=T)
     lens = st["seq_lens"].astype(np.int32)
     rng = np.random.default_rng(3)
-    sk = np.zeros((sp.batch, sp.hkv, T, D), np.float16)
+    sk = np.zeros((sp.batch, sp.hkv, T, d), np.float16)
     sv = np.zeros_like(sk)
     for b, tail in enumerate([0, 40]):
-        sk[b, :, :tail] = rng.standard_normal((sp.hkv, tail, D)).astype(np.float16)
-        sv[b, :, :tail] = rng.standard_normal((sp.hkv, tail, D)).astype(np.float16)
+        sk[b, :, :tail] = rng.standard_normal((sp.hkv, tail, d)).astype(np.float16)
+        sv[b, :, :tail] = rng.standard_normal((sp.hkv, tail, d)).astype(np.float16)
         lens[b] += tail
     q = gen.query(sp, dense=True)
-    sm = 1 / math.sqrt(D)
+    sm = 1 / math.sqrt(d)
     fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
     _write_input(fin, st, sp, q, sk, sv, lens, sm, v_bits)
-    print(f"C client on the GPU: v_bits={v_bits}", flush=True)
+    print(f"C client on the GPU: v_bits={v_bits} head_dim={d}", flush=True)
     res = subprocess.run([client, "run", str(fin), str(fout)], capture_output=True, text=True,
                          timeout=120)
     assert res.returncode == 0, res.stderr
     raw = np.fromfile(fout, np.uint8)
-    n_out = sp.batch * sp.hq * D * 4
-    got = raw[:n_out].view(np.float32).reshape(sp.batch, sp.hq, D)
-    rb = codec.tile_bytes(v_bits)
+    n_out = sp.batch * sp.hq * d * 4
+    got = raw[:n_out].view(np.float32).reshape(sp.batch, sp.hq, d)
+    rb = codec.tile_bytes(v_bits, d)
     pool_g = raw[n_out:].reshape(st["num_blocks"], sp.hkv, rb)
     # the records the C program had the library write, against the oracle's quantisation
     budget = Budget()
