@@ -39,6 +39,9 @@
 // lanes of output token block kb, so probabilities feed the second product without shuffles.
 // The running maximum of a head moves only when a tile's maximum exceeds it by more than
 // 2 (log2 units), so most tiles skip the rescale of the output accumulators.
+// The counts above are for head dimension 128; the tile, merge and dequantisation kernels are
+// templated on the head dimension D (64, 128, 256): D / 32 channel blocks in the score product,
+// D / 16 in the output product, D / 64 channels per lane in the rotations.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -1161,7 +1164,11 @@ constexpr int kMaxSplits = 64;
 #define KVARN_PAIR_MIN_TILES_PER_CU 64
 #endif
 constexpr int kPairMinTilesPerCU = KVARN_PAIR_MIN_TILES_PER_CU;
-constexpr int kMergePreload = 8;          // splits whose o~ is loaded before the weights exist
+#ifndef KVARN_MERGE_PRELOAD
+#define KVARN_MERGE_PRELOAD 8
+#endif
+// splits whose o~ is loaded before the weights exist (and the chunk of the rest)
+constexpr int kMergePreload = KVARN_MERGE_PRELOAD;
 constexpr int kStageChunk = 16;           // staging value rows loaded per round
 
 // <q, k> over kDim channels: k is one fp16 staging row, q the fp32 query in LDS.
