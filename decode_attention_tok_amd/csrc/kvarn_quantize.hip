@@ -46,8 +46,8 @@
 // difference on the upper lane exactly (partner - own), so it adds no sign. Layout B keeps 16
 // channels per wave (D / 16 waves). A row's statistics merge over D / 32 threads; the gauge and
 // the per-channel rounding factor use 1 / D and 1 / sqrt(D). Key codes are staged token-major
-// as at D = 128; value codes are ORed into an LDS copy of the section at the positions of
-// value_code_pos() and then stored.
+// as at D = 128; a thread's value codes form whole bytes (2-bit) or half-words (4-bit) of the
+// section, written into an LDS copy of it at the positions of value_code_pos() and then stored.
 
 #include "kvarn_device.hpp"
 #include "kvarn_kernels.hpp"
@@ -235,19 +235,26 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
       stage[t * (kDim / 8) + q0 + 2 * m + 8 * q1 + 16 * q2] = lo | (hi << 4);
     }
   } else if constexpr (kDim != 128) {
-    // value codes of the other head dimensions: each code ORed into its word of an LDS copy of
-    // the section (cleared by the caller)
-    const int cbase = 8 * q0 + 64 * q1 + 128 * q2;
+    // value codes of the other head dimensions. The four codes of channels
+    // 16 (m + 4 q1 + 8 q2) + n, m = 0..3 (this thread's x[8 m + e], n = 8 q0 + e) share one byte
+    // of the section (2-bit codes, at bits 2 m) or one half-word (4-bit codes, at bits 4 m),
+    // byte-aligned at the position of the m = 0 channel: each is written whole into an LDS
+    // copy of the section, which the writes cover exactly once
+    uint8_t* sb = reinterpret_cast<uint8_t*>(stage);
+    const int c0 = 16 * (4 * q1 + 8 * q2) + 8 * q0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int e = 0; e < 8; ++e) {
+      uint32_t packed = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t code = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, 0, 0);
-        uint32_t byte_off;
-        int shift;
-        value_code_pos<kVBits, kDim>(t, cbase + 16 * m + e, byte_off, shift);
-        atomicOr(&stage[byte_off >> 2], code << (8 * (byte_off & 3u) + shift));
-      }
+      for (int m = 0; m < 4; ++m)
+        packed |= put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, 0, 0) << (kVBits * m);
+      uint32_t byte_off;
+      int shift;
+      value_code_pos<kVBits, kDim>(t, c0 + e, byte_off, shift);   // shift is 0 here
+      if constexpr (kVBits == 2)
+        sb[byte_off] = (uint8_t)packed;
+      else
+        *reinterpret_cast<uint16_t*>(sb + byte_off) = (uint16_t)packed;
     }
   } else if constexpr (kVBits == 4) {
     // 4-bit value codes. Channel 16 nb + n with nb = m + 4 q1, n = 8 q0 + e: half-word i % 2 of
@@ -526,12 +533,6 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   __syncthreads();   // also: every read of sm.xt is done, so it may hold the packed codes
   if (tid < kDim / 4) reinterpret_cast<uint32_t*>(rec + meta + L::kC)[tid] = sm.chat[tid];
   uint32_t* stage = reinterpret_cast<uint32_t*>(&sm.xt[0][0]);
-  if constexpr (kDim != 128) {                      // cleared LDS copy of the value section
-    if (is_v) {
-      for (int i = tid; i < L::kVCodeBytes / 16; i += G::kThreads)
-        reinterpret_cast<uint4*>(stage)[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
 
   // ---- asymmetric RTN per token (layout A); p = (+-) y, sign `flip`
   const float qmax = is_v ? (float)((1 << kVBits) - 1) : 15.0f;
@@ -566,9 +567,6 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   if ((tid & (kTPT - 1)) == 0) {
     reinterpret_cast<uint8_t*>(sm.meta)[t] = (uint8_t)scode;
     reinterpret_cast<uint16_t*>(sm.meta + 32)[t] = (uint16_t)zbits;
-  }
-  if constexpr (kDim != 128) {
-    if (is_v) __syncthreads();                      // the cleared section before the ORs
   }
 
   if (scode == 0x7Eu)                                   // s-hat = 448
