@@ -806,12 +806,17 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 // accumulators and everything between and after them (combining the score parts, the softmax,
 // the probability operand, folding the output scales) runs once per pair.
 //
-// One wave per workgroup, one chunk of `chunk` consecutive tiles of one (sequence, KV head) per
-// wave (grid: chunks x KV heads x sequences); each wave writes its own partial (m, l, o~) per
-// virtual head, so waves never wait for each other and a short sequence simply has fewer
-// chunks (the waves past its end write an empty partial and leave). Only a chunk's last pair
-// can be single: its second tile's products are then skipped and its columns carry no
-// probability.
+// Schedule: the tile pairs of every (sequence, KV head) in order (sequence, KV head, pair) form
+// one work list (a unit of n full tiles holds ceil(n / 2) pairs, the last single when n is
+// odd), and the grid is as many one-wave workgroups as the device holds at once (W). The waves
+// split the list into consecutive equal shares (PairSplit) whatever the mix of lengths; all of
+// them run at once, so there is no tail of late waves, and a share never splits a pair. Where a wave's range crosses from one
+// (sequence, KV head) to the next it finishes the first, writes its partial (m, l, o~) per
+// virtual head, and starts the next; the partial goes to slot w - wave_of(T(u)) of the unit u
+// it belongs to (T(u) = the unit's first list position), so a unit fills slots 0 ..
+// wave_of(T(u) + m - 1) - wave_of(T(u)) for its m pairs, and the merge kernel recomputes that
+// count from the sequence lengths. Only a unit's last pair can be single: its second tile's
+// products are then skipped and its columns carry no probability.
 
 struct PairSmem {
   float qrot[4][kD + 4];           // rotated queries of the virtual heads (fp32)
@@ -827,34 +832,125 @@ __device__ __forceinline__ uint32_t dpp_half_mirror_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
 }
 
+// Full tiles of a sequence of length len in the paged table (none when the length is invalid:
+// negative, or more full tiles than the table holds), and the pairs they form (the last one
+// single for an odd count).
+__device__ __forceinline__ int full_tiles(int len, int max_blocks) {
+  return (len < 0 || (len >> 7) > max_blocks) ? 0 : (len >> 7);
+}
+__device__ __forceinline__ int tile_pairs(int len, int max_blocks) {
+  return (full_tiles(len, max_blocks) + 1) >> 1;
+}
+
+// The work list's positions per sequence (tile pairs x KV heads), summed over lanes: lane l
+// holds sequences [l k, l k + k), k = ceil(batch / 64); mine = its positions, excl = those of
+// the lanes before it, total = the list length (the same in every lane). The list is shorter
+// than 2^31: the paired-tile kernel only serves tables of fewer entries than that.
+struct ListScan {
+  int mine, excl, total;
+  int lo, hi;
+};
+
+__device__ __forceinline__ ListScan scan_list(const int32_t* __restrict__ seq_lens, int batch,
+                                              int max_blocks, int hkv, int lane) {
+  ListScan r;
+  const int k = (batch + 63) >> 6;
+  r.lo = min(batch, lane * k);
+  r.hi = min(batch, r.lo + k);
+  int mine = 0;
+  for (int i = r.lo; i < r.hi; ++i) mine += tile_pairs(seq_lens[i], max_blocks);
+  mine *= hkv;
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  r.mine = mine;
+  r.excl = incl - mine;
+  r.total = __builtin_amdgcn_readlane(incl, 63);
+  return r;
+}
+
+// The sequence holding list position pos (0 <= pos < total) and the positions before it.
+__device__ __forceinline__ void locate_position(const ListScan& ls,
+                                                const int32_t* __restrict__ seq_lens,
+                                                int max_blocks, int hkv, int pos, int lane,
+                                                int& seq, int& before) {
+  const unsigned long long m = __ballot(ls.excl + ls.mine > pos);
+  const int owner = m ? (int)__builtin_ctzll(m) : 63;
+  int bef = ls.excl;
+  int sq = ls.lo;
+  if (lane == owner) {
+    for (; sq < ls.hi - 1; ++sq) {
+      const int n = tile_pairs(seq_lens[sq], max_blocks) * hkv;
+      if (pos < bef + n) break;
+      bef += n;
+    }
+  }
+  seq = __builtin_amdgcn_readlane(sq, owner);
+  before = __builtin_amdgcn_readlane(bef, owner);
+}
+
+// List positions before sequence b (0 <= b < batch).
+__device__ __forceinline__ int positions_before(const ListScan& ls,
+                                                const int32_t* __restrict__ seq_lens, int batch,
+                                                int max_blocks, int hkv, int b, int lane) {
+  const int k = (batch + 63) >> 6;
+  const int owner = b / k;
+  int bef = ls.excl;
+  if (lane == owner)
+    for (int i = ls.lo; i < b; ++i) bef += tile_pairs(seq_lens[i], max_blocks) * hkv;
+  return __builtin_amdgcn_readlane(bef, owner);
+}
+
+// Shares of the paired-tile schedule: wave w takes list positions [w share, (w + 1) share),
+// share = max(min_share, ceil(total / W)).
+struct PairSplit {
+  int share;
+  __device__ __forceinline__ long long start(int w) const { return (long long)w * share; }
+  __device__ __forceinline__ int wave_of(int x) const { return x / share; }
+};
+
+__device__ __forceinline__ PairSplit pair_split(int total, int waves, int min_share) {
+  PairSplit r;
+  const long long s = ((long long)total + waves - 1) / waves;
+  r.share = (int)(s > min_share ? s : min_share);
+  return r;
+}
+
+// Issue priority from the wave's progress: 3 in the first quarter of its tiles down to 0 in
+// the last. The two waves a SIMD holds start together with equal work; a SIMD favours its older
+// wave among equal priorities, which would finish it well before the younger one and leave the
+// younger alone (and latency-bound) for the rest of the kernel. Ranking by work left instead
+// keeps the pair level, so they finish together.
+#ifndef KVARN_PAIR_PRIO
+#define KVARN_PAIR_PRIO 1
+#endif
+constexpr bool kPairPrio = KVARN_PAIR_PRIO != 0;
+__device__ __forceinline__ void set_progress_priority(int done, int total) {
+  const int quarter = (4 * done) / total;
+  if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (quarter == 1) __builtin_amdgcn_s_setprio(2);
+  else if (quarter == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// Tiles i0 .. i0 + ntile - 1 (ntile >= 1) of KV head g of sequence b (length len, valid) into
+// partial slot `slot` of each virtual head's row (rows of nslot slots).
 template <bool kCausal, int kVBits>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
-                    const uint8_t* __restrict__ pool, long long num_blocks,
-                    const int32_t* __restrict__ block_table, int max_blocks,
-                    const int32_t* __restrict__ seq_lens, float sm_scale,
-                    float* __restrict__ partials, SignWords signs, int chunk) {
-  __shared__ PairSmem sm;
-  const int nsplit = gridDim.x;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void pair_segment(
+    PairSmem& sm, const __half* __restrict__ q, int hq, int hkv, int nq,
+    const uint8_t* __restrict__ pool, long long num_blocks,
+    const int32_t* __restrict__ block_table, int max_blocks, int len, float sm_scale,
+    float* __restrict__ partials, const SignWords& signs, int b, int g, int i0, int ntile,
+    int slot, int nslot, int done0, int wave_tiles) {
   const int group = hq / hkv, nh = group * nq;                // virtual heads served (1..4)
   const int lane = threadIdx.x;
   auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
     return ((long long)b * nq + v / group) * hq + g * group + v % group;
   };
-  const int len = seq_lens[b];
-  bool bad = len < 0 || (len >> 7) > max_blocks;
-  const int n_full = bad ? 0 : (len >> 7);
-  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
-  const int ntile = i1 - i0;
-  if (ntile == 0) {                                // nothing here: an empty partial per head
-    for (int idx = lane; idx < nh * kPartialFloats; idx += 64) {
-      const int gg = idx / kPartialFloats, k = idx % kPartialFloats;
-      float* pp = partials + (row_of(gg) * nsplit + split) * kPartialFloats;
-      pp[k] = k == 0 ? (bad ? NAN : -INFINITY) : (k == 1 && bad ? NAN : 0.0f);
-    }
-    return;
-  }
+  bool bad = false;
   const int npair = (ntile + 1) >> 1;              // pair p: tiles i0 + 2 p, i0 + 2 p + 1
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0;
   constexpr long long kTileBytes = RecordLayout<kVBits>::kTileBytes;
@@ -937,6 +1033,7 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < npair && !bad; ++p) {
+    if constexpr (kPairPrio) set_progress_priority(done0 + 2 * p, wave_tiles);
     const bool has_y = 2 * p + 1 < ntile;          // wave-uniform
     const uint8_t* nrx = nullptr;
     const uint8_t* nry = nullptr;
@@ -1139,15 +1236,52 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     for (int i = 0; i < 4; ++i) {
       const float both = add_xor16(y[i]);                           // + the lo part
       if (s == 0 && i < nh)
-        partials[(row_of(i) * nsplit + split) * kPartialFloats + 2 + 16 * nb + n] = both;
+        partials[(row_of(i) * nslot + slot) * kPartialFloats + 2 + 16 * nb + n] = both;
     }
   }
   if (s == 0 && colhi && tsel == 0 && colv) {
-    float* pp = partials + (row_of(hh) * nsplit + split) * kPartialFloats;
+    float* pp = partials + (row_of(hh) * nslot + slot) * kPartialFloats;
     pp[0] = bad ? NAN : m_run;
     pp[1] = bad ? NAN : l_run;
   }
 }
+
+
+template <bool kCausal, int kVBits>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
+                    const uint8_t* __restrict__ pool, long long num_blocks,
+                    const int32_t* __restrict__ block_table, int max_blocks,
+                    const int32_t* __restrict__ seq_lens, int batch, float sm_scale,
+                    float* __restrict__ partials, int nslot, SignWords signs, int min_share) {
+  __shared__ PairSmem sm;
+  const int lane = threadIdx.x;
+  const int waves = gridDim.x, w = blockIdx.x;
+  const ListScan ls = scan_list(seq_lens, batch, max_blocks, hkv, lane);
+  const PairSplit split = pair_split(ls.total, waves, min_share);
+  const long long start64 = split.start(w);
+  if (start64 >= ls.total) return;                 // more waves than list positions
+  const int start = (int)start64;
+  const int end = (int)min(split.start(w + 1), (long long)ls.total);
+  for (int cur = start; cur < end;) {
+    int b, before;                                 // the unit holding position cur
+    locate_position(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+    const int len = seq_lens[b];
+    const int nt = full_tiles(len, max_blocks);
+    const int np = (nt + 1) >> 1;                  // > 0: the sequence holds position cur
+    const int g = (cur - before) / np;
+    const int p0 = (cur - before) - g * np;        // first pair of the segment in its unit
+    const int seg = min(np - p0, end - cur);       // pairs
+    const int slot = w - split.wave_of(cur - p0);  // cur - p0 = T(u)
+    if (cur != start) __syncthreads();             // LDS of the last unit read before this one's
+    pair_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
+                                  len, sm_scale, partials, signs, b, g, 2 * p0,
+                                  min(2 * seg, nt - 2 * p0), slot, nslot, 2 * (cur - start),
+                                  2 * (end - start));
+    cur += seg;
+  }
+}
+
 
 // grid (nq * hq, batch), one wave per (sequence, query token, query head): the staging tokens
 // the query token sees (exact fp32
@@ -1164,6 +1298,10 @@ constexpr int kMaxSplits = 64;
 #define KVARN_PAIR_MIN_TILES_PER_CU 64
 #endif
 constexpr int kPairMinTilesPerCU = KVARN_PAIR_MIN_TILES_PER_CU;
+#ifndef KVARN_PAIR_ROUNDS
+#define KVARN_PAIR_ROUNDS 1
+#endif
+constexpr int kPairRounds = KVARN_PAIR_ROUNDS;   // paired-tile waves per resident wave slot
 #ifndef KVARN_MERGE_PRELOAD
 #define KVARN_MERGE_PRELOAD 8
 #endif
@@ -1226,7 +1364,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out,
-                    SignWords signs) {
+                    SignWords signs, int pair_waves, int min_share) {
   constexpr int kPer = kDim / 64;      // output channels per lane: kPer lane .. + kPer - 1
   constexpr int kPF = 2 + kDim;        // floats per partial
   __shared__ float qs[kDim];
@@ -1275,6 +1413,19 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   qw.load(q + row * kDim + kPer * lane);
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
+  // slots holding a partial: all nsplit after the tile kernel; after the paired-tile kernel
+  // (pair_waves > 0) the slots of this (sequence, KV head) in that kernel's schedule
+  int nuse = nsplit;
+  if (pair_waves > 0) {
+    const ListScan ls = scan_list(seq_lens, gridDim.y, max_blocks, hkv, lane);
+    const int np = tile_pairs(len, max_blocks);
+    nuse = 0;
+    if (np > 0) {
+      const PairSplit split = pair_split(ls.total, pair_waves, min_share);
+      const int t0 = positions_before(ls, seq_lens, gridDim.y, max_blocks, hkv, b, lane) + g * np;
+      nuse = split.wave_of(t0 + np - 1) - split.wave_of(t0) + 1;
+    }
+  }
   // staging tokens this query token sees: positions up to len - nq + qi
   const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (kCausal ? nq - 1 - qi : 0));
   const float scale2 = sm_scale * kLog2e;
@@ -1316,14 +1467,16 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
     }
   }
   if (lane + 64 < n_stage) s1 = staging_dot<kDim>(sk + (lane + 64) * kDim, qs) * scale2;
-  const bool invalid = bad || __any(msp != msp);
-  const float mm = wave_max(fmaxf(msp, fmaxf(s0, s1)));
+  const float m_use = lane < nuse ? msp : -INFINITY;
+  const float l_use = lane < nuse ? lsp : 0.0f;
+  const bool invalid = bad || __any(m_use != m_use);
+  const float mm = wave_max(fmaxf(m_use, fmaxf(s0, s1)));
   float ls = 0.0f, wsp = 0.0f, p0 = 0.0f, p1 = 0.0f;
   if (mm != -INFINITY) {
-    wsp = lane < nsplit ? exp2f(msp - mm) : 0.0f;
+    wsp = lane < nuse ? exp2f(m_use - mm) : 0.0f;
     p0 = exp2f(s0 - mm);
     p1 = exp2f(s1 - mm);
-    ls = fmaf(wsp, lsp, p0 + p1);
+    ls = fmaf(wsp, l_use, p0 + p1);
   }
   ls = wave_sum(ls);
   // merged rotated output o~ of this lane's channels
@@ -1333,7 +1486,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   if (mm != -INFINITY && !invalid) {
 #pragma unroll
     for (int sp = 0; sp < kMergePreload; ++sp) {
-      if (sp < nsplit) {
+      if (sp < nuse) {
         const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp));
 #pragma unroll
         for (int i = 0; i < kPer; ++i) o[i] = fmaf(w, ov[sp][i], o[i]);
@@ -1341,11 +1494,11 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
     }
     // the remaining splits kMergePreload at a time, every load of a chunk issued before its
     // values are used
-    for (int sp0 = kMergePreload; sp0 < nsplit; sp0 += kMergePreload) {
+    for (int sp0 = kMergePreload; sp0 < nuse; sp0 += kMergePreload) {
       float v[kMergePreload][kPer];
 #pragma unroll
       for (int k = 0; k < kMergePreload; ++k) {
-        if (sp0 + k < nsplit) {
+        if (sp0 + k < nuse) {
           load_f<kPer>(col + (sp0 + k) * kPF, v[k]);
         } else {
 #pragma unroll
@@ -1354,7 +1507,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
       }
 #pragma unroll
       for (int k = 0; k < kMergePreload; ++k) {
-        if (sp0 + k < nsplit) {
+        if (sp0 + k < nuse) {
           const float w =
               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsp), sp0 + k));
 #pragma unroll
@@ -1809,30 +1962,48 @@ bool pairs_mode(int virtual_heads, int v_bits, int head_dim, int batch, int hkv,
                 int max_blocks) {
   const long long tiles = (long long)batch * hkv * max_blocks;
   return virtual_heads <= 4 && v_bits == 2 && head_dim == 128 &&
-         tiles >= kPairMinTilesPerCU * device_compute_units();
+         tiles >= kPairMinTilesPerCU * device_compute_units() && tiles < (1LL << 31);
 }
 
-// Tiles per chunk of the paired-tile kernel for a plan of `splits` chunks (even, so only a
-// chunk's last pair can be single).
-int pairs_chunk(int max_blocks, int splits) {
-  const int c = (max_blocks + splits - 1) / splits;
-  return c + (c & 1);
+// Smallest share (in tile pairs) of the paired-tile schedule for a table of max_blocks
+// entries: a unit of m <= ceil(max_blocks / 2) pairs at positions [T, T + m) meets waves
+// floor(T / share) .. floor((T + m - 1) / share), at most floor((m - 1) / share) + 2 <=
+// kMaxSplits partial slots.
+int pairs_min_share(int max_blocks) {
+  return ((max_blocks + 1) / 2 - 1) / (kMaxSplits - 2) + 1;
+}
+
+// Waves of the paired-tile kernel: as many one-wave workgroups as the current device holds at
+// once (the kernel's occupancy, read once per device and cached, times the compute units),
+// times KVARN_PAIR_ROUNDS.
+int pairs_waves() {
+  constexpr int kMaxDevices = 64, kDefaultPerCU = 8;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  int per_cu = kDefaultPerCU;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+  } else if (const int c = cache[dev].load(std::memory_order_relaxed); c > 0) {
+    per_cu = c;
+  } else {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&decode_pairs_kernel<false, 2>), 64, 0) !=
+            hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      n = kDefaultPerCU;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    per_cu = n;
+  }
+  return kPairRounds * per_cu * device_compute_units();
 }
 
 int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel) {
   if (pair_kernel) {
-    // one wave per chunk: about four waves per SIMD slot in all (two slots per SIMD) for the
-    // table width, chunks of an even number of tiles, at most kMaxSplits chunks per sequence
-    const long long work = (long long)batch * hkv * max_blocks;
-    const long long waves = 32LL * device_compute_units();
-    long long c = (work + waves - 1) / waves;
-    const long long cmin = (max_blocks + kMaxSplits - 1) / kMaxSplits;
-    if (c < cmin) c = cmin;
-    if (c < 2) c = 2;
-    c += c & 1;
-    long long s = (max_blocks + c - 1) / c;
-    if (s < 1) s = 1;
-    return (int)s;
+    // partial slots per row: the most a unit of the paired-tile schedule can span
+    return ((max_blocks + 1) / 2 - 1) / pairs_min_share(max_blocks) + 2;
   }
   const long long pairs = (long long)batch * hkv > 0 ? (long long)batch * hkv : 1;
   // two workgroups per compute unit (2 waves per SIMD)
@@ -1865,12 +2036,14 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
                            int splits, int batch, SignWords sg, int v_bits, hipStream_t stream) {
   const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
   const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
+  int pair_waves = 0, min_share = 0;
   if (kDim == 128 && pairs_mode(hq / hkv * nq, v_bits, kDim, batch, hkv, max_blocks)) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
-    const int chunk = pairs_chunk(max_blocks, splits);
-    hipLaunchKernelGGL(kern, dim3(splits, hkv, batch), dim3(64), 0, stream, q, hq, hkv, nq,
-                       pool, num_blocks, block_table, max_blocks, seq_lens, sm_scale, partials,
-                       sg, chunk);
+    pair_waves = pairs_waves();
+    min_share = pairs_min_share(max_blocks);
+    hipLaunchKernelGGL(kern, dim3(pair_waves), dim3(64), 0, stream, q, hq, hkv, nq, pool,
+                       num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale, partials,
+                       splits, sg, min_share);
   } else {
     auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4, kDim>
                                        : decode_tiles_kernel<false, 2, kDim>)
@@ -1883,7 +2056,8 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
   if (e != hipSuccess) return e;
   auto merge = nq == 1 ? decode_merge_kernel<true, false, kDim> : decode_merge_kernel<true, true, kDim>;
   hipLaunchKernelGGL(merge, mgrid, dim3(kMThreads), 0, stream, q, hq, hkv, nq, max_blocks,
-                     seq_lens, staging_k, staging_v, sm_scale, partials, splits, out, sg);
+                     seq_lens, staging_k, staging_v, sm_scale, partials, splits, out, sg,
+                     pair_waves, min_share);
   return hipGetLastError();
 }
 
@@ -1931,7 +2105,7 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
   none.hi = none.lo;
   hipLaunchKernelGGL((decode_merge_kernel<false, false, kD>), dim3(hq, batch), dim3(kMThreads), 0,
                      stream, q, hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                     partials, splits, out, none);
+                     partials, splits, out, none, 0, 0);
   return hipGetLastError();
 }
 

@@ -66,7 +66,6 @@ hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
 int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel);
 // Whether a decode of these sizes runs the paired-tile kernel (decode_pairs_kernel).
 bool pairs_mode(int virtual_heads, int v_bits, int head_dim, int batch, int hkv, int max_blocks);
-int pairs_chunk(int max_blocks, int splits);
 int device_compute_units();
 
 }  // namespace kvarn

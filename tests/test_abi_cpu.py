@@ -116,28 +116,30 @@ def test_workspace_follows_the_split_plan(lib):
     unit, at least two tiles per wave unless that leaves fewer than two workgroups per compute
     unit (then one), at most 32 full tiles per split for the longest table (its last entry is
     the staging tile).
-    Paired-tile kernel (otherwise): one wave per chunk of an even number of tiles, about 32
-    chunks per compute unit for the table's entries, at most 64 chunks per sequence."""
+    Paired-tile kernel (otherwise): the sequences' tile pairs form one list that the resident
+    waves share evenly, at least m = (p - 1) // 62 + 1 pairs per wave for p = ceil(entries / 2);
+    a (sequence, KV head) of up to p pairs then spans at most (p - 1) // m + 2 waves, each
+    writing its own partial slot."""
     per = 130 * 4
     # 16K context, batch 16, 8 KV heads, group 8: 512 / 128 pairs = 4 splits of 32 tiles
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 4 * per
     # 4K context, batch 8 (33 entries; 2,112 < 16,384): 8 splits wanted; two tiles per wave
     # would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
     assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
-    # 4K context, batch 64 (16,896 entries), group 4: paired tiles, chunks of
-    # ceil(16,896 / 8,192) = 3 -> 4 tiles, 9 chunks per sequence
-    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 9 * per
+    # 4K context, batch 64 (16,896 entries), group 4: paired tiles, p = 17, m = 1,
+    # 16 // 1 + 2 = 18 slots (the tile plan of the same sizes needs 1)
+    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 18 * per
     # the same with 4-bit values: tile kernel, 512 pairs fill the device with one split
     assert kv.decode_workspace_bytes(kv.default_config(8, v_bits=4), 64, 32, 33) == 64 * 32 * per
     # ragged batch up to 32K tokens, batch 32, 10 KV heads, group 4 (82,240 entries): paired
-    # tiles, chunks of ceil(82,240 / 8,192) = 11 -> 12 tiles, 22 chunks per sequence
-    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 22 * per
+    # tiles, p = 129, m = 128 // 62 + 1 = 3, 128 // 3 + 2 = 44 slots
+    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 44 * per
     # the same batch with group 8: tile kernel, 2 splits wanted, 256 full tiles need 8
     assert kv.decode_workspace_bytes(kv.default_config(10), 32, 80, 257) == 32 * 80 * 8 * per
-    # 128K context, batch 64, 8 KV heads, group 4 (524,800 entries): paired tiles in chunks of
-    # ceil(524,800 / 8,192) = 65 -> 66 tiles, 16 chunks; the fp16 comparison decode of the same
-    # sizes runs the tile plan, whose 1,024 full tiles need 32 splits: the size covers both
-    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 1025) == 64 * 32 * 32 * per
+    # 128K context, batch 64, 8 KV heads, group 4 (524,800 entries): paired tiles, p = 513,
+    # m = 9, 512 // 9 + 2 = 58 slots; the fp16 comparison decode of the same sizes runs the tile
+    # plan (32 splits): the size covers both
+    assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 1025) == 64 * 32 * 58 * per
 
 
 def test_multi_workspace_and_query_token_limits(lib):
