@@ -146,15 +146,12 @@ kvarn_status multi_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32
       num_q_heads / cfg->num_kv_heads > kvarn::kMaxGroup || n_query < 1 ||
       n_query > kvarn::kMaxQuery)
     return KVARN_ERR_BAD_SHAPE;
-  const bool pairs = kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits,
-                                       cfg->head_dim, batch, cfg->num_kv_heads,
-                                       max_blocks_per_seq);
-  int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq, pairs);
-  // the fp16 comparison decode of the same sizes runs the four-wave tile plan: the size
-  // covers both plans, so one workspace serves either call
-  if (pairs)
-    splits = std::max(splits, kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq,
-                                                   false));
+  // the packed decode's partial slots per row; the fp16 comparison decode of the same sizes
+  // runs the split grid: the size covers both, so one workspace serves either call
+  const int splits = std::max(
+      kvarn::decode_slots(batch, cfg->num_kv_heads, max_blocks_per_seq,
+                          num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, cfg->head_dim),
+      kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq));
   *bytes = (size_t)batch * (size_t)n_query * (size_t)num_q_heads * (size_t)splits *
            (size_t)kvarn::partial_floats(cfg->head_dim) * sizeof(float);
   return KVARN_OK;
@@ -181,10 +178,9 @@ kvarn_status decode_multi(const kvarn_config* cfg, const void* q, int32_t num_q_
       !aligned16(block_pool))
     return KVARN_ERR_BAD_SHAPE;
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(
-      batch, cfg->num_kv_heads, max_blocks_per_seq,
-      kvarn::pairs_mode(num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits, cfg->head_dim,
-                        batch, cfg->num_kv_heads, max_blocks_per_seq));
+  const int splits = kvarn::decode_slots(batch, cfg->num_kv_heads, max_blocks_per_seq,
+                                         num_q_heads / cfg->num_kv_heads * n_query, cfg->v_bits,
+                                         cfg->head_dim);
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
   return from_hip(kvarn::launch_decode(
       static_cast<const __half*>(q), num_q_heads, cfg->num_kv_heads, n_query,
@@ -333,7 +329,7 @@ kvarn_status kvarn_decode_attention_fp16(const kvarn_config* cfg, const void* q,
     return KVARN_ERR_BAD_SHAPE;
   if (!(sm_scale == sm_scale)) return KVARN_ERR_BAD_SHAPE;
   if ((long long)batch > 65535 || cfg->num_kv_heads > 65535) return KVARN_ERR_BAD_SHAPE;
-  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq, false);
+  const int splits = kvarn::decode_splits(batch, cfg->num_kv_heads, max_blocks_per_seq);
   if (workspace_bytes < (size_t)batch * (size_t)num_q_heads * (size_t)splits *
                             (size_t)kvarn::kPartialFloats * sizeof(float))
     return KVARN_ERR_WORKSPACE;                 // covered by the size above; checked anyway

@@ -47,6 +47,9 @@
 #include "kvarn_kernels.hpp"
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace kvarn {
 
@@ -136,6 +139,17 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_v, uint32_t
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask_v), "s"(c_s));
   return r;
+}
+
+// a where the mask is all ones, b where it is zero: one v_bfi_b32 on a per-lane all-ones /
+// zero word. Written out because the optimiser otherwise rewrites a pair of selects between
+// two components of an MFMA result into a read at a runtime index (a chain of three compares
+// and three selects per value).
+__device__ __forceinline__ uint32_t lane_mask(bool c) { return c ? 0xFFFFFFFFu : 0u; }
+__device__ __forceinline__ float pick(uint32_t m, float a, float b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(__float_as_uint(a)), "v"(__float_as_uint(b)));
+  return __uint_as_float(r);
 }
 
 __device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -437,59 +451,163 @@ __device__ __forceinline__ void load_h(const __half* __restrict__ p, float (&v)[
 // the score products run channel block by channel block (one query operand live at a time),
 // and the tile's codes and 16 output accumulators need more than the 256 registers of two
 // waves per SIMD, so that instantiation runs one wave per SIMD.
+// Full tiles of a sequence of length len in the paged table (none when the length is invalid:
+// negative, or more full tiles than the table holds), and the pairs they form (the last one
+// single for an odd count).
+__device__ __forceinline__ int full_tiles(int len, int max_blocks) {
+  return (len < 0 || (len >> 7) > max_blocks) ? 0 : (len >> 7);
+}
+__device__ __forceinline__ int tile_pairs(int len, int max_blocks) {
+  return (full_tiles(len, max_blocks) + 1) >> 1;
+}
+// List positions of a sequence: its full tiles (kUnit 1) or tile pairs (kUnit 2).
+template <int kUnit>
+__device__ __forceinline__ int unit_positions(int len, int max_blocks) {
+  return kUnit == 1 ? full_tiles(len, max_blocks) : tile_pairs(len, max_blocks);
+}
+
+// The work list's positions per sequence (full tiles or tile pairs, x KV heads), summed over
+// lanes: lane l
+// holds sequences [l k, l k + k), k = ceil(batch / 64); mine = its positions, excl = those of
+// the lanes before it, total = the list length (the same in every lane). The list is shorter
+// than 2^31: the paired-tile kernel only serves tables of fewer entries than that.
+struct ListScan {
+  int mine, excl, total;
+  int lo, hi;
+};
+
+template <int kUnit>
+__device__ __forceinline__ ListScan scan_list(const int32_t* __restrict__ seq_lens, int batch,
+                                              int max_blocks, int hkv, int lane) {
+  ListScan r;
+  const int k = (batch + 63) >> 6;
+  r.lo = min(batch, lane * k);
+  r.hi = min(batch, r.lo + k);
+  int mine = 0;
+  for (int i = r.lo; i < r.hi; ++i) mine += unit_positions<kUnit>(seq_lens[i], max_blocks);
+  mine *= hkv;
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  r.mine = mine;
+  r.excl = incl - mine;
+  r.total = __builtin_amdgcn_readlane(incl, 63);
+  return r;
+}
+
+// The sequence holding list position pos (0 <= pos < total) and the positions before it.
+template <int kUnit>
+__device__ __forceinline__ void locate_position(const ListScan& ls,
+                                                const int32_t* __restrict__ seq_lens,
+                                                int max_blocks, int hkv, int pos, int lane,
+                                                int& seq, int& before) {
+  const unsigned long long m = __ballot(ls.excl + ls.mine > pos);
+  const int owner = m ? (int)__builtin_ctzll(m) : 63;
+  int bef = ls.excl;
+  int sq = ls.lo;
+  if (lane == owner) {
+    for (; sq < ls.hi - 1; ++sq) {
+      const int n = unit_positions<kUnit>(seq_lens[sq], max_blocks) * hkv;
+      if (pos < bef + n) break;
+      bef += n;
+    }
+  }
+  seq = __builtin_amdgcn_readlane(sq, owner);
+  before = __builtin_amdgcn_readlane(bef, owner);
+}
+
+// List positions before sequence b (0 <= b < batch).
+template <int kUnit>
+__device__ __forceinline__ int positions_before(const ListScan& ls,
+                                                const int32_t* __restrict__ seq_lens, int batch,
+                                                int max_blocks, int hkv, int b, int lane) {
+  const int k = (batch + 63) >> 6;
+  const int owner = b / k;
+  int bef = ls.excl;
+  if (lane == owner)
+    for (int i = ls.lo; i < b; ++i) bef += unit_positions<kUnit>(seq_lens[i], max_blocks) * hkv;
+  return __builtin_amdgcn_readlane(bef, owner);
+}
+
+// Shares of a list schedule over W workers (waves or workgroups): worker w takes list
+// positions [w share, (w + 1) share), share = max(min_share, ceil(total / W)).
+struct PairSplit {
+  int share;
+  __device__ __forceinline__ long long start(int w) const { return (long long)w * share; }
+  __device__ __forceinline__ int wave_of(int x) const { return x / share; }
+};
+
+__device__ __forceinline__ PairSplit pair_split(int total, int waves, int min_share) {
+  PairSplit r;
+  const long long s = ((long long)total + waves - 1) / waves;
+  r.share = (int)(s > min_share ? s : min_share);
+  return r;
+}
+
+// Partial slots unit (b, g) fills in a list schedule of `workers` workers (0 when the sequence
+// has no list positions).
+template <int kUnit>
+__device__ __forceinline__ int list_slots(const int32_t* __restrict__ seq_lens, int batch,
+                                          int max_blocks, int hkv, int b, int g, int len,
+                                          int workers, int min_share, int lane) {
+  const ListScan ls = scan_list<kUnit>(seq_lens, batch, max_blocks, hkv, lane);
+  const int np = unit_positions<kUnit>(len, max_blocks);
+  if (np == 0) return 0;
+  const PairSplit split = pair_split(ls.total, workers, min_share);
+  const int t0 = positions_before<kUnit>(ls, seq_lens, batch, max_blocks, hkv, b, lane) + g * np;
+  return split.wave_of(t0 + np - 1) - split.wave_of(t0) + 1;
+}
+
+// Issue priority from the wave's progress: 3 in the first quarter of its tiles down to 0 in
+// the last. The two waves a SIMD holds start together with equal work; a SIMD favours its older
+// wave among equal priorities, which would finish it well before the younger one and leave the
+// younger alone (and latency-bound) for the rest of the kernel. Ranking by work left instead
+// keeps the pair level, so they finish together.
+#ifndef KVARN_PAIR_PRIO
+#define KVARN_PAIR_PRIO 1
+#endif
+constexpr bool kPairPrio = KVARN_PAIR_PRIO != 0;
+__device__ __forceinline__ void set_progress_priority(int done, int total) {
+  const int quarter = (4 * done) / total;
+  if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (quarter == 1) __builtin_amdgcn_s_setprio(2);
+  else if (quarter == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+#ifndef KVARN_TILE_PRIO
+#define KVARN_TILE_PRIO 1
+#endif
+constexpr bool kTilePrio = KVARN_TILE_PRIO != 0;
+
+// Tiles i0 .. i0 + ntile - 1 (ntile >= 0) of KV head g of sequence b (length len; bad: the
+// sequence is invalid) for the virtual heads of head group hg, by the workgroup's four waves
+// (wave w takes tiles i0 + w + 4 j); one partial per virtual head into slot `slot` of rows of
+// nslot slots. done0 / total: the workgroup's progress before this segment, in tiles, for the
+// issue priority.
 template <bool kCausal, int kVBits, int kDim>
-__global__ void __launch_bounds__(kTThreads)
-__attribute__((amdgpu_waves_per_eu(kDim == 256 ? 1 : 2, kDim == 256 ? 1 : 2)))
-decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
-                    const uint8_t* __restrict__ pool, long long num_blocks,
-                    const int32_t* __restrict__ block_table, int max_blocks,
-                    const int32_t* __restrict__ seq_lens, float sm_scale,
-                    float* __restrict__ partials, SignWords signs) {
+__device__ __forceinline__ void tile_segment(
+    TileSmem<kDim>& sm, const __half* __restrict__ q, int hq, int hkv, int nq,
+    const uint8_t* __restrict__ pool, long long num_blocks,
+    const int32_t* __restrict__ block_table, int max_blocks, int len, float sm_scale,
+    float* __restrict__ partials, const SignWords& signs, int b, int g, int hg, int i0,
+    int ntile, bool bad, int slot, int nslot, int done0, int total) {
   constexpr int kKW = kDim / 32;        // key words per lane and token block = channel blocks
   constexpr int kNB = kDim / 16;        // output channel blocks
   constexpr int kPer = kDim / 64;       // channels per lane in the query rotation
   constexpr int kPF = 2 + kDim;         // floats per partial
-  __shared__ TileSmem<kDim> sm;
-  const int nsplit = gridDim.x;
-  // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
-  // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
   const int group = hq / hkv, vgroup = group * nq;
-  const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
-  int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
-  if (ngroups > 1) {
-    // workgroups that read the same tiles (same split, KV head, sequence; different head
-    // groups) take dispatch ids 8 apart, so they run on the same XCD and share its L2
-    const int L = blockIdx.x + nsplit * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int P = nsplit * hkv * gridDim.z;
-    const int full = P & ~7;
-    int p;
-    if (L < full * ngroups) {
-      const int r = L % (8 * ngroups);
-      hg = r >> 3;
-      p = (L / (8 * ngroups)) * 8 + (r & 7);
-    } else {
-      const int rem = P - full, r = L - full * ngroups;
-      hg = r / rem;
-      p = full + r % rem;
-    }
-    split = p % nsplit;
-    g = (p / nsplit) % hkv;
-    b = p / (nsplit * hkv);
-  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int vbase = hg * kHeadGroup;
   const int nh = min(kHeadGroup, vgroup - vbase);             // rows served (1..8)
   auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
     return ((long long)b * nq + v / group) * hq + g * group + v % group;
   };
-  const int len = seq_lens[b];
-  bool bad = len < 0 || (len >> 7) > max_blocks;
-  const int n_full = bad ? 0 : (len >> 7);
-  const int chunk = (n_full + nsplit - 1) / nsplit;
-  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
   // this wave's tiles: i0 + wave + 4 j, j < nw. Block ids are scalar loads (the row pointer
   // and j are wave-uniform), each issued one tile before the tile that needs it.
-  const int ntile = i1 - i0;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
   const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
@@ -557,6 +675,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const int gq = n & 7;                              // head of this column / row
   const bool colv = gq < nh;                         // column carries a real head
   const bool colhi = n < 8;
+  const uint32_t hi_m = lane_mask(colhi);
   const float negk = colhi ? 0.0f : -1.0f;           // hi parts on columns 0-7, lo on 8-15
   const int ih = colhi ? 0 : 2;                      // this lane's rows of each score block
   const uint32_t vmask_col = colv ? 0xFFFFFFFFu : 0u;
@@ -586,6 +705,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   // loaded into the key registers once the score products have consumed them, and the next
   // value codes into the value registers once the output products have.
   for (int j = 0; j < nw && !bad; ++j) {
+    if constexpr (kTilePrio) set_progress_priority(done0 + kWaves * j, total);
     const uint8_t* nrec = nullptr;
     if (j + 1 < nw) {
       const long long blk = id_next;
@@ -655,10 +775,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     const int tlim = qlim - tpos;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const float snd0 = colhi ? sc[mb][2] : sc[mb][0];
-      const float snd1 = colhi ? sc[mb][3] : sc[mb][1];
-      const float own0 = colhi ? sc[mb][0] : sc[mb][2];
-      const float own1 = colhi ? sc[mb][1] : sc[mb][3];
+      const float snd0 = pick(hi_m, sc[mb][2], sc[mb][0]);
+      const float snd1 = pick(hi_m, sc[mb][3], sc[mb][1]);
+      const float own0 = pick(hi_m, sc[mb][0], sc[mb][2]);
+      const float own1 = pick(hi_m, sc[mb][1], sc[mb][3]);
       const float d0 = own0 + dpp_ror8(snd0), d1 = own1 + dpp_ror8(snd1);
       const int t0 = 16 * mb + 4 * s + ih;
       const float2 ks2 = *reinterpret_cast<const float2*>(ks + t0);
@@ -752,7 +872,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     if (nrec != nullptr) load_values(nrec, lo, cur);
   }
 
-  // ---- combine the waves' states in LDS and write one partial per (split, head)
+  // ---- combine the waves' states in LDS and write one partial per (slot, head)
   // (score lanes s == 0 hold m, l of column n; rows 4 s + i hold o~ hi (s < 2) and lo parts)
   __syncthreads();
   if (s == 0 && colhi) {
@@ -786,13 +906,89 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
         oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
       }
     }
-    float* p = partials + (row_of(vbase + gg) * nsplit + split) * kPF;
+    float* p = partials + (row_of(vbase + gg) * nslot + slot) * kPF;
     if (jj == 0) {
       p[0] = wbad ? NAN : mm;
       p[1] = wbad ? NAN : ll;
     }
     p[2 + jj] = oo;
   }
+}
+
+// kList: the list schedule (one head group; grid = the resident workgroups); otherwise the
+// split grid (splits x KV heads x head groups, sequences).
+template <bool kCausal, int kVBits, int kDim, bool kList>
+__global__ void __launch_bounds__(kTThreads)
+__attribute__((amdgpu_waves_per_eu(kDim == 256 ? 1 : 2, kDim == 256 ? 1 : 2)))
+decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
+                    const uint8_t* __restrict__ pool, long long num_blocks,
+                    const int32_t* __restrict__ block_table, int max_blocks,
+                    const int32_t* __restrict__ seq_lens, int batch, float sm_scale,
+                    float* __restrict__ partials, int nslot, SignWords signs, int min_share) {
+  __shared__ TileSmem<kDim> sm;
+  if constexpr (kList) {
+    // one head group: the full tiles of every (sequence, KV head) form one list that the
+    // workgroups share evenly, as in the paired-tile schedule (with tiles for positions)
+    const int lane = threadIdx.x & 63;
+    const int wgs = gridDim.x, w = blockIdx.x;
+    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hkv, lane);
+    const PairSplit split = pair_split(ls.total, wgs, min_share);
+    const long long start64 = split.start(w);
+    if (start64 >= ls.total) return;
+    const int start = (int)start64;
+    const int end = (int)min(split.start(w + 1), (long long)ls.total);
+    for (int cur = start; cur < end;) {
+      int b, before;
+      locate_position<1>(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+      const int len = seq_lens[b];
+      const int nt = full_tiles(len, max_blocks);  // > 0: the sequence holds position cur
+      const int g = (cur - before) / nt;
+      const int t0 = (cur - before) - g * nt;
+      const int seg = min(nt - t0, end - cur);
+      const int slot = w - split.wave_of(cur - t0);
+      if (cur != start) __syncthreads();           // LDS of the last unit read before this one's
+      tile_segment<kCausal, kVBits, kDim>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
+                                          max_blocks, len, sm_scale, partials, signs, b, g, 0,
+                                          t0, seg, false, slot, nslot, cur - start,
+                                          end - start);
+      cur += seg;
+    }
+    return;
+  }
+  const int nsplit = gridDim.x;
+  // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
+  // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
+  const int group = hq / hkv, vgroup = group * nq;
+  const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
+  int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
+  if (ngroups > 1) {
+    // workgroups that read the same tiles (same split, KV head, sequence; different head
+    // groups) take dispatch ids 8 apart, so they run on the same XCD and share its L2
+    const int L = blockIdx.x + nsplit * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int P = nsplit * hkv * gridDim.z;
+    const int full = P & ~7;
+    int p;
+    if (L < full * ngroups) {
+      const int r = L % (8 * ngroups);
+      hg = r >> 3;
+      p = (L / (8 * ngroups)) * 8 + (r & 7);
+    } else {
+      const int rem = P - full, r = L - full * ngroups;
+      hg = r / rem;
+      p = full + r % rem;
+    }
+    split = p % nsplit;
+    g = (p / nsplit) % hkv;
+    b = p / (nsplit * hkv);
+  }
+  const int len = seq_lens[b];
+  const bool bad = len < 0 || (len >> 7) > max_blocks;
+  const int n_full = bad ? 0 : (len >> 7);
+  const int chunk = (n_full + nsplit - 1) / nsplit;
+  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  tile_segment<kCausal, kVBits, kDim>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
+                                      max_blocks, len, sm_scale, partials, signs, b, g, hg, i0,
+                                      i1 - i0, bad, split, nsplit, 0, i1 - i0);
 }
 
 // ------------------------------------------------------------------ paired tiles (<= 4 heads)
@@ -832,109 +1028,7 @@ __device__ __forceinline__ uint32_t dpp_half_mirror_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
 }
 
-// Full tiles of a sequence of length len in the paged table (none when the length is invalid:
-// negative, or more full tiles than the table holds), and the pairs they form (the last one
-// single for an odd count).
-__device__ __forceinline__ int full_tiles(int len, int max_blocks) {
-  return (len < 0 || (len >> 7) > max_blocks) ? 0 : (len >> 7);
-}
-__device__ __forceinline__ int tile_pairs(int len, int max_blocks) {
-  return (full_tiles(len, max_blocks) + 1) >> 1;
-}
 
-// The work list's positions per sequence (tile pairs x KV heads), summed over lanes: lane l
-// holds sequences [l k, l k + k), k = ceil(batch / 64); mine = its positions, excl = those of
-// the lanes before it, total = the list length (the same in every lane). The list is shorter
-// than 2^31: the paired-tile kernel only serves tables of fewer entries than that.
-struct ListScan {
-  int mine, excl, total;
-  int lo, hi;
-};
-
-__device__ __forceinline__ ListScan scan_list(const int32_t* __restrict__ seq_lens, int batch,
-                                              int max_blocks, int hkv, int lane) {
-  ListScan r;
-  const int k = (batch + 63) >> 6;
-  r.lo = min(batch, lane * k);
-  r.hi = min(batch, r.lo + k);
-  int mine = 0;
-  for (int i = r.lo; i < r.hi; ++i) mine += tile_pairs(seq_lens[i], max_blocks);
-  mine *= hkv;
-  int incl = mine;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(incl, d);
-    if (lane >= d) incl += t;
-  }
-  r.mine = mine;
-  r.excl = incl - mine;
-  r.total = __builtin_amdgcn_readlane(incl, 63);
-  return r;
-}
-
-// The sequence holding list position pos (0 <= pos < total) and the positions before it.
-__device__ __forceinline__ void locate_position(const ListScan& ls,
-                                                const int32_t* __restrict__ seq_lens,
-                                                int max_blocks, int hkv, int pos, int lane,
-                                                int& seq, int& before) {
-  const unsigned long long m = __ballot(ls.excl + ls.mine > pos);
-  const int owner = m ? (int)__builtin_ctzll(m) : 63;
-  int bef = ls.excl;
-  int sq = ls.lo;
-  if (lane == owner) {
-    for (; sq < ls.hi - 1; ++sq) {
-      const int n = tile_pairs(seq_lens[sq], max_blocks) * hkv;
-      if (pos < bef + n) break;
-      bef += n;
-    }
-  }
-  seq = __builtin_amdgcn_readlane(sq, owner);
-  before = __builtin_amdgcn_readlane(bef, owner);
-}
-
-// List positions before sequence b (0 <= b < batch).
-__device__ __forceinline__ int positions_before(const ListScan& ls,
-                                                const int32_t* __restrict__ seq_lens, int batch,
-                                                int max_blocks, int hkv, int b, int lane) {
-  const int k = (batch + 63) >> 6;
-  const int owner = b / k;
-  int bef = ls.excl;
-  if (lane == owner)
-    for (int i = ls.lo; i < b; ++i) bef += tile_pairs(seq_lens[i], max_blocks) * hkv;
-  return __builtin_amdgcn_readlane(bef, owner);
-}
-
-// Shares of the paired-tile schedule: wave w takes list positions [w share, (w + 1) share),
-// share = max(min_share, ceil(total / W)).
-struct PairSplit {
-  int share;
-  __device__ __forceinline__ long long start(int w) const { return (long long)w * share; }
-  __device__ __forceinline__ int wave_of(int x) const { return x / share; }
-};
-
-__device__ __forceinline__ PairSplit pair_split(int total, int waves, int min_share) {
-  PairSplit r;
-  const long long s = ((long long)total + waves - 1) / waves;
-  r.share = (int)(s > min_share ? s : min_share);
-  return r;
-}
-
-// Issue priority from the wave's progress: 3 in the first quarter of its tiles down to 0 in
-// the last. The two waves a SIMD holds start together with equal work; a SIMD favours its older
-// wave among equal priorities, which would finish it well before the younger one and leave the
-// younger alone (and latency-bound) for the rest of the kernel. Ranking by work left instead
-// keeps the pair level, so they finish together.
-#ifndef KVARN_PAIR_PRIO
-#define KVARN_PAIR_PRIO 1
-#endif
-constexpr bool kPairPrio = KVARN_PAIR_PRIO != 0;
-__device__ __forceinline__ void set_progress_priority(int done, int total) {
-  const int quarter = (4 * done) / total;
-  if (quarter <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (quarter == 1) __builtin_amdgcn_s_setprio(2);
-  else if (quarter == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
 
 // Tiles i0 .. i0 + ntile - 1 (ntile >= 1) of KV head g of sequence b (length len, valid) into
 // partial slot `slot` of each virtual head's row (rows of nslot slots).
@@ -1013,6 +1107,7 @@ __device__ __forceinline__ void pair_segment(
   const int tsel = n >> 3;                         // first or second tile of the pair
   const int pos = n & 7;
   const bool colhi = pos < 4;
+  const uint32_t hi_m = lane_mask(colhi);
   const int hh = colhi ? pos : 7 - pos;            // virtual head of this column / row
   const bool colv = hh < nh;
   const float negk = colhi ? 0.0f : -1.0f;         // hi parts at positions 0-3, lo at 4-7
@@ -1111,10 +1206,10 @@ __device__ __forceinline__ void pair_segment(
     const int tlim = qlim - tpos;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const float snd0 = colhi ? sc[mb][2] : sc[mb][0];
-      const float snd1 = colhi ? sc[mb][3] : sc[mb][1];
-      const float own0 = colhi ? sc[mb][0] : sc[mb][2];
-      const float own1 = colhi ? sc[mb][1] : sc[mb][3];
+      const float snd0 = pick(hi_m, sc[mb][2], sc[mb][0]);
+      const float snd1 = pick(hi_m, sc[mb][3], sc[mb][1]);
+      const float own0 = pick(hi_m, sc[mb][0], sc[mb][2]);
+      const float own1 = pick(hi_m, sc[mb][1], sc[mb][3]);
       const float d0 = own0 + dpp_half_mirror(snd0), d1 = own1 + dpp_half_mirror(snd1);
       const int t0 = 16 * mb + 4 * s + ih;
       const float2 ks2 = *reinterpret_cast<const float2*>(ks + t0);
@@ -1257,15 +1352,17 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   __shared__ PairSmem sm;
   const int lane = threadIdx.x;
   const int waves = gridDim.x, w = blockIdx.x;
-  const ListScan ls = scan_list(seq_lens, batch, max_blocks, hkv, lane);
+  const ListScan ls = scan_list<2>(seq_lens, batch, max_blocks, hkv, lane);
   const PairSplit split = pair_split(ls.total, waves, min_share);
   const long long start64 = split.start(w);
   if (start64 >= ls.total) return;                 // more waves than list positions
   const int start = (int)start64;
   const int end = (int)min(split.start(w + 1), (long long)ls.total);
-  for (int cur = start; cur < end;) {
+  // one segment per call: the first outside any loop (most waves have no other), the rest in
+  // a loop
+  auto segment = [&](int cur) -> int {
     int b, before;                                 // the unit holding position cur
-    locate_position(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+    locate_position<2>(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
     const int len = seq_lens[b];
     const int nt = full_tiles(len, max_blocks);
     const int np = (nt + 1) >> 1;                  // > 0: the sequence holds position cur
@@ -1273,12 +1370,16 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     const int p0 = (cur - before) - g * np;        // first pair of the segment in its unit
     const int seg = min(np - p0, end - cur);       // pairs
     const int slot = w - split.wave_of(cur - p0);  // cur - p0 = T(u)
-    if (cur != start) __syncthreads();             // LDS of the last unit read before this one's
     pair_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
                                   len, sm_scale, partials, signs, b, g, 2 * p0,
                                   min(2 * seg, nt - 2 * p0), slot, nslot, 2 * (cur - start),
                                   2 * (end - start));
-    cur += seg;
+    return cur + seg;
+  };
+  int cur = segment(start);
+  while (cur < end) {
+    __syncthreads();                               // LDS of the last unit read before this one's
+    cur = segment(cur);
   }
 }
 
@@ -1364,7 +1465,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out,
-                    SignWords signs, int pair_waves, int min_share) {
+                    SignWords signs, int sk_workers, int sk_unit, int min_share) {
   constexpr int kPer = kDim / 64;      // output channels per lane: kPer lane .. + kPer - 1
   constexpr int kPF = 2 + kDim;        // floats per partial
   __shared__ float qs[kDim];
@@ -1413,18 +1514,15 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   qw.load(q + row * kDim + kPer * lane);
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
-  // slots holding a partial: all nsplit after the tile kernel; after the paired-tile kernel
-  // (pair_waves > 0) the slots of this (sequence, KV head) in that kernel's schedule
+  // slots holding a partial: all nsplit after a split grid; after a list schedule of
+  // sk_workers workers over units of sk_unit tiles (1 or 2) the slots this (sequence, KV head)
+  // meets in that schedule
   int nuse = nsplit;
-  if (pair_waves > 0) {
-    const ListScan ls = scan_list(seq_lens, gridDim.y, max_blocks, hkv, lane);
-    const int np = tile_pairs(len, max_blocks);
-    nuse = 0;
-    if (np > 0) {
-      const PairSplit split = pair_split(ls.total, pair_waves, min_share);
-      const int t0 = positions_before(ls, seq_lens, gridDim.y, max_blocks, hkv, b, lane) + g * np;
-      nuse = split.wave_of(t0 + np - 1) - split.wave_of(t0) + 1;
-    }
+  if (sk_workers > 0) {
+    nuse = sk_unit == 1 ? list_slots<1>(seq_lens, gridDim.y, max_blocks, hkv, b, g, len,
+                                        sk_workers, min_share, lane)
+                        : list_slots<2>(seq_lens, gridDim.y, max_blocks, hkv, b, g, len,
+                                        sk_workers, min_share, lane);
   }
   // staging tokens this query token sees: positions up to len - nq + qi
   const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (kCausal ? nq - 1 - qi : 0));
@@ -1973,38 +2071,71 @@ int pairs_min_share(int max_blocks) {
   return ((max_blocks + 1) / 2 - 1) / (kMaxSplits - 2) + 1;
 }
 
-// Waves of the paired-tile kernel: as many one-wave workgroups as the current device holds at
-// once (the kernel's occupancy, read once per device and cached, times the compute units),
-// times KVARN_PAIR_ROUNDS.
-int pairs_waves() {
-  constexpr int kMaxDevices = 64, kDefaultPerCU = 8;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  int per_cu = kDefaultPerCU;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+// Workgroups of `kernel` (block threads) the current device holds at once: its occupancy per
+// compute unit (read once per device and kernel, and cached) times the compute units. A host
+// without a usable device plans for `fallback` per compute unit.
+int resident_workgroups(const void* kernel, int threads, int fallback) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0, per_cu = fallback;
+  if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
-  } else if (const int c = cache[dev].load(std::memory_order_relaxed); c > 0) {
-    per_cu = c;
   } else {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&decode_pairs_kernel<false, 2>), 64, 0) !=
-            hipSuccess ||
-        n <= 0) {
-      (void)hipGetLastError();
-      n = kDefaultPerCU;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) {
+      per_cu = it->second;
+    } else {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess ||
+          n <= 0) {
+        (void)hipGetLastError();
+        n = fallback;
+      }
+      cache[{dev, kernel}] = n;
+      per_cu = n;
     }
-    cache[dev].store(n, std::memory_order_relaxed);
-    per_cu = n;
   }
-  return kPairRounds * per_cu * device_compute_units();
+  return per_cu * device_compute_units();
 }
 
-int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel) {
-  if (pair_kernel) {
-    // partial slots per row: the most a unit of the paired-tile schedule can span
-    return ((max_blocks + 1) / 2 - 1) / pairs_min_share(max_blocks) + 2;
+// Smallest share (in tiles, at least one per wave) of the tile kernel's list schedule: a unit
+// of n <= max_blocks tiles spans at most floor((max_blocks - 1) / share) + 2 <= kMaxSplits
+// partial slots.
+int tiles_min_share(int max_blocks) {
+  const int m = (max_blocks - 1) / (kMaxSplits - 2) + 1;
+  return m > kWaves ? m : kWaves;
+}
+
+// Which kernel and schedule a packed decode of these sizes runs: the paired-tile kernel (list
+// schedule over tile pairs), the tile kernel with one head group on a large table (list
+// schedule over tiles), or the tile kernel over a grid of splits (several head groups per KV
+// head, or a table of fewer than kPairMinTilesPerCU entries per compute unit, where the list
+// schedule's longer start-up is not repaid).
+DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
+                       int head_dim) {
+  if (pairs_mode(virtual_heads, v_bits, head_dim, batch, hkv, max_blocks))
+    return DecodeKind::kPairList;
+  const long long tiles = (long long)batch * hkv * max_blocks;
+  if (virtual_heads <= kHeadGroup && tiles >= kPairMinTilesPerCU * device_compute_units() &&
+      tiles < (1LL << 31))
+    return DecodeKind::kTileList;
+  return DecodeKind::kTileGrid;
+}
+
+int decode_slots(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
+                 int head_dim) {
+  switch (decode_kind(batch, hkv, max_blocks, virtual_heads, v_bits, head_dim)) {
+    case DecodeKind::kPairList:
+      return ((max_blocks + 1) / 2 - 1) / pairs_min_share(max_blocks) + 2;
+    case DecodeKind::kTileList:
+      return (max_blocks - 1) / tiles_min_share(max_blocks) + 2;
+    default:
+      return decode_splits(batch, hkv, max_blocks);
   }
+}
+
+int decode_splits(int batch, int hkv, int max_blocks) {
   const long long pairs = (long long)batch * hkv > 0 ? (long long)batch * hkv : 1;
   // two workgroups per compute unit (2 waves per SIMD)
   const long long target = 2LL * device_compute_units();
@@ -2033,31 +2164,48 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
                            long long num_blocks, const int32_t* block_table, int max_blocks,
                            const int32_t* seq_lens, const __half* staging_k,
                            const __half* staging_v, float sm_scale, float* out, float* partials,
-                           int splits, int batch, SignWords sg, int v_bits, hipStream_t stream) {
-  const int ngroups = (hq / hkv * nq + kHeadGroup - 1) / kHeadGroup;
-  const dim3 grid(splits, hkv * ngroups, batch), mgrid(hq * nq, batch);
-  int pair_waves = 0, min_share = 0;
-  if (kDim == 128 && pairs_mode(hq / hkv * nq, v_bits, kDim, batch, hkv, max_blocks)) {
+                           int slots, int batch, SignWords sg, int v_bits, hipStream_t stream) {
+  const int vh = hq / hkv * nq;
+  const DecodeKind kind = decode_kind(batch, hkv, max_blocks, vh, v_bits, kDim);
+  int workers = 0, unit = 0, min_share = 0;
+  if (kDim == 128 && kind == DecodeKind::kPairList) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
-    pair_waves = pairs_waves();
+    workers = kPairRounds * resident_workgroups(reinterpret_cast<const void*>(kern), 64, 8);
+    unit = 2;
     min_share = pairs_min_share(max_blocks);
-    hipLaunchKernelGGL(kern, dim3(pair_waves), dim3(64), 0, stream, q, hq, hkv, nq, pool,
+    hipLaunchKernelGGL(kern, dim3(workers), dim3(64), 0, stream, q, hq, hkv, nq, pool,
                        num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale, partials,
-                       splits, sg, min_share);
+                       slots, sg, min_share);
   } else {
-    auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4, kDim>
-                                       : decode_tiles_kernel<false, 2, kDim>)
-                        : (v_bits == 4 ? decode_tiles_kernel<true, 4, kDim>
-                                       : decode_tiles_kernel<true, 2, kDim>);
-    hipLaunchKernelGGL(kern, grid, dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool, num_blocks,
-                       block_table, max_blocks, seq_lens, sm_scale, partials, sg);
+    if (kind == DecodeKind::kTileList) {
+      auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4, kDim, true>
+                                         : decode_tiles_kernel<false, 2, kDim, true>)
+                          : (v_bits == 4 ? decode_tiles_kernel<true, 4, kDim, true>
+                                         : decode_tiles_kernel<true, 2, kDim, true>);
+      workers = resident_workgroups(reinterpret_cast<const void*>(kern), kTThreads,
+                                    kDim == 256 ? 1 : 2);
+      unit = 1;
+      min_share = tiles_min_share(max_blocks);
+      hipLaunchKernelGGL(kern, dim3(workers), dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool,
+                         num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale,
+                         partials, slots, sg, min_share);
+    } else {
+      auto kern = nq == 1 ? (v_bits == 4 ? decode_tiles_kernel<false, 4, kDim, false>
+                                         : decode_tiles_kernel<false, 2, kDim, false>)
+                          : (v_bits == 4 ? decode_tiles_kernel<true, 4, kDim, false>
+                                         : decode_tiles_kernel<true, 2, kDim, false>);
+      const int ngroups = (vh + kHeadGroup - 1) / kHeadGroup;
+      hipLaunchKernelGGL(kern, dim3(slots, hkv * ngroups, batch), dim3(kTThreads), 0, stream, q,
+                         hq, hkv, nq, pool, num_blocks, block_table, max_blocks, seq_lens, batch,
+                         sm_scale, partials, slots, sg, 0);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto merge = nq == 1 ? decode_merge_kernel<true, false, kDim> : decode_merge_kernel<true, true, kDim>;
-  hipLaunchKernelGGL(merge, mgrid, dim3(kMThreads), 0, stream, q, hq, hkv, nq, max_blocks,
-                     seq_lens, staging_k, staging_v, sm_scale, partials, splits, out, sg,
-                     pair_waves, min_share);
+  hipLaunchKernelGGL(merge, dim3(hq * nq, batch), dim3(kMThreads), 0, stream, q, hq, hkv, nq,
+                     max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, slots, out,
+                     sg, workers, unit, min_share);
   return hipGetLastError();
 }
 
@@ -2067,12 +2215,12 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
-                         int splits, int batch, const uint32_t* signs, int v_bits, int head_dim,
+                         int slots, int batch, const uint32_t* signs, int v_bits, int head_dim,
                          hipStream_t stream) {
   const SignWords sg = sign_words(signs);
 #define KVARN_D(DIM)                                                                         \
   launch_decode_t<DIM>(q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks, seq_lens,   \
-                       staging_k, staging_v, sm_scale, out, partials, splits, batch, sg,       \
+                       staging_k, staging_v, sm_scale, out, partials, slots, batch, sg,        \
                        v_bits, stream)
   if (head_dim == 64) return KVARN_D(64);
   if (head_dim == 256) return KVARN_D(256);
@@ -2105,7 +2253,7 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
   none.hi = none.lo;
   hipLaunchKernelGGL((decode_merge_kernel<false, false, kD>), dim3(hq, batch), dim3(kMThreads), 0,
                      stream, q, hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                     partials, splits, out, none, 0, 0);
+                     partials, splits, out, none, 0, 0, 0);
   return hipGetLastError();
 }
 

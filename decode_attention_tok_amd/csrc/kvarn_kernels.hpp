@@ -35,7 +35,7 @@ hipError_t launch_decode(const __half* q, int hq, int hkv, int nq, const uint8_t
                          long long num_blocks, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, const __half* staging_k,
                          const __half* staging_v, float sm_scale, float* out, float* partials,
-                         int splits, int batch, const uint32_t* signs, int v_bits, int head_dim,
+                         int slots, int batch, const uint32_t* signs, int v_bits, int head_dim,
                          hipStream_t stream);
 
 // signs: the eight words of optional per-channel sign flips before the rotation (host array;
@@ -61,11 +61,19 @@ hipError_t launch_dequantize_tiles(const uint8_t* pool, long long num_blocks,
                                    float* v_out, const uint32_t* signs, int v_bits, int head_dim,
                                    hipStream_t stream);
 
-// Number of splits of each sequence's tiles for a decode launch: depends on the sizes and on
-// the compute-unit count of the current device (read once per device and cached).
-int decode_splits(int batch, int hkv, int max_blocks, bool pair_kernel);
+// Splits of each sequence's tiles for the split grid of the four-wave tile kernels (the fp16
+// comparison decode, and packed decodes with several head groups per KV head): depends on the
+// sizes and on the compute-unit count of the current device (read once per device and cached).
+int decode_splits(int batch, int hkv, int max_blocks);
 // Whether a decode of these sizes runs the paired-tile kernel (decode_pairs_kernel).
 bool pairs_mode(int virtual_heads, int v_bits, int head_dim, int batch, int hkv, int max_blocks);
+// The kernel and schedule of a packed decode (virtual heads = query heads per KV head x query
+// tokens), and the partial slots per (sequence, query token, query head) row it needs.
+enum class DecodeKind { kPairList, kTileList, kTileGrid };
+DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
+                       int head_dim);
+int decode_slots(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
+                 int head_dim);
 int device_compute_units();
 
 }  // namespace kvarn

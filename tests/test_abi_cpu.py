@@ -109,36 +109,41 @@ def test_workspace_bytes_depends_only_on_sizes_and_device(lib):
 
 
 def test_workspace_follows_the_split_plan(lib):
-    """The workspace holds 130 floats per (sequence, query head, split). This host has no GPU:
-    the plan assumes 256 compute units.
-    Four-wave tile kernel (more than four virtual heads per KV head, 4-bit values, or fewer
-    than 64 table entries x KV heads x sequences per compute unit): two workgroups per compute
-    unit, at least two tiles per wave unless that leaves fewer than two workgroups per compute
-    unit (then one), at most 32 full tiles per split for the longest table (its last entry is
-    the staging tile).
-    Paired-tile kernel (otherwise): the sequences' tile pairs form one list that the resident
-    waves share evenly, at least m = (p - 1) // 62 + 1 pairs per wave for p = ceil(entries / 2);
-    a (sequence, KV head) of up to p pairs then spans at most (p - 1) // m + 2 waves, each
-    writing its own partial slot."""
+    """The workspace holds 130 floats per (sequence, query head, partial slot). This host has
+    no GPU: the plan assumes 256 compute units.
+    List schedules, for tables of at least 64 entries x KV heads x sequences per compute unit:
+    the sequences' full tiles (four-wave tile kernel, at most 8 virtual heads per KV head) or
+    tile pairs (paired-tile kernel: at most four virtual heads, 2-bit values, head dimension
+    128) form one list that the resident workers share evenly, at least m positions each: tiles,
+    m = max(4, (entries - 1) // 62 + 1); pairs, m = (p - 1) // 62 + 1 for p = ceil(entries / 2).
+    A (sequence, KV head) of up to n positions (entries or p) then meets at most
+    (n - 1) // m + 2 workers, each writing its own partial slot.
+    Split grid (more than 8 virtual heads per KV head, or a smaller table; also the fp16
+    comparison decode, whose need the size always covers): two workgroups per compute unit, at
+    least two tiles per wave
+    unless that leaves fewer than two workgroups per compute unit (then one), at most 32 full
+    tiles per split for the longest table (its last entry is the staging tile)."""
     per = 130 * 4
-    # 16K context, batch 16, 8 KV heads, group 8: 512 / 128 pairs = 4 splits of 32 tiles
-    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 4 * per
-    # 4K context, batch 8 (33 entries; 2,112 < 16,384): 8 splits wanted; two tiles per wave
-    # would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
+    # 16K context, batch 16, 8 KV heads, group 8: tile list, m = 4, 128 // 4 + 2 = 34 slots
+    # (the split grid of the same sizes needs 4)
+    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 34 * per
+    # the same with group 16 (two head groups): split grid, 512 / 128 pairs = 4 splits
+    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 128, 129) == 16 * 128 * 4 * per
+    # 4K context, batch 8 (33 entries; 2,112 < 16,384): split grid, 8 splits wanted; two tiles
+    # per wave would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
     assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
     # 4K context, batch 64 (16,896 entries), group 4: paired tiles, p = 17, m = 1,
-    # 16 // 1 + 2 = 18 slots (the tile plan of the same sizes needs 1)
+    # 16 // 1 + 2 = 18 slots
     assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 33) == 64 * 32 * 18 * per
-    # the same with 4-bit values: tile kernel, 512 pairs fill the device with one split
-    assert kv.decode_workspace_bytes(kv.default_config(8, v_bits=4), 64, 32, 33) == 64 * 32 * per
+    # the same with 4-bit values: tile list, 10 slots
+    assert kv.decode_workspace_bytes(kv.default_config(8, v_bits=4), 64, 32, 33) == 64 * 32 * 10 * per
     # ragged batch up to 32K tokens, batch 32, 10 KV heads, group 4 (82,240 entries): paired
     # tiles, p = 129, m = 128 // 62 + 1 = 3, 128 // 3 + 2 = 44 slots
     assert kv.decode_workspace_bytes(kv.default_config(10), 32, 40, 257) == 32 * 40 * 44 * per
-    # the same batch with group 8: tile kernel, 2 splits wanted, 256 full tiles need 8
-    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 80, 257) == 32 * 80 * 8 * per
+    # the same batch with group 8: tile list, m = 256 // 62 + 1 = 5, 256 // 5 + 2 = 53 slots
+    assert kv.decode_workspace_bytes(kv.default_config(10), 32, 80, 257) == 32 * 80 * 53 * per
     # 128K context, batch 64, 8 KV heads, group 4 (524,800 entries): paired tiles, p = 513,
-    # m = 9, 512 // 9 + 2 = 58 slots; the fp16 comparison decode of the same sizes runs the tile
-    # plan (32 splits): the size covers both
+    # m = 9, 512 // 9 + 2 = 58 slots; the split grid of the same sizes needs 32
     assert kv.decode_workspace_bytes(kv.default_config(8), 64, 32, 1025) == 64 * 32 * 58 * per
 
 
@@ -146,7 +151,8 @@ def test_multi_workspace_and_query_token_limits(lib):
     cfg = kv.default_config(8)
     one = kv.decode_workspace_bytes(cfg, 16, 64, 128)
     assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 1, 128) == one
-    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 4, 128) == 4 * one
+    # four query tokens x group 8 = 32 virtual heads: the split grid (4 splits) for 4x the rows
+    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 4, 128) == 16 * 4 * 64 * 4 * 130 * 4
     assert kv.decode_multi_workspace_bytes(cfg, 16, 64, kv.MAX_QUERY_TOKENS, 128) > 0
     for bad in (0, -1, kv.MAX_QUERY_TOKENS + 1):
         with pytest.raises(RuntimeError):

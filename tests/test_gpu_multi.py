@@ -171,3 +171,24 @@ def test_multi_pair_kernel_matches_oracle(name, over, tails, nq):
     err = np.abs(got - ref).max()
     _say(f"multi pair kernel {name} {over} tails={tails} nq={nq}: max abs err {err:.3g}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("name,over,tails,nq,v_bits", [
+    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), [0, 5, 127], 2, 2),     # 4 x 2 rows
+    ("qwen3-4b", dict(batch=2, ctx=896, hkv=2, hq=4), [100, 9], 4, 4),         # 2 x 4 rows
+    ("qwen3-4b", dict(batch=4, ctx=640, hkv=2, hq=2), [0, 1, 64, 127], 3, 4),  # 1 x 3 rows, 4-bit
+])
+def test_multi_tile_list_matches_oracle(name, over, tails, nq, v_bits):
+    """Several query tokens with five to eight virtual heads per KV head (or 4-bit values) on
+    a wide block table: the four-wave tile kernel's list schedule, causal masks included."""
+    from test_gpu_parity import widen
+    sp = gen.spec(name, **over)
+    pool, bt, lens, sk, sv, _, sm = _decode_case(sp, tails, v_bits=v_bits)
+    q = gen.query_tokens(sp, nq)
+    cfg = kv.default_config(sp.hkv, v_bits=v_bits)
+    got = gpu_multi(cfg, q, pool, widen(bt, sp.hkv), lens, sk, sv, sm)
+    ref = oatt.decode_attention_multi(q, pool, bt, lens, sk, sv, sm)
+    err = np.abs(got - ref).max()
+    _say(f"multi tile list {name} {over} tails={tails} nq={nq} v_bits={v_bits}: "
+         f"max abs err {err:.3g}")
+    assert err <= TOL
