@@ -431,6 +431,61 @@ def read_probe_measure(torch, lib_path, n_bytes=4 << 30, repeats=5):
             "frac_of_peak": round(n_bytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def record_probe_measure(torch, lib_path, rec_sizes=(13312, 65536), n_bytes=2 << 30,
+                         read_bytes=640 << 20, repeats=9):
+    """Achievable read bandwidth in the decode's access pattern: whole tile records (packed and
+    fp16) at random places in a 2 GiB buffer, one wave per record stream, two waves per SIMD,
+    about 640 MB per launch (the Phi-4-like decode's size). Launches rotate through three
+    disjoint record sets, so none finds its records in the 256 MB last-level cache; median of
+    the repeats. Context, never a denominator."""
+    import ctypes
+    import numpy as np
+    if not os.path.exists(lib_path):
+        return None
+    plib = ctypes.CDLL(lib_path)
+    plib.kvarn_probe_records.restype = ctypes.c_int
+    plib.kvarn_probe_records.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(5)
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    waves = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    res = []
+    for rb in rec_sizes:
+        nrec = n_bytes // rb
+        per_wave = max(1, read_bytes // rb // waves)
+        per_set = waves * per_wave
+        if 3 * per_set > nrec:
+            continue
+        perm = np.random.default_rng(11).permutation(nrec)[:3 * per_set].astype(np.int32)
+        sets = [torch.from_numpy(perm[k * per_set:(k + 1) * per_set].copy()).cuda()
+                for k in range(3)]
+        def launch(k):
+            assert plib.kvarn_probe_records(buf.data_ptr(), n_bytes, rb, sets[k % 3].data_ptr(),
+                                            waves, per_wave, 0x9E3779B9, out.data_ptr(),
+                                            stream.cuda_stream) == 0
+        for k in range(3):
+            launch(k)
+        torch.cuda.synchronize()
+        ts = []
+        for k in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(k)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(ts)[len(ts) // 2]
+        nb = per_set * rb
+        res.append({"rec_bytes": rb, "waves": waves, "read_bytes": nb,
+                    "gbps": round(nb / t / 1e9, 1), "frac_of_peak": round(nb / t / 1e9 / HBM_PEAK_GBPS, 4)})
+        print(f"# record probe: {rb}-byte records at random places, {nb / 1e6:.0f} MB: "
+              f"{nb / t / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    del buf
+    return res
+
+
 def warm_decode_measure(lib, calls, torch, steps=50):
     """The decode of the main loop launched back to back on ONE replica: its pool may then be
     served partly from the 256 MB last-level cache (context, not the metric)."""
@@ -771,10 +826,11 @@ def main():
         k4v4 = k4v4_measure(args, kv, lib, cfg, sp, st, bt, bt_np, lens, lens_np, R, sm, torch,
                             dev)
 
-    hbm = rprobe = warm = rounds = layer_stream = wstream = None
+    hbm = rprobe = recprobe = warm = rounds = layer_stream = wstream = None
     if not args.no_extras:
         hbm = hbm_copy_measure(torch)
         rprobe = read_probe_measure(torch, kbuild.PROBE_LIB)
+        recprobe = record_probe_measure(torch, kbuild.PROBE_LIB)
         tw = warm_decode_measure(lib, W["calls"], torch)
         warm = {"us": round(tw * 1e6, 2), "gbps": round(d_bytes / tw / 1e9, 1),
                 "pool_bytes": st["num_blocks"] * sp.hkv * TILE}
@@ -819,8 +875,8 @@ def main():
                            "append": "kvarn_append_token (append_token_kernel<2, 128>)",
                            "decode": "kvarn_decode_attention (decode_pairs_kernel<false, 2> on "
                                      "large tables with at most 4 query heads per KV head, else "
-                                     "decode_tiles_kernel<false, 2, 128>; then "
-                                     "decode_merge_kernel<true, false, 128>)"}[dominant],
+                                     "decode_tiles_kernel<false, 2, 128, list schedule on large "
+                                     "tables>; then decode_merge_kernel<true, false, 128>)"}[dominant],
                 "algorithmic_bytes_per_launch": byts[dominant],
                 "avg_launch_us": round(timings[dominant] * 1e6, 2)}
     decode_gbps = d_bytes / td / 1e9
@@ -843,6 +899,7 @@ def main():
         "preset_k4v4": k4v4,
         "hbm_copy": hbm,
         "hbm_read_probe": rprobe,
+        "hbm_record_probe": recprobe,
         "decode_warm": warm,
         "quantise_rounds": rounds,
         "decode_layer_stream": layer_stream,
