@@ -1403,6 +1403,12 @@ constexpr int kPairMinTilesPerCU = KVARN_PAIR_MIN_TILES_PER_CU;
 #define KVARN_PAIR_ROUNDS 1
 #endif
 constexpr int kPairRounds = KVARN_PAIR_ROUNDS;   // paired-tile waves per resident wave slot
+#ifndef KVARN_TILE_LIST_MAX_PER_CU
+#define KVARN_TILE_LIST_MAX_PER_CU 2
+#endif
+// four-wave workgroups per compute unit on the tile list at most (D = 64 fits 3, and the
+// shorter workers lose more to their start-up than the extra occupancy gains)
+constexpr int kTileListMaxPerCU = KVARN_TILE_LIST_MAX_PER_CU;
 #ifndef KVARN_MERGE_PRELOAD
 #define KVARN_MERGE_PRELOAD 8
 #endif
@@ -2072,9 +2078,9 @@ int pairs_min_share(int max_blocks) {
 }
 
 // Workgroups of `kernel` (block threads) the current device holds at once: its occupancy per
-// compute unit (read once per device and kernel, and cached) times the compute units. A host
-// without a usable device plans for `fallback` per compute unit.
-int resident_workgroups(const void* kernel, int threads, int fallback) {
+// compute unit (read once per device and kernel, and cached; at most max_per_cu) times the
+// compute units. A host without a usable device plans for `fallback` per compute unit.
+int resident_workgroups(const void* kernel, int threads, int fallback, int max_per_cu) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0, per_cu = fallback;
@@ -2096,7 +2102,7 @@ int resident_workgroups(const void* kernel, int threads, int fallback) {
       per_cu = n;
     }
   }
-  return per_cu * device_compute_units();
+  return (per_cu < max_per_cu ? per_cu : max_per_cu) * device_compute_units();
 }
 
 // Smallest share (in tiles, at least one per wave) of the tile kernel's list schedule: a unit
@@ -2170,7 +2176,7 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
   int workers = 0, unit = 0, min_share = 0;
   if (kDim == 128 && kind == DecodeKind::kPairList) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
-    workers = kPairRounds * resident_workgroups(reinterpret_cast<const void*>(kern), 64, 8);
+    workers = kPairRounds * resident_workgroups(reinterpret_cast<const void*>(kern), 64, 8, 64);
     unit = 2;
     min_share = pairs_min_share(max_blocks);
     hipLaunchKernelGGL(kern, dim3(workers), dim3(64), 0, stream, q, hq, hkv, nq, pool,
@@ -2183,7 +2189,7 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
                           : (v_bits == 4 ? decode_tiles_kernel<true, 4, kDim, true>
                                          : decode_tiles_kernel<true, 2, kDim, true>);
       workers = resident_workgroups(reinterpret_cast<const void*>(kern), kTThreads,
-                                    kDim == 256 ? 1 : 2);
+                                    kDim == 256 ? 1 : 2, kTileListMaxPerCU);
       unit = 1;
       min_share = tiles_min_share(max_blocks);
       hipLaunchKernelGGL(kern, dim3(workers), dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool,
