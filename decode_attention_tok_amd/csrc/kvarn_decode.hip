@@ -519,18 +519,6 @@ __device__ __forceinline__ void locate_position(const ListScan& ls,
   before = __builtin_amdgcn_readlane(bef, owner);
 }
 
-// List positions before sequence b (0 <= b < batch).
-template <int kUnit>
-__device__ __forceinline__ int positions_before(const ListScan& ls,
-                                                const int32_t* __restrict__ seq_lens, int batch,
-                                                int max_blocks, int hkv, int b, int lane) {
-  const int k = (batch + 63) >> 6;
-  const int owner = b / k;
-  int bef = ls.excl;
-  if (lane == owner)
-    for (int i = ls.lo; i < b; ++i) bef += unit_positions<kUnit>(seq_lens[i], max_blocks) * hkv;
-  return __builtin_amdgcn_readlane(bef, owner);
-}
 
 // Shares of a list schedule over W workers (waves or workgroups): worker w takes list
 // positions [w share, (w + 1) share), share = max(min_share, ceil(total / W)).
@@ -547,19 +535,6 @@ __device__ __forceinline__ PairSplit pair_split(int total, int waves, int min_sh
   return r;
 }
 
-// Partial slots unit (b, g) fills in a list schedule of `workers` workers (0 when the sequence
-// has no list positions).
-template <int kUnit>
-__device__ __forceinline__ int list_slots(const int32_t* __restrict__ seq_lens, int batch,
-                                          int max_blocks, int hkv, int b, int g, int len,
-                                          int workers, int min_share, int lane) {
-  const ListScan ls = scan_list<kUnit>(seq_lens, batch, max_blocks, hkv, lane);
-  const int np = unit_positions<kUnit>(len, max_blocks);
-  if (np == 0) return 0;
-  const PairSplit split = pair_split(ls.total, workers, min_share);
-  const int t0 = positions_before<kUnit>(ls, seq_lens, batch, max_blocks, hkv, b, lane) + g * np;
-  return split.wave_of(t0 + np - 1) - split.wave_of(t0) + 1;
-}
 
 // Issue priority from the wave's progress: 3 in the first quarter of its tiles down to 0 in
 // the last. The two waves a SIMD holds start together with equal work; a SIMD favours its older
@@ -587,14 +562,14 @@ constexpr bool kTilePrio = KVARN_TILE_PRIO != 0;
 // sequence is invalid) for the virtual heads of head group hg, by the workgroup's four waves
 // (wave w takes tiles i0 + w + 4 j); one partial per virtual head into slot `slot` of rows of
 // nslot slots. done0 / total: the workgroup's progress before this segment, in tiles, for the
-// issue priority.
+// issue priority. end_mark: also mark the next slot as the rows' end (m = +inf).
 template <bool kCausal, int kVBits, int kDim>
 __device__ __forceinline__ void tile_segment(
     TileSmem<kDim>& sm, const __half* __restrict__ q, int hq, int hkv, int nq,
     const uint8_t* __restrict__ pool, long long num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, int len, float sm_scale,
     float* __restrict__ partials, const SignWords& signs, int b, int g, int hg, int i0,
-    int ntile, bool bad, int slot, int nslot, int done0, int total) {
+    int ntile, bool bad, int slot, int nslot, int done0, int total, bool end_mark) {
   constexpr int kKW = kDim / 32;        // key words per lane and token block = channel blocks
   constexpr int kNB = kDim / 16;        // output channel blocks
   constexpr int kPer = kDim / 64;       // channels per lane in the query rotation
@@ -910,6 +885,7 @@ __device__ __forceinline__ void tile_segment(
     if (jj == 0) {
       p[0] = wbad ? NAN : mm;
       p[1] = wbad ? NAN : ll;
+      if (end_mark) p[kPF] = INFINITY;             // m of the next slot: the row ends here
     }
     p[2 + jj] = oo;
   }
@@ -950,7 +926,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
       tile_segment<kCausal, kVBits, kDim>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
                                           max_blocks, len, sm_scale, partials, signs, b, g, 0,
                                           t0, seg, false, slot, nslot, cur - start,
-                                          end - start);
+                                          end - start, t0 + seg == nt && slot + 1 < nslot);
       cur += seg;
     }
     return;
@@ -988,7 +964,7 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
   const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
   tile_segment<kCausal, kVBits, kDim>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
                                       max_blocks, len, sm_scale, partials, signs, b, g, hg, i0,
-                                      i1 - i0, bad, split, nsplit, 0, i1 - i0);
+                                      i1 - i0, bad, split, nsplit, 0, i1 - i0, false);
 }
 
 // ------------------------------------------------------------------ paired tiles (<= 4 heads)
@@ -1010,9 +986,10 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
 // (sequence, KV head) to the next it finishes the first, writes its partial (m, l, o~) per
 // virtual head, and starts the next; the partial goes to slot w - wave_of(T(u)) of the unit u
 // it belongs to (T(u) = the unit's first list position), so a unit fills slots 0 ..
-// wave_of(T(u) + m - 1) - wave_of(T(u)) for its m pairs, and the merge kernel recomputes that
-// count from the sequence lengths. Only a unit's last pair can be single: its second tile's
-// products are then skipped and its columns carry no probability.
+// wave_of(T(u) + m - 1) - wave_of(T(u)) for its m pairs. The wave that finishes a unit marks
+// the slot after its own with m = +inf (where the row has one), which is how the merge kernel
+// finds the row's end without redoing the schedule. Only a unit's last pair can be single: its
+// second tile's products are then skipped and its columns carry no probability.
 
 struct PairSmem {
   float qrot[4][kD + 4];           // rotated queries of the virtual heads (fp32)
@@ -1031,14 +1008,15 @@ __device__ __forceinline__ uint32_t dpp_half_mirror_u(uint32_t v) {
 
 
 // Tiles i0 .. i0 + ntile - 1 (ntile >= 1) of KV head g of sequence b (length len, valid) into
-// partial slot `slot` of each virtual head's row (rows of nslot slots).
+// partial slot `slot` of each virtual head's row (rows of nslot slots); end_mark: also mark
+// the next slot as the rows' end (m = +inf).
 template <bool kCausal, int kVBits>
 __device__ __forceinline__ void pair_segment(
     PairSmem& sm, const __half* __restrict__ q, int hq, int hkv, int nq,
     const uint8_t* __restrict__ pool, long long num_blocks,
     const int32_t* __restrict__ block_table, int max_blocks, int len, float sm_scale,
     float* __restrict__ partials, const SignWords& signs, int b, int g, int i0, int ntile,
-    int slot, int nslot, int done0, int wave_tiles) {
+    int slot, int nslot, int done0, int wave_tiles, bool end_mark) {
   const int group = hq / hkv, nh = group * nq;                // virtual heads served (1..4)
   const int lane = threadIdx.x;
   auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
@@ -1338,6 +1316,7 @@ __device__ __forceinline__ void pair_segment(
     float* pp = partials + (row_of(hh) * nslot + slot) * kPartialFloats;
     pp[0] = bad ? NAN : m_run;
     pp[1] = bad ? NAN : l_run;
+    if (end_mark) pp[kPartialFloats] = INFINITY;   // m of the next slot: the row ends here
   }
 }
 
@@ -1373,7 +1352,7 @@ decode_pairs_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     pair_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
                                   len, sm_scale, partials, signs, b, g, 2 * p0,
                                   min(2 * seg, nt - 2 * p0), slot, nslot, 2 * (cur - start),
-                                  2 * (end - start));
+                                  2 * (end - start), p0 + seg == np && slot + 1 < nslot);
     return cur + seg;
   };
   int cur = segment(start);
@@ -1471,7 +1450,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
                     const int32_t* __restrict__ seq_lens, const __half* __restrict__ staging_k,
                     const __half* __restrict__ staging_v, float sm_scale,
                     const float* __restrict__ partials, int nsplit, float* __restrict__ out,
-                    SignWords signs, int sk_workers, int sk_unit, int min_share) {
+                    SignWords signs, int list) {
   constexpr int kPer = kDim / 64;      // output channels per lane: kPer lane .. + kPer - 1
   constexpr int kPF = 2 + kDim;        // floats per partial
   __shared__ float qs[kDim];
@@ -1520,15 +1499,13 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
   qw.load(q + row * kDim + kPer * lane);
   const int len = seq_lens[b];
   const bool bad = len < 0 || (len >> 7) > max_blocks;
-  // slots holding a partial: all nsplit after a split grid; after a list schedule of
-  // sk_workers workers over units of sk_unit tiles (1 or 2) the slots this (sequence, KV head)
-  // meets in that schedule
+  // slots holding a partial: all nsplit after a split grid; after a list schedule, none for a
+  // sequence without full tiles, else those before the first slot whose m is +inf (written by
+  // the worker that finished the row's last tile; none when the row fills every slot)
   int nuse = nsplit;
-  if (sk_workers > 0) {
-    nuse = sk_unit == 1 ? list_slots<1>(seq_lens, gridDim.y, max_blocks, hkv, b, g, len,
-                                        sk_workers, min_share, lane)
-                        : list_slots<2>(seq_lens, gridDim.y, max_blocks, hkv, b, g, len,
-                                        sk_workers, min_share, lane);
+  if (list) {
+    const unsigned long long ends = __ballot(lane < nsplit && msp == INFINITY);
+    nuse = (bad || (len >> 7) == 0) ? 0 : (ends ? (int)__builtin_ctzll(ends) : nsplit);
   }
   // staging tokens this query token sees: positions up to len - nq + qi
   const int n_stage = bad ? 0 : max(0, (len & (kT - 1)) - (kCausal ? nq - 1 - qi : 0));
@@ -2173,11 +2150,10 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
                            int slots, int batch, SignWords sg, int v_bits, hipStream_t stream) {
   const int vh = hq / hkv * nq;
   const DecodeKind kind = decode_kind(batch, hkv, max_blocks, vh, v_bits, kDim);
-  int workers = 0, unit = 0, min_share = 0;
+  int workers = 0, min_share = 0;
   if (kDim == 128 && kind == DecodeKind::kPairList) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
     workers = kPairRounds * resident_workgroups(reinterpret_cast<const void*>(kern), 64, 8, 64);
-    unit = 2;
     min_share = pairs_min_share(max_blocks);
     hipLaunchKernelGGL(kern, dim3(workers), dim3(64), 0, stream, q, hq, hkv, nq, pool,
                        num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale, partials,
@@ -2190,7 +2166,6 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
                                          : decode_tiles_kernel<true, 2, kDim, true>);
       workers = resident_workgroups(reinterpret_cast<const void*>(kern), kTThreads,
                                     kDim == 256 ? 1 : 2, kTileListMaxPerCU);
-      unit = 1;
       min_share = tiles_min_share(max_blocks);
       hipLaunchKernelGGL(kern, dim3(workers), dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool,
                          num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale,
@@ -2211,7 +2186,7 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
   auto merge = nq == 1 ? decode_merge_kernel<true, false, kDim> : decode_merge_kernel<true, true, kDim>;
   hipLaunchKernelGGL(merge, dim3(hq * nq, batch), dim3(kMThreads), 0, stream, q, hq, hkv, nq,
                      max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, slots, out,
-                     sg, workers, unit, min_share);
+                     sg, kind != DecodeKind::kTileGrid ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -2259,7 +2234,7 @@ hipError_t launch_decode_fp16(const __half* q, int hq, int hkv, const uint8_t* p
   none.hi = none.lo;
   hipLaunchKernelGGL((decode_merge_kernel<false, false, kD>), dim3(hq, batch), dim3(kMThreads), 0,
                      stream, q, hq, hkv, 1, max_blocks, seq_lens, staging_k, staging_v, sm_scale,
-                     partials, splits, out, none, 0, 0, 0);
+                     partials, splits, out, none, 0);
   return hipGetLastError();
 }
 
