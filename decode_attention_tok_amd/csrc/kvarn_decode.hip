@@ -967,6 +967,373 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                                       i1 - i0, bad, split, nsplit, 0, i1 - i0, false);
 }
 
+// ------------------------------------------------------------------ 16 virtual heads per tile
+//
+// With more than 8 virtual heads per KV head (D = 128), a workgroup serves 16 of them, one per
+// MFMA column, and a query's fp32-accurate operand enters as its fp16 hi and lo parts along the
+// K dimension instead of in two columns: two products with the same unpacked key operand
+// accumulate into one column, so the codes are unpacked once per 16 virtual heads instead of
+// once per 8. The output product works the same way: a lane's probabilities (column n = head
+// n, tokens 16 mb + 4 s + i) are exactly the elements of its operand row n, so its hi and lo
+// parts feed two products with one unpacked value operand, and no lane exchanges any value.
+// Output rows are heads 4 s + i. Registers per lane stay those of the 8-head kernel.
+
+constexpr int kWideGroup = 16;
+
+struct WideSmem {
+  float qrot[kWideGroup][kD + 4];    // rotated queries (fp32)
+  WaveMeta<kD> wm[kWaves];
+  float comb_m[kWaves][kWideGroup], comb_l[kWaves][kWideGroup];
+  float comb_o[kWaves][kWideGroup][kD];
+  float red[kWaves];
+};
+
+// As tile_segment, for the 16 virtual heads vbase = 16 hg .. of KV head g.
+template <bool kCausal, int kVBits>
+__device__ __forceinline__ void wide_segment(
+    WideSmem& sm, const __half* __restrict__ q, int hq, int hkv, int nq,
+    const uint8_t* __restrict__ pool, long long num_blocks,
+    const int32_t* __restrict__ block_table, int max_blocks, int len, float sm_scale,
+    float* __restrict__ partials, const SignWords& signs, int b, int g, int hg, int i0,
+    int ntile, bool bad, int slot, int nslot, int done0, int total, bool end_mark) {
+  constexpr int kKW = kD / 32, kNB = kD / 16, kPer = kD / 64, kPF = 2 + kD;
+  const int group = hq / hkv, vgroup = group * nq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vbase = hg * kWideGroup;
+  const int nh = min(kWideGroup, vgroup - vbase);             // rows served (1..16)
+  auto row_of = [&](int v) -> long long {                     // row in [B][nq][hq]
+    return ((long long)b * nq + v / group) * hq + g * group + v % group;
+  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int nw = ntile > wave_u ? (ntile - wave_u + kWaves - 1) / kWaves : 0;
+  const int32_t* bt_row = block_table + (long long)b * max_blocks + i0 + wave_u;
+  constexpr long long kTileBytes = RecordLayout<kVBits, kD>::kTileBytes;
+  const LaneOffsets<kD> lo = lane_offsets<kVBits, kD>(lane);
+  TileRegs<kVBits, kD> cur;
+  int id_next = nw > 1 ? bt_row[kWaves] : 0;        // tile 1
+  if (nw > 0) {
+    const long long blk = bt_row[0];
+    if (blk < 0 || blk >= num_blocks) {
+      bad = true;
+    } else {
+      const uint8_t* rec = pool + (blk * hkv + g) * (long long)kTileBytes;
+      load_keys(rec, lo, cur);
+      load_values(rec, lo, cur);
+    }
+  }
+
+  // ---- rotated queries in LDS: wave w rotates heads 4 w .. 4 w + 3 (channels 2 lane, + 1)
+  float qmax = 0.0f;
+  const uint32_t sb = lane_sign_bits_d<kPer>(signs, lane);       // optional sign flips
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int gg = 4 * wave + k;
+    float o[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) o[i] = 0.0f;
+    if (gg < nh) {
+      load_h<kPer>(q + row_of(vbase + gg) * kD + kPer * lane, o);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) o[i] = (sb >> i) & 1u ? -o[i] : o[i];
+    }
+    fwht_lanes<kPer>(o, lane);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      o[i] *= 0.08838834764831845f;
+      sm.qrot[gg][kPer * lane + i] = o[i];
+      qmax = fmaxf(qmax, fabsf(o[i]));
+    }
+  }
+  qmax = wave_max_nonneg(qmax);
+  if (lane == 0) sm.red[wave] = qmax;
+  __syncthreads();
+  qmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+  int qe = 0;
+  frexpf(fmaxf(qmax, 1e-30f) * 448.0f, &qe);
+  const float pq = ldexpf(1.0f, 14 - qe);          // |q~ * pq| <= 2^14: hi parts stay finite
+  const float scale2 = sm_scale * kLog2e;
+  const float kfac = scale2 * 64.0f / pq;
+  const float kzfac = scale2 / pq;
+  float fm[TileRegs<kVBits, kD>::kM8];
+#pragma unroll
+  for (int k = 0; k < TileRegs<kVBits, kD>::kM8; ++k)
+    fm[k] = meta_chunk_factor<kD>(lane + 64 * k, pq, kfac);
+  const float fz = lane < 32 ? kzfac : 1.0f;
+
+  // lane roles: column n = virtual head n (scores, operand rows of the output product); s
+  // for token rows 4 s + i of the score blocks and the K groups; output rows 4 s + i = heads
+  const int n = lane & 15, s = lane >> 4;
+  const uint32_t vmask_col = n < nh ? 0xFFFFFFFFu : 0u;
+  const int qlim = len - nq + (vbase + n) / group;
+  WaveMeta<kD>& wm = sm.wm[wave];
+  const float* kc = wm.f8;
+  const float* ks = wm.f8 + kD;
+  const float* vc = wm.f8 + kD + kT;
+  const float* vs = wm.f8 + 2 * kD + kT;
+  const float* kz = wm.h16;
+  const float* vz = wm.h16 + kT;
+  uint32_t kmask = 0x03C003C0u, vmask = 0x03000300u;
+  asm volatile("" : "+v"(kmask), "+v"(vmask));
+  const uint32_t one16 = __builtin_amdgcn_readfirstlane(0x3C003C00u);
+  const KeyConsts kcon = key_consts();
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4v oacc[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) oacc[nb] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < nw && !bad; ++j) {
+    if constexpr (kTilePrio) set_progress_priority(done0 + kWaves * j, total);
+    const uint8_t* nrec = nullptr;
+    if (j + 1 < nw) {
+      const long long blk = id_next;
+      if (j + 2 < nw) id_next = bt_row[kWaves * (j + 2)];
+      if (blk >= 0 && blk < num_blocks) nrec = pool + (blk * hkv + g) * (long long)kTileBytes;
+      else bad = true;                             // finishes this tile, then stops
+    }
+#pragma unroll
+    for (int k = 0; k < TileRegs<kVBits, kD>::kM8; ++k)
+      decode_meta8(cur.m8[k], wm.f8 + 8 * (lane + 64 * k), fm[k]);
+    decode_meta16(cur.m16, wm.h16 + 4 * lane, fz);
+
+    // ---- query operands of channel block c, hi and lo parts of q' = pq * q_rot * c-hat^K;
+    // element e is channel 32 s + 8 c + {0,4,1,5,2,6,3,7}[e]
+    float asum = 0.0f;
+    const float4* qr4 = reinterpret_cast<const float4*>(sm.qrot[n] + 32 * s);
+    const float4* kc4 = reinterpret_cast<const float4*>(kc + 32 * s);
+    half8 qh[kKW], ql[kKW];
+#pragma unroll
+    for (int c = 0; c < kKW; ++c) {
+      const float4 qa = qr4[2 * c], qc = qr4[2 * c + 1];
+      const float4 ka = kc4[2 * c], kk = kc4[2 * c + 1];
+      const float x0 = qa.x * ka.x, x1 = qa.y * ka.y, x2 = qa.z * ka.z, x3 = qa.w * ka.w;
+      const float x4 = qc.x * kk.x, x5 = qc.y * kk.y, x6 = qc.z * kk.z, x7 = qc.w * kk.w;
+      asum += ((x0 + x1) + (x2 + x3)) + ((x4 + x5) + (x6 + x7));
+      const uint32_t h0 = pack_h2(x0, x4), h1 = pack_h2(x1, x5);
+      const uint32_t h2 = pack_h2(x2, x6), h3 = pack_h2(x3, x7);
+      qh[c] = as_h8(h0 & vmask_col, h1 & vmask_col, h2 & vmask_col, h3 & vmask_col);
+      ql[c] = as_h8(lo_of(h0, x0, x4) & vmask_col, lo_of(h1, x1, x5) & vmask_col,
+                    lo_of(h2, x2, x6) & vmask_col, lo_of(h3, x3, x7) & vmask_col);
+    }
+    asum = add_xor32(add_xor16(asum));            // over all 128 channels of column n
+    const float asum_c = 0.125f * asum;           // the centring term, 8 / 64 * asum
+
+    // ---- scores: 8 token blocks x 4 channel blocks, hi and lo products per block
+    float4v sc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kKW; ++c) {
+        const half8 kop = key_operand(cur.kw[mb][c], kcon);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, ql[c], acc, 0, 0, 0);
+      }
+      sc[mb] = acc;
+    }
+    if (nrec != nullptr) load_keys(nrec, lo, cur);
+    // log2-domain scores of this lane's tokens 16 mb + 4 s + i
+    float tmax = -INFINITY;
+    const int tpos = kT * (i0 + wave_u + kWaves * j);
+    const bool masked = kCausal && tpos + kT - 1 > len - nq;   // wave-uniform
+    const int tlim = qlim - tpos;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int t0 = 16 * mb + 4 * s;
+      const float4 ks4 = *reinterpret_cast<const float4*>(ks + t0);
+      const float4 kz4 = *reinterpret_cast<const float4*>(kz + t0);
+      const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w}, kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = fmaf(ksv[i], sc[mb][i] + asum_c, kzv[i] * asum);
+        if (masked) v = t0 + i > tlim ? -INFINITY : v;
+        sc[mb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = max_xor32(max_xor16(tmax));
+    const bool upd = tmax > m_run + kLazy;        // also true on the first tile
+    const float mnew = upd ? tmax : m_run;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+    const bool rescale = __any(upd) && j > 0;     // wave-uniform
+    float psum = 0.0f, beta = 0.0f, wsum = 0.0f;
+    // probabilities -> this lane's operand row n: element e of token block kb is token
+    // 32 kb + 16 (e / 4) + 4 s + e % 4, i.e. score block 2 kb + e / 4, element e % 4
+    half8 wh[4], wl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t hh[4], ll[4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mb = 2 * kb + h2, t0 = 16 * mb + 4 * s;
+        const float4 vs4 = *reinterpret_cast<const float4*>(vs + t0);
+        const float4 vz4 = *reinterpret_cast<const float4*>(vz + t0);
+        const float p0 = __builtin_amdgcn_exp2f(sc[mb][0] - mnew);
+        const float p1 = __builtin_amdgcn_exp2f(sc[mb][1] - mnew);
+        const float p2 = __builtin_amdgcn_exp2f(sc[mb][2] - mnew);
+        const float p3 = __builtin_amdgcn_exp2f(sc[mb][3] - mnew);
+        psum += (p0 + p1) + (p2 + p3);
+        beta = fmaf(p0, vz4.x, fmaf(p1, vz4.y, fmaf(p2, vz4.z, fmaf(p3, vz4.w, beta))));
+        const float w0 = p0 * vs4.x, w1 = p1 * vs4.y, w2 = p2 * vs4.z, w3 = p3 * vs4.w;
+        wsum += (w0 + w1) + (w2 + w3);
+        hh[2 * h2] = pack_h2(w0, w1);
+        hh[2 * h2 + 1] = pack_h2(w2, w3);
+        ll[2 * h2] = lo_of(hh[2 * h2], w0, w1);
+        ll[2 * h2 + 1] = lo_of(hh[2 * h2 + 1], w2, w3);
+      }
+      wh[kb] = as_h8(hh[0] & vmask_col, hh[1] & vmask_col, hh[2] & vmask_col, hh[3] & vmask_col);
+      wl[kb] = as_h8(ll[0] & vmask_col, ll[1] & vmask_col, ll[2] & vmask_col, ll[3] & vmask_col);
+    }
+    psum = add_xor32(add_xor16(psum));
+    beta = add_xor32(add_xor16(beta));
+    wsum = add_xor32(add_xor16(wsum));
+    constexpr float kVOut = kVBits == 4 ? 0.5f : 0.125f;
+    beta = fmaf(-kVOut, wsum, beta);
+    l_run = fmaf(alpha, l_run, psum);
+    m_run = mnew;
+    if (s == 0) {
+      wm.alpha[n] = alpha;
+      wm.beta[n] = beta;
+    }
+
+    // ---- output: 8 channel blocks x 4 token blocks x hi, lo; rows 4 s + i are heads
+    {
+      const float4 b4 = *reinterpret_cast<const float4*>(wm.beta + 4 * s);
+      const float br[4] = {b4.x, b4.y, b4.z, b4.w};
+      if (rescale) {
+        const float4 a4 = *reinterpret_cast<const float4*>(wm.alpha + 4 * s);
+        const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[nb][i] *= ar[i];
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        float4v po = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const half8 vop = value_operand<kVBits, kD>(cur.vw, nb, kb, vmask, kmask, one16);
+          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[kb], vop, po, 0, 0, 0);
+          po = __builtin_amdgcn_mfma_f32_16x16x32_f16(wl[kb], vop, po, 0, 0, 0);
+        }
+        const float cv = vc[16 * nb + n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nb][i] = fmaf(cv, fmaf(po[i], kVOut, br[i]), oacc[nb][i]);
+      }
+    }
+    if (nrec != nullptr) load_values(nrec, lo, cur);
+  }
+
+  // ---- combine the waves' states in LDS and write one partial per (slot, head)
+  __syncthreads();
+  if (s == 0) {
+    sm.comb_m[wave][n] = m_run;
+    sm.comb_l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.comb_o[wave][4 * s + i][16 * nb + n] = oacc[nb][i];
+  }
+  __syncthreads();
+  const int wbad = __syncthreads_or(bad ? 1 : 0);
+  for (int idx = tid; idx < nh * kD; idx += kTThreads) {
+    const int gg = idx / kD, jj = idx % kD;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm.comb_m[w][gg]);
+    float ll = 0.0f, oo = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(sm.comb_m[w][gg] - mm);
+        ll = fmaf(f, sm.comb_l[w][gg], ll);
+        oo = fmaf(f, sm.comb_o[w][gg][jj], oo);
+      }
+    }
+    float* p = partials + (row_of(vbase + gg) * nslot + slot) * kPF;
+    if (jj == 0) {
+      p[0] = wbad ? NAN : mm;
+      p[1] = wbad ? NAN : ll;
+      if (end_mark) p[kPF] = INFINITY;             // m of the next slot: the row ends here
+    }
+    p[2 + jj] = oo;
+  }
+}
+
+// kList: the list schedule (at most 16 virtual heads; grid = the resident workgroups);
+// otherwise the split grid (splits x KV heads x head groups of 16, sequences).
+template <bool kCausal, int kVBits, bool kList>
+__global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_wide_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
+                   const uint8_t* __restrict__ pool, long long num_blocks,
+                   const int32_t* __restrict__ block_table, int max_blocks,
+                   const int32_t* __restrict__ seq_lens, int batch, float sm_scale,
+                   float* __restrict__ partials, int nslot, SignWords signs, int min_share) {
+  __shared__ WideSmem sm;
+  if constexpr (kList) {
+    const int lane = threadIdx.x & 63;
+    const int wgs = gridDim.x, w = blockIdx.x;
+    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hkv, lane);
+    const PairSplit split = pair_split(ls.total, wgs, min_share);
+    const long long start64 = split.start(w);
+    if (start64 >= ls.total) return;
+    const int start = (int)start64;
+    const int end = (int)min(split.start(w + 1), (long long)ls.total);
+    for (int cur = start; cur < end;) {
+      int b, before;
+      locate_position<1>(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+      const int len = seq_lens[b];
+      const int nt = full_tiles(len, max_blocks);  // > 0: the sequence holds position cur
+      const int g = (cur - before) / nt;
+      const int t0 = (cur - before) - g * nt;
+      const int seg = min(nt - t0, end - cur);
+      const int slot = w - split.wave_of(cur - t0);
+      if (cur != start) __syncthreads();           // LDS of the last unit read before this one's
+      wide_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
+                                    max_blocks, len, sm_scale, partials, signs, b, g, 0, t0, seg,
+                                    false, slot, nslot, cur - start, end - start,
+                                    t0 + seg == nt && slot + 1 < nslot);
+      cur += seg;
+    }
+    return;
+  }
+  const int nsplit = gridDim.x;
+  const int vgroup = hq / hkv * nq;
+  const int ngroups = (vgroup + kWideGroup - 1) / kWideGroup;
+  int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
+  if (ngroups > 1) {
+    // workgroups that read the same tiles (same split, KV head, sequence; different head
+    // groups) take dispatch ids 8 apart, so they run on the same XCD and share its L2
+    const int L = blockIdx.x + nsplit * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int P = nsplit * hkv * gridDim.z;
+    const int full = P & ~7;
+    int p;
+    if (L < full * ngroups) {
+      const int r = L % (8 * ngroups);
+      hg = r >> 3;
+      p = (L / (8 * ngroups)) * 8 + (r & 7);
+    } else {
+      const int rem = P - full, r = L - full * ngroups;
+      hg = r / rem;
+      p = full + r % rem;
+    }
+    split = p % nsplit;
+    g = (p / nsplit) % hkv;
+    b = p / (nsplit * hkv);
+  }
+  const int len = seq_lens[b];
+  const bool bad = len < 0 || (len >> 7) > max_blocks;
+  const int n_full = bad ? 0 : (len >> 7);
+  const int chunk = (n_full + nsplit - 1) / nsplit;
+  const int i0 = min(split * chunk, n_full), i1 = min(i0 + chunk, n_full);
+  wide_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table, max_blocks,
+                                len, sm_scale, partials, signs, b, g, hg, i0, i1 - i0, bad, split,
+                                nsplit, 0, i1 - i0, false);
+}
+
 // ------------------------------------------------------------------ paired tiles (<= 4 heads)
 //
 // With at most four virtual heads per KV head (G * nq <= 4) one tile fills only half of the 16
@@ -1388,6 +1755,10 @@ constexpr int kPairRounds = KVARN_PAIR_ROUNDS;   // paired-tile waves per reside
 // four-wave workgroups per compute unit on the tile list at most (D = 64 fits 3, and the
 // shorter workers lose more to their start-up than the extra occupancy gains)
 constexpr int kTileListMaxPerCU = KVARN_TILE_LIST_MAX_PER_CU;
+#ifndef KVARN_WIDE_HEADS
+#define KVARN_WIDE_HEADS 1
+#endif
+constexpr bool kWideHeads = KVARN_WIDE_HEADS != 0;   // 16-head kernel for > 8 virtual heads
 #ifndef KVARN_MERGE_PRELOAD
 #define KVARN_MERGE_PRELOAD 8
 #endif
@@ -2091,18 +2462,21 @@ int tiles_min_share(int max_blocks) {
 }
 
 // Which kernel and schedule a packed decode of these sizes runs: the paired-tile kernel (list
-// schedule over tile pairs), the tile kernel with one head group on a large table (list
-// schedule over tiles), or the tile kernel over a grid of splits (several head groups per KV
-// head, or a table of fewer than kPairMinTilesPerCU entries per compute unit, where the list
-// schedule's longer start-up is not repaid).
+// schedule over tile pairs); at head dimension 128 with more than 8 virtual heads per KV head
+// the 16-head kernel (list schedule over tiles for at most 16 on a large table, else a grid of
+// splits x head groups of 16); else the tile kernel with one head group on a large table (list
+// schedule over tiles) or over a grid of splits (several head groups of 8, or a table of fewer
+// than kPairMinTilesPerCU entries per compute unit, where the list schedule's longer start-up
+// is not repaid).
 DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
                        int head_dim) {
   if (pairs_mode(virtual_heads, v_bits, head_dim, batch, hkv, max_blocks))
     return DecodeKind::kPairList;
   const long long tiles = (long long)batch * hkv * max_blocks;
-  if (virtual_heads <= kHeadGroup && tiles >= kPairMinTilesPerCU * device_compute_units() &&
-      tiles < (1LL << 31))
-    return DecodeKind::kTileList;
+  const bool large = tiles >= kPairMinTilesPerCU * device_compute_units() && tiles < (1LL << 31);
+  if (head_dim == 128 && virtual_heads > kHeadGroup && kWideHeads)
+    return virtual_heads <= kWideGroup && large ? DecodeKind::kWideList : DecodeKind::kWideGrid;
+  if (virtual_heads <= kHeadGroup && large) return DecodeKind::kTileList;
   return DecodeKind::kTileGrid;
 }
 
@@ -2112,6 +2486,7 @@ int decode_slots(int batch, int hkv, int max_blocks, int virtual_heads, int v_bi
     case DecodeKind::kPairList:
       return ((max_blocks + 1) / 2 - 1) / pairs_min_share(max_blocks) + 2;
     case DecodeKind::kTileList:
+    case DecodeKind::kWideList:
       return (max_blocks - 1) / tiles_min_share(max_blocks) + 2;
     default:
       return decode_splits(batch, hkv, max_blocks);
@@ -2151,7 +2526,29 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
   const int vh = hq / hkv * nq;
   const DecodeKind kind = decode_kind(batch, hkv, max_blocks, vh, v_bits, kDim);
   int workers = 0, min_share = 0;
-  if (kDim == 128 && kind == DecodeKind::kPairList) {
+  if (kDim == 128 && (kind == DecodeKind::kWideList || kind == DecodeKind::kWideGrid)) {
+    if (kind == DecodeKind::kWideList) {
+      auto kern = nq == 1 ? (v_bits == 4 ? decode_wide_kernel<false, 4, true>
+                                         : decode_wide_kernel<false, 2, true>)
+                          : (v_bits == 4 ? decode_wide_kernel<true, 4, true>
+                                         : decode_wide_kernel<true, 2, true>);
+      workers = resident_workgroups(reinterpret_cast<const void*>(kern), kTThreads, 2,
+                                    kTileListMaxPerCU);
+      min_share = tiles_min_share(max_blocks);
+      hipLaunchKernelGGL(kern, dim3(workers), dim3(kTThreads), 0, stream, q, hq, hkv, nq, pool,
+                         num_blocks, block_table, max_blocks, seq_lens, batch, sm_scale,
+                         partials, slots, sg, min_share);
+    } else {
+      auto kern = nq == 1 ? (v_bits == 4 ? decode_wide_kernel<false, 4, false>
+                                         : decode_wide_kernel<false, 2, false>)
+                          : (v_bits == 4 ? decode_wide_kernel<true, 4, false>
+                                         : decode_wide_kernel<true, 2, false>);
+      const int ngroups = (vh + kWideGroup - 1) / kWideGroup;
+      hipLaunchKernelGGL(kern, dim3(slots, hkv * ngroups, batch), dim3(kTThreads), 0, stream, q,
+                         hq, hkv, nq, pool, num_blocks, block_table, max_blocks, seq_lens, batch,
+                         sm_scale, partials, slots, sg, 0);
+    }
+  } else if (kDim == 128 && kind == DecodeKind::kPairList) {
     auto kern = nq == 1 ? decode_pairs_kernel<false, 2> : decode_pairs_kernel<true, 2>;
     workers = kPairRounds * resident_workgroups(reinterpret_cast<const void*>(kern), 64, 8, 64);
     min_share = pairs_min_share(max_blocks);
@@ -2186,7 +2583,8 @@ hipError_t launch_decode_t(const __half* q, int hq, int hkv, int nq, const uint8
   auto merge = nq == 1 ? decode_merge_kernel<true, false, kDim> : decode_merge_kernel<true, true, kDim>;
   hipLaunchKernelGGL(merge, dim3(hq * nq, batch), dim3(kMThreads), 0, stream, q, hq, hkv, nq,
                      max_blocks, seq_lens, staging_k, staging_v, sm_scale, partials, slots, out,
-                     sg, kind != DecodeKind::kTileGrid ? 1 : 0);
+                     sg, (kind == DecodeKind::kPairList || kind == DecodeKind::kTileList ||
+                          kind == DecodeKind::kWideList) ? 1 : 0);
   return hipGetLastError();
 }
 

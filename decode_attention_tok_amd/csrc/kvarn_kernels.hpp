@@ -69,7 +69,7 @@ int decode_splits(int batch, int hkv, int max_blocks);
 bool pairs_mode(int virtual_heads, int v_bits, int head_dim, int batch, int hkv, int max_blocks);
 // The kernel and schedule of a packed decode (virtual heads = query heads per KV head x query
 // tokens), and the partial slots per (sequence, query token, query head) row it needs.
-enum class DecodeKind { kPairList, kTileList, kTileGrid };
+enum class DecodeKind { kPairList, kWideList, kWideGrid, kTileList, kTileGrid };
 DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,
                        int head_dim);
 int decode_slots(int batch, int hkv, int max_blocks, int virtual_heads, int v_bits,

@@ -112,13 +112,15 @@ def test_workspace_follows_the_split_plan(lib):
     """The workspace holds 130 floats per (sequence, query head, partial slot). This host has
     no GPU: the plan assumes 256 compute units.
     List schedules, for tables of at least 64 entries x KV heads x sequences per compute unit:
-    the sequences' full tiles (four-wave tile kernel, at most 8 virtual heads per KV head) or
-    tile pairs (paired-tile kernel: at most four virtual heads, 2-bit values, head dimension
-    128) form one list that the resident workers share evenly, at least m positions each: tiles,
+    the sequences' full tiles (four-wave tile kernel, at most 8 virtual heads per KV head; at
+    head dimension 128 the 16-head kernel for 9 to 16) or tile pairs (paired-tile kernel: at
+    most four virtual heads, 2-bit values, head dimension 128) form one list that the resident
+    workers share evenly, at least m positions each: tiles,
     m = max(4, (entries - 1) // 62 + 1); pairs, m = (p - 1) // 62 + 1 for p = ceil(entries / 2).
     A (sequence, KV head) of up to n positions (entries or p) then meets at most
     (n - 1) // m + 2 workers, each writing its own partial slot.
-    Split grid (more than 8 virtual heads per KV head, or a smaller table; also the fp16
+    Split grid (more head groups than one — of 16 at head dimension 128, else of 8 — or a
+    smaller table; also the fp16
     comparison decode, whose need the size always covers): two workgroups per compute unit, at
     least two tiles per wave
     unless that leaves fewer than two workgroups per compute unit (then one), at most 32 full
@@ -127,8 +129,12 @@ def test_workspace_follows_the_split_plan(lib):
     # 16K context, batch 16, 8 KV heads, group 8: tile list, m = 4, 128 // 4 + 2 = 34 slots
     # (the split grid of the same sizes needs 4)
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 34 * per
-    # the same with group 16 (two head groups): split grid, 512 / 128 pairs = 4 splits
-    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 128, 129) == 16 * 128 * 4 * per
+    # the same with group 16: the 16-head kernel on the tile list, 34 slots
+    assert kv.decode_workspace_bytes(kv.default_config(8), 16, 128, 129) == 16 * 128 * 34 * per
+    # group 16 x 2 query tokens (two groups of 16): the 16-head kernel on the split grid, 4
+    # splits, for 2 x the rows
+    assert (kv.decode_multi_workspace_bytes(kv.default_config(8), 16, 128, 2, 129)
+            == 16 * 2 * 128 * 4 * per)
     # 4K context, batch 8 (33 entries; 2,112 < 16,384): split grid, 8 splits wanted; two tiles
     # per wave would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
     assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
