@@ -167,10 +167,11 @@ KVARN_API kvarn_status kvarn_append_token(const kvarn_config* cfg, const void* k
 
 /* Size of the workspace kvarn_decode_attention needs for these sizes, into *bytes (host).
  * It depends on the arguments and on the compute-unit count of the current HIP device (the
- * split plan fills the device; 256 compute units are assumed when no device is usable), so
- * query it with the device current that will run the decode. It grows with head_dim (one
- * partial of 2 + head_dim floats per query head and split). The same size also serves
- * kvarn_decode_attention_fp16 at these sizes. */
+ * work is planned for the device's compute units; 256 are assumed when no device is usable),
+ * so query it with the device current that will run the decode. It holds one partial result
+ * of 2 + head_dim floats per query head and partial slot: the slots of a sequence's tiles
+ * are at most 64, from the table width alone (the actual lengths are read on the device).
+ * The same size also serves kvarn_decode_attention_fp16 at these sizes. */
 KVARN_API kvarn_status kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch,
                                           int32_t num_q_heads, int32_t max_blocks_per_seq,
                                           size_t* bytes);
