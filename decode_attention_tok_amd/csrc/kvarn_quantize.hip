@@ -17,33 +17,37 @@
 //      down of the token minimum, scale = FP8 round up of (max - zero-point) / (2^bits - 1),
 //      code = clamp(rne((y - zero-point) / scale), 0, 2^bits - 1).
 //
-// Work layout. Layout A gives thread (t, q0, q1) = (tid / 4, tid % 2, (tid / 2) % 2) the 32
-// channels c = e + 8 q0 + 16 m + 64 q1 (e = 0..7, m = 0..3) of token t, held as x[8 m + e]:
-// channel bits 0-2 and 4-5 live in registers and bits 3 and 6 across the four lanes of a quad.
-// It does the transform (five butterfly stages in registers, two across lanes as DPP-sourced
-// fused multiply-adds), the row statistics and the codes; a thread's eight values of one m are
-// exactly one word of key nibbles, its four values of one e are one byte of 2-bit value codes
-// or one 16-bit half-word of 4-bit value codes.
+// Work layout. Layout A gives thread (t, q0, q1) the 32 channels c = e + 8 q0 + 16 m + 64 q1
+// (e = 0..7, m = 0..3) of token t, held as x[8 m + e]: channel bits 0-2 and 4-5 live in
+// registers and bits 3 and 6 across four lanes. At D = 128, t = 16 wave + lane % 16 and
+// (q0, q1) = lane bits 4, 5: the transform runs on the matrix cores (rotate_mfma below), whose
+// 16 x 16 output blocks put one token per lane column and four channel rows per lane group.
+// Layout A does the row statistics and the codes; a thread's eight values of one m are exactly
+// one word of key nibbles, its four values of one e are one byte of 2-bit value codes or one
+// 16-bit half-word of 4-bit value codes.
 // Layout B gives lane (j, th) = (16 wave + lane % 16, lane / 16) the 32 tokens th, th + 4, ...,
 // th + 124 of channel j: the column statistics, read from a copy of the rotated tile kept in LDS
 // for the whole normalisation and merged over the four lanes of a channel with permlane swaps,
-// so a round needs two barriers (after the columns, after the rows).
+// so a round needs two barriers (after the columns, after the rows). At D = 128 the 16-byte
+// chunks of each LDS row are XOR-swizzled by (row / 2) % 4 and the staged key and 2-bit value
+// codes use 17-word rows, so the 16 tokens of a wave, which write the same channels, do not
+// share banks.
 //
-// Sign folding. A cross-lane butterfly computes x + s * partner with s = -1 on the lane holding
-// the upper index, which leaves that lane's values negated; after both cross stages a thread's
-// values carry the factor (-1)^(q0 + q1), the same for all of them. Column variances do not see
-// it, and the row statistics and the rounding stage apply it once per thread. The 1/sqrt(128)
-// scale of the transform is folded into the rounding stage's per-channel factor (the
-// normalisation is scale-free up to the gauge, and the floor is relative to the tile's
+// The 1/sqrt(D) scale of the transform is folded into the rounding stage's per-channel factor
+// (the normalisation is scale-free up to the gauge, and the floor is relative to the tile's
 // largest value).
 //
 // Variances use shifted one-pass sums (shift = the thread's first value), merged between the
 // threads sharing a row or column with Chan et al.'s pairwise update.
 //
-// Other head dimensions. A token has D / 32 threads (lane bits 0 .. log2(D / 32) - 1): channel
-// c = e + 8 q0 + 16 m + 64 q1 + 128 q2 with q2 = lane bit 2 at D = 256, and no q1 at D = 64.
-// The butterfly on channel bit 7 (D = 256) crosses lanes through ds_swizzle and computes the
-// difference on the upper lane exactly (partner - own), so it adds no sign. Layout B keeps 16
+// Other head dimensions. A token has D / 32 threads (t = tid / (D / 32), lane bits
+// 0 .. log2(D / 32) - 1 = q0, q1, q2): channel c = e + 8 q0 + 16 m + 64 q1 + 128 q2 with q2 at
+// D = 256 only, no q1 at D = 64. The transform is a butterfly network: five stages in registers,
+// then the cross-lane stages as DPP-sourced fused multiply-adds x + s * partner with s = -1 on
+// the lane holding the upper index, which leaves that lane's values negated (one factor
+// (-1)^(q0 + q1) per thread, applied once by the row statistics and the rounding stage; column
+// variances do not see it); the stage on channel bit 7 (D = 256) crosses lanes through
+// ds_swizzle and computes the upper lane's difference exactly (partner - own). Layout B keeps 16
 // channels per wave (D / 16 waves). A row's statistics merge over D / 32 threads; the gauge and
 // the per-channel rounding factor use 1 / D and 1 / sqrt(D). Key codes are staged token-major
 // as at D = 128; a thread's value codes form whole bytes (2-bit) or half-words (4-bit) of the
@@ -232,7 +236,9 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
         lo = put_code<kClamp>(fmaf(x[8 * m + e], ca, cb), qmax, e >> 1, lo);
         hi = put_code<kClamp>(fmaf(x[8 * m + e + 1], ca, cb), qmax, e >> 1, hi);
       }
-      stage[t * (kDim / 8) + q0 + 2 * m + 8 * q1 + 16 * q2] = lo | (hi << 4);
+      // at kDim = 128 token rows are 17 words apart, so the 16 tokens of a wave (lanes 0..15)
+      // writing the same word fall in 16 different banks
+      stage[t * (kDim == 128 ? 17 : kDim / 8) + q0 + 2 * m + 8 * q1 + 16 * q2] = lo | (hi << 4);
     }
   } else if constexpr (kDim != 128) {
     // value codes of the other head dimensions. The four codes of channels
@@ -261,11 +267,11 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
     // section word 512 kb + 256 q1 + 4 (16 s + n) + 2 h + i / 2 holds the codes of
     // nb % 4 = m = 0..3 at bits 4 m (t = 32 kb + 16 h + 4 s + i). The section is staged in
     // 16-byte chunks (chunk = word / 4 = 128 kb + 64 q1 + 16 s + 8 q0 + e) with the chunk's low
-    // three bits XORed with s + 4 q1, so one instruction's 64 half-word writes spread over
-    // 32 banks instead of 8; the store undoes the swizzle.
+    // three bits XORed with s + 4 (q1 ^ q0), so one instruction's 64 half-word writes spread
+    // over the banks; the store undoes the swizzle.
     uint16_t* sh = reinterpret_cast<uint16_t*>(stage);
     const int kb = t >> 5, h = (t >> 4) & 1, s4 = (t >> 2) & 3, i = t & 3;
-    const int sw = s4 + 4 * q1;
+    const int sw = s4 + 4 * (q1 ^ q0);
     const int c0 = 128 * kb + 64 * q1 + 16 * s4 + 8 * q0;
     const int lo = 2 * (2 * h + (i >> 1)) + (i & 1);        // half-word within the chunk
 #pragma unroll
@@ -279,8 +285,9 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
     }
   } else {
     // value codes. Byte e of this thread holds the codes of channel n = 8 q0 + e, hf = q1,
-    // nb' = m at bits 2 m; it is staged at byte 2 (t % 2) + hf of LDS word 16 (t / 2) + n,
-    // which makes every LDS word one word of the section.
+    // nb' = m at bits 2 m; it is staged at byte 2 (t % 2) + hf of LDS word 17 (t / 2) + n, which
+    // makes every LDS word one word of the section (rows of 17 words: the 16 tokens of a wave
+    // writing the same n fall in different banks).
     uint8_t* sb = reinterpret_cast<uint8_t*>(stage);
 #pragma unroll
     for (int eh = 0; eh < 8; eh += 4) {
@@ -295,7 +302,7 @@ __device__ __forceinline__ void stage_codes(const float* x, float ca, float cb, 
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sb[((t >> 1) * 16 + 8 * q0 + eh + e) * 4 + (t & 1) * 2 + q1] = (uint8_t)(d >> (8 * e));
+        sb[((t >> 1) * 17 + 8 * q0 + eh + e) * 4 + (t & 1) * 2 + q1] = (uint8_t)(d >> (8 * e));
     }
   }
 }
@@ -313,6 +320,62 @@ __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, i
   if (tid < kDim / 4) reinterpret_cast<uint32_t*>(rec + meta + L::kC)[tid] = 0x38383838u;
   if (tid < 32) reinterpret_cast<uint32_t*>(rec + meta + L::kS)[tid] = 0u;
   if (tid < 64) reinterpret_cast<uint32_t*>(rec + meta + L::kZ)[tid] = 0u;
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float min_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float min_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The 128-point transform of a wave's 16 tokens on the matrix cores (head dimension 128).
+// Lane l = 16 (2 q1 + q0) + n holds token n's fp16 channels 16 m + 8 q0 + 64 q1 + j (j = 0..7)
+// in w[m]; on return x[8 m' + e] is rotated channel e + 8 q0 + 16 m' + 64 q1 of the same token,
+// exactly the butterfly layout but with lane bits 4, 5 in place of 0, 1 and no sign folding.
+// The Sylvester matrix factorises over channel bits: H[o][c] = prod_b (-1)^(o_b c_b). Channel
+// bits 0-3 and 6 are contracted inside v_mfma_f32_16x16x32_f16 (B operand = w[m]: k = 8 (l >> 4)
+// + j is channel bits 0-2 = j, 3 = q0, 6 = q1; output row rho = 4 (l >> 4) + r of block mb is
+// channel bits 0-1 = r, 2 = mb, 3 = bit 2 of rho, 6 = bit 3 of rho), and channel bits 4-5 (the
+// group m) by accumulating four products whose ±1 operand is negated where popcount(m & m')
+// is odd. Every product is an exact fp16 times +-1, summed in fp32.
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
+}
+
+__device__ __forceinline__ void rotate_mfma(const uint4 (&w)[4], int lane, float* x) {
+  const int rho = lane & 15, g0 = (lane >> 4) & 1, g1 = lane >> 5;
+  constexpr uint32_t kNeg = 0x80008000u;                     // both halves' sign bits
+  // A fragment (row rho, halves j of k-group (g0, g1)): sign over bits 0-1 from (rho & 3, j & 3),
+  // bit 3 from (bit 2 of rho, g0), bit 6 from (bit 3 of rho, g1); bit 2 (j >= 4) from mb
+  const uint32_t all = ((((rho >> 2) & g0) ^ ((rho >> 3) & g1)) & 1) ? kNeg : 0u;
+  const uint32_t d0 = 0x3C003C00u ^ all ^ ((rho & 1) ? 0x80000000u : 0u);   // j = 0, 1
+  const uint32_t d1 = d0 ^ ((rho & 2) ? kNeg : 0u);                          // j = 2, 3
+  const half8 ap[2] = {as_half8(d0, d1, d0, d1), as_half8(d0, d1, d0 ^ kNeg, d1 ^ kNeg)};
+  const half8 an[2] = {as_half8(d0 ^ kNeg, d1 ^ kNeg, d0 ^ kNeg, d1 ^ kNeg),
+                       as_half8(d0 ^ kNeg, d1 ^ kNeg, d0, d1)};
+  half8 b[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) b[m] = __builtin_bit_cast(half8, w[m]);
+#pragma unroll
+  for (int mp = 0; mp < 4; ++mp) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16((__builtin_popcount(m & mp) & 1) ? an[mb]
+                                                                                    : ap[mb],
+                                                     b[m], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[8 * mp + 4 * mb + r] = acc[r];
+    }
+  }
 }
 
 // ds_swizzle across lane bit 2 (bit-mask mode: and 0x1F, xor 4, within 32 lanes).
@@ -336,13 +399,18 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t = tid / kTPT, q0 = tid & 1;                       // layout A
-  const int q1 = kDim >= 128 ? (tid >> 1) & 1 : 0;
+  // layout A: at D = 128 token t = 16 wave + lane % 16 with q0, q1 = lane bits 4, 5 (the
+  // matrix-core transform's output); otherwise t = tid / kTPT with q0, q1, q2 = tid bits 0, 1, 2
+  constexpr bool kMfma = kDim == 128;
+  const int t = kMfma ? 16 * wave + (lane & 15) : tid / kTPT;
+  const int q0 = kMfma ? (lane >> 4) & 1 : tid & 1;
+  const int q1 = kDim >= 128 ? (kMfma ? lane >> 5 : (tid >> 1) & 1) : 0;
   const int q2 = kDim == 256 ? (tid >> 2) & 1 : 0;
+  const bool lead = kMfma ? lane < 16 : (tid & (kTPT - 1)) == 0;   // one thread per token
   const int jj = 16 * wave + (lane & 15), th = lane >> 4;     // layout B
   const int cbase = 8 * q0 + 64 * q1 + 128 * q2;                // channel of x[0]
   const int pbase = cpos(cbase);                                // its LDS position
-  const bool flip = (q0 ^ q1) != 0;                             // values carry a factor -1
+  const bool flip = !kMfma && (q0 ^ q1) != 0;                  // values carry a factor -1
 
   // ---- load (layout A) and rotate
   float x[32];
@@ -369,30 +437,33 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
         w[m].x ^= sg.x; w[m].y ^= sg.y; w[m].z ^= sg.z; w[m].w ^= sg.w;
       }
     }
+    if constexpr (kMfma) {
+      rotate_mfma(w, lane, x);
+    } else {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) unpack_h8(w[m], x + 8 * m);
+      for (int m = 0; m < 4; ++m) unpack_h8(w[m], x + 8 * m);
+    }
   }
+  if constexpr (!kMfma) {                      // butterflies: in registers, then across lanes
 #pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
+    for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if ((i & h) == 0) {
-        const float a = x[i], b = x[i + h];
-        x[i] = a + b;
-        x[i + h] = a - b;
+      for (int i = 0; i < 32; ++i) {
+        if ((i & h) == 0) {
+          const float a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
       }
     }
-  }
-  {
-    const float s1 = q0 ? -1.0f : 1.0f, s2 = q1 ? -1.0f : 1.0f;
+    const float s1 = q0 ? -1.0f : 1.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) fmac_xor1(x + 8 * g, s1);      // channel bit 3
-    if constexpr (kDim >= 128) {
+    if constexpr (kDim == 256) {
+      const float s2 = q1 ? -1.0f : 1.0f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) fmac_xor2(x + 8 * g, s2);    // channel bit 6
-    }
-    if constexpr (kDim == 256) {                                // channel bit 7, exact
-      const float s4 = q2 ? -1.0f : 1.0f;
+      const float s4 = q2 ? -1.0f : 1.0f;                       // channel bit 7, exact
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] = fmaf(s4, x[i], swz_xor4(x[i]));
     }
@@ -405,11 +476,16 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   // ---- transpose A -> B through LDS
   {
     float4* row4 = reinterpret_cast<float4*>(&sm.xt[t][0]);   // rows are 16-byte aligned
+    // at D = 128 the 16-byte chunks of row t are XOR-swizzled by (t >> 1) & 3: the 16 tokens
+    // of a wave write the same channels, and the swizzle spreads them over the banks
+    // (the XOR touches position bits 2-3 only, so it commutes with adding 16 m)
+    const int sw = kMfma ? 4 * ((t >> 1) & 3) : 0;
+    const int p0 = (pbase ^ sw) >> 2, p1 = ((pbase + 4) ^ sw) >> 2;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int h = 0; h < 8; h += 4)
-        row4[(pbase >> 2) + 4 * m + (h >> 2)] =
+        row4[(h ? p1 : p0) + 4 * m] =
             make_float4(x[8 * m + h], x[8 * m + h + 1], x[8 * m + h + 2], x[8 * m + h + 3]);
     }
   }
@@ -422,30 +498,35 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     store_record_zero_tile<kVBits, kDim>(rec, is_v, tid);
     return;
   }
-  const float* xcol = &sm.xt[th][cpos(jj)];       // column jj, tokens th + 4 i, stride 4 kXs
+  // column jj, tokens th + 4 i (stride 4 kXs); row th + 4 i carries the swizzle th / 2 for even
+  // i and 2 + th / 2 for odd i
+  const float* xce = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (th >> 1) : 0)];
+  const float* xco = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (2 + (th >> 1)) : 0)];
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
   constexpr float kInvD = 1.0f / kDim;
   float umax = 1.0f;
   for (int it = 0; it < iters; ++it) {
-    // column step (layout B): std over tokens of xt_tj * u_t
+    // column step (layout B): std over tokens of xt_tj * u_t. The shift k0 is the first
+    // term itself, whose shifted value (zero, or the rounding residual of its product) is left
+    // out of the sums.
     {
       float s1 = 0.0f, s2 = 0.0f, k0;
       if (it == 0) {
-        k0 = xcol[0];
+        k0 = xce[0];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float y = xcol[4 * i * kXs] - k0;
+        for (int i = 1; i < 32; ++i) {
+          const float y = ((i & 1) ? xco : xce)[4 * i * kXs] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       } else {
         const float* uu = sm.u[th];
-        k0 = xcol[0] * uu[0];
+        k0 = xce[0] * uu[0];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float y = fmaf(xcol[4 * i * kXs], uu[i], -k0);
+        for (int i = 1; i < 32; ++i) {
+          const float y = fmaf(((i & 1) ? xco : xce)[4 * i * kXs], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
@@ -471,10 +552,10 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     // row step (layout A): std over channels of xt_tj * v_j
     {
       const float* vv = sm.vinv + pbase;
-      const float k0 = x[0] * vv[0];
+      const float k0 = x[0] * vv[0];             // shift: the first term (left out, as above)
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 1; i < 32; ++i) {
         const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
         s1 += y;
         s2 = fmaf(y, y, s2);
@@ -482,25 +563,28 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       float mh = fmaf(s1, 0.03125f, k0);
       if (flip) mh = -mh;
       float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
-      {                                          // Chan merges with quad partners
-        const float d = dpp_sub<kDppXor1>(mh, mh);   // partner - own (only d^2 is used)
-        const float qs = dpp_add<kDppXor1>(qh, qh);
-        mh = 0.5f * dpp_add<kDppXor1>(mh, mh);
-        qh = fmaf(16.0f * d, d, qs);
-      }
-      if constexpr (kDim >= 128) {
-        const float d = dpp_sub<kDppXor2>(mh, mh);
-        const float qs = dpp_add<kDppXor2>(qh, qh);
-        if constexpr (kDim == 256) mh = 0.5f * dpp_add<kDppXor2>(mh, mh);
-        qh = fmaf(32.0f * d, d, qs);
-      }
-      if constexpr (kDim == 256) {               // and across lane bit 2 (128 channels each)
-        const float d = swz_xor4(mh) - mh;
-        qh = fmaf(64.0f * d, d, qh + swz_xor4(qh));
+      if constexpr (kMfma) {                     // Chan merges over lane bits 4, then 5
+        merge_pair<16>(mh, qh, 16.0f);
+        merge_pair<32>(mh, qh, 32.0f);
+      } else {                                   // with quad partners (lane bits 0, 1)
+        {
+          const float d = dpp_sub<kDppXor1>(mh, mh);   // partner - own (only d^2 is used)
+          const float qs = dpp_add<kDppXor1>(qh, qh);
+          mh = 0.5f * dpp_add<kDppXor1>(mh, mh);
+          qh = fmaf(16.0f * d, d, qs);
+        }
+        if constexpr (kDim == 256) {
+          const float d = dpp_sub<kDppXor2>(mh, mh);
+          const float qs = dpp_add<kDppXor2>(qh, qh);
+          mh = 0.5f * dpp_add<kDppXor2>(mh, mh);
+          qh = fmaf(32.0f * d, d, qs);
+          const float d4 = swz_xor4(mh) - mh;      // and across lane bit 2 (128 channels each)
+          qh = fmaf(64.0f * d4, d4, qh + swz_xor4(qh));
+        }
       }
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * kInvD), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
-      if ((tid & (kTPT - 1)) == 0) sm.u[t & 3][t >> 2] = uinv;
+      if (lead) sm.u[t & 3][t >> 2] = uinv;
       const float um = max_xor48_nn(row16_max(uinv));
       if (lane == 0) sm.red[2 * kQW + wave] = um;
     }
@@ -547,9 +631,14 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     }
   }
   float mn = flip ? -pmax : pmin, mx = flip ? -pmin : pmax;
-  mn = fminf(mn, quad_swap<kDppXor1>(mn));
-  mx = fmaxf(mx, quad_swap<kDppXor1>(mx));
-  if constexpr (kDim >= 128) {
+  if constexpr (kMfma) {
+    mn = min_xor32(min_xor16(mn));
+    mx = max_xor32(max_xor16(mx));
+  } else {
+    mn = fminf(mn, quad_swap<kDppXor1>(mn));
+    mx = fmaxf(mx, quad_swap<kDppXor1>(mx));
+  }
+  if constexpr (kDim == 256) {
     mn = fminf(mn, quad_swap<kDppXor2>(mn));
     mx = fmaxf(mx, quad_swap<kDppXor2>(mx));
   }
@@ -564,7 +653,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   const float inv_s = sf > 0.0f ? 1.0f / sf : 0.0f;
   const float ca = flip ? -inv_s : inv_s;          // (y - z) / s = p * ca + cb
   const float cb = -zf * inv_s;
-  if ((tid & (kTPT - 1)) == 0) {
+  if (lead) {
     reinterpret_cast<uint8_t*>(sm.meta)[t] = (uint8_t)scode;
     reinterpret_cast<uint16_t*>(sm.meta + 32)[t] = (uint16_t)zbits;
   }
@@ -575,14 +664,21 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     stage_codes<false, kVBits, kDim>(x, ca, cb, qmax, is_v, t, q0, q1, q2, stage);
   if (!is_v) {                                         // staged as the section: 64 kDim bytes
     __syncthreads();
-    reinterpret_cast<uint4*>(rec + L::kKCodes)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
+    uint4 c;
+    if constexpr (kDim == 128) {                       // token rows of 17 words
+      const uint32_t* r = stage + 17 * (tid >> 2) + 4 * (tid & 3);
+      c = make_uint4(r[0], r[1], r[2], r[3]);
+    } else {
+      c = reinterpret_cast<const uint4*>(stage)[tid];
+    }
+    reinterpret_cast<uint4*>(rec + L::kKCodes)[tid] = c;
   } else if constexpr (kDim != 128) {
     __syncthreads();
     if (tid < L::kVCodeBytes / 16)
       reinterpret_cast<uint4*>(rec + L::kVCodes)[tid] = reinterpret_cast<const uint4*>(stage)[tid];
-  } else if constexpr (kVBits == 4) {                  // chunk tid sits at tid ^ (s + 4 q1)
+  } else if constexpr (kVBits == 4) {                  // chunk tid sits at tid ^ (s + 4 (q1 ^ q0))
     __syncthreads();
-    const int sw = ((tid >> 4) & 3) + 4 * ((tid >> 6) & 1);
+    const int sw = ((tid >> 4) & 3) + 4 * (((tid >> 6) ^ (tid >> 3)) & 1);
     reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] =
         reinterpret_cast<const uint4*>(stage)[tid ^ sw];
   } else {
@@ -593,7 +689,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       for (int d = 0; d < 4; ++d) {
         const int w = 4 * tid + d;                 // word index in the section
         const int kb = w >> 8, s = (w >> 6) & 3, n = (w >> 2) & 15, h = d >> 1, i2 = d & 1;
-        out[d] = stage[(16 * kb + 8 * h + 2 * s + i2) * 16 + n];
+        out[d] = stage[(16 * kb + 8 * h + 2 * s + i2) * 17 + n];
       }
       reinterpret_cast<uint4*>(rec + kVCodesOff)[tid] = make_uint4(out[0], out[1], out[2], out[3]);
     }
