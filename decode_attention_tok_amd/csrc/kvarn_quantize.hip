@@ -26,9 +26,11 @@
 // one word of key nibbles, its four values of one e are one byte of 2-bit value codes or one
 // 16-bit half-word of 4-bit value codes.
 // Layout B gives lane (j, th) = (16 wave + lane % 16, lane / 16) the 32 tokens th, th + 4, ...,
-// th + 124 of channel j: the column statistics, read from a copy of the rotated tile kept in LDS
-// for the whole normalisation and merged over the four lanes of a channel with permlane swaps,
-// so a round needs two barriers (after the columns, after the rows). At D = 128 the 16-byte
+// th + 124 of channel j: the column statistics. The rotated tile goes through LDS once (layout
+// A writes it, layout B reads its 32 values into registers), so both layouts stay in registers
+// for the whole normalisation; a column's sums merge over its four lanes with permlane swaps,
+// and a round needs two barriers (after the columns, after the rows: the multipliers one layout
+// computes for the other pass through LDS). At D = 128 the 16-byte
 // chunks of each LDS row are XOR-swizzled by (row / 2) % 4 and the staged key and 2-bit value
 // codes use 17-word rows, so the 16 tokens of a wave, which write the same channels, do not
 // share banks.
@@ -498,10 +500,15 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     store_record_zero_tile<kVBits, kDim>(rec, is_v, tid);
     return;
   }
-  // column jj, tokens th + 4 i (stride 4 kXs); row th + 4 i carries the swizzle th / 2 for even
-  // i and 2 + th / 2 for odd i
-  const float* xce = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (th >> 1) : 0)];
-  const float* xco = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (2 + (th >> 1)) : 0)];
+  // layout B in registers for the whole normalisation: xb[i] = column jj, token th + 4 i (row
+  // th + 4 i carries the swizzle th / 2 for even i and 2 + th / 2 for odd i)
+  float xb[32];
+  {
+    const float* xce = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (th >> 1) : 0)];
+    const float* xco = &sm.xt[th][cpos(jj) ^ (kMfma ? 4 * (2 + (th >> 1)) : 0)];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xb[i] = ((i & 1) ? xco : xce)[4 * i * kXs];
+  }
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
@@ -514,19 +521,19 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     {
       float s1 = 0.0f, s2 = 0.0f, k0;
       if (it == 0) {
-        k0 = xce[0];
+        k0 = xb[0];
 #pragma unroll
         for (int i = 1; i < 32; ++i) {
-          const float y = ((i & 1) ? xco : xce)[4 * i * kXs] - k0;
+          const float y = xb[i] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       } else {
         const float* uu = sm.u[th];
-        k0 = xce[0] * uu[0];
+        k0 = xb[0] * uu[0];
 #pragma unroll
         for (int i = 1; i < 32; ++i) {
-          const float y = fmaf(((i & 1) ? xco : xce)[4 * i * kXs], uu[i], -k0);
+          const float y = fmaf(xb[i], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
