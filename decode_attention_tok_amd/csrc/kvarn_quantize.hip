@@ -336,6 +336,10 @@ __device__ __forceinline__ float min_xor32(float x) {
   return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
+}
+
 // The 128-point transform of a wave's 16 tokens on the matrix cores (head dimension 128).
 // Lane l = 16 (2 q1 + q0) + n holds token n's fp16 channels 16 m + 8 q0 + 64 q1 + j (j = 0..7)
 // in w[m]; on return x[8 m' + e] is rotated channel e + 8 q0 + 16 m' + 64 q1 of the same token,
@@ -346,10 +350,6 @@ __device__ __forceinline__ float min_xor32(float x) {
 // channel bits 0-1 = r, 2 = mb, 3 = bit 2 of rho, 6 = bit 3 of rho), and channel bits 4-5 (the
 // group m) by accumulating four products whose ±1 operand is negated where popcount(m & m')
 // is odd. Every product is an exact fp16 times +-1, summed in fp32.
-__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
-}
-
 __device__ __forceinline__ void rotate_mfma(const uint4 (&w)[4], int lane, float* x) {
   const int rho = lane & 15, g0 = (lane >> 4) & 1, g1 = lane >> 5;
   constexpr uint32_t kNeg = 0x80008000u;                     // both halves' sign bits
