@@ -327,13 +327,34 @@ __device__ __forceinline__ void store_record_zero_tile(uint8_t* rec, int is_v, i
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// Minimum / maximum of the pair of lanes l, l ^ 16 (or l ^ 32) of a finite value, every lane
+// getting the result. One v_min_f32 / v_max_f32 on the swapped pair: fminf would first quiet
+// possible signalling NaNs coming out of the lane exchange, which finite values never are.
+__device__ __forceinline__ float fmin_raw(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float fmax_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float min_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmin_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float min_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmin_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16_raw(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32_raw(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -519,11 +540,13 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     // term itself, whose shifted value (zero, or the rounding residual of its product) is left
     // out of the sums.
     {
-      float s1 = 0.0f, s2 = 0.0f, k0;
+      float s1, s2, k0;
       if (it == 0) {
         k0 = xb[0];
+        s1 = xb[1] - k0;
+        s2 = s1 * s1;
 #pragma unroll
-        for (int i = 1; i < 32; ++i) {
+        for (int i = 2; i < 32; ++i) {
           const float y = xb[i] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
@@ -531,8 +554,10 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       } else {
         const float* uu = sm.u[th];
         k0 = xb[0] * uu[0];
+        s1 = fmaf(xb[1], uu[1], -k0);
+        s2 = s1 * s1;
 #pragma unroll
-        for (int i = 1; i < 32; ++i) {
+        for (int i = 2; i < 32; ++i) {
           const float y = fmaf(xb[i], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
@@ -560,9 +585,10 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     {
       const float* vv = sm.vinv + pbase;
       const float k0 = x[0] * vv[0];             // shift: the first term (left out, as above)
-      float s1 = 0.0f, s2 = 0.0f;
+      float s1 = fmaf(x[1], vv[1], -k0);
+      float s2 = s1 * s1;
 #pragma unroll
-      for (int i = 1; i < 32; ++i) {
+      for (int i = 2; i < 32; ++i) {
         const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
         s1 += y;
         s2 = fmaf(y, y, s2);
@@ -592,7 +618,8 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * kInvD), floor_unit * vmax);
       const float uinv = __builtin_amdgcn_rcpf(sd);
       if (lead) sm.u[t & 3][t >> 2] = uinv;
-      const float um = max_xor48_nn(row16_max(uinv));
+      // the wave's largest multiplier: at D = 128 each 16-lane row holds all 16 of its tokens
+      const float um = kMfma ? row16_max(uinv) : max_xor48_nn(row16_max(uinv));
       if (lane == 0) sm.red[2 * kQW + wave] = um;
     }
     __syncthreads();
@@ -640,7 +667,7 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
   float mn = flip ? -pmax : pmin, mx = flip ? -pmin : pmax;
   if constexpr (kMfma) {
     mn = min_xor32(min_xor16(mn));
-    mx = max_xor32(max_xor16(mx));
+    mx = max_xor32_raw(max_xor16_raw(mx));
   } else {
     mn = fminf(mn, quad_swap<kDppXor1>(mn));
     mx = fmaxf(mx, quad_swap<kDppXor1>(mx));
