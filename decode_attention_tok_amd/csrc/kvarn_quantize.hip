@@ -39,8 +39,10 @@
 // (the normalisation is scale-free up to the gauge, and the floor is relative to the tile's
 // largest value).
 //
-// Variances use shifted one-pass sums (shift = the thread's first value), merged between the
-// threads sharing a row or column with Chan et al.'s pairwise update.
+// Variances use shifted one-pass sums. A column's sums are shifted by its token 0 in all four of
+// its lanes, so they merge by plain addition; so are a row's at D = 128 (by its channel 0). At
+// D = 64 and 256 a row's threads shift by their own first value and merge with Chan et al.'s
+// pairwise update.
 //
 // Other head dimensions. A token has D / 32 threads (t = tid / (D / 32), lane bits
 // 0 .. log2(D / 32) - 1 = q0, q1, q2): channel c = e + 8 q0 + 16 m + 64 q1 + 128 q2 with q2 at
@@ -530,43 +532,45 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
 #pragma unroll
     for (int i = 0; i < 32; ++i) xb[i] = ((i & 1) ? xco : xce)[4 * i * kXs];
   }
+  // shifts of the variance sums, the same in every lane of a column or row so that the lanes'
+  // sums just add: the column's token 0 and (at D = 128) the token's channel 0
+  const float xc0 = sm.xt[0][cpos(jj)];
+  const float xr0 = kMfma ? sm.xt[t][4 * ((t >> 1) & 3)] : 0.0f;
 
   // ---- alternating normalisation
   const float floor_unit = big * 1.52587890625e-05f;   // 2^-16 * max |rotated|
   constexpr float kInvD = 1.0f / kDim;
   float umax = 1.0f;
   for (int it = 0; it < iters; ++it) {
-    // column step (layout B): std over tokens of xt_tj * u_t. The shift k0 is the first
-    // term itself, whose shifted value (zero, or the rounding residual of its product) is left
-    // out of the sums.
+    // column step (layout B): std over tokens of xt_tj * u_t, from sums shifted by the
+    // column's token 0, added over the four lanes of the column (lane bits 4, 5)
     {
-      float s1, s2, k0;
+      float s1, s2;
       if (it == 0) {
-        k0 = xb[0];
-        s1 = xb[1] - k0;
+        const float k0 = xc0;
+        s1 = xb[0] - k0;
         s2 = s1 * s1;
 #pragma unroll
-        for (int i = 2; i < 32; ++i) {
+        for (int i = 1; i < 32; ++i) {
           const float y = xb[i] - k0;
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       } else {
         const float* uu = sm.u[th];
-        k0 = xb[0] * uu[0];
-        s1 = fmaf(xb[1], uu[1], -k0);
+        const float k0 = xc0 * sm.u[0][0];        // token 0's multiplier is u[0][0]
+        s1 = fmaf(xb[0], uu[0], -k0);
         s2 = s1 * s1;
 #pragma unroll
-        for (int i = 2; i < 32; ++i) {
+        for (int i = 1; i < 32; ++i) {
           const float y = fmaf(xb[i], uu[i], -k0);
           s1 += y;
           s2 = fmaf(y, y, s2);
         }
       }
-      float mh = fmaf(s1, 0.03125f, k0);
-      float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
-      merge_pair<16>(mh, qh, 16.0f);              // token sets th, th ^ 1 (32 tokens each)
-      merge_pair<32>(mh, qh, 32.0f);              // then th ^ 2 (64 each)
+      s1 = add_xor32(add_xor16(s1));
+      s2 = add_xor32(add_xor16(s2));
+      const float qh = fmaxf(fmaf(-s1 * 0.0078125f, s1, s2), 0.0f);   // centred, 128 tokens
       const float sd = fmaxf(__builtin_amdgcn_sqrtf(qh * 0.0078125f), floor_unit * umax);
       if (th == 0) sm.cs[jj] = sd;
       if (it < iters - 1) {                       // the last row step does not change c
@@ -584,22 +588,38 @@ __device__ __forceinline__ void quantize_tile(const __half* __restrict__ src,
     // row step (layout A): std over channels of xt_tj * v_j
     {
       const float* vv = sm.vinv + pbase;
-      const float k0 = x[0] * vv[0];             // shift: the first term (left out, as above)
-      float s1 = fmaf(x[1], vv[1], -k0);
-      float s2 = s1 * s1;
+      float qh;
+      if constexpr (kMfma) {
+        // sums shifted by the token's channel 0 (v of channel 0 at vinv[0]), added over the
+        // token's four lanes (lane bits 4, 5)
+        const float k0 = xr0 * sm.vinv[0];
+        float s1 = fmaf(x[0], vv[0], -k0);
+        float s2 = s1 * s1;
 #pragma unroll
-      for (int i = 2; i < 32; ++i) {
-        const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
-        s1 += y;
-        s2 = fmaf(y, y, s2);
-      }
-      float mh = fmaf(s1, 0.03125f, k0);
-      if (flip) mh = -mh;
-      float qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
-      if constexpr (kMfma) {                     // Chan merges over lane bits 4, then 5
-        merge_pair<16>(mh, qh, 16.0f);
-        merge_pair<32>(mh, qh, 32.0f);
-      } else {                                   // with quad partners (lane bits 0, 1)
+        for (int i = 1; i < 32; ++i) {
+          const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
+          s1 += y;
+          s2 = fmaf(y, y, s2);
+        }
+        s1 = add_xor32(add_xor16(s1));
+        s2 = add_xor32(add_xor16(s2));
+        qh = fmaxf(fmaf(-s1 * kInvD, s1, s2), 0.0f);
+      } else {
+        // per-thread shift (its first term, left out of the sums: its shifted value is the
+        // rounding residual of its product), merged with Chan's update over the token's
+        // threads, whose values may carry the butterflies' factor -1
+        const float k0 = x[0] * vv[0];
+        float s1 = fmaf(x[1], vv[1], -k0);
+        float s2 = s1 * s1;
+#pragma unroll
+        for (int i = 2; i < 32; ++i) {
+          const float y = fmaf(x[i], vv[16 * (i >> 3) + (i & 7)], -k0);
+          s1 += y;
+          s2 = fmaf(y, y, s2);
+        }
+        float mh = fmaf(s1, 0.03125f, k0);
+        if (flip) mh = -mh;
+        qh = fmaxf(fmaf(-s1 * 0.03125f, s1, s2), 0.0f);
         {
           const float d = dpp_sub<kDppXor1>(mh, mh);   // partner - own (only d^2 is used)
           const float qs = dpp_add<kDppXor1>(qh, qh);
