@@ -1764,7 +1764,7 @@ constexpr bool kWideHeads = KVARN_WIDE_HEADS != 0;   // 16-head kernel for > 8 v
 #endif
 // splits whose o~ is loaded before the weights exist (and the chunk of the rest)
 constexpr int kMergePreload = KVARN_MERGE_PRELOAD;
-constexpr int kStageChunk = 16;           // staging value rows loaded per round
+constexpr int kStageChunk = 32;           // staging value rows loaded per round
 
 // <q, k> over kDim channels: k is one fp16 staging row, q the fp32 query in LDS.
 template <int kDim>
@@ -1983,7 +1983,7 @@ decode_merge_kernel(const __half* __restrict__ q, int hq, int hkv, int nq, int m
 #pragma unroll
   for (int i = 0; i < kPer; ++i) r[i] = 0.0f;
   const __half* vcol = sv + kPer * lane;
-  // 16 staging rows per round of loads (rows past n_stage are loaded, always inside the
+  // kStageChunk staging rows per round of loads (rows past n_stage are loaded, always inside the
   // staging tile, but never used: they may hold anything)
   for (int t0 = 0; t0 < n_stage; t0 += kStageChunk) {
     HalfBits<kPer> w[kStageChunk];
