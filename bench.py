@@ -372,11 +372,42 @@ def write_stream_measure(kv, lib, torch, np, dev, steps=None):
     torch.cuda.synchronize()
     ta = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     td = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    # the same steps captured once into a HIP graph and replayed: no launch or event between
+    # the kernels. A replay repeats every write with the same values (the appends rewrite the
+    # same staging slots and completed records), so each replay is the whole stream again.
+    graph_step = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(steps):
+                assert fa(cp, V(kn[i].data_ptr()), V(vn[i].data_ptr()), V(pos[i].data_ptr()),
+                          V(bt.data_ptr()), bt_np.shape[1], V(sk.data_ptr()), V(sv.data_ptr()),
+                          V(pool.data_ptr()), st["num_blocks"], sp.batch, V(cs.cuda_stream)) == 0
+                assert fd(cp, V(q.data_ptr()), sp.hq, V(pool.data_ptr()), st["num_blocks"],
+                          V(bt.data_ptr()), bt_np.shape[1], V(lens[i].data_ptr()),
+                          V(sk.data_ptr()), V(sv.data_ptr()), ctypes.c_float(1.0 / math.sqrt(D)),
+                          V(out.data_ptr()), V(ws.data_ptr()), max(ws_bytes, 256), sp.batch,
+                          V(cs.cuda_stream)) == 0
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_step = e0.elapsed_time(e1) * 1e-3 / (reps * steps)
+        del g
+    except Exception as exc:                     # reported, never fatal for the bench line
+        print(f"# write stream: graph capture failed: {exc}", file=sys.stderr, flush=True)
     burst = np.array([int(lens0[0] + i) % T == T - 1 for i in range(steps)])
     dbytes = sum(algorithmic_bytes(lens0 + i + 1, sp.hkv, sp.hq, True) for i in range(steps))
     tile_heads_burst = sp.batch * sp.hkv
     print(f"# write stream: {steps} steps, append {ta.mean() * 1e6:.1f} us "
-          f"(bursts {ta[burst].mean() * 1e6:.1f} us), decode {td.mean() * 1e6:.1f} us",
+          f"(bursts {ta[burst].mean() * 1e6:.1f} us), decode {td.mean() * 1e6:.1f} us"
+          + (f"; in one HIP graph {graph_step * 1e6:.1f} us per step" if graph_step else ""),
           file=sys.stderr, flush=True)
     return {"workload": "write-stream", "batch": sp.batch, "kv_heads": sp.hkv, "q_heads": sp.hq,
             "start_context": int(lens0[0]), "steps": steps,
@@ -387,6 +418,7 @@ def write_stream_measure(kv, lib, torch, np, dev, steps=None):
             "burst_tile_heads_per_s": (round(tile_heads_burst / ta[burst].mean(), 1)
                                        if burst.any() else None),
             "decode_us_mean": round(td.mean() * 1e6, 2),
+            "graph_step_us": round(graph_step * 1e6, 2) if graph_step else None,
             "decode_gbps": round(dbytes / td.sum() / 1e9, 1),
             "decode_frac_of_peak": round(dbytes / td.sum() / 1e9 / HBM_PEAK_GBPS, 4)}
 
