@@ -1263,8 +1263,8 @@ __device__ __forceinline__ void wide_segment(
   }
 }
 
-// kList: the list schedule (at most 16 virtual heads; grid = the resident workgroups);
-// otherwise the split grid (splits x KV heads x head groups of 16, sequences).
+// kList: the list schedule over (sequence, KV head, head group) units (grid = the resident
+// workgroups); otherwise the split grid (splits x KV heads x head groups of 16, sequences).
 template <bool kCausal, int kVBits, bool kList>
 __global__ void __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_wide_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
@@ -1273,10 +1273,15 @@ decode_wide_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                    const int32_t* __restrict__ seq_lens, int batch, float sm_scale,
                    float* __restrict__ partials, int nslot, SignWords signs, int min_share) {
   __shared__ WideSmem sm;
+  const int vgroup = hq / hkv * nq;
+  const int ngroups = (vgroup + kWideGroup - 1) / kWideGroup;
   if constexpr (kList) {
+    // units are (sequence, KV head, head group of 16): the list runs over hkv * ngroups units
+    // per sequence, unit u = g * ngroups + hg
     const int lane = threadIdx.x & 63;
     const int wgs = gridDim.x, w = blockIdx.x;
-    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hkv, lane);
+    const int hu = hkv * ngroups;
+    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hu, lane);
     const PairSplit split = pair_split(ls.total, wgs, min_share);
     const long long start64 = split.start(w);
     if (start64 >= ls.total) return;
@@ -1284,25 +1289,23 @@ decode_wide_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     const int end = (int)min(split.start(w + 1), (long long)ls.total);
     for (int cur = start; cur < end;) {
       int b, before;
-      locate_position<1>(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+      locate_position<1>(ls, seq_lens, max_blocks, hu, cur, lane, b, before);
       const int len = seq_lens[b];
       const int nt = full_tiles(len, max_blocks);  // > 0: the sequence holds position cur
-      const int g = (cur - before) / nt;
-      const int t0 = (cur - before) - g * nt;
+      const int u = (cur - before) / nt;
+      const int t0 = (cur - before) - u * nt;
       const int seg = min(nt - t0, end - cur);
       const int slot = w - split.wave_of(cur - t0);
       if (cur != start) __syncthreads();           // LDS of the last unit read before this one's
       wide_segment<kCausal, kVBits>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
-                                    max_blocks, len, sm_scale, partials, signs, b, g, 0, t0, seg,
-                                    false, slot, nslot, cur - start, end - start,
-                                    t0 + seg == nt && slot + 1 < nslot);
+                                    max_blocks, len, sm_scale, partials, signs, b, u / ngroups,
+                                    u % ngroups, t0, seg, false, slot, nslot, cur - start,
+                                    end - start, t0 + seg == nt && slot + 1 < nslot);
       cur += seg;
     }
     return;
   }
   const int nsplit = gridDim.x;
-  const int vgroup = hq / hkv * nq;
-  const int ngroups = (vgroup + kWideGroup - 1) / kWideGroup;
   int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
   if (ngroups > 1) {
     // workgroups that read the same tiles (same split, KV head, sequence; different head
@@ -2474,8 +2477,11 @@ DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, in
     return DecodeKind::kPairList;
   const long long tiles = (long long)batch * hkv * max_blocks;
   const bool large = tiles >= kPairMinTilesPerCU * device_compute_units() && tiles < (1LL << 31);
-  if (head_dim == 128 && virtual_heads > kHeadGroup && kWideHeads)
-    return virtual_heads <= kWideGroup && large ? DecodeKind::kWideList : DecodeKind::kWideGrid;
+  if (head_dim == 128 && virtual_heads > kHeadGroup && kWideHeads) {
+    // the list runs over (sequence, KV head, head group of 16) units
+    const long long groups = (virtual_heads + kWideGroup - 1) / kWideGroup;
+    return large && tiles * groups < (1LL << 31) ? DecodeKind::kWideList : DecodeKind::kWideGrid;
+  }
   if (virtual_heads <= kHeadGroup && large) return DecodeKind::kTileList;
   return DecodeKind::kTileGrid;
 }

@@ -113,14 +113,14 @@ def test_workspace_follows_the_split_plan(lib):
     no GPU: the plan assumes 256 compute units.
     List schedules, for tables of at least 64 entries x KV heads x sequences per compute unit:
     the sequences' full tiles (four-wave tile kernel, at most 8 virtual heads per KV head; at
-    head dimension 128 the 16-head kernel for 9 to 16) or tile pairs (paired-tile kernel: at
-    most four virtual heads, 2-bit values, head dimension 128) form one list that the resident
-    workers share evenly, at least m positions each: tiles,
+    head dimension 128 the 16-head kernel for more, one list unit per head group of 16) or
+    tile pairs (paired-tile kernel: at most four virtual heads, 2-bit values, head dimension
+    128) form one list that the resident workers share evenly, at least m positions each: tiles,
     m = max(4, (entries - 1) // 62 + 1); pairs, m = (p - 1) // 62 + 1 for p = ceil(entries / 2).
     A (sequence, KV head) of up to n positions (entries or p) then meets at most
     (n - 1) // m + 2 workers, each writing its own partial slot.
-    Split grid (more head groups than one — of 16 at head dimension 128, else of 8 — or a
-    smaller table; also the fp16
+    Split grid (more head groups than one of 8 at head dimensions 64 and 256, or a smaller
+    table; also the fp16
     comparison decode, whose need the size always covers): two workgroups per compute unit, at
     least two tiles per wave
     unless that leaves fewer than two workgroups per compute unit (then one), at most 32 full
@@ -131,10 +131,10 @@ def test_workspace_follows_the_split_plan(lib):
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 64, 129) == 16 * 64 * 34 * per
     # the same with group 16: the 16-head kernel on the tile list, 34 slots
     assert kv.decode_workspace_bytes(kv.default_config(8), 16, 128, 129) == 16 * 128 * 34 * per
-    # group 16 x 2 query tokens (two groups of 16): the 16-head kernel on the split grid, 4
-    # splits, for 2 x the rows
+    # group 16 x 2 query tokens (two groups of 16): the 16-head kernel on the tile list, one
+    # unit per head group, 34 slots for 2 x the rows
     assert (kv.decode_multi_workspace_bytes(kv.default_config(8), 16, 128, 2, 129)
-            == 16 * 2 * 128 * 4 * per)
+            == 16 * 2 * 128 * 34 * per)
     # 4K context, batch 8 (33 entries; 2,112 < 16,384): split grid, 8 splits wanted; two tiles
     # per wave would allow 4, or 256 workgroups, so one tile per wave is allowed: 8
     assert kv.decode_workspace_bytes(kv.default_config(8), 8, 32, 33) == 8 * 32 * 8 * per
@@ -157,8 +157,9 @@ def test_multi_workspace_and_query_token_limits(lib):
     cfg = kv.default_config(8)
     one = kv.decode_workspace_bytes(cfg, 16, 64, 128)
     assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 1, 128) == one
-    # four query tokens x group 8 = 32 virtual heads: the split grid (4 splits) for 4x the rows
-    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 4, 128) == 16 * 4 * 64 * 4 * 130 * 4
+    # four query tokens x group 8 = 32 virtual heads: two head groups of 16 on the tile list
+    # (16,384 entries), m = 4, 127 // 4 + 2 = 33 slots for 4x the rows
+    assert kv.decode_multi_workspace_bytes(cfg, 16, 64, 4, 128) == 16 * 4 * 64 * 33 * 130 * 4
     assert kv.decode_multi_workspace_bytes(cfg, 16, 64, kv.MAX_QUERY_TOKENS, 128) > 0
     for bad in (0, -1, kv.MAX_QUERY_TOKENS + 1):
         with pytest.raises(RuntimeError):

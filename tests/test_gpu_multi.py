@@ -192,3 +192,24 @@ def test_multi_tile_list_matches_oracle(name, over, tails, nq, v_bits):
     _say(f"multi tile list {name} {over} tails={tails} nq={nq} v_bits={v_bits}: "
          f"max abs err {err:.3g}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("name,over,tails,nq", [
+    ("qwen3-32b-16k", dict(batch=2, ctx=640, hkv=2, hq=16), [3, 0], 4),     # 32 rows: 2 groups
+    ("qwen3-4b", dict(batch=2, ctx=768, hkv=2, hq=24), [90, 1], 2),         # 24 rows: 16 + 8
+    ("qwen3-4b", dict(batch=3, ctx=512, hkv=1, hq=16), [0, 17, 127], 3),    # 48 rows: 3 groups
+])
+def test_multi_wide_list_head_groups_matches_oracle(name, over, tails, nq):
+    """More than 16 virtual heads per KV head on a wide block table: the 16-head kernel's list
+    schedule with one list unit per (sequence, KV head, head group of 16), causal masks
+    included."""
+    from test_gpu_parity import widen
+    sp = gen.spec(name, **over)
+    pool, bt, lens, sk, sv, _, sm = _decode_case(sp, tails)
+    q = gen.query_tokens(sp, nq)
+    cfg = kv.default_config(sp.hkv)
+    got = gpu_multi(cfg, q, pool, widen(bt, sp.hkv), lens, sk, sv, sm)
+    ref = oatt.decode_attention_multi(q, pool, bt, lens, sk, sv, sm)
+    err = np.abs(got - ref).max()
+    _say(f"multi wide list {name} {over} tails={tails} nq={nq}: max abs err {err:.3g}")
+    assert err <= TOL
