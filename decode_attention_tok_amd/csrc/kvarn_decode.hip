@@ -902,12 +902,18 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
                     const int32_t* __restrict__ seq_lens, int batch, float sm_scale,
                     float* __restrict__ partials, int nslot, SignWords signs, int min_share) {
   __shared__ TileSmem<kDim> sm;
+  // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
+  // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
+  const int group = hq / hkv, vgroup = group * nq;
+  const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
   if constexpr (kList) {
-    // one head group: the full tiles of every (sequence, KV head) form one list that the
-    // workgroups share evenly, as in the paired-tile schedule (with tiles for positions)
+    // the full tiles of every (sequence, KV head, head group of 8) form one list that the
+    // workgroups share evenly, as in the paired-tile schedule (with tiles for positions);
+    // unit u = g * ngroups + hg
     const int lane = threadIdx.x & 63;
     const int wgs = gridDim.x, w = blockIdx.x;
-    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hkv, lane);
+    const int hu = hkv * ngroups;
+    const ListScan ls = scan_list<1>(seq_lens, batch, max_blocks, hu, lane);
     const PairSplit split = pair_split(ls.total, wgs, min_share);
     const long long start64 = split.start(w);
     if (start64 >= ls.total) return;
@@ -915,27 +921,24 @@ decode_tiles_kernel(const __half* __restrict__ q, int hq, int hkv, int nq,
     const int end = (int)min(split.start(w + 1), (long long)ls.total);
     for (int cur = start; cur < end;) {
       int b, before;
-      locate_position<1>(ls, seq_lens, max_blocks, hkv, cur, lane, b, before);
+      locate_position<1>(ls, seq_lens, max_blocks, hu, cur, lane, b, before);
       const int len = seq_lens[b];
       const int nt = full_tiles(len, max_blocks);  // > 0: the sequence holds position cur
-      const int g = (cur - before) / nt;
-      const int t0 = (cur - before) - g * nt;
+      const int u = (cur - before) / nt;
+      const int t0 = (cur - before) - u * nt;
       const int seg = min(nt - t0, end - cur);
       const int slot = w - split.wave_of(cur - t0);
       if (cur != start) __syncthreads();           // LDS of the last unit read before this one's
       tile_segment<kCausal, kVBits, kDim>(sm, q, hq, hkv, nq, pool, num_blocks, block_table,
-                                          max_blocks, len, sm_scale, partials, signs, b, g, 0,
-                                          t0, seg, false, slot, nslot, cur - start,
-                                          end - start, t0 + seg == nt && slot + 1 < nslot);
+                                          max_blocks, len, sm_scale, partials, signs, b,
+                                          u / ngroups, u % ngroups, t0, seg, false, slot, nslot,
+                                          cur - start, end - start,
+                                          t0 + seg == nt && slot + 1 < nslot);
       cur += seg;
     }
     return;
   }
   const int nsplit = gridDim.x;
-  // query rows: (query token i, head h) pairs of KV head g, virtual head v = i * group + l for
-  // head h = g * group + l; a workgroup serves virtual heads vbase .. vbase + nh - 1
-  const int group = hq / hkv, vgroup = group * nq;
-  const int ngroups = (vgroup + kHeadGroup - 1) / kHeadGroup;
   int split = blockIdx.x, g = blockIdx.y / ngroups, hg = blockIdx.y % ngroups, b = blockIdx.z;
   if (ngroups > 1) {
     // workgroups that read the same tiles (same split, KV head, sequence; different head
@@ -2482,7 +2485,9 @@ DecodeKind decode_kind(int batch, int hkv, int max_blocks, int virtual_heads, in
     const long long groups = (virtual_heads + kWideGroup - 1) / kWideGroup;
     return large && tiles * groups < (1LL << 31) ? DecodeKind::kWideList : DecodeKind::kWideGrid;
   }
-  if (virtual_heads <= kHeadGroup && large) return DecodeKind::kTileList;
+  // the list runs over (sequence, KV head, head group of 8) units
+  const long long groups = (virtual_heads + kHeadGroup - 1) / kHeadGroup;
+  if (large && tiles * groups < (1LL << 31)) return DecodeKind::kTileList;
   return DecodeKind::kTileGrid;
 }
 

@@ -119,8 +119,8 @@ def test_workspace_follows_the_split_plan(lib):
     m = max(4, (entries - 1) // 62 + 1); pairs, m = (p - 1) // 62 + 1 for p = ceil(entries / 2).
     A (sequence, KV head) of up to n positions (entries or p) then meets at most
     (n - 1) // m + 2 workers, each writing its own partial slot.
-    Split grid (more head groups than one of 8 at head dimensions 64 and 256, or a smaller
-    table; also the fp16
+    (At head dimensions 64 and 256 the tile kernel's list likewise makes one unit per head
+    group of 8.) Split grid (a smaller table; also the fp16
     comparison decode, whose need the size always covers): two workgroups per compute unit, at
     least two tiles per wave
     unless that leaves fewer than two workgroups per compute unit (then one), at most 32 full

@@ -298,6 +298,33 @@ def test_multi_token_decode(d, vb, nq):
     assert np.abs(out.cpu().numpy() - ref).max() <= TOL
 
 
+@pytest.mark.parametrize("d,vb", [(64, 2), (256, 4)])
+@pytest.mark.parametrize("nq", [2, 5])
+def test_multi_token_decode_tile_list(d, vb, nq):
+    """The same several-token decodes on a wide block table: the tile kernel's list schedule,
+    one unit per (sequence, KV head, head group of 8), so more than 8 virtual heads per KV head
+    make several units."""
+    from test_gpu_parity import widen
+    _say(f"multi tile list d={d} vb={vb} nq={nq}")
+    sp = _spec(d, batch=2, ctx=384, hq=8)
+    st = gen.prefill(sp, max_new_tokens=T)
+    pool = oracle_pool(st, sp.hkv, d, vb)
+    sk, sv = staging(sp, [2, 90])
+    lens = st["seq_lens"] + np.array([2, 90], np.int32)
+    q = gen.query_tokens(sp, nq, dense=True)
+    sm = 1 / math.sqrt(d)
+    cfg = kv.default_config(sp.hkv, v_bits=vb, head_dim=d)
+    bt = widen(st["block_table"], sp.hkv)
+    ws = torch.empty(max(kv.decode_multi_workspace_bytes(cfg, 2, 8, nq, bt.shape[1]), 256),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((2, nq, 8, d), -7.0, dtype=torch.float32, device="cuda")
+    kv.decode_attention_multi(cfg, dev(q), dev(pool), dev(bt), dev(lens), dev(sk), dev(sv), sm,
+                              out, ws)
+    torch.cuda.synchronize()
+    ref = oatt.decode_attention_multi(q, pool, st["block_table"], lens, sk, sv, sm)
+    assert np.abs(out.cpu().numpy() - ref).max() <= TOL
+
+
 # ------------------------------------------------------------------ dequantisation
 
 
