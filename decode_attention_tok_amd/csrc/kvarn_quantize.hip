@@ -71,8 +71,11 @@ struct QGeom {
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kTPT = kDim / 32;                    // threads per token (layout A)
   // LDS row stride of the rotated tile: the row plus the cpos padding, rounded so that the
-  // four token rows th = 0..3 read by one layout-B instruction start 16 banks apart
-  static constexpr int kXs = kDim == 64 ? 80 : (kDim == 128 ? 144 : 272);
+  // four token rows th = 0..3 read by one layout-B instruction start 16 banks apart — except at
+  // D = 64, where the unrounded 68 keeps the workgroup under 40 KB of LDS, so four fit on a
+  // compute unit instead of three (the layout-B reads happen once per tile, so their bank
+  // conflicts cost less than the lost occupancy)
+  static constexpr int kXs = kDim == 64 ? 68 : (kDim == 128 ? 144 : 272);
   static constexpr int kCp = kDim + 4 * (kDim / 64);        // padded per-channel array length
   static constexpr float kInvSqrt = kDim == 64 ? 0.125f
                                   : (kDim == 128 ? 0.08838834764831845f : 0.0625f);
