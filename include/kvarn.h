@@ -29,9 +29,9 @@
  *   - Every call only enqueues kernel launches (no allocation, no memset, no copy, no host
  *     synchronisation), so a sequence of calls on `stream` may be captured into a HIP graph
  *     and replayed; a replay computes what the captured calls compute on the buffers' contents
- *     at replay time. Only the per-device occupancy and compute-unit queries behind the
- *     decode's work split run on the host the first time a device is seen; make one call
- *     before capturing.
+ *     at replay time. The decode's work split queries the device's compute-unit count and
+ *     each kernel's occupancy on the host the first time they are needed, and caches them;
+ *     make the same calls once before capturing, so that no query falls inside the capture.
  *   - Device-side preconditions that the host cannot see (block ids, positions, lengths) are
  *     bounds-checked in the kernels: an out-of-range block id or length never causes an
  *     out-of-bounds access; see each entry point for the result it then produces.
