@@ -4,7 +4,8 @@ launches on the caller's stream (no allocation, no memset, no host synchronisati
 replay of a captured step gives bitwise the eager results. Each replay is checked, with eager
 work and synchronisations between the replays. The cases cover the split-grid decode of a small
 table, the paired-tile list schedule of a large one (its end marks live in the workspace), the
-4-bit value preset, head dimension 256, and the several-token decode on the 16-head list."""
+4-bit value preset, head dimension 256, the several-token decode on the 16-head list, and the
+allocation-free decode (its static scratch in place of the workspace) on both schedules."""
 
 import math
 
@@ -42,14 +43,16 @@ def _state(name, v_bits, **over):
     return sp, st, cfg, pool
 
 
-@pytest.mark.parametrize("name,over,steps,v_bits,nq", [
-    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), 3, 2, 1),           # split grid
-    ("qwen3-32b-16k", dict(batch=16, ctx=8192, hkv=16, hq=64), 2, 2, 1),   # paired-tile list
-    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), 2, 4, 1),           # 4-bit values
-    ("qwen3-4b", dict(batch=2, ctx=640, hkv=2, hq=8, head_dim=256), 2, 2, 1),
-    ("qwen3-32b-16k", dict(batch=16, ctx=8192, hkv=8, hq=64), 2, 2, 4),    # 32 virtual heads
+@pytest.mark.parametrize("name,over,steps,v_bits,nq,noalloc", [
+    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), 3, 2, 1, False),          # split grid
+    ("qwen3-32b-16k", dict(batch=16, ctx=8192, hkv=16, hq=64), 2, 2, 1, False),  # paired list
+    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), 2, 4, 1, False),          # 4-bit values
+    ("qwen3-4b", dict(batch=2, ctx=640, hkv=2, hq=8, head_dim=256), 2, 2, 1, False),
+    ("qwen3-32b-16k", dict(batch=16, ctx=8192, hkv=8, hq=64), 2, 2, 4, False),   # 32 heads
+    ("qwen3-4b", dict(batch=3, ctx=1024, hkv=2, hq=8), 2, 2, 1, True),           # static scratch
+    ("qwen3-32b-16k", dict(batch=16, ctx=8192, hkv=8, hq=32), 2, 2, 1, True),
 ])
-def test_captured_steps_replay_bitwise(name, over, steps, v_bits, nq):
+def test_captured_steps_replay_bitwise(name, over, steps, v_bits, nq, noalloc):
     sp, st, cfg, pool = _state(name, v_bits, **over)
     b, hq, D = sp.batch, sp.hq, sp.head_dim
     bt = dev(st["block_table"])
@@ -74,7 +77,9 @@ def test_captured_steps_replay_bitwise(name, over, steps, v_bits, nq):
     pool0, sk0, sv0 = pool.clone(), sk.clone(), sv.clone()
 
     def decode(lens_i, scale, out):
-        if nq == 1:
+        if noalloc:
+            kv.decode_attention_noalloc(cfg, q, pool, bt, lens_i, sk, sv, scale, out)
+        elif nq == 1:
             kv.decode_attention(cfg, q, pool, bt, lens_i, sk, sv, scale, out, ws)
         else:
             kv.decode_attention_multi(cfg, q, pool, bt, lens_i, sk, sv, scale, out, ws)
